@@ -1,0 +1,351 @@
+"""FP64 CPU oracle for the routed int4 Mixture-of-Experts layer.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
+execute this module: only the tests, the smoke check of the graft entry point
+and the CPU-baseline leg of the benchmark use it. It shares no code with the
+HIP library and imports nothing from it.
+
+What it computes follows the routing contract of TensorFold issue #931,
+"Qwen3.6-35B-A3B (qwen3_5_moe) on the native Metal engine: proposal and gate",
+section "What I'd build":
+  * fp32 logits over the routed experts and the shared expert's gate;
+  * top-k by logit, ties going to the lower expert id;
+  * pick weights exp(l - l_top) over the k picks (normalised over the picks),
+    rounded to bf16;
+  * the shared expert is one more slot, weighted bf16(sigmoid(bf16(gate)));
+  * the weighted sum is rounded once to bf16.
+Same section: experts are affine 4-bit in groups of 64, routers 8-bit. Section
+"What it is": the routed experts replace the dense MLP (256 experts, 8 picked,
+one shared expert). Section "Gate": an FP64 reference per projection class
+(router logits, expert gate/up, expert down, combine) on prompt and decode rows;
+every stage below is callable on its own so a check can feed it another
+implementation's previous-stage output.
+
+Arithmetic: every value is carried in float64; the only roundings are the ones
+the contract (or a stated reading) fixes: logits to fp32, pick weights, the
+shared weight and its gate to bf16, the SwiGLU intermediate to bf16 (reading),
+the combined output to bf16, and (layer stack) the RMSNorm output and the
+residual sum to bf16 (reading). Library primitives used as steps: numpy matmul
+in float64, numpy.exp, a stable lexicographic sort.
+
+Readings where the pages are silent are listed in the design notes; the ones
+that shape this file are repeated at the function that takes them.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 64
+
+
+# ---------------------------------------------------------------- number formats
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64 values (exact)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def round_bf16(v) -> np.ndarray:
+    """Round float64 values to bf16 with round-to-nearest-even; return bit patterns.
+
+    One rounding, straight from the float64 value (no fp32 step, so no double
+    rounding). bf16 has 8 significant bits; normal values have exponents
+    -126..127, subnormals are multiples of 2^-133. Values at or beyond
+    (2 - 2^-8) * 2^127 become infinity; NaN becomes 0x7FC0.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    with np.errstate(over="ignore", invalid="ignore"):
+        _, e = np.frexp(a)  # a = m * 2^e, m in [0.5, 1)
+        qexp = np.maximum(e - 8, -133)  # quantum of the bf16 binade holding a
+        big = a >= 2.0 ** 128
+        n = np.rint(np.ldexp(np.where(big | ~np.isfinite(a), 0.0, a), -qexp))  # half-to-even
+        r = np.ldexp(n, qexp)  # exactly a bf16 value, hence exactly an fp32 value
+        bits = (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    bits = np.where(big | np.isinf(a), np.uint16(0x7F80), bits)
+    bits = np.where(np.signbit(v), bits | np.uint16(0x8000), bits)
+    bits = np.where(np.isnan(v), np.uint16(0x7FC0), bits)
+    return bits.astype(np.uint16)
+
+
+def round_f32(v) -> np.ndarray:
+    """float64 -> fp32 with IEEE round-to-nearest-even (numpy's cast)."""
+    return np.asarray(v, dtype=np.float64).astype(np.float32)
+
+
+# ---------------------------------------------------------------- dequantisation
+
+def dequant_int4(q_packed, scale_bits, bias_bits) -> np.ndarray:
+    """Affine 4-bit groups of 64: w = scale * q + bias, exact in float64.
+
+    Storage (TensorFold #931, "What I'd build": MLX affine 4-bit, groups of 64):
+    q_packed [..., rows, cols/2] uint8 with element 2j in the low nibble of
+    byte j and element 2j+1 in the high nibble; scale and bias are bf16
+    [..., rows, cols/64]; group g covers columns 64g..64g+63 of its row.
+    """
+    q_packed = np.asarray(q_packed, dtype=np.uint8)
+    lo = (q_packed & 0x0F).astype(np.float64)
+    hi = (q_packed >> 4).astype(np.float64)
+    q = np.stack([lo, hi], axis=-1).reshape(*q_packed.shape[:-1], q_packed.shape[-1] * 2)
+    s = np.repeat(bf16_to_f64(scale_bits), GROUP, axis=-1)
+    b = np.repeat(bf16_to_f64(bias_bits), GROUP, axis=-1)
+    return s * q + b
+
+
+def dequant_int8(q, scale_bits, bias_bits) -> np.ndarray:
+    """Affine 8-bit groups of 64 (the router format): w = scale * q + bias."""
+    q = np.asarray(q, dtype=np.uint8).astype(np.float64)
+    s = np.repeat(bf16_to_f64(scale_bits), GROUP, axis=-1)
+    b = np.repeat(bf16_to_f64(bias_bits), GROUP, axis=-1)
+    return s * q + b
+
+
+def router_matrix(layer) -> np.ndarray:
+    """Router [E(+1), H] in float64: fp32 rows, or dequantised 8-bit affine rows."""
+    if getattr(layer, "router_f32", None) is not None:
+        return np.asarray(layer.router_f32, dtype=np.float32).astype(np.float64)
+    return dequant_int8(layer.router_q, layer.router_s, layer.router_b)
+
+
+# ---------------------------------------------------------------- a1: router logits
+
+def router_logits(x_bits, W, logit_bias=None, n_experts=None) -> np.ndarray:
+    """fp32 logits [T, R] = round_fp32(sum_h x[t,h] * W[r,h] (+ bias[r] for r < E)).
+
+    Contract: fp32 logits over the experts and the shared expert's gate. The
+    products of bf16 activations and dequantised weights are exact in float64;
+    the sum is accumulated in float64 and rounded to fp32 once. The optional
+    per-expert logit bias is part of the routed logits only (reading: the shared
+    gate is a plain N=1 projection with no bias).
+    """
+    x = bf16_to_f64(x_bits)
+    acc = x @ np.asarray(W, dtype=np.float64).T
+    if logit_bias is not None:
+        E = len(logit_bias) if n_experts is None else n_experts
+        acc[:, :E] = acc[:, :E] + np.asarray(logit_bias, dtype=np.float32).astype(np.float64)
+    return round_f32(acc)
+
+
+# ---------------------------------------------------------------- a2: top-k, weights, shared weight
+
+def topk(logits_routed, k: int) -> np.ndarray:
+    """Ids [T, k] of the k largest logits, largest first, ties to the lower id.
+
+    Contract: top-k by logit with ties going to the lower id. IEEE comparison,
+    so -0 and +0 tie. NaN logits rank below every number (reading: never picked
+    while k non-NaN logits exist).
+    """
+    l = np.asarray(logits_routed, dtype=np.float32).astype(np.float64)
+    T, E = l.shape
+    ids = np.broadcast_to(np.arange(E), (T, E))
+    nan = np.isnan(l)
+    neg = np.where(nan, 0.0, -l)
+    out = np.empty((T, k), dtype=np.int32)
+    for t in range(T):
+        order = np.lexsort((ids[t], neg[t], nan[t]))  # last key is primary
+        out[t] = order[:k]
+    return out
+
+
+def pick_weights(logits_routed, ids) -> np.ndarray:
+    """bf16 weights [T, k]: w_i = exp(l_i - l_top) / sum_j exp(l_j - l_top) over the k picks.
+
+    Contract: weights exp(l - l_top) over the k picks, rounded to bf16. Reading:
+    normalised over the picks (a softmax over the k picked logits), evaluated in
+    float64 from the fp32 logits and rounded once to bf16, with no renormalisation
+    after rounding. The sum runs over the picks in slot order.
+    """
+    l = np.asarray(logits_routed, dtype=np.float32)
+    T, k = ids.shape
+    out = np.empty((T, k), dtype=np.uint16)
+    for t in range(T):
+        lt = l[t, ids[t]].astype(np.float64)
+        e = np.exp(lt - lt[0])
+        s = 0.0
+        for j in range(k):
+            s += e[j]
+        out[t] = round_bf16(e / s)
+    return out
+
+
+def sigmoid64(v) -> np.ndarray:
+    """1 / (1 + exp(-v)) in float64."""
+    v = np.asarray(v, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-v))
+
+
+def shared_weight(gate_logit) -> np.ndarray:
+    """bf16(sigmoid(bf16(gate))): the shared expert's slot weight [T].
+
+    Contract: the shared expert is one more slot weighted bf16(sigmoid(bf16(gate))).
+    The fp32 gate logit is rounded to bf16, the sigmoid is taken in float64 and
+    rounded to bf16.
+    """
+    with np.errstate(invalid="ignore"):  # signalling-NaN patterns widen with the invalid flag
+        g64 = np.asarray(gate_logit, dtype=np.float32).astype(np.float64)
+    g = bf16_to_f64(round_bf16(g64))
+    return round_bf16(sigmoid64(g))
+
+
+# ---------------------------------------------------------------- a3: dispatch
+
+def dispatch(ids, n_experts: int, has_shared: bool):
+    """Histogram and expert-sorted order of the picks.
+
+    Returns (counts [E(+1)] int32, offsets [E(+1)+1] int32, order [T*S] int32):
+    counts[e] = #{(t, s): ids[t, s] = e}; the shared expert (index E) takes every
+    token once. offsets is the exclusive prefix sum. order lists the pick
+    indices p = t*S + s grouped by expert (ascending e), and within an expert by
+    ascending p. S = k (+1 with the shared slot, whose s is k).
+    """
+    ids = np.asarray(ids, dtype=np.int64)
+    T, k = ids.shape
+    S = k + (1 if has_shared else 0)
+    nE = n_experts + (1 if has_shared else 0)
+    e_of = np.full((T, S), -1, dtype=np.int64)
+    e_of[:, :k] = ids
+    if has_shared:
+        e_of[:, k] = n_experts
+    flat = e_of.reshape(-1)
+    counts = np.bincount(flat, minlength=nE).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    order = np.argsort(flat, kind="stable").astype(np.int32)
+    return counts, offsets, order
+
+
+# ---------------------------------------------------------------- a4/a5: experts
+
+def silu64(z) -> np.ndarray:
+    """silu(z) = z / (1 + exp(-z)) in float64."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def expert_ffn(x64, q_gate, s_gate, b_gate, q_up, s_up, b_up, q_down, s_down, b_down):
+    """One expert on rows x64 [n, H]: returns (h bf16 bits [n, I], y float64 [n, H]).
+
+    gate/up pair then down (TensorFold #931, "Gate": "the expert gate/up pair,
+    expert down"); SwiGLU: h = silu(x Wg^T) * (x Wu^T). Reading: h is rounded to
+    bf16 (the model's activation type) before the down projection; y is kept in
+    float64 because the contract rounds only the weighted sum.
+    """
+    Wg = dequant_int4(q_gate, s_gate, b_gate)
+    Wu = dequant_int4(q_up, s_up, b_up)
+    Wd = dequant_int4(q_down, s_down, b_down)
+    g = x64 @ Wg.T
+    u = x64 @ Wu.T
+    h = round_bf16(silu64(g) * u)
+    y = bf16_to_f64(h) @ Wd.T
+    return h, y
+
+
+def expert_outputs(x_bits, ids, layer, n_experts: int, has_shared: bool):
+    """Per-slot expert outputs y [T, S, H] (float64) and h [T, S, I] (bf16 bits).
+
+    Slot s < k holds expert ids[t, s]; slot k (when present) the shared expert,
+    stored as expert index E.
+    """
+    x = bf16_to_f64(x_bits)
+    ids = np.asarray(ids)
+    T, k = ids.shape
+    S = k + (1 if has_shared else 0)
+    H = x.shape[1]
+    I = layer.q_gate.shape[1]
+    y = np.zeros((T, S, H), dtype=np.float64)
+    h = np.zeros((T, S, I), dtype=np.uint16)
+    experts = sorted(set(int(e) for e in ids.reshape(-1)))
+    if has_shared:
+        experts.append(n_experts)
+    for e in experts:
+        if e == n_experts and has_shared:
+            rows_t = np.arange(T)
+            rows_s = np.full(T, k)
+        else:
+            rows_t, rows_s = np.nonzero(ids == e)
+        he, ye = expert_ffn(x[rows_t], layer.q_gate[e], layer.s_gate[e], layer.b_gate[e],
+                            layer.q_up[e], layer.s_up[e], layer.b_up[e],
+                            layer.q_down[e], layer.s_down[e], layer.b_down[e])
+        y[rows_t, rows_s] = ye
+        h[rows_t, rows_s] = he
+    return y, h
+
+
+# ---------------------------------------------------------------- a6: combine
+
+def combine(y, w_bits, wsh_bits=None) -> np.ndarray:
+    """out[t] = bf16( sum_{s<k} w[t,s] * y[t,s] + wsh[t] * y[t,k] ), one rounding.
+
+    Contract: the shared expert is one more slot; the weighted sum is rounded once
+    to bf16. The bf16 weights enter as exact values; the sum is float64.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    w = bf16_to_f64(w_bits)
+    k = w.shape[1]
+    acc = np.zeros((y.shape[0], y.shape[2]), dtype=np.float64)
+    for s in range(k):
+        acc += w[:, s:s + 1] * y[:, s]
+    if wsh_bits is not None:
+        acc += bf16_to_f64(wsh_bits)[:, None] * y[:, k]
+    return round_bf16(acc)
+
+
+# ---------------------------------------------------------------- a7: stack glue (reading)
+
+def rmsnorm_bf16(x_bits, eps: float = 1e-6) -> np.ndarray:
+    """Unit-weight RMSNorm: bf16( x / sqrt(mean(x^2) + eps) ) per row, float64 math.
+
+    Reading for the layer stack (the pages give no norm for an MoE-only stack):
+    a pre-norm residual block, x <- bf16(x + MoE(bf16(RMSNorm(x)))).
+    """
+    x = bf16_to_f64(x_bits)
+    ms = np.mean(x * x, axis=1, keepdims=True)
+    return round_bf16(x / np.sqrt(ms + eps))
+
+
+def residual_bf16(x_bits, out_bits) -> np.ndarray:
+    """bf16(x + out): the residual add between stacked layers."""
+    return round_bf16(bf16_to_f64(x_bits) + bf16_to_f64(out_bits))
+
+
+# ---------------------------------------------------------------- whole layer
+
+def layer_forward(x_bits, layer, top_k: int, has_shared: bool = True):
+    """Route -> experts -> combine for one layer; returns every stage's output."""
+    W = router_matrix(layer)
+    E = W.shape[0] - (1 if has_shared else 0)
+    logits = router_logits(x_bits, W, getattr(layer, "logit_bias", None), E)
+    ids = topk(logits[:, :E], top_k)
+    w = pick_weights(logits[:, :E], ids)
+    wsh = shared_weight(logits[:, E]) if has_shared else None
+    y, h = expert_outputs(x_bits, ids, layer, E, has_shared)
+    out = combine(y, w, wsh)
+    return {"logits": logits, "ids": ids, "w": w, "wsh": wsh, "h": h, "y": y, "out": out}
+
+
+def stack_forward(x_bits, layers, top_k: int, has_shared: bool = True, eps: float = 1e-6):
+    """x_{l+1} = bf16(x_l + MoE_l(bf16(RMSNorm(x_l)))) over the given layers."""
+    xs = [np.asarray(x_bits, dtype=np.uint16)]
+    for L in layers:
+        xn = rmsnorm_bf16(xs[-1], eps)
+        st = layer_forward(xn, L, top_k, has_shared)
+        xs.append(residual_bf16(xs[-1], st["out"]))
+    return xs
+
+
+def bf16_ulp(v) -> np.ndarray:
+    """Spacing of bf16 values at |v| (float64), 2^-133 below the normal range."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    _, e = np.frexp(a)
+    return np.ldexp(1.0, np.maximum(e - 8, -133))
+
+
+def near_tie_tokens(logits_routed, k: int, gap: float = 1e-5) -> np.ndarray:
+    """Tokens whose top k+1 logits hold an adjacent gap below `gap` (boolean [T])."""
+    l = np.sort(np.asarray(logits_routed, dtype=np.float64), axis=1)[:, ::-1]
+    m = min(k + 1, l.shape[1])
+    d = l[:, :m - 1] - l[:, 1:m]
+    return (d < gap).any(axis=1)

@@ -1,0 +1,448 @@
+"""Pins of the FP64 oracle against facts fixed outside it.
+
+Each test checks the oracle against something it cannot agree with by
+construction: brute-force enumeration of the routing rule, closed forms,
+exact rational / 60-digit decimal evaluation of the contract's formulas,
+hand-derived fixtures under tests/golden/, library routines on special cases,
+and invariants. The contract is the one of TensorFold issue #931 ("What I'd
+build"); the staged-reference method is from the same page's "Gate" section.
+"""
+
+import itertools
+import json
+import os
+import struct
+from fractions import Fraction
+from types import SimpleNamespace
+
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+from tests import _exact as X
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def f32_bits(v):
+    return struct.unpack("<I", struct.pack("<f", v))[0]
+
+
+# ------------------------------------------------------------------ number formats
+
+def test_round_bf16_matches_torch_cast_on_fp32_inputs():
+    """For fp32-representable inputs one RNE rounding equals torch's fp32->bf16 cast."""
+    import torch
+
+    rng = np.random.default_rng(123)
+    bits = rng.integers(0, 2 ** 32, size=200_000, dtype=np.uint64).astype(np.uint32)
+    extra = np.array([0, 0x80000000, 0x00000001, 0x007FFFFF, 0x00800000, 0x7F7FFFFF, 0xFF7FFFFF,
+                      0x7F800000, 0xFF800000, 0x3F808000, 0x3F818000, 0x3F80FFFF, 0x00008000,
+                      0x00018000, 0x7F7F8000], dtype=np.uint32)
+    bits = np.concatenate([bits, extra])
+    v = bits.view(np.float32)
+    v = v[~np.isnan(v)]
+    want = torch.from_numpy(v.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = O.round_bf16(v.astype(np.float64))
+    assert np.array_equal(got, want)
+
+
+def test_round_bf16_exact_on_fp64_midpoints():
+    """float64 inputs next to bf16 midpoints (where an fp32 step would double-round)."""
+    rng = np.random.default_rng(7)
+    vals = []
+    for _ in range(3000):
+        e = int(rng.integers(-140, 127))
+        m = int(rng.integers(128, 256))
+        base = Fraction(m) * Fraction(2) ** (e - 7)
+        half = Fraction(2) ** (e - 8)
+        mid = base + half
+        for d in (mid, mid * (1 + Fraction(1, 2 ** 40)), mid * (1 - Fraction(1, 2 ** 40))):
+            f = float(d)
+            if f != 0.0 and np.isfinite(f):
+                vals.append(f if rng.integers(0, 2) else -f)
+    vals = np.array(vals, dtype=np.float64)
+    got = O.round_bf16(vals)
+    want = np.array([X.rne_bf16_bits(Fraction(float(v))) for v in vals], dtype=np.uint16)
+    assert np.array_equal(got, want)
+
+
+def test_round_bf16_special_values():
+    v = np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 2.0 ** 128, (2 - 2 ** -8) * 2.0 ** 127,
+                  (2 - 2 ** -7) * 2.0 ** 127, 2.0 ** -133, 2.0 ** -134, 3 * 2.0 ** -135])
+    got = O.round_bf16(v).tolist()
+    assert got == [0x0000, 0x8000, 0x7F80, 0xFF80, 0x7FC0, 0x7F80, 0x7F80, 0x7F7F, 0x0001, 0x0000, 0x0001]
+
+
+# ------------------------------------------------------------------ dequantisation
+
+def test_dequant_int4_nibble_order_and_groups():
+    """byte j holds element 2j (low nibble) and 2j+1 (high nibble); group g = columns 64g..64g+63."""
+    q = np.zeros((2, 64), dtype=np.uint8)  # 2 rows x 128 columns
+    q[0, 0] = 0x21  # elements 0 -> 1, 1 -> 2
+    q[0, 31] = 0xF3  # elements 62 -> 3, 63 -> 15
+    q[0, 32] = 0x07  # element 64 -> 7 (group 1), 65 -> 0
+    q[1, 63] = 0x5A  # element 126 -> 10, 127 -> 5
+    s = np.array([[0x3F80, 0x4000], [0x3E80, 0x3F00]], dtype=np.uint16)  # 1, 2 | 0.25, 0.5
+    b = np.array([[0x0000, 0xBF80], [0x3F80, 0x0000]], dtype=np.uint16)  # 0, -1 | 1, 0
+    w = O.dequant_int4(q, s, b)
+    assert w.shape == (2, 128)
+    assert (w[0, 0], w[0, 1], w[0, 2]) == (1.0, 2.0, 0.0)
+    assert (w[0, 62], w[0, 63]) == (3.0, 15.0)
+    assert (w[0, 64], w[0, 65], w[0, 127]) == (2 * 7 - 1, -1.0, -1.0)
+    assert (w[1, 0], w[1, 63]) == (1.0, 1.0)
+    assert (w[1, 126], w[1, 127]) == (0.5 * 10, 0.5 * 5)
+
+
+def test_dequant_int8_groups():
+    q = np.arange(128, dtype=np.uint8).reshape(1, 128)
+    s = np.array([[0x3F00, 0x4080]], dtype=np.uint16)  # 0.5, 4.0
+    b = np.array([[0xC000, 0x3F80]], dtype=np.uint16)  # -2, 1
+    w = O.dequant_int8(q, s, b)
+    assert w[0, 0] == -2.0 and w[0, 63] == 0.5 * 63 - 2
+    assert w[0, 64] == 4.0 * 64 + 1 and w[0, 127] == 4.0 * 127 + 1
+
+
+def test_generator_weights_are_exact_in_fp32():
+    """scale*q + bias of the generated int4 data has at most 11 significant bits (exact in fp32)."""
+    from quantized_moe_expert_fp32_amd import synth
+
+    L = synth.make_case("tiny").layers[0]
+    w = O.dequant_int4(L.q_gate, L.s_gate, L.b_gate)
+    assert np.array_equal(w.astype(np.float32).astype(np.float64), w)
+    w = O.dequant_int4(L.q_down, L.s_down, L.b_down)
+    assert np.array_equal(w.astype(np.float32).astype(np.float64), w)
+
+
+# ------------------------------------------------------------------ a1 router logits
+
+def test_router_logits_one_hot_rows():
+    """x = one-hot at h gives logit_e = fp32(W[e, h] + bias_e) (closed form)."""
+    rng = np.random.default_rng(1)
+    H, R = 128, 9
+    W = rng.normal(0, 0.3, size=(R, H)).astype(np.float32)
+    bias = rng.normal(0, 1, size=R - 1).astype(np.float32)
+    x = np.zeros((H, H), dtype=np.uint16)
+    x[np.arange(H), np.arange(H)] = 0x3F80
+    l = O.router_logits(x, W.astype(np.float64), bias, R - 1)
+    for h in range(0, H, 17):
+        for e in range(R):
+            exact = Fraction(float(W[e, h])) + (Fraction(float(bias[e])) if e < R - 1 else 0)
+            assert l[h, e] == np.float32(X.rne_f32(exact))
+
+
+def test_router_logits_exact_rational_sum():
+    """Random bf16 x against an 8-bit affine router: fp32 RNE of the exact rational sum."""
+    from quantized_moe_expert_fp32_amd import synth
+
+    rng = np.random.default_rng(5)
+    H, R = 128, 5
+    w = rng.normal(0, 0.02, size=(R, H)).astype(np.float32)
+    q, s, b = synth.quantise_router_affine8(w)
+    x = synth.random_x(9, 3, H)
+    l = O.router_logits(x, O.dequant_int8(q, s, b), None, R - 1)
+    for t in range(3):
+        xs = [X.frac_of_bf16(int(v)) for v in x[t]]
+        for e in range(R):
+            acc = Fraction(0)
+            for hh in range(H):
+                g = hh // 64
+                wv = X.frac_of_bf16(int(s[e, g])) * int(q[e, hh]) + X.frac_of_bf16(int(b[e, g]))
+                acc += xs[hh] * wv
+            assert l[t, e] == np.float32(X.rne_f32(acc))
+
+
+# ------------------------------------------------------------------ a2 top-k
+
+def _bucket_expect(vec, k):
+    """Top-k for vectors over a few distinct values: ids of the largest value in
+    ascending order, then the next value's ids, and so on (the contract's tie rule)."""
+    out = []
+    for val in sorted(set(vec), reverse=True):
+        out.extend(i for i, v in enumerate(vec) if v == val)
+    return out[:k]
+
+
+@pytest.mark.parametrize("k", [1, 2, 8])
+def test_topk_bruteforce_binary_E16(k):
+    vecs = np.array(list(itertools.product([0.0, 1.0], repeat=16)), dtype=np.float32)
+    got = O.topk(vecs, k)
+    for i in range(0, len(vecs), 1):
+        assert got[i].tolist() == _bucket_expect(vecs[i].tolist(), k)
+
+
+@pytest.mark.parametrize("k", [1, 3, 5])
+def test_topk_bruteforce_ternary_E10(k):
+    vecs = np.array(list(itertools.product([-1.0, 0.0, 1.0], repeat=10)), dtype=np.float32)
+    got = O.topk(vecs, k)
+    for i in range(len(vecs)):
+        assert got[i].tolist() == _bucket_expect(vecs[i].tolist(), k)
+
+
+def test_topk_signed_zero_and_nan():
+    l = np.array([[-0.0, 0.0, -1.0, np.nan],
+                  [0.0, -0.0, np.nan, -np.inf],
+                  [np.nan, np.nan, -np.inf, -np.inf],
+                  [np.nan, 1e-30, -1e-30, 0.0]], dtype=np.float32)
+    got = O.topk(l, 3).tolist()
+    assert got[0] == [0, 1, 2]  # -0 ties +0: lower id first
+    assert got[1] == [0, 1, 3]  # NaN below -inf
+    assert got[2] == [2, 3, 0]
+    assert got[3] == [1, 3, 2]
+
+
+# ------------------------------------------------------------------ a2 weights
+
+def test_pick_weights_closed_forms():
+    # all k logits equal -> 1/k each
+    for k in (1, 2, 4, 8):
+        l = np.full((1, 16), 0.25, dtype=np.float32)
+        ids = O.topk(l, k)
+        w = O.pick_weights(l, ids)
+        assert (O.bf16_to_f64(w) == 1.0 / k).all()
+    # k = 3 equal -> bf16(1/3) = 0x3EAB
+    l = np.zeros((1, 8), dtype=np.float32)
+    assert O.pick_weights(l, O.topk(l, 3)).tolist() == [[0x3EAB] * 3]
+    # k = 2, gap fp32(ln 2): weights sigmoid(+-d) -> 0.66796875, 0.333984375
+    d = np.float32(np.log(2.0))
+    l = np.array([[0.0, -d, -5.0, -6.0]], dtype=np.float32)
+    ids = O.topk(l, 2)
+    w = O.bf16_to_f64(O.pick_weights(l, ids))
+    assert ids.tolist() == [[0, 1]] and w.tolist() == [[0.66796875, 0.333984375]]
+    # no renormalisation after rounding: the two weights sum to 1.001953125
+    assert w.sum() == 1.001953125
+
+
+def test_pick_weights_decimal_random():
+    rng = np.random.default_rng(11)
+    T, E, k = 400, 64, 8
+    l = rng.normal(0, 1.5, size=(T, E)).astype(np.float32)
+    ids = O.topk(l, k)
+    w = O.pick_weights(l, ids)
+    for t in range(T):
+        picks = [Fraction(float(l[t, i])) for i in ids[t]]
+        want = [X.rne_bf16_bits(v) for v in X.softmax_picks_dec(picks)]
+        assert w[t].tolist() == want
+
+
+def test_shared_weight_exhaustive_bf16():
+    """All 65,536 bf16 gate values: bf16(sigmoid(g)) against 60-digit decimal + exact RNE."""
+    pats = np.arange(65536, dtype=np.uint32)
+    g32 = (pats << 16).view(np.float32)
+    got = O.shared_weight(g32)
+    for p in range(65536):
+        v = float(g32[p])
+        if np.isnan(v):
+            assert got[p] == 0x7FC0
+            continue
+        if np.isinf(v):
+            assert got[p] == (0x3F80 if v > 0 else 0x0000)
+            continue
+        assert got[p] == X.rne_bf16_bits(X.sigmoid_dec(Fraction(v))), hex(p)
+
+
+def test_shared_weight_rounds_gate_to_bf16_first():
+    """bf16(gate) first: fp32 gates in one bf16 rounding interval share a weight."""
+    g = np.array([1.0, 1.0 + 2 ** -9, 1.0 + 2 ** -8 + 2 ** -12], dtype=np.float32)
+    w = O.shared_weight(g)
+    assert w[0] == w[1]  # 1 + 2^-9 rounds to 1.0 in bf16
+    assert w[2] == X.rne_bf16_bits(X.sigmoid_dec(Fraction(1) + Fraction(1, 128)))
+
+
+# ------------------------------------------------------------------ a6 combine
+
+def test_rounded_once_golden():
+    gold = json.load(open(os.path.join(GOLDEN, "rounded_once.json")))
+    y = np.zeros((1, 2, 64))
+    y[0, 0, :] = gold["y"][0]
+    y[0, 1, :] = gold["y"][1]
+    w = np.array([gold["w_bits"]], dtype=np.uint16)
+    out = O.combine(y, w, None)
+    assert (out == gold["expected_out_bits"]).all()
+    assert gold["expected_out_bits"] != gold["per_term_rounding_bits"]
+
+
+# ------------------------------------------------------------------ whole layer
+
+def _const_layer(H, I, E, router_rows, qbyte, sbits, bbits):
+    M = E + 1
+    return SimpleNamespace(
+        router_f32=np.array(router_rows, dtype=np.float32),
+        logit_bias=None,
+        q_gate=np.full((M, I, H // 2), qbyte, np.uint8), s_gate=np.full((M, I, H // 64), sbits, np.uint16),
+        b_gate=np.full((M, I, H // 64), bbits, np.uint16),
+        q_up=np.full((M, I, H // 2), qbyte, np.uint8), s_up=np.full((M, I, H // 64), sbits, np.uint16),
+        b_up=np.full((M, I, H // 64), bbits, np.uint16),
+        q_down=np.full((M, H, I // 2), qbyte, np.uint8), s_down=np.full((M, H, I // 64), sbits, np.uint16),
+        b_down=np.full((M, H, I // 64), bbits, np.uint16))
+
+
+def test_worked_layer_golden():
+    gold = json.load(open(os.path.join(GOLDEN, "worked_layer.json")))
+    H = I = 64
+    rows = [[v] * H for v in gold["router_f32_rows"]]
+    L = _const_layer(H, I, 2, rows, 0x99, 0x3C80, 0xBE00)
+    x = np.full((1, H), 0x3F80, np.uint16)
+    st = O.layer_forward(x, L, top_k=1, has_shared=True)
+    ex = gold["expected"]
+    assert st["ids"].tolist() == ex["ids"]
+    assert st["w"].tolist() == ex["w_bits"]
+    assert st["wsh"].tolist() == ex["wsh_bits"]
+    assert (st["h"] == ex["h_bits"]).all()
+    assert (st["out"] == ex["out_bits"]).all()
+    assert (O.bf16_to_f64(st["out"]) == ex["out_value"]).all()
+
+
+def _random_layer(rng, H, I, E, router_fp32=True):
+    from quantized_moe_expert_fp32_amd import synth
+
+    shape = synth.Shape(hidden=H, inter=I, n_experts=E, top_k=2, has_shared=1,
+                        router_fmt=synth.ROUTER_F32 if router_fp32 else synth.ROUTER_AFFINE8)
+    return synth.make_layer(shape, int(rng.integers(0, 2 ** 31)), 0)
+
+
+def _bruteforce_layer(x_bits, L, E, k):
+    """The contract evaluated with exact rationals (dot products) and 60-digit
+    decimals (exp, sigmoid), reading the canonical bytes directly."""
+    T, H = x_bits.shape
+    I = L.q_gate.shape[1]
+
+    def wmat(q, s, b, e, r):
+        qs = X.unpack_int4_row(q[e, r])
+        return [X.frac_of_bf16(int(s[e, r, c // 64])) * qs[c] + X.frac_of_bf16(int(b[e, r, c // 64]))
+                for c in range(len(qs))]
+
+    res = []
+    for t in range(T):
+        xs = [X.frac_of_bf16(int(v)) for v in x_bits[t]]
+        logits = []
+        for e in range(E + 1):
+            acc = sum((xs[h] * Fraction(float(L.router_f32[e, h])) for h in range(H)), Fraction(0))
+            logits.append(X.rne_f32(acc))
+        order = sorted(range(E), key=lambda e: (-logits[e], e))[:k]
+        wd = X.softmax_picks_dec([Fraction(logits[e]) for e in order])
+        w = [X.rne_bf16_bits(v) for v in wd]
+        gate_bf16 = X.rne_bf16_bits(Fraction(logits[E]))
+        wsh = X.rne_bf16_bits(X.sigmoid_dec(X.frac_of_bf16(gate_bf16)))
+        slots = list(order) + [E]
+        weights = [X.frac_of_bf16(v) for v in w] + [X.frac_of_bf16(wsh)]
+        total = [Fraction(0)] * H
+        hs = []
+        for e, ws in zip(slots, weights):
+            h = []
+            for i in range(I):
+                g = sum((a * c for a, c in zip(xs, wmat(L.q_gate, L.s_gate, L.b_gate, e, i))), Fraction(0))
+                u = sum((a * c for a, c in zip(xs, wmat(L.q_up, L.s_up, L.b_up, e, i))), Fraction(0))
+                h.append(X.rne_bf16_bits(X.silu_dec(g) * X.dec(u)))
+            hs.append(h)
+            hf = [X.frac_of_bf16(v) for v in h]
+            for n in range(H):
+                y = sum((a * c for a, c in zip(hf, wmat(L.q_down, L.s_down, L.b_down, e, n))), Fraction(0))
+                total[n] += ws * y
+        out = [X.rne_bf16_bits(v) for v in total]
+        res.append(dict(logits=logits, ids=order, w=w, wsh=wsh, h=hs, out=out))
+    return res
+
+
+def test_bruteforce_exact_tiny_layer():
+    """Whole layer against an exact-arithmetic evaluation of the contract (H=I=64, E=4, k=2)."""
+    rng = np.random.default_rng(2024)
+    H, I, E, k = 64, 64, 4, 2
+    L = _random_layer(rng, H, I, E)
+    # larger router weights so the picks are well separated
+    L.router_f32 = (L.router_f32 * 10).astype(np.float32)
+    from quantized_moe_expert_fp32_amd import synth
+
+    x = synth.random_x(77, 2, H)
+    st = O.layer_forward(x, L, top_k=k, has_shared=True)
+    bf = _bruteforce_layer(x, L, E, k)
+    for t in range(2):
+        assert st["logits"][t].tolist() == [np.float32(v) for v in bf[t]["logits"]]
+        assert st["ids"][t].tolist() == bf[t]["ids"]
+        assert st["w"][t].tolist() == bf[t]["w"]
+        assert int(st["wsh"][t]) == bf[t]["wsh"]
+        for s in range(k + 1):
+            assert st["h"][t, s].tolist() == bf[t]["h"][s]
+        assert st["out"][t].tolist() == bf[t]["out"]
+
+
+def test_dense_special_case_matches_torch():
+    """E=1, k=1: the layer is a dense SwiGLU MLP plus the shared expert (library matmuls)."""
+    import torch
+    import torch.nn.functional as F
+
+    rng = np.random.default_rng(99)
+    H, I = 128, 64
+    L = _random_layer(rng, H, I, 1)
+    from quantized_moe_expert_fp32_amd import synth
+
+    x = synth.random_x(5, 6, H)
+    st = O.layer_forward(x, L, top_k=1, has_shared=True)
+    assert (st["ids"] == 0).all() and (st["w"] == 0x3F80).all()
+    xt = torch.from_numpy(O.bf16_to_f64(x))
+    for e, s in ((0, 0), (1, 1)):
+        Wg = torch.from_numpy(O.dequant_int4(L.q_gate[e], L.s_gate[e], L.b_gate[e]))
+        Wu = torch.from_numpy(O.dequant_int4(L.q_up[e], L.s_up[e], L.b_up[e]))
+        Wd = torch.from_numpy(O.dequant_int4(L.q_down[e], L.s_down[e], L.b_down[e]))
+        pre = F.silu(F.linear(xt, Wg)) * F.linear(xt, Wu)
+        h_want = np.array([[X.rne_bf16_bits(Fraction(float(v))) for v in row] for row in pre.numpy()])
+        assert np.array_equal(st["h"][:, s], h_want)
+        y = F.linear(torch.from_numpy(O.bf16_to_f64(st["h"][:, s])), Wd).numpy()
+        assert np.allclose(st["y"][:, s], y, rtol=1e-13, atol=1e-13)
+
+
+def test_token_independence_and_relabelling():
+    """Rows are independent (T rows == T single-row runs); relabelling experts permutes ids only."""
+    from quantized_moe_expert_fp32_amd import synth
+
+    case = synth.make_case("tiny")
+    L = case.layers[0]
+    st = O.layer_forward(case.x, L, 2)
+    for t in range(case.T):
+        s1 = O.layer_forward(case.x[t:t + 1], L, 2)
+        assert np.array_equal(s1["out"][0], st["out"][t])
+        assert np.array_equal(s1["ids"][0], st["ids"][t])
+    E = 16
+    perm = np.random.default_rng(3).permutation(E)  # new id of old expert e is perm[e]
+    inv = np.argsort(perm)
+    P = SimpleNamespace(**{k: getattr(L, k) for k in vars(L)})
+    full = np.concatenate([inv, [E]])  # new index j holds old expert full[j]
+    P.router_f32 = L.router_f32[full]
+    for nm in ("q_gate", "s_gate", "b_gate", "q_up", "s_up", "b_up", "q_down", "s_down", "b_down"):
+        setattr(P, nm, getattr(L, nm)[full])
+    sp = O.layer_forward(case.x, P, 2)
+    assert np.array_equal(sp["ids"], perm[st["ids"]])
+    assert np.array_equal(sp["out"], st["out"])
+
+
+def test_rmsnorm_and_residual_closed_forms():
+    # rows alternating 3, 4: mean square 12.5
+    x = np.tile(np.array([0x4040, 0x4080], dtype=np.uint16), 32)[None, :]
+    xn = O.rmsnorm_bf16(x, 1e-6)
+    from decimal import Decimal, localcontext
+
+    with localcontext() as c:
+        c.prec = 60
+        r = Decimal(1) / (Decimal("12.5") + X.dec(Fraction(1e-6))).sqrt()
+        want3 = X.rne_bf16_bits(Decimal(3) * r)
+        want4 = X.rne_bf16_bits(Decimal(4) * r)
+    assert xn[0, 0] == want3 and xn[0, 1] == want4
+    # constant rows normalise to bf16(1 - ~5e-7) = 1.0
+    assert (O.rmsnorm_bf16(np.full((2, 64), 0x3F80, np.uint16)) == 0x3F80).all()
+    # residual: one rounding of the exact sum of two bf16 values
+    a = np.array([[0x3F80, 0x3F80]], np.uint16)  # 1, 1
+    b = np.array([[0x3B80, 0x3C00]], np.uint16)  # 2^-8 (exact tie -> even 1.0), 2^-7 -> 1.0078125
+    assert O.residual_bf16(a, b).tolist() == [[0x3F80, 0x3F81]]
+
+
+def test_dispatch_matches_bruteforce():
+    rng = np.random.default_rng(4)
+    T, k, E = 37, 3, 8
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    counts, offsets, order = O.dispatch(ids, E, True)
+    S = k + 1
+    assert counts[E] == T and counts[:E].sum() == T * k
+    for e in range(E + 1):
+        want = [t * S + s for t in range(T) for s in range(S)
+                if (ids[t, s] == e if s < k else e == E)]
+        assert order[offsets[e]:offsets[e + 1]].tolist() == want
