@@ -1,0 +1,202 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) routed int4 Mixture-of-Experts layer.
+ *
+ * The layer is the routed-expert block of Qwen3.6-35B-A3B: E routed experts,
+ * top-k routing plus one shared expert, SwiGLU experts whose gate, up and down
+ * projections are affine 4-bit in groups of 64, and an 8-bit (or fp32) router.
+ * Sources (the pages are cited by title and section):
+ *   [P3-build] TensorFold issue #931, "Qwen3.6-35B-A3B (qwen3_5_moe) on the native
+ *              Metal engine: proposal and gate", section "What I'd build": the routing
+ *              contract (fp32 logits over the experts and the shared gate; top-k by
+ *              logit, ties to the lower id; weights exp(l - l_top) over the k picks
+ *              rounded to bf16; the shared expert as one more slot weighted
+ *              bf16(sigmoid(bf16(gate))); the weighted sum rounded once to bf16),
+ *              affine 4-bit experts in groups of 64, 8-bit routers, and the refusal
+ *              of other bit widths; "windows of 1 to 16 rows" for decode.
+ *   [P3-what]  same page, section "What it is": routed experts replace the dense MLP;
+ *              256 experts, 8 picked per token, one shared expert.
+ *   [P3-gate]  same page, section "Gate": the expert gate/up pair, expert down and the
+ *              combine as the projection classes of the layer.
+ *   [P1-phase] "POC for qwen3.5 / qwen3.6 support optimized for AGX Orin", summary
+ *              "Phase 1-4" (parallel top-k router, GEMV MoE path at batch 1) and
+ *              "Phase 9b" (MoE GEMM with int4 dequant and lookup-table dispatch).
+ *   [P4-run]   "Qwen-3.6-35B-A3B-SIQ-K6+K4K3", section "How to run": the shared
+ *              expert gate is an N=1 projection.
+ *
+ * Conventions for every call:
+ *   - Pointers named *_host are host memory; every other pointer is device memory
+ *     on the current HIP device, 16-byte aligned. The library never allocates or
+ *     frees memory: the caller owns every buffer (inputs, outputs, workspace).
+ *   - `stream` is a hipStream_t (NULL = the default stream). Every call that
+ *     launches work is asynchronous on that stream and never synchronises the host.
+ *   - Arguments are validated on the host before any launch; a failed check returns
+ *     MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED / MOE_ERR_WORKSPACE and launches
+ *     nothing. A failed launch returns MOE_ERR_HIP. moe_last_error() then holds a
+ *     message (per host thread). No C++ exception crosses this boundary.
+ *   - bf16 values are passed as uint16_t bit patterns.
+ *   - T is the number of token rows; S = top_k + has_shared slots per token; slot
+ *     s < top_k belongs to expert ids[t, s], slot top_k (if has_shared) to the
+ *     shared expert. R = n_experts + has_shared router rows (row n_experts is the
+ *     shared-expert gate, [P4-run]).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1, /* bad pointer, size or shape field                */
+    MOE_ERR_UNSUPPORTED = -2, /* well-formed but not served (bit width, group ...) */
+    MOE_ERR_WORKSPACE = -3,   /* caller buffer smaller than the documented size   */
+    MOE_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed        */
+} moe_status;
+
+enum { MOE_ROUTER_F32 = 0, MOE_ROUTER_AFFINE8 = 1 };
+
+/* Layer shape and formats. Served: bits == 4, group == 64 ([P3-build]; any other
+ * bit width or group is refused with MOE_ERR_UNSUPPORTED); hidden is a power of
+ * two in [64, 8192], inter a power of two in [64, 2048]; 1 <= top_k <= min(n_experts, 16);
+ * 1 <= n_experts <= 1024; has_shared in {0, 1}; router_fmt one of MOE_ROUTER_*. */
+typedef struct moe_shape {
+    int32_t hidden;     /* H: model width                          */
+    int32_t inter;      /* I: expert intermediate width            */
+    int32_t n_experts;  /* E: routed experts                       */
+    int32_t top_k;      /* k: experts picked per token             */
+    int32_t has_shared; /* 1: one shared expert (expert index E)   */
+    int32_t group;      /* quantisation group along the input dim  */
+    int32_t bits;       /* expert weight bits                      */
+    int32_t router_fmt; /* MOE_ROUTER_F32 or MOE_ROUTER_AFFINE8    */
+} moe_shape;
+
+/* Canonical expert weights ([P3-build]: affine 4-bit, groups of 64), device memory.
+ * For each of the M = n_experts + has_shared experts (index n_experts = shared):
+ *   q_gate, q_up [M][I][H/2] uint8, q_down [M][H][I/2] uint8: row-major matrices
+ *     [out, in] with input element 2j in the low nibble of byte j and 2j+1 in the
+ *     high nibble; q in 0..15.
+ *   s_*, b_* [M][rows][in/64] bf16: scale and bias of each group of 64 consecutive
+ *     input elements; the weight is scale * q + bias. */
+typedef struct moe_expert_canon {
+    const uint8_t* q_gate;
+    const uint16_t* s_gate;
+    const uint16_t* b_gate;
+    const uint8_t* q_up;
+    const uint16_t* s_up;
+    const uint16_t* b_up;
+    const uint8_t* q_down;
+    const uint16_t* s_down;
+    const uint16_t* b_down;
+} moe_expert_canon;
+
+/* ABI revision of this header. */
+int32_t moe_abi_version(void);
+
+/* Static text for a status code. */
+const char* moe_status_str(int32_t status);
+
+/* Message for the last non-OK status returned on this host thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Checks a shape against the served set; MOE_OK if every call below accepts it. */
+moe_status moe_shape_check(const moe_shape* shape);
+
+/* ---------------------------------------------------------------- weight packing
+ * The kernels read one packed buffer per layer. Per expert m (stride
+ * moe_experts_packed_bytes / M), in this order:
+ *   gate q [I][H/2] | up q [I][H/2] | down q [H][I/2] |
+ *   gate sb [I][H/64] | up sb [I][H/64] | down sb [H][I/64]
+ * where every sb entry is a uint32 holding the group's bf16 scale in the low and
+ * bf16 bias in the high half. q bytes are copied unchanged. */
+size_t moe_experts_packed_bytes(const moe_shape* shape);
+
+/* Packs canonical expert weights (device) into `packed` (device, packed_bytes >=
+ * moe_experts_packed_bytes). Async on `stream`. */
+moe_status moe_pack_experts(const moe_shape* shape, const moe_expert_canon* src_host,
+                            void* packed, size_t packed_bytes, void* stream);
+
+/* Packed router: MOE_ROUTER_AFFINE8: q [R][H] uint8 | sb [R][H/64] uint32 (scale low,
+ * bias high); MOE_ROUTER_F32: w [R][H] float. [P3-build]: routers at 8 bits. */
+size_t moe_router_packed_bytes(const moe_shape* shape);
+
+/* Packs the router. AFFINE8: w = q [R][H] uint8, s and b bf16 [R][H/64].
+ * F32: w = float [R][H], s and b must be NULL. Device pointers; async on `stream`. */
+moe_status moe_pack_router(const moe_shape* shape, const void* w, const uint16_t* s,
+                           const uint16_t* b, void* packed, size_t packed_bytes, void* stream);
+
+/* ---------------------------------------------------------------- a1 + a2: routing
+ * [P3-build] routing contract; parallel top-k router as in [P1-phase].
+ * Inputs: router_packed (moe_pack_router layout); logit_bias [E] float or NULL,
+ * added to the routed logits only; x [T][H] bf16.
+ * Outputs: logits [T][R] float (fp32 logits; row-major; written first and then
+ * read by the selection step), ids [T][k] int32 (descending logit, ties to the
+ * lower id), w [T][k] bf16 (exp(l_i - l_0) / sum_j exp(l_j - l_0) over the picks,
+ * evaluated in fp64 and rounded once), w_shared [T] bf16 (bf16(sigmoid(bf16(gate)))
+ * in fp64; NULL when has_shared == 0). NaN logits rank below -inf; -0 ties +0.
+ * Logits: exact products accumulated in fp64 in a fixed order, rounded once to
+ * fp32; a token's logits do not depend on T. T >= 1. */
+moe_status moe_route(const moe_shape* shape, const void* router_packed, const float* logit_bias,
+                     const uint16_t* x, int32_t T, float* logits, int32_t* ids, uint16_t* w,
+                     uint16_t* w_shared, void* stream);
+
+/* The selection step alone, from caller-given fp32 logits [T][R] (same outputs). */
+moe_status moe_route_from_logits(const moe_shape* shape, const float* logits, int32_t T,
+                                 int32_t* ids, uint16_t* w, uint16_t* w_shared, void* stream);
+
+/* ---------------------------------------------------------------- a4 + a5: experts, decode
+ * GEMV path for 1 <= T <= 16 rows ([P1-phase]: the GEMV MoE path at batch 1;
+ * [P3-build]: windows of 1 to 16 rows). For every token t and slot s with expert
+ * e (ids[t,s], or the shared expert for s == k):
+ *   h = bf16(silu(x Wg_e^T) * (x Wu_e^T))   (SwiGLU; the bf16 rounding is a reading)
+ *   y[t][s][:] = h Wd_e^T                   (fp32, not rounded to bf16: [P3-build])
+ * ws: device scratch of moe_decode_workspace_bytes(shape, T) bytes (holds h).
+ * Each row's result does not depend on T or on the other rows. */
+size_t moe_decode_workspace_bytes(const moe_shape* shape, int32_t T);
+moe_status moe_experts_decode(const moe_shape* shape, const void* experts_packed,
+                              const uint16_t* x, int32_t T, const int32_t* ids, void* ws,
+                              size_t ws_bytes, float* y, void* stream);
+
+/* ---------------------------------------------------------------- a3: dispatch
+ * Histogram and expert-sorted order of the T*S picks ([P1-phase] Phase 9b:
+ * lookup-table dispatch). counts [M] int32 (counts[E] = T for the shared expert),
+ * offsets [M+1] int32 exclusive prefix sums, order [T*S] int32: pick indices
+ * p = t*S + s grouped by ascending expert; the order of picks inside one expert's
+ * segment is unspecified (every valid order gives the same layer output). */
+moe_status moe_dispatch(const moe_shape* shape, const int32_t* ids, int32_t T, int32_t* counts,
+                        int32_t* offsets, int32_t* order, void* stream);
+
+/* ---------------------------------------------------------------- a3..a5: experts, prefill
+ * Grouped-GEMM path for any T >= 1 ([P1-phase] Phase 9b: MoE GEMM with int4
+ * dequant and dispatch table). Same y as moe_experts_decode up to fp32
+ * summation order. Runs moe_dispatch internally into `ws`, then the gate/up GEMM
+ * with the SwiGLU epilogue, then the down GEMM scattering rows back to y[t][s].
+ * ws: device scratch of moe_prefill_workspace_bytes(shape, T) bytes. */
+size_t moe_prefill_workspace_bytes(const moe_shape* shape, int32_t T);
+moe_status moe_experts_prefill(const moe_shape* shape, const void* experts_packed,
+                               const uint16_t* x, int32_t T, const int32_t* ids, void* ws,
+                               size_t ws_bytes, float* y, void* stream);
+
+/* ---------------------------------------------------------------- a6: combine
+ * out[t][n] = bf16( sum_{s<k} w[t][s] * y[t][s][n] + w_shared[t] * y[t][k][n] )
+ * with one rounding ([P3-build]); fp32 sum in slot order. If residual != NULL
+ * (a [T][H] bf16 array, may alias out) the result is bf16(residual + that value):
+ * the residual add of a stacked block. w_shared must be NULL iff has_shared == 0. */
+moe_status moe_combine(const moe_shape* shape, const float* y, const uint16_t* w,
+                       const uint16_t* w_shared, int32_t T, const uint16_t* residual,
+                       uint16_t* out, void* stream);
+
+/* ---------------------------------------------------------------- a7: stack glue
+ * Unit-weight RMSNorm per row: out = bf16(x / sqrt(mean(x^2) + eps)), fp32 math.
+ * (Reading: the pages give no norm for an MoE-only stack; a pre-norm residual block
+ * x <- x + MoE(RMSNorm(x)) keeps stacked activations in range.) out may not alias x. */
+moe_status moe_rmsnorm(int32_t hidden, const uint16_t* x, int32_t T, float eps, uint16_t* out,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,153 @@
+// C-ABI plumbing: status strings, per-thread last error, shape validation, packing.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+static thread_local char g_last_error[512] = "";
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+void clear_error() { g_last_error[0] = 0; }
+
+moe_status check_launch(const char* what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return MOE_OK;
+}
+
+static bool pow2_in(int32_t v, int32_t lo, int32_t hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
+
+moe_status validate_shape(const moe_shape* sh) {
+    if (!sh) return fail(MOE_ERR_INVALID_ARG, "shape is NULL");
+    if (sh->bits != 4) return fail(MOE_ERR_UNSUPPORTED, "expert bit width %d is not served (4-bit only)", sh->bits);
+    if (sh->group != 64) return fail(MOE_ERR_UNSUPPORTED, "group %d is not served (64 only)", sh->group);
+    if (sh->router_fmt != MOE_ROUTER_F32 && sh->router_fmt != MOE_ROUTER_AFFINE8)
+        return fail(MOE_ERR_UNSUPPORTED, "router format %d is not served", sh->router_fmt);
+    if (!pow2_in(sh->hidden, 64, 8192))
+        return fail(MOE_ERR_UNSUPPORTED, "hidden %d: need a power of two in [64, 8192]", sh->hidden);
+    if (!pow2_in(sh->inter, 64, 2048))
+        return fail(MOE_ERR_UNSUPPORTED, "inter %d: need a power of two in [64, 2048]", sh->inter);
+    if (sh->n_experts < 1 || sh->n_experts > 1024)
+        return fail(MOE_ERR_INVALID_ARG, "n_experts %d out of [1, 1024]", sh->n_experts);
+    if (sh->has_shared != 0 && sh->has_shared != 1)
+        return fail(MOE_ERR_INVALID_ARG, "has_shared must be 0 or 1");
+    if (sh->top_k < 1 || sh->top_k > 16 || sh->top_k > sh->n_experts)
+        return fail(MOE_ERR_INVALID_ARG, "top_k %d out of [1, min(n_experts, 16)]", sh->top_k);
+    return MOE_OK;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int32_t moe_abi_version(void) { return 1; }
+
+extern "C" const char* moe_status_str(int32_t st) {
+    switch (st) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape or format";
+        case MOE_ERR_WORKSPACE: return "buffer too small";
+        case MOE_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+extern "C" const char* moe_last_error(void) { return g_last_error; }
+
+extern "C" moe_status moe_shape_check(const moe_shape* shape) { return validate_shape(shape); }
+
+// ------------------------------------------------------------------ packing
+
+extern "C" size_t moe_experts_packed_bytes(const moe_shape* sh) {
+    if (validate_shape(sh) != MOE_OK) return 0;
+    return expert_layout(*sh).stride * (size_t)n_mats(*sh);
+}
+
+extern "C" size_t moe_router_packed_bytes(const moe_shape* sh) {
+    if (validate_shape(sh) != MOE_OK) return 0;
+    const size_t R = (size_t)router_rows(*sh), H = (size_t)sh->hidden;
+    if (sh->router_fmt == MOE_ROUTER_F32) return R * H * 4;
+    return R * H + R * (H / 64) * 4;
+}
+
+// Copies n16 16-byte units per expert from src (stride src_stride bytes) to dst.
+__global__ void pack_copy_kernel(const uint4* __restrict__ src, size_t src_stride16, uint4* __restrict__ dst,
+                                 size_t dst_stride16, size_t n16) {
+    const size_t m = blockIdx.y;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+        dst[m * dst_stride16 + i] = src[m * src_stride16 + i];
+}
+
+// sb[m][i] = scale | bias << 16 for n entries per expert.
+__global__ void pack_sb_kernel(const uint16_t* __restrict__ s, const uint16_t* __restrict__ b, size_t n,
+                               uint32_t* __restrict__ dst, size_t dst_stride4) {
+    const size_t m = blockIdx.y;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        dst[m * dst_stride4 + i] = (uint32_t)s[m * n + i] | ((uint32_t)b[m * n + i] << 16);
+}
+
+static moe_status copy_q(const void* src, size_t bytes, char* dst, size_t stride, int M, hipStream_t st) {
+    if (!src || !aligned16(src)) return fail(MOE_ERR_INVALID_ARG, "q source NULL or not 16-byte aligned");
+    size_t n16 = bytes / 16;
+    dim3 grid((unsigned)((n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024), (unsigned)M);
+    hipLaunchKernelGGL(pack_copy_kernel, grid, dim3(256), 0, st, (const uint4*)src, n16, (uint4*)dst, stride / 16, n16);
+    return check_launch("pack_copy_kernel");
+}
+
+static moe_status copy_sb(const uint16_t* s, const uint16_t* b, size_t n, char* dst, size_t stride, int M,
+                          hipStream_t st) {
+    if (!s || !b) return fail(MOE_ERR_INVALID_ARG, "scale/bias source NULL");
+    dim3 grid((unsigned)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024), (unsigned)M);
+    hipLaunchKernelGGL(pack_sb_kernel, grid, dim3(256), 0, st, s, b, n, (uint32_t*)dst, stride / 4);
+    return check_launch("pack_sb_kernel");
+}
+
+extern "C" moe_status moe_pack_experts(const moe_shape* sh, const moe_expert_canon* src, void* packed,
+                                       size_t packed_bytes, void* stream) {
+    clear_error();
+    moe_status st = validate_shape(sh);
+    if (st != MOE_OK) return st;
+    if (!src || !packed || !aligned16(packed)) return fail(MOE_ERR_INVALID_ARG, "NULL or unaligned pointer");
+    const ExpertLayout L = expert_layout(*sh);
+    const int M = n_mats(*sh);
+    if (packed_bytes < L.stride * (size_t)M) return fail(MOE_ERR_WORKSPACE, "packed buffer too small");
+    const size_t H = sh->hidden, I = sh->inter;
+    hipStream_t s = (hipStream_t)stream;
+    char* d = (char*)packed;
+    if ((st = copy_q(src->q_gate, I * H / 2, d + L.gate_q, L.stride, M, s)) != MOE_OK) return st;
+    if ((st = copy_q(src->q_up, I * H / 2, d + L.up_q, L.stride, M, s)) != MOE_OK) return st;
+    if ((st = copy_q(src->q_down, H * I / 2, d + L.down_q, L.stride, M, s)) != MOE_OK) return st;
+    if ((st = copy_sb(src->s_gate, src->b_gate, I * (H / 64), d + L.gate_sb, L.stride, M, s)) != MOE_OK) return st;
+    if ((st = copy_sb(src->s_up, src->b_up, I * (H / 64), d + L.up_sb, L.stride, M, s)) != MOE_OK) return st;
+    if ((st = copy_sb(src->s_down, src->b_down, H * (I / 64), d + L.down_sb, L.stride, M, s)) != MOE_OK) return st;
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_pack_router(const moe_shape* sh, const void* w, const uint16_t* s, const uint16_t* b,
+                                      void* packed, size_t packed_bytes, void* stream) {
+    clear_error();
+    moe_status st = validate_shape(sh);
+    if (st != MOE_OK) return st;
+    if (!w || !packed || !aligned16(packed) || !aligned16(w))
+        return fail(MOE_ERR_INVALID_ARG, "NULL or unaligned pointer");
+    const size_t need = moe_router_packed_bytes(sh);
+    if (packed_bytes < need) return fail(MOE_ERR_WORKSPACE, "router buffer too small");
+    const size_t R = router_rows(*sh), H = sh->hidden;
+    hipStream_t hs = (hipStream_t)stream;
+    if (sh->router_fmt == MOE_ROUTER_F32) {
+        if (s || b) return fail(MOE_ERR_INVALID_ARG, "fp32 router takes no scale/bias");
+        return copy_q(w, R * H * 4, (char*)packed, 0, 1, hs);
+    }
+    if ((st = copy_q(w, R * H, (char*)packed, 0, 1, hs)) != MOE_OK) return st;
+    return copy_sb(s, b, R * (H / 64), (char*)packed + R * H, 0, 1, hs);
+}

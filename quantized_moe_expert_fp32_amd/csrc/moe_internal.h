@@ -1,0 +1,123 @@
+// Internal helpers shared by the HIP kernels and the C-ABI entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------ host side
+
+moe_status fail(moe_status st, const char* fmt, ...);
+moe_status check_launch(const char* what);
+void clear_error();
+
+// Validates the shape for every entry point (formats served, size limits).
+moe_status validate_shape(const moe_shape* sh);
+
+inline int32_t n_mats(const moe_shape& s) { return s.n_experts + (s.has_shared ? 1 : 0); }
+inline int32_t n_slots(const moe_shape& s) { return s.top_k + (s.has_shared ? 1 : 0); }
+inline int32_t router_rows(const moe_shape& s) { return s.n_experts + (s.has_shared ? 1 : 0); }
+
+// Byte offsets of one expert's segments inside the packed buffer.
+struct ExpertLayout {
+    size_t gate_q, up_q, down_q, gate_sb, up_sb, down_sb, stride;
+};
+
+inline ExpertLayout expert_layout(const moe_shape& s) {
+    const size_t H = (size_t)s.hidden, I = (size_t)s.inter, G = 64;
+    ExpertLayout L;
+    L.gate_q = 0;
+    L.up_q = L.gate_q + I * H / 2;
+    L.down_q = L.up_q + I * H / 2;
+    L.gate_sb = L.down_q + H * I / 2;
+    L.up_sb = L.gate_sb + I * (H / G) * 4;
+    L.down_sb = L.up_sb + I * (H / G) * 4;
+    L.stride = L.down_sb + H * (I / G) * 4;
+    return L;
+}
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ------------------------------------------------------------------ device side
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN -> 0x7FC0 (keeps the sign bit clear).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// fp64 -> bf16 bits with one round-to-nearest-even step (no fp32 intermediate).
+// The value is sig * 2^(e-52) with a 53-bit significand; the bf16 quantum is
+// 2^max(e-7, -133). The encoding ((qe + 134) << 7) + n - 128 covers normal
+// results, subnormal results (qe = -133, n < 128) and the carry into the next
+// binade (n = 256); an exponent field of 255 is infinity.
+__device__ __forceinline__ uint32_t f64_to_bf16(double d) {
+    const uint64_t u = (uint64_t)__double_as_longlong(d);
+    const uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
+    const uint64_t a = u & 0x7FFFFFFFFFFFFFFFull;
+    if (a > 0x7FF0000000000000ull) return 0x7FC0u;
+    if (a == 0x7FF0000000000000ull) return sign | 0x7F80u;
+    const int bexp = (int)(a >> 52);
+    if (bexp == 0) return sign;  // fp64 subnormal: far below half the least bf16 subnormal
+    const int e = bexp - 1023;
+    if (e >= 128) return sign | 0x7F80u;
+    if (e < -135) return sign;
+    const uint64_t sig = (a & 0x000FFFFFFFFFFFFFull) | 0x0010000000000000ull;
+    const int qe = e - 7 > -133 ? e - 7 : -133;
+    const int sh = 52 + qe - e;  // 45 for normal results, up to 54 here
+    uint64_t n = sig >> sh;
+    const uint64_t rem = sig & ((1ull << sh) - 1);
+    const uint64_t half = 1ull << (sh - 1);
+    if (rem > half || (rem == half && (n & 1))) ++n;
+    uint32_t bits = (uint32_t)(((int64_t)(qe + 134) << 7) + (int64_t)n - 128);
+    if (bits >= 0x7F80u) bits = 0x7F80u;
+    return sign | bits;
+}
+
+// Eight int4 weights of one dword (element j in bits 4j..4j+3) as four bf16 pairs
+// holding 1 + q/16 exactly, paired (0,4), (1,5), (2,6), (3,7). A dot product
+// with activations packed in the same pair order gives sum x * (1 + q/16).
+__device__ __forceinline__ void int4x8_to_bf16_pairs(uint32_t v, uint32_t out[4]) {
+    out[0] = ((v << 3) & 0x00780078u) | 0x3F803F80u;
+    out[1] = ((v >> 1) & 0x00780078u) | 0x3F803F80u;
+    out[2] = ((v >> 5) & 0x00780078u) | 0x3F803F80u;
+    out[3] = ((v >> 9) & 0x00780078u) | 0x3F803F80u;
+}
+
+// Repacks eight consecutive bf16 values (four dwords, natural order) into the
+// pair order (0,4), (1,5), (2,6), (3,7) used by int4x8_to_bf16_pairs.
+__device__ __forceinline__ void bf16x8_to_pair_order(const uint32_t in[4], uint32_t out[4]) {
+    // in[0] = (x1:x0), in[1] = (x3:x2), in[2] = (x5:x4), in[3] = (x7:x6)
+    out[0] = __builtin_amdgcn_perm(in[2], in[0], 0x05040100u);  // (x4:x0)
+    out[1] = __builtin_amdgcn_perm(in[2], in[0], 0x07060302u);  // (x5:x1)
+    out[2] = __builtin_amdgcn_perm(in[3], in[1], 0x05040100u);  // (x6:x2)
+    out[3] = __builtin_amdgcn_perm(in[3], in[1], 0x07060302u);  // (x7:x3)
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Unsigned key ordering fp32 logits: larger logit -> larger key; -0 equals +0;
+// NaN gets key 0, below every number.
+__device__ __forceinline__ uint32_t ordered_logit(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0u;
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace moe

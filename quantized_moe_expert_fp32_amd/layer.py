@@ -1,0 +1,122 @@
+"""Device-resident MoE layers and the per-step call sequence over the C ABI.
+
+torch allocates device memory and supplies the stream; every step of the layer
+(routing, dispatch, expert GEMV/GEMM, combine, RMSNorm) is a call into
+libmoe.so. Host arrays come in the canonical storage format documented in
+include/moe.h.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import moe
+
+DECODE_MAX_T = 16
+
+
+def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
+    """numpy array -> contiguous device tensor with the same bytes (uint16 -> int16)."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device)
+
+
+def bits_to_numpy(t: torch.Tensor) -> np.ndarray:
+    """int16 device tensor of bf16 bits -> numpy uint16."""
+    return t.cpu().numpy().view(np.uint16)
+
+
+def make_shape(s) -> moe.Shape:
+    """moe.Shape from any object with hidden/inter/n_experts/top_k/has_shared/router_fmt."""
+    return moe.Shape.make(s.hidden, s.inter, s.n_experts, s.top_k, s.has_shared, s.router_fmt)
+
+
+class DeviceLayer:
+    """One layer's packed expert buffer, packed router and optional logit bias on the GPU."""
+
+    def __init__(self, shape: moe.Shape, host_layer, device="cuda"):
+        self.shape = shape
+        self.device = device
+        nb = moe.moe_experts_packed_bytes(shape)
+        if nb == 0:
+            raise moe.MoeError(moe.moe_shape_check(shape), "moe_experts_packed_bytes")
+        self.experts = torch.empty(nb, dtype=torch.uint8, device=device)
+        src = {n: to_device(getattr(host_layer, n), device) for n in
+               ("q_gate", "s_gate", "b_gate", "q_up", "s_up", "b_up", "q_down", "s_down", "b_down")}
+        moe.moe_pack_experts(shape, src, self.experts)
+        self.router = torch.empty(moe.moe_router_packed_bytes(shape), dtype=torch.uint8, device=device)
+        if shape.router_fmt == moe.ROUTER_F32:
+            moe.moe_pack_router(shape, to_device(host_layer.router_f32, device), None, None, self.router)
+        else:
+            moe.moe_pack_router(shape, to_device(host_layer.router_q, device), to_device(host_layer.router_s, device),
+                                to_device(host_layer.router_b, device), self.router)
+        lb = getattr(host_layer, "logit_bias", None)
+        self.logit_bias = None if lb is None else to_device(lb.astype(np.float32), device)
+        torch.cuda.current_stream().synchronize()  # canonical copies may be freed after this
+        del src
+
+
+@dataclass
+class StepBuffers:
+    T: int
+    logits: torch.Tensor
+    ids: torch.Tensor
+    w: torch.Tensor
+    wsh: Optional[torch.Tensor]
+    ws: torch.Tensor
+    y: torch.Tensor
+    out: torch.Tensor
+
+
+def alloc_buffers(shape: moe.Shape, T: int, path: str, device="cuda") -> StepBuffers:
+    R = shape.n_experts + shape.has_shared
+    S = shape.slots
+    ws_bytes = (moe.moe_decode_workspace_bytes(shape, T) if path == "decode"
+                else moe.moe_prefill_workspace_bytes(shape, T))
+    return StepBuffers(
+        T=T,
+        logits=torch.empty((T, R), dtype=torch.float32, device=device),
+        ids=torch.empty((T, shape.top_k), dtype=torch.int32, device=device),
+        w=torch.empty((T, shape.top_k), dtype=torch.int16, device=device),
+        wsh=torch.empty((T,), dtype=torch.int16, device=device) if shape.has_shared else None,
+        ws=torch.empty(ws_bytes, dtype=torch.uint8, device=device),
+        y=torch.empty((T, S, shape.hidden), dtype=torch.float32, device=device),
+        out=torch.empty((T, shape.hidden), dtype=torch.int16, device=device),
+    )
+
+
+def pick_path(T: int) -> str:
+    return "decode" if T <= DECODE_MAX_T else "prefill"
+
+
+def layer_step(layer: DeviceLayer, x: torch.Tensor, buf: StepBuffers, path: Optional[str] = None,
+               residual: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None, stream=None):
+    """route -> experts (decode GEMV or prefill grouped GEMM) -> combine, all on one stream."""
+    sh, T = layer.shape, buf.T
+    path = path or pick_path(T)
+    moe.moe_route(sh, layer.router, layer.logit_bias, x, T, buf.logits, buf.ids, buf.w, buf.wsh, stream)
+    if path == "decode":
+        moe.moe_experts_decode(sh, layer.experts, x, T, buf.ids, buf.ws, buf.y, stream)
+    else:
+        moe.moe_experts_prefill(sh, layer.experts, x, T, buf.ids, buf.ws, buf.y, stream)
+    dst = buf.out if out is None else out
+    moe.moe_combine(sh, buf.y, buf.w, buf.wsh, T, residual, dst, stream)
+    return dst
+
+
+def stack_step(layers, x: torch.Tensor, xn: torch.Tensor, buf: StepBuffers, eps: float = 1e-6,
+               path: Optional[str] = None, stream=None, keep: Optional[list] = None):
+    """x <- bf16(x + MoE(bf16(RMSNorm(x)))) for every layer, in place on x."""
+    sh = layers[0].shape
+    for L in layers:
+        moe.moe_rmsnorm(sh.hidden, x, buf.T, eps, xn, stream)
+        layer_step(L, xn, buf, path, residual=x, out=x, stream=stream)
+        if keep is not None:
+            keep.append(x.clone())
+    return x

@@ -1,0 +1,113 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+that include/moe.h declares, and refuses bad arguments on the host before any
+launch (the 4-bit / group-64 check refuses other formats, as the Metal gate of
+TensorFold issue #931, "What I'd build", refuses 8-bit checkpoints)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def moe():
+    from quantized_moe_expert_fp32_amd import moe as m
+
+    return m
+
+
+def test_library_exports_every_declared_symbol(moe):
+    syms = _declared_symbols()
+    assert len(syms) >= 17
+    lib = ctypes.CDLL(moe.library_path())
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert set(syms) == set(moe.EXPORTS)
+
+
+def test_abi_version_and_strings(moe):
+    assert moe.moe_abi_version() == 1
+    lib = ctypes.CDLL(moe.library_path())
+    lib.moe_status_str.restype = ctypes.c_char_p
+    assert lib.moe_status_str(0) == b"ok"
+    assert lib.moe_status_str(-2) == b"unsupported shape or format"
+
+
+def _big(moe, **kw):
+    d = dict(hidden=2048, inter=512, n_experts=256, top_k=8, has_shared=1, router_fmt=moe.ROUTER_AFFINE8)
+    d.update(kw)
+    return moe.Shape.make(**d)
+
+
+def test_shape_check_refuses_other_formats(moe):
+    assert moe.moe_shape_check(_big(moe)) == moe.OK
+    assert moe.moe_shape_check(_big(moe, bits=8)) == moe.ERR_UNSUPPORTED
+    assert moe.moe_shape_check(_big(moe, bits=3)) == moe.ERR_UNSUPPORTED
+    assert moe.moe_shape_check(_big(moe, group=128)) == moe.ERR_UNSUPPORTED
+    assert moe.moe_shape_check(_big(moe, router_fmt=7)) == moe.ERR_UNSUPPORTED
+    assert moe.moe_shape_check(_big(moe, hidden=192)) == moe.ERR_UNSUPPORTED
+    assert moe.moe_shape_check(_big(moe, inter=4096)) == moe.ERR_UNSUPPORTED
+    assert moe.moe_shape_check(_big(moe, top_k=0)) == moe.ERR_INVALID_ARG
+    assert moe.moe_shape_check(_big(moe, top_k=17)) == moe.ERR_INVALID_ARG
+    assert moe.moe_shape_check(_big(moe, n_experts=4, top_k=5)) == moe.ERR_INVALID_ARG
+    assert moe.moe_shape_check(_big(moe, has_shared=2)) == moe.ERR_INVALID_ARG
+
+
+def test_sizes(moe):
+    sh = _big(moe)
+    assert moe.moe_experts_packed_bytes(sh) == 257 * 1_769_472
+    assert moe.moe_router_packed_bytes(sh) == 257 * 2048 + 257 * 32 * 4
+    assert moe.moe_decode_workspace_bytes(sh, 1) == 9 * 512 * 2 + (256 - (9 * 512 * 2) % 256) % 256
+    assert moe.moe_prefill_workspace_bytes(sh, 4096) > 4096 * 9 * 512 * 2
+    assert moe.moe_experts_packed_bytes(_big(moe, bits=8)) == 0
+
+
+def test_host_argument_checks_launch_nothing(moe):
+    """Each call fails validation on the host; the fake device pointers are never touched."""
+    sh = _big(moe)
+    P = 0x10000  # aligned, never dereferenced
+    byref = ctypes.byref
+    v = ctypes.c_void_p
+    # decode takes 1..16 rows
+    st = moe.raw_call("moe_experts_decode", byref(sh), v(P), v(P), 17, v(P), v(P), 1 << 20, v(P), None)
+    assert st == moe.ERR_INVALID_ARG
+    # workspace too small
+    st = moe.raw_call("moe_experts_decode", byref(sh), v(P), v(P), 4, v(P), v(P), 16, v(P), None)
+    assert st == moe.ERR_WORKSPACE
+    st = moe.raw_call("moe_experts_prefill", byref(sh), v(P), v(P), 512, v(P), v(P), 1024, v(P), None)
+    assert st == moe.ERR_WORKSPACE
+    # unaligned pointer
+    st = moe.raw_call("moe_experts_prefill", byref(sh), v(P + 4), v(P), 512, v(P), v(P), 1 << 30, v(P), None)
+    assert st == moe.ERR_INVALID_ARG
+    # T = 0
+    st = moe.raw_call("moe_route", byref(sh), v(P), None, v(P), 0, v(P), v(P), v(P), v(P), None)
+    assert st == moe.ERR_INVALID_ARG
+    # shared weight output required iff the layer has a shared expert
+    st = moe.raw_call("moe_route", byref(sh), v(P), None, v(P), 1, v(P), v(P), v(P), None, None)
+    assert st == moe.ERR_INVALID_ARG
+    st = moe.raw_call("moe_combine", byref(sh), v(P), v(P), None, 1, None, v(P), None)
+    assert st == moe.ERR_INVALID_ARG
+    # refused formats never reach a kernel
+    st = moe.raw_call("moe_route", byref(_big(moe, bits=8)), v(P), None, v(P), 1, v(P), v(P), v(P), v(P), None)
+    assert st == moe.ERR_UNSUPPORTED
+    # rmsnorm aliasing is refused
+    st = moe.raw_call("moe_rmsnorm", 2048, v(P), 1, ctypes.c_float(1e-6), v(P), None)
+    assert st == moe.ERR_INVALID_ARG
+
+
+def test_last_error_message(moe):
+    sh = _big(moe, bits=8)
+    st = moe.raw_call("moe_route", ctypes.byref(sh), None, None, None, 1, None, None, None, None, None)
+    assert st == moe.ERR_UNSUPPORTED
+    from quantized_moe_expert_fp32_amd.moe import _lib
+
+    assert b"4-bit" in _lib.moe_last_error()

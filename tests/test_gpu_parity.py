@@ -1,0 +1,436 @@
+"""GPU parity: every stage of the HIP path (called through the C ABI) against the
+FP64 oracle on the same seeded inputs.
+
+Bars (routing contract of TensorFold issue #931, "What I'd build"; staged
+reference per projection class from its "Gate" section):
+  * integer work (picks, dispatch) bit-exact; end-to-end picks exempt a token whose
+    top k+1 oracle logits hold an adjacent gap below 1e-5 (counted);
+  * pick and shared weights bit-exact when computed from the same fp32 logits;
+  * logits within 1 fp32 ulp of the oracle's fp32 rounding of the fp64 sum;
+  * layer outputs: |gpu - ref| <= max(2 bf16 ulp(ref), 1e-2 |ref|, 1e-2 rms(ref row)).
+"""
+
+import functools
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from quantized_moe_expert_fp32_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------ helpers
+
+@functools.lru_cache(maxsize=None)
+def case(name, T=None):
+    return synth.make_case(name, T=T)
+
+
+def _L():
+    from quantized_moe_expert_fp32_amd import layer as L
+
+    return L
+
+
+def dev_layer(gpu, c, idx=0, shape=None):
+    L = _L()
+    sh = shape or L.make_shape(c.shape)
+    return L.DeviceLayer(sh, c.layers[idx])
+
+
+def run_path(gpu, dl, x_np, path):
+    """route -> experts -> combine on the GPU; returns numpy copies of every stage."""
+    L = _L()
+    T = x_np.shape[0]
+    buf = L.alloc_buffers(dl.shape, T, path)
+    x = L.to_device(x_np)
+    L.layer_step(dl, x, buf, path)
+    torch.cuda.synchronize()
+    return dict(logits=buf.logits.cpu().numpy(), ids=buf.ids.cpu().numpy(), w=L.bits_to_numpy(buf.w),
+                wsh=None if buf.wsh is None else L.bits_to_numpy(buf.wsh), y=buf.y.cpu().numpy(),
+                out=L.bits_to_numpy(buf.out))
+
+
+def out_tolerance_check(gpu_bits, ref_bits, rows=None):
+    g = O.bf16_to_f64(gpu_bits)
+    r = O.bf16_to_f64(ref_bits)
+    if rows is not None:
+        g, r = g[rows], r[rows]
+    err = np.abs(g - r)
+    ulp = O.bf16_ulp(r)
+    rms = np.sqrt(np.mean(r * r, axis=1, keepdims=True))
+    tol = np.maximum(np.maximum(2 * ulp, 1e-2 * np.abs(r)), 1e-2 * rms)
+    bad = err > tol
+    stats = dict(max_ulp=float((err / ulp).max()), frac_gt_2ulp=float((err > 2 * ulp).mean()),
+                 frac_exact=float((err == 0).mean()), n_bad=int(bad.sum()))
+    assert stats["n_bad"] == 0, stats
+    return stats
+
+
+def check_logits(gpu_logits, ref_logits):
+    g = gpu_logits.astype(np.float32)
+    r = ref_logits.astype(np.float32)
+    gi = g.view(np.int32).astype(np.int64)
+    ri = r.view(np.int32).astype(np.int64)
+    diff = np.abs(gi - ri)
+    assert diff.max() <= 1, diff.max()
+    return float((diff == 0).mean())
+
+
+def check_picks(gpu_ids, ref_logits, k, E):
+    ref_ids = O.topk(ref_logits[:, :E], k)
+    tie = O.near_tie_tokens(ref_logits[:, :E], k)
+    mism = (gpu_ids != ref_ids).any(axis=1)
+    assert not (mism & ~tie).any(), np.nonzero(mism & ~tie)
+    return int(tie.sum()), int((mism & tie).sum())
+
+
+def staged_route_check(gpu, res, E, k, has_shared=True):
+    """Selection step from the GPU's own logits: ids, weights and shared weight bit-exact."""
+    lg = res["logits"]
+    ids = O.topk(lg[:, :E], k)
+    assert np.array_equal(res["ids"], ids)
+    assert np.array_equal(res["w"], O.pick_weights(lg[:, :E], ids))
+    if has_shared:
+        assert np.array_equal(res["wsh"], O.shared_weight(lg[:, E]))
+
+
+def staged_layer_check(res, x_np, host_layer, E, has_shared=True):
+    """Oracle experts and combine fed the GPU's picks and weights."""
+    y, _ = O.expert_outputs(x_np, res["ids"], host_layer, E, has_shared)
+    out = O.combine(y, res["w"], res["wsh"] if has_shared else None)
+    return out_tolerance_check(res["out"], out), y
+
+
+# ------------------------------------------------------------------ packing
+
+def test_pack_layout_matches_header(gpu):
+    c = case("tiny")
+    dl = dev_layer(gpu, c)
+    L0 = c.layers[0]
+    p = dl.experts.cpu().numpy()
+    H, I, M = 256, 64, 17
+    stride = p.size // M
+    for m in (0, 5, 16):
+        b = p[m * stride:(m + 1) * stride]
+        o = 0
+        for q in (L0.q_gate[m], L0.q_up[m], L0.q_down[m]):
+            assert np.array_equal(b[o:o + q.size], q.reshape(-1))
+            o += q.size
+        for s, bb in ((L0.s_gate[m], L0.b_gate[m]), (L0.s_up[m], L0.b_up[m]), (L0.s_down[m], L0.b_down[m])):
+            sb = b[o:o + 4 * s.size].view(np.uint32)
+            assert np.array_equal(sb, s.reshape(-1).astype(np.uint32) | (bb.reshape(-1).astype(np.uint32) << 16))
+            o += 4 * s.size
+        assert o == stride
+    r = dl.router.cpu().numpy().view(np.float32).reshape(17, H)
+    assert np.array_equal(r, L0.router_f32)
+
+
+# ------------------------------------------------------------------ a2 selection
+
+def _route_from_logits(gpu, logits, E, k, has_shared=1):
+    sh = gpu.Shape.make(64, 64, E, k, has_shared, gpu.ROUTER_F32)
+    T = logits.shape[0]
+    lg = torch.from_numpy(np.ascontiguousarray(logits, dtype=np.float32)).cuda()
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.int16, device="cuda")
+    wsh = torch.empty((T,), dtype=torch.int16, device="cuda") if has_shared else None
+    gpu.moe_route_from_logits(sh, lg, T, ids, w, wsh)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), w.cpu().numpy().view(np.uint16), None if wsh is None else wsh.cpu().numpy().view(
+        np.uint16)
+
+
+@pytest.mark.parametrize("k", [1, 2, 8])
+def test_topk_bruteforce_binary_E16(gpu, k):
+    v = np.array(list(itertools.product([0.0, 1.0], repeat=16)), dtype=np.float32)
+    logits = np.concatenate([v, np.zeros((len(v), 1), np.float32)], axis=1)
+    ids, w, wsh = _route_from_logits(gpu, logits, 16, k)
+    ref = O.topk(v, k)
+    assert np.array_equal(ids, ref)
+    assert np.array_equal(w, O.pick_weights(v, ref))
+    assert (wsh == 0x3F00).all()
+
+
+@pytest.mark.parametrize("k", [1, 3, 5])
+def test_topk_bruteforce_ternary_E10(gpu, k):
+    v = np.array(list(itertools.product([-1.0, 0.0, 1.0], repeat=10)), dtype=np.float32)
+    logits = np.concatenate([v, np.ones((len(v), 1), np.float32)], axis=1)
+    ids, w, wsh = _route_from_logits(gpu, logits, 10, k)
+    ref = O.topk(v, k)
+    assert np.array_equal(ids, ref)
+    assert np.array_equal(w, O.pick_weights(v, ref))
+
+
+def test_topk_special_values(gpu):
+    l = np.array([[-0.0, 0.0, -1.0, np.nan, 0.0],
+                  [0.0, -0.0, np.nan, -np.inf, 0.0],
+                  [np.nan, np.nan, -np.inf, -np.inf, 0.0],
+                  [np.nan, 1e-30, -1e-30, 0.0, 0.0],
+                  [3e38, -3e38, 1.0, 2.0, 0.0]], dtype=np.float32)
+    ids, w, _ = _route_from_logits(gpu, l, 4, 3)
+    assert np.array_equal(ids, O.topk(l[:, :4], 3))
+    assert np.array_equal(w, O.pick_weights(l[:, :4], ids))
+
+
+def test_shared_weight_all_bf16_patterns(gpu):
+    pats = np.arange(65536, dtype=np.uint32)
+    g = (pats << 16).view(np.float32)
+    logits = np.zeros((65536, 5), np.float32)
+    logits[:, :4] = [1, 2, 3, 4]
+    logits[:, 4] = g
+    _, _, wsh = _route_from_logits(gpu, logits, 4, 2)
+    assert np.array_equal(wsh, O.shared_weight(g))
+
+
+def test_selection_random_logits_with_ties(gpu):
+    rng = np.random.default_rng(31)
+    T, E, k = 4096, 256, 8
+    lg = rng.normal(0, 1, size=(T, E + 1)).astype(np.float32)
+    # force ties: quantise a third of the rows to a coarse grid
+    lg[: T // 3] = np.round(lg[: T // 3] * 4) / 4
+    ids, w, wsh = _route_from_logits(gpu, lg, E, k)
+    ref = O.topk(lg[:, :E], k)
+    assert np.array_equal(ids, ref)
+    assert np.array_equal(w, O.pick_weights(lg[:, :E], ref))
+    assert np.array_equal(wsh, O.shared_weight(lg[:, E]))
+
+
+# ------------------------------------------------------------------ a1 logits + whole layer
+
+@pytest.mark.parametrize("name,T", [("tiny", None), ("decode", None), ("decode", 16), ("prefill512", None)])
+def test_router_logits_and_picks(gpu, name, T):
+    c = case(name, T)
+    dl = dev_layer(gpu, c)
+    res = run_path(gpu, dl, c.x, "decode" if c.T <= 16 else "prefill")
+    W = O.router_matrix(c.layers[0])
+    E = c.shape.n_experts
+    ref = O.router_logits(c.x, W, c.layers[0].logit_bias, E)
+    exact = check_logits(res["logits"], ref)
+    assert exact > 0.999
+    check_picks(res["ids"], ref, c.shape.top_k, E)
+    staged_route_check(gpu, res, E, c.shape.top_k)
+
+
+@pytest.mark.parametrize("path", ["decode", "prefill"])
+def test_tiny_layer_end_to_end(gpu, path):
+    c = case("tiny")
+    dl = dev_layer(gpu, c)
+    res = run_path(gpu, dl, c.x, path)
+    st = O.layer_forward(c.x, c.layers[0], 2)
+    assert np.array_equal(res["ids"], st["ids"])
+    assert np.array_equal(res["w"], st["w"]) and np.array_equal(res["wsh"], st["wsh"])
+    out_tolerance_check(res["out"], st["out"])
+    staged_layer_check(res, c.x, c.layers[0], 16)
+
+
+def test_decode_T1_end_to_end(gpu):
+    c = case("decode")
+    dl = dev_layer(gpu, c)
+    res = run_path(gpu, dl, c.x, "decode")
+    st = O.layer_forward(c.x, c.layers[0], 8)
+    check_picks(res["ids"], st["logits"], 8, 256)
+    stats, y = staged_layer_check(res, c.x, c.layers[0], 256)
+    if np.array_equal(res["ids"], st["ids"]):
+        out_tolerance_check(res["out"], st["out"])
+    # fp32 slot outputs against the float64 ones
+    rel = np.abs(res["y"] - y) / (np.sqrt(np.mean(y * y, axis=2, keepdims=True)))
+    assert rel.max() < 1e-2
+
+
+def test_decode_batch_invariance(gpu):
+    """16 rows in one call equal 16 one-row calls, bit for bit (row windows of 1..16)."""
+    c = case("decode")
+    dl = dev_layer(gpu, c)
+    x = synth.random_x(101, 16, 2048)
+    full = run_path(gpu, dl, x, "decode")
+    for t in range(16):
+        one = run_path(gpu, dl, x[t:t + 1], "decode")
+        assert np.array_equal(one["ids"][0], full["ids"][t])
+        assert np.array_equal(one["y"][0], full["y"][t])
+        assert np.array_equal(one["out"][0], full["out"][t])
+    for T in (3, 7):
+        part = run_path(gpu, dl, x[:T], "decode")
+        assert np.array_equal(part["out"], full["out"][:T])
+
+
+def test_decode_vs_prefill_same_tokens(gpu):
+    c = case("decode")
+    dl = dev_layer(gpu, c)
+    x = synth.random_x(102, 16, 2048)
+    a = run_path(gpu, dl, x, "decode")
+    b = run_path(gpu, dl, x, "prefill")
+    assert np.array_equal(a["ids"], b["ids"]) and np.array_equal(a["w"], b["w"])
+    rms = np.sqrt(np.mean(a["y"] ** 2, axis=2, keepdims=True))
+    assert (np.abs(a["y"] - b["y"]) / rms).max() < 1e-3
+    out_tolerance_check(b["out"], a["out"])
+
+
+@pytest.mark.parametrize("name", ["prefill512", "prefill4096"])
+def test_prefill_full_size(gpu, name):
+    c = case(name)
+    dl = dev_layer(gpu, c)
+    res = run_path(gpu, dl, c.x, "prefill")
+    E, k = 256, 8
+    W = O.router_matrix(c.layers[0])
+    ref_logits = O.router_logits(c.x, W, c.layers[0].logit_bias, E)
+    check_logits(res["logits"], ref_logits)
+    n_tie, n_flip = check_picks(res["ids"], ref_logits, k, E)
+    print(name, "near-tie tokens", n_tie, "flipped among them", n_flip)
+    staged_route_check(gpu, res, E, k)
+    stats, _ = staged_layer_check(res, c.x, c.layers[0], E)
+    print(name, stats)
+
+
+@pytest.mark.parametrize("T", [1, 2, 17, 63, 64, 65, 130, 1000])
+def test_prefill_ragged_T(gpu, T):
+    c = case("decode")
+    dl = dev_layer(gpu, c)
+    x = synth.random_x(200 + T, T, 2048)
+    res = run_path(gpu, dl, x, "prefill")
+    staged_route_check(gpu, res, 256, 8)
+    staged_layer_check(res, x, c.layers[0], 256)
+
+
+def test_dispatch_matches_oracle(gpu):
+    c = case("prefill4096")
+    rng = np.random.default_rng(5)
+    T, E, k = 3000, 256, 8
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    ids[:1000, 0] = 7  # a heavily loaded expert
+    sh = gpu.Shape.make(2048, 512, E, k, 1, gpu.ROUTER_AFFINE8)
+    d_ids = torch.from_numpy(ids).cuda()
+    counts = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 2, dtype=torch.int32, device="cuda")
+    order = torch.empty(T * (k + 1), dtype=torch.int32, device="cuda")
+    gpu.moe_dispatch(sh, d_ids, T, counts, offsets, order)
+    torch.cuda.synchronize()
+    rc, ro, rord = O.dispatch(ids, E, True)
+    assert np.array_equal(counts.cpu().numpy(), rc)
+    assert np.array_equal(offsets.cpu().numpy(), ro)
+    go = order.cpu().numpy()
+    for e in range(E + 1):
+        seg = slice(ro[e], ro[e + 1])
+        assert np.array_equal(np.sort(go[seg]), rord[seg])
+    del c
+
+
+def test_invalid_ids_give_zero_rows(gpu):
+    c = case("tiny")
+    dl = dev_layer(gpu, c)
+    L = _L()
+    T = 4
+    for path in ("decode", "prefill"):
+        buf = L.alloc_buffers(dl.shape, T, path)
+        x = L.to_device(c.x)
+        ids = torch.tensor([[1, 99], [3, -1], [0, 2], [5, 6]], dtype=torch.int32, device="cuda")
+        buf.y.fill_(7.0)
+        if path == "decode":
+            dl_mod = _moe()
+            dl_mod.moe_experts_decode(dl.shape, dl.experts, x, T, ids, buf.ws, buf.y)
+        else:
+            _moe().moe_experts_prefill(dl.shape, dl.experts, x, T, ids, buf.ws, buf.y)
+        torch.cuda.synchronize()
+        y = buf.y.cpu().numpy()
+        assert (y[0, 1] == 0).all() and (y[1, 1] == 0).all()
+        ref, _ = O.expert_outputs(c.x[2:3], ids.cpu().numpy()[2:3], c.layers[0], 16, True)
+        rms = np.sqrt(np.mean(ref[0] ** 2, axis=1, keepdims=True))
+        assert (np.abs(y[2] - ref[0]) / rms).max() < 1e-3
+
+
+def _moe():
+    from quantized_moe_expert_fp32_amd import moe
+
+    return moe
+
+
+def test_no_shared_expert_variant(gpu):
+    from types import SimpleNamespace
+
+    c = case("tiny")
+    L0 = c.layers[0]
+    E = 16
+    NL = SimpleNamespace(router_f32=L0.router_f32[:E].copy(), logit_bias=None,
+                         **{n: getattr(L0, n)[:E].copy() for n in
+                            ("q_gate", "s_gate", "b_gate", "q_up", "s_up", "b_up", "q_down", "s_down", "b_down")})
+    sh = gpu.Shape.make(256, 64, E, 2, 0, gpu.ROUTER_F32)
+    dl = _L().DeviceLayer(sh, NL)
+    for path in ("decode", "prefill"):
+        res = run_path(gpu, dl, c.x, path)
+        st = O.layer_forward(c.x, NL, 2, has_shared=False)
+        assert np.array_equal(res["ids"], st["ids"]) and np.array_equal(res["w"], st["w"])
+        out_tolerance_check(res["out"], st["out"])
+
+
+# ------------------------------------------------------------------ a6 combine, a7 stack glue
+
+def test_combine_rounds_once_and_residual(gpu):
+    rng = np.random.default_rng(8)
+    T, H, k = 33, 256, 2
+    sh = gpu.Shape.make(H, 64, 16, k, 1, gpu.ROUTER_F32)
+    y = rng.normal(0, 2, size=(T, k + 1, H)).astype(np.float32)
+    y[0, :, :] = 0
+    y[0, 0, :] = 1.0
+    y[0, 1, :] = 1.0087890625
+    w = synth._to_bf16_bits(rng.uniform(0, 1, size=(T, k)).astype(np.float32))
+    w[0] = [0x3F00, 0x3F00]
+    wsh = synth._to_bf16_bits(rng.uniform(0, 1, size=(T,)).astype(np.float32))
+    wsh[0] = 0
+    res = synth._to_bf16_bits(rng.normal(0, 1, size=(T, H)).astype(np.float32))
+    L = _L()
+    dy, dw, dws, dres = (torch.from_numpy(y).cuda(), L.to_device(w), L.to_device(wsh), L.to_device(res))
+    out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    gpu.moe_combine(sh, dy, dw, dws, T, None, out)
+    torch.cuda.synchronize()
+    o = L.bits_to_numpy(out)
+    ref = O.combine(y.astype(np.float64), w, wsh)
+    assert (o[0] == 0x3F81).all()  # rounded once: 1.0078125, not 1.0
+    out_tolerance_check(o, ref)
+    assert ((o != ref).mean()) < 1e-3
+    gpu.moe_combine(sh, dy, dw, dws, T, dres, dres)  # residual aliasing out
+    torch.cuda.synchronize()
+    assert np.array_equal(L.bits_to_numpy(dres), O.residual_bf16(res, o))
+
+
+def test_rmsnorm(gpu):
+    L = _L()
+    x = synth.random_x(9, 40, 2048)
+    x[0] = 0x3F80
+    dx = L.to_device(x)
+    out = torch.empty_like(dx)
+    gpu.moe_rmsnorm(2048, dx, 40, 1e-6, out)
+    torch.cuda.synchronize()
+    o = L.bits_to_numpy(out)
+    ref = O.rmsnorm_bf16(x, 1e-6)
+    assert (o[0] == 0x3F80).all()
+    d = np.abs(o.astype(np.int32) - ref.astype(np.int32))
+    assert d.max() <= 1 and (d > 0).mean() < 1e-3
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_stack_layers_staged(gpu, T):
+    """Three stacked layers: each layer's GPU output against the oracle layer fed the
+    GPU's own input to that layer (exact staged layer references)."""
+    L = _L()
+    c = synth.make_case("stack", T=T, n_layers=3)
+    sh = L.make_shape(c.shape)
+    layers = [L.DeviceLayer(sh, hl) for hl in c.layers]
+    x = L.to_device(c.x)
+    xn = torch.empty_like(x)
+    buf = L.alloc_buffers(sh, T, "decode")
+    keep = []
+    L.stack_step(layers, x, xn, buf, keep=keep)
+    torch.cuda.synchronize()
+    xs = [c.x] + [L.bits_to_numpy(k) for k in keep]
+    for l in range(3):
+        xin = xs[l]
+        xnorm = O.rmsnorm_bf16(xin)
+        st = O.layer_forward(xnorm, c.layers[l], 8)
+        ref = O.residual_bf16(xin, st["out"])
+        tie = O.near_tie_tokens(st["logits"][:, :256], 8)
+        rows = ~tie
+        out_tolerance_check(xs[l + 1], ref, rows=rows)
