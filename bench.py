@@ -181,7 +181,7 @@ def main():
             xin = xs[(j % xs.shape[0]):(j % xs.shape[0]) + 1] if wl == "decode" else xs
             moe.moe_route(shape, dl.router, dl.logit_bias, xin, T, buf.logits, buf.ids, buf.w, buf.wsh)
             starts[j].record(stream)
-            if path == "decode":
+            if path in ("decode", "fused"):
                 moe.moe_experts_decode(shape, dl.experts, xin, T, buf.ids, buf.ws, buf.y)
             else:
                 moe.moe_experts_prefill(shape, dl.experts, xin, T, buf.ids, buf.ws, buf.y)
@@ -198,7 +198,7 @@ def main():
     distinct = len(set(ids_np.reshape(-1).tolist())) + shape.has_shared
     alg_bytes = distinct * EXPERT_BYTES + T * 2048 * 2
     flops = T * S * 3 * 2 * 2048 * 512
-    if path == "decode":
+    if path in ("decode", "fused"):
         roof = dict(bound="hbm", achieved=alg_bytes / (expert_us * 1e-6) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
     else:
         if wl == "prefill4096":
@@ -209,7 +209,7 @@ def main():
                         unit="GB/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = None
-    roof["kernel"] = "experts stage: " + ("decode_gateup_kernel + decode_down_kernel" if path == "decode"
+    roof["kernel"] = "experts stage: " + ("decode_gateup_kernel + decode_down_kernel" if path != "prefill"
                                           else "dispatch_kernel + gateup_gemm_kernel + down_gemm_kernel")
     roof["avg_us"] = expert_us
     roof["alg_bytes_per_launch"] = int(alg_bytes)

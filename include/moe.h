@@ -153,12 +153,28 @@ moe_status moe_route_from_logits(const moe_shape* shape, const float* logits, in
  * e (ids[t,s], or the shared expert for s == k):
  *   h = bf16(silu(x Wg_e^T) * (x Wu_e^T))   (SwiGLU; the bf16 rounding is a reading)
  *   y[t][s][:] = h Wd_e^T                   (fp32, not rounded to bf16: [P3-build])
- * ws: device scratch of moe_decode_workspace_bytes(shape, T) bytes (holds h).
- * Each row's result does not depend on T or on the other rows. */
+ * ws: device scratch of moe_decode_workspace_bytes(shape, T) bytes (holds h and,
+ * for moe_decode_layer, one counter word). Each row's result does not depend on T
+ * or on the other rows. Expert ids outside [0, E) give zero y rows. */
 size_t moe_decode_workspace_bytes(const moe_shape* shape, int32_t T);
 moe_status moe_experts_decode(const moe_shape* shape, const void* experts_packed,
                               const uint16_t* x, int32_t T, const int32_t* ids, void* ws,
                               size_t ws_bytes, float* y, void* stream);
+
+/* The whole decode layer (1 <= T <= 16) in three launches: router logits with
+ * the selection done by the last workgroup to finish, the gate/up GEMV with
+ * SwiGLU, and the down GEMV with the combine (same arithmetic as moe_route,
+ * moe_experts_decode and moe_combine, so the outputs are bit-identical to those
+ * three calls). Outputs: logits, ids, w, w_shared as moe_route; y [T][S][H] fp32
+ * or NULL; out [T][H] bf16 (bf16(residual + out) if residual != NULL; residual
+ * may alias out). ws must be zero-filled before its first use with this call;
+ * every call leaves its counter word at zero again. Calls that share a ws must
+ * not overlap in time. [P3-build], [P1-phase]. */
+moe_status moe_decode_layer(const moe_shape* shape, const void* router_packed,
+                            const float* logit_bias, const void* experts_packed,
+                            const uint16_t* x, int32_t T, void* ws, size_t ws_bytes,
+                            float* logits, int32_t* ids, uint16_t* w, uint16_t* w_shared,
+                            float* y, const uint16_t* residual, uint16_t* out, void* stream);
 
 /* ---------------------------------------------------------------- a3: dispatch
  * Histogram and expert-sorted order of the T*S picks ([P1-phase] Phase 9b:

@@ -77,7 +77,7 @@ class StepBuffers:
 def alloc_buffers(shape: moe.Shape, T: int, path: str, device="cuda") -> StepBuffers:
     R = shape.n_experts + shape.has_shared
     S = shape.slots
-    ws_bytes = (moe.moe_decode_workspace_bytes(shape, T) if path == "decode"
+    ws_bytes = (moe.moe_decode_workspace_bytes(shape, T) if path in ("decode", "fused")
                 else moe.moe_prefill_workspace_bytes(shape, T))
     return StepBuffers(
         T=T,
@@ -85,27 +85,33 @@ def alloc_buffers(shape: moe.Shape, T: int, path: str, device="cuda") -> StepBuf
         ids=torch.empty((T, shape.top_k), dtype=torch.int32, device=device),
         w=torch.empty((T, shape.top_k), dtype=torch.int16, device=device),
         wsh=torch.empty((T,), dtype=torch.int16, device=device) if shape.has_shared else None,
-        ws=torch.empty(ws_bytes, dtype=torch.uint8, device=device),
+        ws=torch.zeros(ws_bytes, dtype=torch.uint8, device=device),
         y=torch.empty((T, S, shape.hidden), dtype=torch.float32, device=device),
         out=torch.empty((T, shape.hidden), dtype=torch.int16, device=device),
     )
 
 
 def pick_path(T: int) -> str:
-    return "decode" if T <= DECODE_MAX_T else "prefill"
+    return "fused" if T <= DECODE_MAX_T else "prefill"
 
 
 def layer_step(layer: DeviceLayer, x: torch.Tensor, buf: StepBuffers, path: Optional[str] = None,
                residual: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None, stream=None):
-    """route -> experts (decode GEMV or prefill grouped GEMM) -> combine, all on one stream."""
+    """One layer on one stream. path "fused" (T <= 16): moe_decode_layer (three launches);
+    "decode" / "prefill": moe_route, then moe_experts_decode or moe_experts_prefill, then
+    moe_combine."""
     sh, T = layer.shape, buf.T
     path = path or pick_path(T)
+    dst = buf.out if out is None else out
+    if path == "fused":
+        moe.moe_decode_layer(sh, layer.router, layer.logit_bias, layer.experts, x, T, buf.ws, buf.logits, buf.ids,
+                             buf.w, buf.wsh, buf.y, residual, dst, stream)
+        return dst
     moe.moe_route(sh, layer.router, layer.logit_bias, x, T, buf.logits, buf.ids, buf.w, buf.wsh, stream)
     if path == "decode":
         moe.moe_experts_decode(sh, layer.experts, x, T, buf.ids, buf.ws, buf.y, stream)
     else:
         moe.moe_experts_prefill(sh, layer.experts, x, T, buf.ids, buf.ws, buf.y, stream)
-    dst = buf.out if out is None else out
     moe.moe_combine(sh, buf.y, buf.w, buf.wsh, T, residual, dst, stream)
     return dst
 

@@ -81,6 +81,8 @@ _lib.moe_decode_workspace_bytes.restype = _SZ
 _lib.moe_decode_workspace_bytes.argtypes = [_S, _I32]
 _lib.moe_experts_decode.restype = _I32
 _lib.moe_experts_decode.argtypes = [_S, _P, _P, _I32, _P, _P, _SZ, _P, _P]
+_lib.moe_decode_layer.restype = _I32
+_lib.moe_decode_layer.argtypes = [_S, _P, _P, _P, _P, _I32, _P, _SZ, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.moe_dispatch.restype = _I32
 _lib.moe_dispatch.argtypes = [_S, _P, _I32, _P, _P, _P, _P]
 _lib.moe_prefill_workspace_bytes.restype = _SZ
@@ -94,7 +96,7 @@ _lib.moe_rmsnorm.argtypes = [_I32, _P, _I32, ctypes.c_float, _P, _P]
 
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_last_error", "moe_shape_check",
            "moe_experts_packed_bytes", "moe_pack_experts", "moe_router_packed_bytes", "moe_pack_router",
-           "moe_route", "moe_route_from_logits", "moe_decode_workspace_bytes", "moe_experts_decode",
+           "moe_route", "moe_route_from_logits", "moe_decode_workspace_bytes", "moe_experts_decode", "moe_decode_layer",
            "moe_dispatch", "moe_prefill_workspace_bytes", "moe_experts_prefill", "moe_combine", "moe_rmsnorm")
 
 
@@ -177,6 +179,14 @@ def moe_route_from_logits(shape, logits, T, ids, w, w_shared, stream=None):
 def moe_experts_decode(shape, experts_packed, x, T, ids, ws, y, stream=None):
     _check(_lib.moe_experts_decode(ctypes.byref(shape), _ptr(experts_packed), _ptr(x), T, _ptr(ids), _ptr(ws),
                                    _nbytes(ws), _ptr(y), _stream(stream)), "moe_experts_decode")
+
+
+def moe_decode_layer(shape, router_packed, logit_bias, experts_packed, x, T, ws, logits, ids, w, w_shared, y,
+                     residual, out, stream=None):
+    _check(_lib.moe_decode_layer(ctypes.byref(shape), _ptr(router_packed), _ptr(logit_bias), _ptr(experts_packed),
+                                 _ptr(x), T, _ptr(ws), _nbytes(ws), _ptr(logits), _ptr(ids), _ptr(w),
+                                 _ptr(w_shared), _ptr(y), _ptr(residual), _ptr(out), _stream(stream)),
+           "moe_decode_layer")
 
 
 def moe_dispatch(shape, ids, T, counts, offsets, order, stream=None):

@@ -258,6 +258,37 @@ def test_decode_batch_invariance(gpu):
         assert np.array_equal(part["out"], full["out"][:T])
 
 
+@pytest.mark.parametrize("T", [1, 5, 16])
+def test_fused_decode_layer_matches_staged_calls(gpu, T):
+    """moe_decode_layer (three launches) gives bit-identical outputs to moe_route +
+    moe_experts_decode + moe_combine, and the oracle bar end to end."""
+    c = case("decode")
+    dl = dev_layer(gpu, c)
+    x = synth.random_x(300 + T, T, 2048)
+    a = run_path(gpu, dl, x, "decode")
+    b = run_path(gpu, dl, x, "fused")
+    b2 = run_path(gpu, dl, x, "fused")  # the counter word was left at zero
+    for key in ("logits", "ids", "w", "wsh", "y", "out"):
+        assert np.array_equal(a[key], b[key]), key
+        assert np.array_equal(b[key], b2[key]), key
+    staged_route_check(gpu, b, 256, 8)
+    staged_layer_check(b, x, c.layers[0], 256)
+
+
+def test_fused_decode_residual_alias(gpu):
+    L = _L()
+    c = case("decode")
+    dl = dev_layer(gpu, c)
+    x = synth.random_x(400, 4, 2048)
+    buf = L.alloc_buffers(dl.shape, 4, "fused")
+    dx = L.to_device(x)
+    res = dx.clone()
+    L.layer_step(dl, dx, buf, "fused", residual=res, out=res)
+    torch.cuda.synchronize()
+    plain = run_path(gpu, dl, x, "fused")
+    assert np.array_equal(L.bits_to_numpy(res), O.residual_bf16(x, plain["out"]))
+
+
 def test_decode_vs_prefill_same_tokens(gpu):
     c = case("decode")
     dl = dev_layer(gpu, c)
@@ -265,8 +296,12 @@ def test_decode_vs_prefill_same_tokens(gpu):
     a = run_path(gpu, dl, x, "decode")
     b = run_path(gpu, dl, x, "prefill")
     assert np.array_equal(a["ids"], b["ids"]) and np.array_equal(a["w"], b["w"])
+    # fp32 summation orders differ; where a bf16 rounding of h flips between the two
+    # paths, a slot moves by about one bf16 step of h times the down weights
     rms = np.sqrt(np.mean(a["y"] ** 2, axis=2, keepdims=True))
-    assert (np.abs(a["y"] - b["y"]) / rms).max() < 1e-3
+    rel = (np.abs(a["y"] - b["y"]) / rms).max(axis=2)
+    assert rel.max() < 1e-2
+    assert (rel > 1e-4).mean() < 0.25
     out_tolerance_check(b["out"], a["out"])
 
 
