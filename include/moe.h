@@ -161,15 +161,19 @@ moe_status moe_experts_decode(const moe_shape* shape, const void* experts_packed
                               const uint16_t* x, int32_t T, const int32_t* ids, void* ws,
                               size_t ws_bytes, float* y, void* stream);
 
-/* The whole decode layer (1 <= T <= 16) in three launches: router logits with
- * the selection done by the last workgroup to finish, the gate/up GEMV with
- * SwiGLU, and the down GEMV with the combine (same arithmetic as moe_route,
- * moe_experts_decode and moe_combine, so the outputs are bit-identical to those
- * three calls). Outputs: logits, ids, w, w_shared as moe_route; y [T][S][H] fp32
+/* The whole decode layer (1 <= T <= 16) in one launch: router logits, selection,
+ * the gate/up GEMV with SwiGLU, and the down GEMV with the combine (same
+ * arithmetic as moe_route, moe_experts_decode and moe_combine, so the outputs are
+ * bit-identical to those three calls). Outputs: logits, ids, w, w_shared as moe_route; y [T][S][H] fp32
  * or NULL; out [T][H] bf16 (bf16(residual + out) if residual != NULL; residual
- * may alias out). ws must be zero-filled before its first use with this call;
- * every call leaves its counter word at zero again. Calls that share a ws must
- * not overlap in time. [P3-build], [P1-phase]. */
+ * may alias out). One persistent launch (at most one workgroup per compute unit,
+ * all resident): workgroups hand data to each other through words of ws tagged
+ * with a per-launch epoch. ws must be zero-filled before its first use with this
+ * call and is then ready for every later call without clearing; calls that share
+ * a ws must not overlap in time, and the launch must not share the GPU with work
+ * that keeps its workgroups from being resident (its waits are bounded: on a
+ * timeout it sets an error word in ws and its outputs are undefined).
+ * [P3-build], [P1-phase]. */
 moe_status moe_decode_layer(const moe_shape* shape, const void* router_packed,
                             const float* logit_bias, const void* experts_packed,
                             const uint16_t* x, int32_t T, void* ws, size_t ws_bytes,

@@ -3,9 +3,9 @@
 // issue #931, "What I'd build"). Expert gate/up pair with SwiGLU, then down.
 //
 // Data movement: every weight row is streamed once with 16-byte loads; a
-// wavefront covers a row with consecutive lanes (one 1 KiB line per load for a
-// 2048-wide row). Each lane keeps its slice of the activation row in registers
-// for the whole kernel, so the only HBM traffic is the weights.
+// wavefront covers a 2048-wide int4 row with one 1 KiB load; every weight load of
+// a work item is issued before the first is consumed. Each lane keeps its slice
+// of the activation row in registers, so the HBM traffic is the weights.
 //
 // Arithmetic (exact weights): a group's weights are scale*q + bias. A lane's 32
 // activations x meet the 32 nibbles q of the same group through
@@ -13,7 +13,10 @@
 // where 1 + q/16 is exactly a bf16 whose mantissa is q (one shift and one
 // and-or per two weights) and sum x*(1 + q/16) is a chain of bf16 dot2
 // instructions accumulating in fp32.
+#include <algorithm>
+
 #include "moe_internal.h"
+#include "route_device.h"
 #include "route_internal.h"
 
 namespace moe {
@@ -81,31 +84,31 @@ __device__ __forceinline__ float chunk_dot(const ChunkLoad& c, const uint32_t* x
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.f + expf(-g)); }
 
-// ---------------------------------------------------------------- gate/up + SwiGLU
-// Grid: (I / 16, S, T); block 256 = 4 wavefronts, each owning 4 consecutive
-// intermediate rows (gate row and up row). Every weight load of a wavefront is
-// issued before the first one is consumed (up to 2 x 4 x CPL 16-byte loads per
-// lane in flight). Writes h[t][s][i] (bf16).
-constexpr int GU_ROWS_PER_WG = 16;
+// ---------------------------------------------------------------- gate/up work item
+// 16 intermediate rows (gate row and up row each) of expert e for one token, by
+// one workgroup: wavefront w owns rows rb*16 + 4w .. +4. Writes h (bf16) at hrow.
+constexpr int GU_ROWS = 16;
 constexpr int GU_IT = 4;  // row iterations per wavefront (rows per iteration = 64 / lanes per row)
 
+// With htag (the tagged copy of the same h row, one 64-bit word per bf16 pair) the
+// rows are published there with tag `tag` instead of being stored to hrow.
 template <int CPL>
-__global__ __launch_bounds__(256) void decode_gateup_kernel(const uint8_t* __restrict__ packed, ExpertLayout L, int H,
-                                                            int I, int E, int k, int has_shared,
-                                                            const uint16_t* __restrict__ x,
-                                                            const int32_t* __restrict__ ids,
-                                                            uint16_t* __restrict__ hbuf) {
-    const int t = blockIdx.z, s = blockIdx.y, S = k + has_shared;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int e = s < k ? ids[(size_t)t * k + s] : E;
-    const bool valid = s < k ? (e >= 0 && e < E) : true;
-    uint16_t* hrow = hbuf + ((size_t)t * S + s) * I;
+__device__ __forceinline__ void gateup_item(const uint8_t* __restrict__ packed, const ExpertLayout& L, int H, int I,
+                                            int e, bool valid, const uint16_t* __restrict__ xrow,
+                                            uint16_t* __restrict__ hrow, uint64_t* htag, uint32_t tag, int rb,
+                                            int wave, int lane) {
     const int C = H / 32, lpr = C < 64 ? C : 64, rpw = 64 / lpr;
     const int lr = lane % lpr, rsub = lane / lpr;
-    constexpr int per_wave = GU_ROWS_PER_WG / 4;
-    const int r0 = blockIdx.x * GU_ROWS_PER_WG + wave * per_wave;
+    constexpr int per_wave = GU_ROWS / 4;
+    const int r0 = rb * GU_ROWS + wave * per_wave;
+    uint32_t* hrow32 = reinterpret_cast<uint32_t*>(hrow + r0);  // r0 is even: 4 rows = 2 dwords
     if (!valid) {
-        if (lane < per_wave) hrow[r0 + lane] = 0;
+        if (lane < 2) {
+            if (htag)
+                store_tagged(htag + r0 / 2 + lane, tag, 0u);
+            else
+                hrow32[lane] = 0u;
+        }
         return;
     }
     const uint8_t* base = packed + (size_t)e * L.stride;
@@ -129,7 +132,8 @@ __global__ __launch_bounds__(256) void decode_gateup_kernel(const uint8_t* __res
         }
     }
     XSlice<CPL> xs;
-    load_xslice(x + (size_t)t * H, lr, lpr, xs);
+    load_xslice(xrow, lr, lpr, xs);
+    uint32_t hb[GU_IT] = {0u, 0u, 0u, 0u};  // bf16 of row it*rpw + rsub, in lanes with lr == 0
 #pragma unroll
     for (int it = 0; it < GU_IT; ++it) {
         const int rr = it * rpw + rsub;
@@ -143,44 +147,58 @@ __global__ __launch_bounds__(256) void decode_gateup_kernel(const uint8_t* __res
                 u += chunk_dot(lu[it][c], xs.p[c], xs.s[c]);
             }
         }
-        for (int off = lpr >> 1; off >= 1; off >>= 1) {
-            g += __shfl_xor(g, off);
-            u += __shfl_xor(u, off);
-        }
-        if (act && lr == 0) hrow[r0 + rr] = (uint16_t)f32_to_bf16(silu_f32(g) * u);
+        g = group_sum(g, lpr);
+        u = group_sum(u, lpr);
+        hb[it] = f32_to_bf16(silu_f32(g) * u);
+    }
+    // gather the wavefront's 4 rows (row q sits in the last lane of group q % rpw,
+    // iteration q / rpw)
+    uint32_t r4[per_wave];
+#pragma unroll
+    for (int q = 0; q < per_wave; ++q) {
+        const int it = q / rpw;
+        const uint32_t v = it == 0 ? hb[0] : it == 1 ? hb[1] : it == 2 ? hb[2] : hb[3];
+        r4[q] = (uint32_t)__builtin_amdgcn_readlane((int)v, (q % rpw) * lpr + lpr - 1);
+    }
+    if (lane < 2) {
+        const uint32_t v = lane == 0 ? (r4[0] | (r4[1] << 16)) : (r4[2] | (r4[3] << 16));
+        if (htag)
+            store_tagged(htag + r0 / 2 + lane, tag, v);
+        else
+            hrow32[lane] = v;
     }
 }
 
-// ---------------------------------------------------------------- down (+ combine)
-// Grid: (H / 8, T); block 256. A workgroup computes y[t][s][n] for its 8 output
-// rows n and every slot s (S*8 row dot products of length I, lpr = I/32 lanes
-// each), keeps them in LDS, and optionally writes
-//   out[t][n] = bf16(sum_{s<k} w[t][s] * y[t][s][n] + wsh[t] * y[t][k][n])
-// (then bf16(residual + out) when a residual is given) with the same fp32
-// slot-order arithmetic as moe_combine. Weight loads depend only on ids, so they
-// are issued before the h rows produced by the gate/up kernel are read.
-constexpr int DN_ROWS_PER_WG = 8;
+// ---------------------------------------------------------------- down (+ combine) work item
+// Output rows n0 .. n0+7 of token t for every slot s (S*8 row dot products of
+// length I, I/32 lanes each) by one workgroup. Results go to LDS (ysh), then to
+// y[t][s][n] when y is given, and
+//   out[t][n] = bf16(sum_{s<k} w[s] * y[s][n] + wsh * y[k][n])
+// (then bf16(residual + out)) when out is given, with the same fp32 slot-order
+// arithmetic as moe_combine. The weight loads depend only on the expert ids, so
+// they are issued first; with WAIT the workgroup then waits until *ready >= target
+// (the h rows of token t are complete) before it reads h.
+constexpr int DN_ROWS = 8;
 constexpr int DN_BATCH = 5;  // 9 slots x 8 rows at I = 512: 18 iterations, 4.5 per wavefront
 
-__global__ __launch_bounds__(256) void decode_down_kernel(const uint8_t* __restrict__ packed, ExpertLayout L, int H,
-                                                          int I, int E, int k, int has_shared,
-                                                          const uint16_t* __restrict__ hbuf,
-                                                          const int32_t* __restrict__ ids, float* __restrict__ y,
-                                                          const uint16_t* __restrict__ w,
-                                                          const uint16_t* __restrict__ wsh, const uint16_t* residual,
-                                                          uint16_t* out) {
-    __shared__ float ysh[17][DN_ROWS_PER_WG];
-    const int t = blockIdx.y, S = k + has_shared;
-    const int n0 = blockIdx.x * DN_ROWS_PER_WG;
+// hsh: LDS of S * I bf16, the token's h rows of every slot, staged with one round
+// of parallel loads before the dot products. With TAGGED the rows are read from
+// their tagged copy (published in this launch), each word polled until it carries
+// `tag`; the weight loads are issued before that wait.
+template <bool TAGGED>
+__device__ __forceinline__ void down_item(const uint8_t* __restrict__ packed, const ExpertLayout& L, int H, int I,
+                                          int E, int k, int has_shared, int t, int n0,
+                                          const uint16_t* __restrict__ hbuf, const int32_t* ids_t,
+                                          const uint16_t* w_t, const uint16_t* wsh_t, float* __restrict__ y,
+                                          const uint16_t* residual, uint16_t* out, float (*ysh)[DN_ROWS],
+                                          uint32_t* hsh, const uint64_t* htag_t, uint32_t tag, unsigned* err) {
+    const int S = k + has_shared;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int lpr = I / 32, rpw = 64 / lpr;  // I <= 2048: one chunk per lane
     const int lr = lane % lpr, rsub = lane / lpr;
-    const int n_dots = S * DN_ROWS_PER_WG;
+    const int n_dots = S * DN_ROWS;
     const int n_it = (n_dots + rpw - 1) / rpw;
     const size_t qstride = I / 2, sbstride = I / 64;
-
-    // iterations it = wave + 4 j; processed in batches of DN_BATCH per wavefront with
-    // every weight load of a batch issued before the batch is consumed
     for (int j0 = 0; 4 * j0 < n_it; j0 += DN_BATCH) {
         ChunkLoad ld[DN_BATCH];
         int slot[DN_BATCH];
@@ -190,19 +208,36 @@ __global__ __launch_bounds__(256) void decode_down_kernel(const uint8_t* __restr
             const int it = wave + 4 * (j0 + j);
             const int q = it * rpw + rsub;
             ok[j] = it < n_it && q < n_dots;
-            slot[j] = ok[j] ? q / DN_ROWS_PER_WG : 0;
+            slot[j] = ok[j] ? q / DN_ROWS : 0;
             if (ok[j]) {
                 const int s = slot[j];
-                const int e = s < k ? ids[(size_t)t * k + s] : E;
+                const int e = s < k ? ids_t[s] : E;
                 if (s < k && (e < 0 || e >= E)) {
                     ok[j] = false;  // invalid expert id: this y row is zero
                 } else {
-                    const int n = n0 + q % DN_ROWS_PER_WG;
+                    const int n = n0 + q % DN_ROWS;
                     const uint8_t* base = packed + (size_t)e * L.stride;
                     ld[j] = load_chunk(base + L.down_q + n * qstride,
                                        reinterpret_cast<const uint32_t*>(base + L.down_sb) + n * sbstride, lr);
                 }
             }
+        }
+        if (j0 == 0) {
+            const int nw = S * I / 2;
+            if (TAGGED) {
+                for (int i0 = threadIdx.x; i0 < nw; i0 += 256 * 16) {
+                    uint32_t v[16];
+                    const int n = min(16, (nw - 1 - i0) / 256 + 1);
+                    load_tagged_many<16>(htag_t + i0, 256, n, tag, err, v);
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        if (j < n) hsh[i0 + 256 * j] = v[j];
+                }
+            } else {
+                const uint32_t* src = reinterpret_cast<const uint32_t*>(hbuf + (size_t)t * S * I);
+                for (int i = threadIdx.x; i < nw; i += 256) hsh[i] = src[i];
+            }
+            __syncthreads();
         }
 #pragma unroll
         for (int j = 0; j < DN_BATCH; ++j) {
@@ -212,28 +247,182 @@ __global__ __launch_bounds__(256) void decode_down_kernel(const uint8_t* __restr
             float v = 0.f;
             if (ok[j]) {
                 XSlice<1> hs;
-                load_xslice(hbuf + ((size_t)t * S + slot[j]) * I, lr, lpr, hs);
+                load_xslice(reinterpret_cast<const uint16_t*>(hsh) + (size_t)slot[j] * I, lr, lpr, hs);
                 v = chunk_dot(ld[j], hs.p[0], hs.s[0]);
             }
-            for (int off = lpr >> 1; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-            if (lr == 0 && q < n_dots) ysh[q / DN_ROWS_PER_WG][q % DN_ROWS_PER_WG] = v;
+            v = group_sum(v, lpr);
+            if (lr == lpr - 1 && q < n_dots) ysh[q / DN_ROWS][q % DN_ROWS] = v;
         }
     }
     __syncthreads();
     const int tid = threadIdx.x;
     if (y) {
         for (int i = tid; i < n_dots; i += 256)
-            y[((size_t)t * S + i / DN_ROWS_PER_WG) * H + n0 + i % DN_ROWS_PER_WG] =
-                ysh[i / DN_ROWS_PER_WG][i % DN_ROWS_PER_WG];
+            y[((size_t)t * S + i / DN_ROWS) * H + n0 + i % DN_ROWS] = ysh[i / DN_ROWS][i % DN_ROWS];
     }
-    if (out && tid < DN_ROWS_PER_WG) {
+    if (out && tid < DN_ROWS) {
         float a = 0.f;
-        for (int s = 0; s < k; ++s) a = fmaf(bf16_to_f32(w[(size_t)t * k + s]), ysh[s][tid], a);
-        if (has_shared) a = fmaf(bf16_to_f32(wsh[t]), ysh[k][tid], a);
+        for (int s = 0; s < k; ++s) a = fmaf(bf16_to_f32(w_t[s]), ysh[s][tid], a);
+        if (has_shared) a = fmaf(bf16_to_f32(*wsh_t), ysh[k][tid], a);
         uint32_t b = f32_to_bf16(a);
         const size_t o = (size_t)t * H + n0 + tid;
         if (residual) b = f32_to_bf16(bf16_to_f32(residual[o]) + bf16_to_f32(b));
         out[o] = (uint16_t)b;
+    }
+    __syncthreads();  // ysh is reused by the next item
+}
+
+// ---------------------------------------------------------------- two-launch expert stage
+// Grid (I / 16, S, T): one gate/up item per workgroup.
+template <int CPL>
+__global__ __launch_bounds__(256) void decode_gateup_kernel(const uint8_t* __restrict__ packed, ExpertLayout L, int H,
+                                                            int I, int E, int k, int has_shared,
+                                                            const uint16_t* __restrict__ x,
+                                                            const int32_t* __restrict__ ids,
+                                                            uint16_t* __restrict__ hbuf) {
+    const int t = blockIdx.z, s = blockIdx.y, S = k + has_shared;
+    const int e = s < k ? ids[(size_t)t * k + s] : E;
+    const bool valid = s < k ? (e >= 0 && e < E) : true;
+    gateup_item<CPL>(packed, L, H, I, e, valid, x + (size_t)t * H, hbuf + ((size_t)t * S + s) * I, nullptr, 0u,
+                     blockIdx.x, threadIdx.x >> 6, threadIdx.x & 63);
+}
+
+// Grid (H / 8, T): one down item per workgroup; combine when out is given.
+__global__ __launch_bounds__(256) void decode_down_kernel(const uint8_t* __restrict__ packed, ExpertLayout L, int H,
+                                                          int I, int E, int k, int has_shared,
+                                                          const uint16_t* __restrict__ hbuf,
+                                                          const int32_t* __restrict__ ids, float* __restrict__ y,
+                                                          const uint16_t* __restrict__ w,
+                                                          const uint16_t* __restrict__ wsh, const uint16_t* residual,
+                                                          uint16_t* out) {
+    __shared__ float ysh[17][DN_ROWS];
+    extern __shared__ __attribute__((aligned(16))) uint32_t hsh_dyn[];
+    const int t = blockIdx.y;
+    down_item<false>(packed, L, H, I, E, k, has_shared, t, blockIdx.x * DN_ROWS, hbuf, ids + (size_t)t * k,
+                     w ? w + (size_t)t * k : nullptr, wsh ? wsh + t : nullptr, y, residual, out, ysh, hsh_dyn,
+                     nullptr, 0u, nullptr);
+}
+
+// ---------------------------------------------------------------- single-launch decode layer
+// Control words in the workspace. A launch publishes with tag epoch + 1; the last
+// workgroup to leave stores the new epoch, so stale words of earlier launches never
+// carry the current tag and nothing has to be cleared between launches.
+struct DecodeCtl {
+    unsigned epoch;       // tag of the last completed launch
+    unsigned exit_count;  // workgroups finished (back to zero after each launch)
+    unsigned error;       // a bounded poll timed out (sticky)
+    unsigned pad;
+};
+
+struct LayerArgs {
+    const uint8_t* router;
+    const float* logit_bias;
+    const uint8_t* experts;
+    const uint16_t* x;
+    float* logits;
+    int32_t* ids;
+    uint16_t* w;
+    uint16_t* wsh;
+    float* y;
+    const uint16_t* residual;
+    uint16_t* out;
+    DecodeCtl* ctl;
+    uint64_t* tlogits;  // tagged logits [T][R]
+    uint64_t* th;       // tagged h [T][S][I/2] (bf16 pairs)
+    ExpertLayout L;
+    int T, H, I, E, k, has_shared, R;
+};
+
+// Persistent kernel, at most one workgroup per CU, every workgroup resident.
+// Work items (token-minor numbering; item i of a phase goes to workgroup i mod G):
+//   A: router rows (4 per item) and the shared expert's gate/up items, which do
+//      not depend on routing;
+//   B: the routed gate/up items (16 rows of one token, one slot);
+//   C: down items (8 output rows of one token, all slots) with the combine.
+// Every workgroup computes the selection of the tokens it needs (DPP top-k, reading
+// the tagged logits as they arrive) into LDS before its B items. A C item issues
+// its down-weight loads, then stages its token's tagged h rows (polling each word).
+template <int CPL, int TT, bool AFF8>
+__global__ __launch_bounds__(256) void decode_layer_kernel(LayerArgs a) {
+    __shared__ int32_t s_ids[16][16];
+    __shared__ uint16_t s_w[16][16];
+    __shared__ uint16_t s_wsh[16];
+    __shared__ float ysh[17][DN_ROWS];
+    extern __shared__ __attribute__((aligned(16))) uint32_t hsh_dyn[];
+    const int G = gridDim.x, wg = blockIdx.x;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int T = a.T, H = a.H, I = a.I, E = a.E, k = a.k, R = a.R;
+    const int S = k + a.has_shared;
+    DecodeCtl* ctl = a.ctl;
+    const uint32_t tag = load_coherent(&ctl->epoch) + 1u;
+    const int n_router = (R + 3) / 4;
+    const int gu_per_tok = I / GU_ROWS;
+    const int n_shared = a.has_shared ? T * gu_per_tok : 0;
+    const int n_A = n_router + n_shared;
+    const int n_B = T * k * gu_per_tok;
+    const int n_C = T * (H / DN_ROWS);
+
+    // ---- phase A
+    for (int item = wg; item < n_A; item += G) {
+        if (item < n_router) {
+            const int r = item * 4 + wave;
+            if (r < R)
+                router_row<TT, AFF8>(a.router, a.logit_bias, a.x, 0, T, H, R, E, r, lane, a.logits, false, a.tlogits,
+                                     tag);
+        } else {
+            const int j = item - n_router, t = j % T, rb = j / T;
+            const size_t row = (size_t)t * S + k;
+            gateup_item<CPL>(a.experts, a.L, H, I, E, true, a.x + (size_t)t * H, nullptr, a.th + row * (I / 2), tag,
+                             rb, wave, lane);
+        }
+    }
+
+    // ---- selection of the tokens this workgroup needs
+    uint32_t need = 0;
+    for (int item = wg; item < n_B; item += G) need |= 1u << (item % T);
+    for (int item = wg; item < n_C; item += G) need |= 1u << (item % T);
+    if (wg < T) need |= 1u << wg;
+    for (int t = 0, c = 0; t < T; ++t) {
+        if (need >> t & 1u) {
+            if ((c & 3) == wave) {
+                const LogitSrc src{nullptr, a.tlogits + (size_t)t * R, tag, &ctl->error, false};
+                select_token_any(src, E, k, a.has_shared, lane, s_ids[t], s_w[t], &s_wsh[t]);
+            }
+            ++c;
+        }
+    }
+    __syncthreads();
+    if (wg < T) {
+        if (tid < k) {
+            a.ids[(size_t)wg * k + tid] = s_ids[wg][tid];
+            a.w[(size_t)wg * k + tid] = s_w[wg][tid];
+        }
+        if (a.has_shared && tid == 0) a.wsh[wg] = s_wsh[wg];
+    }
+
+    // ---- phase B
+    for (int item = wg; item < n_B; item += G) {
+        const int t = item % T, j = item / T, s = j / gu_per_tok, rb = j % gu_per_tok;
+        const size_t row = (size_t)t * S + s;
+        gateup_item<CPL>(a.experts, a.L, H, I, s_ids[t][s], true, a.x + (size_t)t * H, nullptr, a.th + row * (I / 2),
+                         tag, rb, wave, lane);
+    }
+
+    // ---- phase C
+    for (int item = wg; item < n_C; item += G) {
+        const int t = item % T, ng = item / T;
+        down_item<true>(a.experts, a.L, H, I, E, k, a.has_shared, t, ng * DN_ROWS, nullptr, s_ids[t], s_w[t],
+                        &s_wsh[t], a.y, a.residual, a.out, ysh, hsh_dyn, a.th + (size_t)t * S * (I / 2), tag,
+                        &ctl->error);
+    }
+
+    // ---- exit: the last workgroup out publishes the new epoch
+    __syncthreads();
+    if (tid == 0) {
+        if (atomicAdd(&ctl->exit_count, 1u) == (unsigned)G - 1) {
+            atomicExch(&ctl->exit_count, 0u);
+            atomicExch(&ctl->epoch, tag);
+        }
     }
 }
 
@@ -242,7 +431,7 @@ static int cpl_for(int K) { return K / 32 <= 64 ? 1 : (K / 32) / 64; }
 static void launch_gateup(const moe_shape& sh, const ExpertLayout& L, const uint8_t* p, const uint16_t* x, int T,
                           const int32_t* ids, uint16_t* hbuf, hipStream_t hs) {
     const int S = n_slots(sh), H = sh.hidden, I = sh.inter;
-    dim3 g1(I / GU_ROWS_PER_WG, S, T);
+    dim3 g1(I / GU_ROWS, S, T);
     switch (cpl_for(H)) {
         case 1: hipLaunchKernelGGL(decode_gateup_kernel<1>, g1, dim3(256), 0, hs, p, L, H, I, sh.n_experts, sh.top_k,
                                    sh.has_shared, x, ids, hbuf); break;
@@ -253,17 +442,59 @@ static void launch_gateup(const moe_shape& sh, const ExpertLayout& L, const uint
     }
 }
 
+static int device_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (!cache[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+// LDS for one token's h rows of every slot.
+static size_t hsh_bytes(const moe_shape& sh) { return (size_t)n_slots(sh) * sh.inter * 2; }
+
+template <int CPL, int TT>
+static void launch_layer_tt(const LayerArgs& a, bool aff8, int G, size_t lds, hipStream_t hs) {
+    if (aff8)
+        hipLaunchKernelGGL((decode_layer_kernel<CPL, TT, true>), dim3(G), dim3(256), lds, hs, a);
+    else
+        hipLaunchKernelGGL((decode_layer_kernel<CPL, TT, false>), dim3(G), dim3(256), lds, hs, a);
+}
+
+template <int CPL>
+static void launch_layer(const LayerArgs& a, bool aff8, int G, size_t lds, hipStream_t hs) {
+    if (a.T <= 1) launch_layer_tt<CPL, 1>(a, aff8, G, lds, hs);
+    else if (a.T <= 4) launch_layer_tt<CPL, 4>(a, aff8, G, lds, hs);
+    else launch_layer_tt<CPL, 16>(a, aff8, G, lds, hs);
+}
+
 }  // namespace moe
 
 using namespace moe;
 
-static size_t hbuf_bytes(const moe_shape& sh, int T) {
-    return align_up((size_t)T * n_slots(sh) * sh.inter * 2, 256);
+static size_t hbuf_bytes(const moe_shape& sh, int T) { return align_up((size_t)T * n_slots(sh) * sh.inter * 2, 256); }
+
+// Workspace: h rows (bf16) | control words (256 B) | tagged logits | tagged h.
+struct DecodeWs {
+    size_t ctl, tlogits, th, total;
+};
+
+static DecodeWs decode_ws_layout(const moe_shape& sh, int T) {
+    DecodeWs w;
+    w.ctl = hbuf_bytes(sh, T);
+    w.tlogits = w.ctl + 256;
+    w.th = w.tlogits + align_up((size_t)T * router_rows(sh) * 8, 256);
+    w.total = w.th + align_up((size_t)T * n_slots(sh) * (sh.inter / 2) * 8, 256);
+    return w;
 }
 
 extern "C" size_t moe_decode_workspace_bytes(const moe_shape* shape, int32_t T) {
     if (validate_shape(shape) != MOE_OK || T < 1) return 0;
-    return hbuf_bytes(*shape, T) + 256;  // h rows, then the fused-routing counter word
+    return decode_ws_layout(*shape, T).total;
 }
 
 static moe_status check_decode_args(const moe_shape* shape, const void* experts_packed, const uint16_t* x, int T,
@@ -274,6 +505,8 @@ static moe_status check_decode_args(const moe_shape* shape, const void* experts_
     if (!experts_packed || !x || !ws || !aligned16(experts_packed) || !aligned16(x) || !aligned16(ws))
         return fail(MOE_ERR_INVALID_ARG, "NULL or unaligned pointer");
     if (ws_bytes < moe_decode_workspace_bytes(shape, T)) return fail(MOE_ERR_WORKSPACE, "decode workspace too small");
+    if (hsh_bytes(*shape) > 65536)
+        return fail(MOE_ERR_UNSUPPORTED, "decode path: (top_k + shared) * inter * 2 bytes must fit 64 KiB of LDS");
     return MOE_OK;
 }
 
@@ -291,8 +524,9 @@ extern "C" moe_status moe_experts_decode(const moe_shape* shape, const void* exp
     uint16_t* hbuf = (uint16_t*)ws;
     launch_gateup(sh, L, p, x, T, ids, hbuf, hs);
     if ((st = check_launch("decode_gateup_kernel")) != MOE_OK) return st;
-    hipLaunchKernelGGL(decode_down_kernel, dim3(sh.hidden / DN_ROWS_PER_WG, T), dim3(256), 0, hs, p, L, sh.hidden,
-                       sh.inter, sh.n_experts, sh.top_k, sh.has_shared, hbuf, ids, y, (const uint16_t*)nullptr,
+    hipLaunchKernelGGL(decode_down_kernel, dim3(sh.hidden / DN_ROWS, T), dim3(256), hsh_bytes(sh), hs, p, L, sh.hidden,
+                       sh.inter,
+                       sh.n_experts, sh.top_k, sh.has_shared, hbuf, ids, y, (const uint16_t*)nullptr,
                        (const uint16_t*)nullptr, (const uint16_t*)nullptr, (uint16_t*)nullptr);
     return check_launch("decode_down_kernel");
 }
@@ -309,17 +543,40 @@ extern "C" moe_status moe_decode_layer(const moe_shape* shape, const void* route
     if (!router_packed || !logits || !out || !aligned16(router_packed))
         return fail(MOE_ERR_INVALID_ARG, "router, logits or out NULL / unaligned");
     if (y && !aligned16(y)) return fail(MOE_ERR_INVALID_ARG, "y unaligned");
-    const ExpertLayout L = expert_layout(sh);
+    if (cpl_for(sh.hidden) > 2) return fail(MOE_ERR_UNSUPPORTED, "single-launch decode layer serves hidden <= 4096");
+    const int cus = device_cus();
+    if (cus <= 0) return fail(MOE_ERR_HIP, "could not query the compute-unit count");
     hipStream_t hs = (hipStream_t)stream;
-    const uint8_t* p = (const uint8_t*)experts_packed;
-    uint16_t* hbuf = (uint16_t*)ws;
-    unsigned int* counter = (unsigned int*)((char*)ws + hbuf_bytes(sh, T));
-    if ((st = launch_route_fused(sh, router_packed, logit_bias, x, T, logits, counter, ids, w, w_shared, hs)) !=
-        MOE_OK)
-        return st;
-    launch_gateup(sh, L, p, x, T, ids, hbuf, hs);
-    if ((st = check_launch("decode_gateup_kernel")) != MOE_OK) return st;
-    hipLaunchKernelGGL(decode_down_kernel, dim3(sh.hidden / DN_ROWS_PER_WG, T), dim3(256), 0, hs, p, L, sh.hidden,
-                       sh.inter, sh.n_experts, sh.top_k, sh.has_shared, hbuf, ids, y, w, w_shared, residual, out);
-    return check_launch("decode_down_kernel (combine)");
+    LayerArgs a;
+    a.router = (const uint8_t*)router_packed;
+    a.logit_bias = logit_bias;
+    a.experts = (const uint8_t*)experts_packed;
+    a.x = x;
+    a.logits = logits;
+    a.ids = ids;
+    a.w = w;
+    a.wsh = w_shared;
+    a.y = y;
+    a.residual = residual;
+    a.out = out;
+    const DecodeWs W = decode_ws_layout(sh, T);
+    a.ctl = (DecodeCtl*)((char*)ws + W.ctl);
+    a.tlogits = (uint64_t*)((char*)ws + W.tlogits);
+    a.th = (uint64_t*)((char*)ws + W.th);
+    a.L = expert_layout(sh);
+    a.T = T;
+    a.H = sh.hidden;
+    a.I = sh.inter;
+    a.E = sh.n_experts;
+    a.k = sh.top_k;
+    a.has_shared = sh.has_shared;
+    a.R = router_rows(sh);
+    const int n_router = (a.R + 3) / 4;
+    const int n_A = n_router + (sh.has_shared ? T * (a.I / GU_ROWS) : 0);
+    const int items = std::max(std::max(n_A, T * sh.top_k * (a.I / GU_ROWS)), T * (a.H / DN_ROWS));
+    const int G = std::min(cus, items);
+    const bool aff8 = sh.router_fmt == MOE_ROUTER_AFFINE8;
+    if (cpl_for(sh.hidden) == 1) launch_layer<1>(a, aff8, G, hsh_bytes(sh), hs);
+    else launch_layer<2>(a, aff8, G, hsh_bytes(sh), hs);
+    return check_launch("decode_layer_kernel");
 }

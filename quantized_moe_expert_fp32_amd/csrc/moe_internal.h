@@ -111,6 +111,129 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// Coherent (agent-scope) 32-bit accesses for data that one workgroup publishes to
+// others inside a kernel: they go to the device coherence point, so publishing
+// needs no cache-wide write-back or invalidate, only store completion
+// (publish_fence) before the counter that announces them.
+__device__ __forceinline__ void store_coherent(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_coherent(const uint32_t* p) {
+    return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Waits until every memory operation this wavefront issued has completed.
+__device__ __forceinline__ void publish_fence() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Tagged publishing inside one launch: a 64-bit coherent store of (tag, value);
+// a reader polls the word until its tag is the launch's tag, so the data itself
+// announces that it is ready (no separate counter round trip). Polls are bounded:
+// after SPIN_LIMIT polls the error word is set and the stale value is returned.
+constexpr unsigned SPIN_LIMIT = 1u << 20;
+
+__device__ __forceinline__ void store_tagged(uint64_t* p, uint32_t tag, uint32_t v) {
+    __hip_atomic_store(p, ((uint64_t)tag << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_tagged_wait(const uint64_t* p, uint32_t tag, unsigned* err) {
+    uint64_t v = __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned it = 0;
+    while ((uint32_t)(v >> 32) != tag) {
+        if (++it >= SPIN_LIMIT) {
+            atomicOr(err, 1u);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        v = __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return (uint32_t)v;
+}
+
+// N tagged words at p[0], p[stride], ...: all loads issued at once, then only the
+// stale ones are polled again (bounded).
+template <int N>
+__device__ __forceinline__ void load_tagged_many(const uint64_t* p, int stride, int n, uint32_t tag, unsigned* err,
+                                                 uint32_t* out) {
+    uint64_t v[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+        v[j] = j < n ? __hip_atomic_load(const_cast<uint64_t*>(p + (size_t)j * stride), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT)
+                     : ((uint64_t)tag << 32);
+    for (unsigned it = 0;; ++it) {
+        bool ok = true;
+#pragma unroll
+        for (int j = 0; j < N; ++j) ok = ok && (uint32_t)(v[j] >> 32) == tag;
+        if (ok) break;
+        if (it >= SPIN_LIMIT) {
+            atomicOr(err, 1u);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int j = 0; j < N; ++j)
+            if ((uint32_t)(v[j] >> 32) != tag)
+                v[j] = __hip_atomic_load(const_cast<uint64_t*>(p + (size_t)j * stride), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int j = 0; j < N; ++j) out[j] = (uint32_t)v[j];
+}
+
+// DPP move of a 32-bit value (every lane must be active).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Sum over aligned groups of `lpr` lanes (a power of two up to 64) with DPP: quad
+// permutations, half-row and row mirrors, then the row broadcasts 15 and 31. The
+// sum is valid in the last lane of each group (and, for lpr <= 16, in every lane).
+__device__ __forceinline__ float group_sum(float v, int lpr) {
+    if (lpr >= 2) v += __uint_as_float(dpp_u32<0xB1, 0xF>(__float_as_uint(v)));
+    if (lpr >= 4) v += __uint_as_float(dpp_u32<0x4E, 0xF>(__float_as_uint(v)));
+    if (lpr >= 8) v += __uint_as_float(dpp_u32<0x141, 0xF>(__float_as_uint(v)));
+    if (lpr >= 16) v += __uint_as_float(dpp_u32<0x140, 0xF>(__float_as_uint(v)));
+    if (lpr >= 32) v += __uint_as_float(dpp_u32<0x142, 0xA>(__float_as_uint(v)));
+    if (lpr >= 64) v += __uint_as_float(dpp_u32<0x143, 0xC>(__float_as_uint(v)));
+    return v;
+}
+
+__device__ __forceinline__ double dpp_f64_step(double v, int step) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+    switch (step) {
+        case 0: lo = dpp_u32<0xB1, 0xF>(lo); hi = dpp_u32<0xB1, 0xF>(hi); break;
+        case 1: lo = dpp_u32<0x4E, 0xF>(lo); hi = dpp_u32<0x4E, 0xF>(hi); break;
+        case 2: lo = dpp_u32<0x141, 0xF>(lo); hi = dpp_u32<0x141, 0xF>(hi); break;
+        case 3: lo = dpp_u32<0x140, 0xF>(lo); hi = dpp_u32<0x140, 0xF>(hi); break;
+        case 4: lo = dpp_u32<0x142, 0xA>(lo); hi = dpp_u32<0x142, 0xA>(hi); break;
+        default: lo = dpp_u32<0x143, 0xC>(lo); hi = dpp_u32<0x143, 0xC>(hi); break;
+    }
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// fp64 sum over the whole wavefront with DPP; valid in lane 63.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int step = 0; step < 6; ++step) v += dpp_f64_step(v, step);
+    return v;
+}
+
+// Where a selection reads its fp32 logits: a plain array (written by an earlier
+// launch), a coherently written array (same launch, completion announced by a
+// counter), or a tagged array (same launch, tag-polled).
+struct LogitSrc {
+    const float* plain;
+    const uint64_t* tagged;
+    uint32_t tag;
+    unsigned* err;
+    bool coherent;
+    __device__ __forceinline__ uint32_t get(int i) const {
+        if (tagged) return load_tagged_wait(tagged + i, tag, err);
+        if (coherent) return load_coherent(reinterpret_cast<const uint32_t*>(plain) + i);
+        return __float_as_uint(plain[i]);
+    }
+};
+
 // Unsigned key ordering fp32 logits: larger logit -> larger key; -0 equals +0;
 // NaN gets key 0, below every number.
 __device__ __forceinline__ uint32_t ordered_logit(float f) {

@@ -266,8 +266,20 @@ def test_fused_decode_layer_matches_staged_calls(gpu, T):
     dl = dev_layer(gpu, c)
     x = synth.random_x(300 + T, T, 2048)
     a = run_path(gpu, dl, x, "decode")
-    b = run_path(gpu, dl, x, "fused")
-    b2 = run_path(gpu, dl, x, "fused")  # the counter word was left at zero
+    L = _L()
+    buf = L.alloc_buffers(dl.shape, T, "fused")
+    dx = L.to_device(x)
+    outs = []
+    for _ in range(3):  # the control words are left at zero by every call
+        L.layer_step(dl, dx, buf, "fused")
+        torch.cuda.synchronize()
+        outs.append(dict(logits=buf.logits.cpu().numpy(), ids=buf.ids.cpu().numpy(), w=L.bits_to_numpy(buf.w),
+                         wsh=L.bits_to_numpy(buf.wsh), y=buf.y.cpu().numpy(), out=L.bits_to_numpy(buf.out)))
+    off = (T * 9 * 512 * 2 + 255) // 256 * 256  # control words follow the bf16 h rows
+    ctl = buf.ws.cpu().numpy()[off:off + 16].view(np.uint32)
+    assert ctl[2] == 0, "a bounded poll timed out"
+    assert ctl[1] == 0 and ctl[0] == 3  # exit counter back at zero; one epoch per launch
+    b, b2 = outs[0], outs[2]
     for key in ("logits", "ids", "w", "wsh", "y", "out"):
         assert np.array_equal(a[key], b[key]), key
         assert np.array_equal(b[key], b2[key]), key
