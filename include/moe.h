@@ -137,8 +137,11 @@ moe_status moe_pack_router(const moe_shape* shape, const void* w, const uint16_t
  * lower id), w [T][k] bf16 (exp(l_i - l_0) / sum_j exp(l_j - l_0) over the picks,
  * evaluated in fp64 and rounded once), w_shared [T] bf16 (bf16(sigmoid(bf16(gate)))
  * in fp64; NULL when has_shared == 0). NaN logits rank below -inf; -0 ties +0.
- * Logits: exact products accumulated in fp64 in a fixed order, rounded once to
- * fp32; a token's logits do not depend on T. T >= 1. */
+ * Logits: for T <= 16 (and for the fp32 router) exact products accumulated in
+ * fp64 in a fixed order and rounded once to fp32; for T > 16 with the 8-bit
+ * router a matrix-core GEMM accumulating in fp32 (the 1e-5 near-tie allowance of
+ * the pick check covers the difference). A token's logits do not depend on the
+ * other tokens of the call. T >= 1. */
 moe_status moe_route(const moe_shape* shape, const void* router_packed, const float* logit_bias,
                      const uint16_t* x, int32_t T, float* logits, int32_t* ids, uint16_t* w,
                      uint16_t* w_shared, void* stream);

@@ -14,13 +14,13 @@
 // a group is staged once per workgroup in LDS (double-buffered, one barrier per
 // group); the weight fragments are read straight from HBM into registers (each
 // wavefront reads distinct weight rows, so nothing is fetched twice).
+#include "mfma_common.h"
 #include "moe_internal.h"
 
 namespace moe {
 
-constexpr int BM = 64;        // rows per tile
-constexpr int BN = 64;        // output columns per workgroup
-constexpr int A_STRIDE = 72;  // LDS row stride in bf16 (64 + 8 padding)
+constexpr int BM = 64;  // rows per tile
+constexpr int BN = 64;  // output columns per workgroup
 
 struct Tile {
     int32_t expert, row0, nrows, pad;
@@ -138,49 +138,16 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const int32_t* __restric
         for (int t = tid; t < T; t += blockDim.x) order[off[E] + t] = t * S + k;
 }
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
+// ---------------------------------------------------------------- pipelining
+// Both GEMMs walk K in 64-wide groups. Weight fragments (the HBM stream) are
+// loaded PD groups ahead into a register ring; the gathered activation group is
+// loaded two groups ahead into registers and staged into a double-buffered LDS
+// tile one group ahead; one barrier per group. PD is even so the LDS and register
+// slots of group g are g & 1 at every unrolled position.
+constexpr int PD_GU = 4;  // gate/up: 6 words per group in flight per lane
+constexpr int PD_DN = 8;  // down: 3 words per group
 
-__device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b, const f32x4_t& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
-                                                   0, 0, 0);
-}
-
-// B fragment of one 16x32 k-half: four int4 bytes -> eight bf16 (1 + q/16) in pair order.
-__device__ __forceinline__ uint4 bfrag(uint32_t qd) {
-    uint32_t p[4];
-    int4x8_to_bf16_pairs(qd, p);
-    return make_uint4(p[0], p[1], p[2], p[3]);
-}
-
-// Stages one 64x64 activation group into LDS (pair order per 8) and its row sums.
-// Thread tid covers row tid/4, columns 16*(tid%4) .. +16.
-__device__ __forceinline__ void stage_store(uint16_t* __restrict__ a_lds, float* __restrict__ x_lds, int tid,
-                                            const uint4& v0, const uint4& v1) {
-    const int row = tid >> 2, qq = tid & 3;
-    const uint32_t i0[4] = {v0.x, v0.y, v0.z, v0.w};
-    const uint32_t i1[4] = {v1.x, v1.y, v1.z, v1.w};
-    uint32_t p0[4], p1[4];
-    bf16x8_to_pair_order(i0, p0);
-    bf16x8_to_pair_order(i1, p1);
-    uint4* dst = reinterpret_cast<uint4*>(a_lds + row * A_STRIDE + 16 * qq);
-    dst[0] = make_uint4(p0[0], p0[1], p0[2], p0[3]);
-    dst[1] = make_uint4(p1[0], p1[1], p1[2], p1[3]);
-    float s = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        s += bf16_to_f32(i0[j] & 0xFFFFu);
-        s += bf16_to_f32(i0[j] >> 16);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        s += bf16_to_f32(i1[j] & 0xFFFFu);
-        s += bf16_to_f32(i1[j] >> 16);
-    }
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    if (qq == 0) x_lds[row] = s;
-}
+__device__ __forceinline__ uint32_t ld32(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
 
 // ---------------------------------------------------------------- gate/up + SwiGLU
 // Grid: (max_tiles, I / 64). Wavefront w computes gate and up for intermediate
@@ -198,11 +165,10 @@ __global__ __launch_bounds__(256) void gateup_gemm_kernel(const uint8_t* __restr
     const Tile tl = tiles[blockIdx.x];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lg = lane >> 4, lc = lane & 15;
-    const int ib = blockIdx.y;
-    const int i_col = ib * BN + wave * 16 + lc;  // this lane's intermediate column (weight row)
-    const int n_ms = (tl.nrows + 15) >> 4;       // active 16-row subtiles (wave-uniform)
+    const int i_col = blockIdx.y * BN + wave * 16 + lc;  // this lane's intermediate column (weight row)
+    const int n_ms = (tl.nrows + 15) >> 4;               // active 16-row subtiles (wave-uniform)
 
-    // activation rows of this thread's staging slot
+    // activation row of this thread's staging slot
     const int srow = tid >> 2, sq = tid & 3;
     const bool srow_ok = srow < tl.nrows;
     const uint16_t* xsrc = x + (size_t)(srow_ok ? order[tl.row0 + srow] / S : 0) * H + 16 * sq;
@@ -220,51 +186,76 @@ __global__ __launch_bounds__(256) void gateup_gemm_kernel(const uint8_t* __restr
         accu[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     const int G = H / 64;
-    uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
-    if (srow_ok) {
-        v0 = *reinterpret_cast<const uint4*>(xsrc);
-        v1 = *reinterpret_cast<const uint4*>(xsrc + 8);
-    }
-    stage_store(a_lds[0], x_lds[0], tid, v0, v1);
-    __syncthreads();
-    for (int g = 0; g < G; ++g) {
-        const int buf = g & 1;
-        // issue the next group's activation loads and this group's weight loads
-        if (g + 1 < G && srow_ok) {
-            v0 = *reinterpret_cast<const uint4*>(xsrc + 64 * (g + 1));
-            v1 = *reinterpret_cast<const uint4*>(xsrc + 64 * (g + 1) + 8);
-        }
-        const uint32_t qg0 = *reinterpret_cast<const uint32_t*>(gq + 32 * g);
-        const uint32_t qg1 = *reinterpret_cast<const uint32_t*>(gq + 32 * g + 16);
-        const uint32_t qu0 = *reinterpret_cast<const uint32_t*>(uq + 32 * g);
-        const uint32_t qu1 = *reinterpret_cast<const uint32_t*>(uq + 32 * g + 16);
-        const uint32_t sbg = gsb[g], sbu = usb[g];
-        const uint4 bg0 = bfrag(qg0), bg1 = bfrag(qg1), bu0 = bfrag(qu0), bu1 = bfrag(qu1);
-        const float sg = 16.f * bf16_to_f32(sbg & 0xFFFFu), cg = bf16_to_f32(sbg >> 16) - sg;
-        const float su = 16.f * bf16_to_f32(sbu & 0xFFFFu), cu = bf16_to_f32(sbu >> 16) - su;
-        const uint16_t* al = a_lds[buf];
+    uint32_t bq[PD_GU][4], bs[PD_GU][2];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            if (m < n_ms) {
-                const uint4 a0 = *reinterpret_cast<const uint4*>(al + (16 * m + lc) * A_STRIDE + 8 * lg);
-                const uint4 a1 = *reinterpret_cast<const uint4*>(al + (16 * m + lc) * A_STRIDE + 32 + 8 * lg);
-                const float4 xs = *reinterpret_cast<const float4*>(&x_lds[buf][16 * m + 4 * lg]);
-                f32x4_t pg = mfma16x16x32(a0, bg0, f32x4_t{0.f, 0.f, 0.f, 0.f});
-                pg = mfma16x16x32(a1, bg1, pg);
-                f32x4_t pu = mfma16x16x32(a0, bu0, f32x4_t{0.f, 0.f, 0.f, 0.f});
-                pu = mfma16x16x32(a1, bu1, pu);
-                accg[m][0] = fmaf(cg, xs.x, fmaf(sg, pg[0], accg[m][0]));
-                accg[m][1] = fmaf(cg, xs.y, fmaf(sg, pg[1], accg[m][1]));
-                accg[m][2] = fmaf(cg, xs.z, fmaf(sg, pg[2], accg[m][2]));
-                accg[m][3] = fmaf(cg, xs.w, fmaf(sg, pg[3], accg[m][3]));
-                accu[m][0] = fmaf(cu, xs.x, fmaf(su, pu[0], accu[m][0]));
-                accu[m][1] = fmaf(cu, xs.y, fmaf(su, pu[1], accu[m][1]));
-                accu[m][2] = fmaf(cu, xs.z, fmaf(su, pu[2], accu[m][2]));
-                accu[m][3] = fmaf(cu, xs.w, fmaf(su, pu[3], accu[m][3]));
-            }
+    for (int u = 0; u < PD_GU; ++u) {
+        if (u < G) {
+            bq[u][0] = ld32(gq + 32 * u);
+            bq[u][1] = ld32(gq + 32 * u + 16);
+            bq[u][2] = ld32(uq + 32 * u);
+            bq[u][3] = ld32(uq + 32 * u + 16);
+            bs[u][0] = gsb[u];
+            bs[u][1] = usb[u];
         }
-        if (g + 1 < G) stage_store(a_lds[buf ^ 1], x_lds[buf ^ 1], tid, v0, v1);
-        __syncthreads();
+    }
+    uint4 xr[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) xr[i][0] = xr[i][1] = make_uint4(0, 0, 0, 0);
+    if (srow_ok) {
+        xr[0][0] = *reinterpret_cast<const uint4*>(xsrc);
+        xr[0][1] = *reinterpret_cast<const uint4*>(xsrc + 8);
+        if (G > 1) {
+            xr[1][0] = *reinterpret_cast<const uint4*>(xsrc + 64);
+            xr[1][1] = *reinterpret_cast<const uint4*>(xsrc + 72);
+        }
+    }
+    stage_store(a_lds[0], x_lds[0], tid, xr[0][0], xr[0][1]);
+    __syncthreads();
+    for (int g0 = 0; g0 < G; g0 += PD_GU) {
+#pragma unroll
+        for (int u = 0; u < PD_GU; ++u) {
+            const int g = g0 + u;
+            if (g >= G) break;  // uniform
+            if (g + 2 < G && srow_ok) {
+                xr[u & 1][0] = *reinterpret_cast<const uint4*>(xsrc + 64 * (g + 2));
+                xr[u & 1][1] = *reinterpret_cast<const uint4*>(xsrc + 64 * (g + 2) + 8);
+            }
+            const uint4 bg0 = bfrag(bq[u][0]), bg1 = bfrag(bq[u][1]), bu0 = bfrag(bq[u][2]), bu1 = bfrag(bq[u][3]);
+            const float sg = 16.f * bf16_to_f32(bs[u][0] & 0xFFFFu), cg = bf16_to_f32(bs[u][0] >> 16) - sg;
+            const float su = 16.f * bf16_to_f32(bs[u][1] & 0xFFFFu), cu = bf16_to_f32(bs[u][1] >> 16) - su;
+            if (g + PD_GU < G) {
+                bq[u][0] = ld32(gq + 32 * (g + PD_GU));
+                bq[u][1] = ld32(gq + 32 * (g + PD_GU) + 16);
+                bq[u][2] = ld32(uq + 32 * (g + PD_GU));
+                bq[u][3] = ld32(uq + 32 * (g + PD_GU) + 16);
+                bs[u][0] = gsb[g + PD_GU];
+                bs[u][1] = usb[g + PD_GU];
+            }
+            const uint16_t* al = a_lds[u & 1];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                if (m < n_ms) {
+                    const uint4 a0 = *reinterpret_cast<const uint4*>(al + (16 * m + lc) * A_STRIDE + 8 * lg);
+                    const uint4 a1 = *reinterpret_cast<const uint4*>(al + (16 * m + lc) * A_STRIDE + 32 + 8 * lg);
+                    const float4 xs = *reinterpret_cast<const float4*>(&x_lds[u & 1][16 * m + 4 * lg]);
+                    f32x4_t pg = mfma16x16x32(a0, bg0, f32x4_t{0.f, 0.f, 0.f, 0.f});
+                    pg = mfma16x16x32(a1, bg1, pg);
+                    f32x4_t pu = mfma16x16x32(a0, bu0, f32x4_t{0.f, 0.f, 0.f, 0.f});
+                    pu = mfma16x16x32(a1, bu1, pu);
+                    accg[m][0] = fmaf(cg, xs.x, fmaf(sg, pg[0], accg[m][0]));
+                    accg[m][1] = fmaf(cg, xs.y, fmaf(sg, pg[1], accg[m][1]));
+                    accg[m][2] = fmaf(cg, xs.z, fmaf(sg, pg[2], accg[m][2]));
+                    accg[m][3] = fmaf(cg, xs.w, fmaf(sg, pg[3], accg[m][3]));
+                    accu[m][0] = fmaf(cu, xs.x, fmaf(su, pu[0], accu[m][0]));
+                    accu[m][1] = fmaf(cu, xs.y, fmaf(su, pu[1], accu[m][1]));
+                    accu[m][2] = fmaf(cu, xs.z, fmaf(su, pu[2], accu[m][2]));
+                    accu[m][3] = fmaf(cu, xs.w, fmaf(su, pu[3], accu[m][3]));
+                }
+            }
+            if (g + 1 < G) stage_store(a_lds[(u + 1) & 1], x_lds[(u + 1) & 1], tid, xr[(u + 1) & 1][0],
+                                       xr[(u + 1) & 1][1]);
+            __syncthreads();
+        }
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -310,41 +301,63 @@ __global__ __launch_bounds__(256) void down_gemm_kernel(const uint8_t* __restric
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int G = I / 64;
-    uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
-    if (srow_ok) {
-        v0 = *reinterpret_cast<const uint4*>(hsrc);
-        v1 = *reinterpret_cast<const uint4*>(hsrc + 8);
-    }
-    stage_store(a_lds[0], x_lds[0], tid, v0, v1);
-    __syncthreads();
-    for (int g = 0; g < G; ++g) {
-        const int buf = g & 1;
-        if (g + 1 < G && srow_ok) {
-            v0 = *reinterpret_cast<const uint4*>(hsrc + 64 * (g + 1));
-            v1 = *reinterpret_cast<const uint4*>(hsrc + 64 * (g + 1) + 8);
-        }
-        const uint32_t q0 = *reinterpret_cast<const uint32_t*>(dq + 32 * g);
-        const uint32_t q1 = *reinterpret_cast<const uint32_t*>(dq + 32 * g + 16);
-        const uint32_t sb = dsb[g];
-        const uint4 b0 = bfrag(q0), b1 = bfrag(q1);
-        const float sc = 16.f * bf16_to_f32(sb & 0xFFFFu), cc = bf16_to_f32(sb >> 16) - sc;
-        const uint16_t* al = a_lds[buf];
+    uint32_t bq[PD_DN][2], bs[PD_DN];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            if (m < n_ms) {
-                const uint4 a0 = *reinterpret_cast<const uint4*>(al + (16 * m + lc) * A_STRIDE + 8 * lg);
-                const uint4 a1 = *reinterpret_cast<const uint4*>(al + (16 * m + lc) * A_STRIDE + 32 + 8 * lg);
-                const float4 xs = *reinterpret_cast<const float4*>(&x_lds[buf][16 * m + 4 * lg]);
-                f32x4_t p = mfma16x16x32(a0, b0, f32x4_t{0.f, 0.f, 0.f, 0.f});
-                p = mfma16x16x32(a1, b1, p);
-                acc[m][0] = fmaf(cc, xs.x, fmaf(sc, p[0], acc[m][0]));
-                acc[m][1] = fmaf(cc, xs.y, fmaf(sc, p[1], acc[m][1]));
-                acc[m][2] = fmaf(cc, xs.z, fmaf(sc, p[2], acc[m][2]));
-                acc[m][3] = fmaf(cc, xs.w, fmaf(sc, p[3], acc[m][3]));
-            }
+    for (int u = 0; u < PD_DN; ++u) {
+        if (u < G) {
+            bq[u][0] = ld32(dq + 32 * u);
+            bq[u][1] = ld32(dq + 32 * u + 16);
+            bs[u] = dsb[u];
         }
-        if (g + 1 < G) stage_store(a_lds[buf ^ 1], x_lds[buf ^ 1], tid, v0, v1);
-        __syncthreads();
+    }
+    uint4 xr[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) xr[i][0] = xr[i][1] = make_uint4(0, 0, 0, 0);
+    if (srow_ok) {
+        xr[0][0] = *reinterpret_cast<const uint4*>(hsrc);
+        xr[0][1] = *reinterpret_cast<const uint4*>(hsrc + 8);
+        if (G > 1) {
+            xr[1][0] = *reinterpret_cast<const uint4*>(hsrc + 64);
+            xr[1][1] = *reinterpret_cast<const uint4*>(hsrc + 72);
+        }
+    }
+    stage_store(a_lds[0], x_lds[0], tid, xr[0][0], xr[0][1]);
+    __syncthreads();
+    for (int g0 = 0; g0 < G; g0 += PD_DN) {
+#pragma unroll
+        for (int u = 0; u < PD_DN; ++u) {
+            const int g = g0 + u;
+            if (g >= G) break;  // uniform
+            if (g + 2 < G && srow_ok) {
+                xr[u & 1][0] = *reinterpret_cast<const uint4*>(hsrc + 64 * (g + 2));
+                xr[u & 1][1] = *reinterpret_cast<const uint4*>(hsrc + 64 * (g + 2) + 8);
+            }
+            const uint4 b0 = bfrag(bq[u][0]), b1 = bfrag(bq[u][1]);
+            const float sc = 16.f * bf16_to_f32(bs[u] & 0xFFFFu), cc = bf16_to_f32(bs[u] >> 16) - sc;
+            if (g + PD_DN < G) {
+                bq[u][0] = ld32(dq + 32 * (g + PD_DN));
+                bq[u][1] = ld32(dq + 32 * (g + PD_DN) + 16);
+                bs[u] = dsb[g + PD_DN];
+            }
+            const uint16_t* al = a_lds[u & 1];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                if (m < n_ms) {
+                    const uint4 a0 = *reinterpret_cast<const uint4*>(al + (16 * m + lc) * A_STRIDE + 8 * lg);
+                    const uint4 a1 = *reinterpret_cast<const uint4*>(al + (16 * m + lc) * A_STRIDE + 32 + 8 * lg);
+                    const float4 xs = *reinterpret_cast<const float4*>(&x_lds[u & 1][16 * m + 4 * lg]);
+                    f32x4_t p = mfma16x16x32(a0, b0, f32x4_t{0.f, 0.f, 0.f, 0.f});
+                    p = mfma16x16x32(a1, b1, p);
+                    acc[m][0] = fmaf(cc, xs.x, fmaf(sc, p[0], acc[m][0]));
+                    acc[m][1] = fmaf(cc, xs.y, fmaf(sc, p[1], acc[m][1]));
+                    acc[m][2] = fmaf(cc, xs.z, fmaf(sc, p[2], acc[m][2]));
+                    acc[m][3] = fmaf(cc, xs.w, fmaf(sc, p[3], acc[m][3]));
+                }
+            }
+            if (g + 1 < G) stage_store(a_lds[(u + 1) & 1], x_lds[(u + 1) & 1], tid, xr[(u + 1) & 1][0],
+                                       xr[(u + 1) & 1][1]);
+            __syncthreads();
+        }
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {

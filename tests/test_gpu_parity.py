@@ -71,9 +71,15 @@ def out_tolerance_check(gpu_bits, ref_bits, rows=None):
     return stats
 
 
-def check_logits(gpu_logits, ref_logits):
+def check_logits(gpu_logits, ref_logits, fp64_path=True):
+    """fp64-accumulated logits (T <= 16): within 1 fp32 ulp of the oracle's.
+    Matrix-core logits (T > 16, fp32 accumulation): within 2e-6 absolute."""
     g = gpu_logits.astype(np.float32)
     r = ref_logits.astype(np.float32)
+    if not fp64_path:
+        d = np.abs(g.astype(np.float64) - r.astype(np.float64))
+        assert d.max() <= 2e-6, d.max()
+        return float((d == 0).mean())
     gi = g.view(np.int32).astype(np.int64)
     ri = r.view(np.int32).astype(np.int64)
     diff = np.abs(gi - ri)
@@ -210,8 +216,9 @@ def test_router_logits_and_picks(gpu, name, T):
     W = O.router_matrix(c.layers[0])
     E = c.shape.n_experts
     ref = O.router_logits(c.x, W, c.layers[0].logit_bias, E)
-    exact = check_logits(res["logits"], ref)
-    assert exact > 0.999
+    exact = check_logits(res["logits"], ref, fp64_path=c.T <= 16)
+    if c.T <= 16:
+        assert exact > 0.999
     check_picks(res["ids"], ref, c.shape.top_k, E)
     staged_route_check(gpu, res, E, c.shape.top_k)
 
@@ -325,7 +332,7 @@ def test_prefill_full_size(gpu, name):
     E, k = 256, 8
     W = O.router_matrix(c.layers[0])
     ref_logits = O.router_logits(c.x, W, c.layers[0].logit_bias, E)
-    check_logits(res["logits"], ref_logits)
+    check_logits(res["logits"], ref_logits, fp64_path=False)
     n_tie, n_flip = check_picks(res["ids"], ref_logits, k, E)
     print(name, "near-tie tokens", n_tie, "flipped among them", n_flip)
     staged_route_check(gpu, res, E, k)
