@@ -138,46 +138,159 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const int32_t* __restric
         for (int t = tid; t < T; t += blockDim.x) order[off[E] + t] = t * S + k;
 }
 
-// ---------------------------------------------------------------- pipelining
-// Both GEMMs walk K in 64-wide groups. Weight fragments (the HBM stream) are
-// loaded PD groups ahead into a register ring; the gathered activation group is
-// loaded two groups ahead into registers and staged into a double-buffered LDS
-// tile one group ahead; one barrier per group. PD is even so the LDS and register
-// slots of group g are g & 1 at every unrolled position.
-constexpr int PD_GU = 4;  // gate/up: 6 words per group in flight per lane
-constexpr int PD_DN = 8;  // down: 3 words per group
+// ---------------------------------------------------------------- staged GEMM core
+// Both expert GEMMs walk K in chunks of KC = 128 (two quantisation groups). Per
+// chunk a workgroup stages, with coalesced 16-byte loads:
+//   A: 64 activation rows x 128 bf16 (256 contiguous bytes per row; 16 lanes per
+//      row), stored in LDS in pair order with the per-group row sums X;
+//   B: NB int4 weight rows x 64 bytes (4 lanes per row) and their two (scale, bias)
+//      words.
+// The next chunk's loads are issued into registers before the current chunk is
+// multiplied, so they are in flight during the MFMAs; two barriers per chunk.
+constexpr int KC = 128;
+constexpr int AS = KC + 8;       // A row stride in LDS (bf16)
+constexpr int BS = KC / 2 + 16;  // B row stride in LDS (bytes)
 
-__device__ __forceinline__ uint32_t ld32(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+// Sum over aligned groups of 8 lanes (DPP); the result is in every lane of the group.
+__device__ __forceinline__ float sum8_lanes(float v) {
+    v += __uint_as_float(dpp_u32<0xB1, 0xF>(__float_as_uint(v)));
+    v += __uint_as_float(dpp_u32<0x4E, 0xF>(__float_as_uint(v)));
+    v += __uint_as_float(dpp_u32<0x141, 0xF>(__float_as_uint(v)));
+    return v;
+}
+
+// A chunk: thread tid holds 16-byte piece c16 = tid % 16 of rows tid/16 + 16 j.
+struct AChunk {
+    uint4 v[4];
+};
+
+__device__ __forceinline__ void load_a(const uint16_t* const rowp[4], int c, int kc_valid, int tid, AChunk& a) {
+    const int c16 = tid & 15;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        a.v[j] = (rowp[j] && 8 * c16 < kc_valid) ? *reinterpret_cast<const uint4*>(rowp[j] + c * KC + 8 * c16)
+                                                 : make_uint4(0, 0, 0, 0);
+}
+
+__device__ __forceinline__ void store_a(uint16_t* __restrict__ a_lds, float (*x_lds)[64], const AChunk& a, int tid) {
+    const int c16 = tid & 15;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = (tid >> 4) + 16 * j;
+        const uint32_t in[4] = {a.v[j].x, a.v[j].y, a.v[j].z, a.v[j].w};
+        uint32_t out[4];
+        bf16x8_to_pair_order(in, out);
+        *reinterpret_cast<uint4*>(a_lds + row * AS + 8 * c16) = make_uint4(out[0], out[1], out[2], out[3]);
+        float sm = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sm += bf16_to_f32(in[i] & 0xFFFFu);
+            sm += bf16_to_f32(in[i] >> 16);
+        }
+        sm = sum8_lanes(sm);
+        if ((c16 & 7) == 0) x_lds[c16 >> 3][row] = sm;
+    }
+}
+
+// B chunk of NB rows: thread tid holds 16-byte piece tid % 4 of rows tid/4 + 64 j,
+// and (tid < NB) the two (scale, bias) words of row tid.
+template <int NB>
+struct BChunk {
+    uint4 v[NB / 64];
+    uint2 sb;
+};
+
+template <int NB, typename RowQ, typename RowSB>
+__device__ __forceinline__ void load_b(RowQ rowq, RowSB rowsb, int c, int kc_valid, int tid, BChunk<NB>& b) {
+    const int c4 = tid & 3;
+#pragma unroll
+    for (int j = 0; j < NB / 64; ++j) {
+        const int row = (tid >> 2) + 64 * j;
+        b.v[j] = 16 * c4 < kc_valid / 2 ? *reinterpret_cast<const uint4*>(rowq(row) + c * (KC / 2) + 16 * c4)
+                                        : make_uint4(0, 0, 0, 0);
+    }
+    if (tid < NB) {
+        const uint32_t* sp = rowsb(tid) + c * (KC / 64);
+        b.sb.x = sp[0];
+        b.sb.y = kc_valid > 64 ? sp[1] : 0u;
+    }
+}
+
+template <int NB>
+__device__ __forceinline__ void store_b(uint8_t* __restrict__ b_lds, uint2* __restrict__ sb_lds, const BChunk<NB>& b,
+                                        int tid) {
+    const int c4 = tid & 3;
+#pragma unroll
+    for (int j = 0; j < NB / 64; ++j) {
+        const int row = (tid >> 2) + 64 * j;
+        *reinterpret_cast<uint4*>(b_lds + row * BS + 16 * c4) = b.v[j];
+    }
+    if (tid < NB) sb_lds[tid] = b.sb;
+}
+
+// One 64-wide group gi of the staged chunk for weight row br: accumulates
+// 16*s*P + (b - 16*s)*X into acc for the m-subtiles below n_ms.
+__device__ __forceinline__ void mma_group(const uint16_t* __restrict__ a_lds, const float (*x_lds)[64],
+                                          const uint8_t* __restrict__ b_lds, const uint2* __restrict__ sb_lds, int br,
+                                          int gi, int n_ms, int lc, int lg, f32x4_t acc[4]) {
+    const uint8_t* bp = b_lds + br * BS + 32 * gi + 4 * lg;
+    const uint4 b0 = bfrag(*reinterpret_cast<const uint32_t*>(bp));
+    const uint4 b1 = bfrag(*reinterpret_cast<const uint32_t*>(bp + 16));
+    const uint2 sbw = sb_lds[br];
+    const uint32_t sb = gi ? sbw.y : sbw.x;
+    const float s16 = 16.f * bf16_to_f32(sb & 0xFFFFu), cc = bf16_to_f32(sb >> 16) - s16;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        if (m < n_ms) {
+            const uint16_t* ar = a_lds + (16 * m + lc) * AS + 64 * gi + 8 * lg;
+            const uint4 a0 = *reinterpret_cast<const uint4*>(ar);
+            const uint4 a1 = *reinterpret_cast<const uint4*>(ar + 32);
+            const float4 xs = *reinterpret_cast<const float4*>(&x_lds[gi][16 * m + 4 * lg]);
+            f32x4_t p = mfma16x16x32(a0, b0, f32x4_t{0.f, 0.f, 0.f, 0.f});
+            p = mfma16x16x32(a1, b1, p);
+            acc[m][0] = fmaf(cc, xs.x, fmaf(s16, p[0], acc[m][0]));
+            acc[m][1] = fmaf(cc, xs.y, fmaf(s16, p[1], acc[m][1]));
+            acc[m][2] = fmaf(cc, xs.z, fmaf(s16, p[2], acc[m][2]));
+            acc[m][3] = fmaf(cc, xs.w, fmaf(s16, p[3], acc[m][3]));
+        }
+    }
+}
 
 // ---------------------------------------------------------------- gate/up + SwiGLU
-// Grid: (max_tiles, I / 64). Wavefront w computes gate and up for intermediate
-// columns ib*64 + 16w .. +16 over the tile's rows and writes
-// h[row][i] = bf16(silu(gate) * up) in expert-sorted row order.
+// Grid: (max_tiles, I / 64). B rows 0..63 are gate rows ib*64 .., rows 64..127 the
+// matching up rows. Wavefront w computes gate and up for intermediate columns
+// ib*64 + 16w .. +16 over the tile's rows and writes h[row][i] = bf16(silu(gate) * up)
+// in expert-sorted row order.
 __global__ __launch_bounds__(256) void gateup_gemm_kernel(const uint8_t* __restrict__ packed, ExpertLayout L, int H,
                                                           int I, int S, const uint16_t* __restrict__ x,
                                                           const int32_t* __restrict__ ntiles,
                                                           const Tile* __restrict__ tiles,
                                                           const int32_t* __restrict__ order,
                                                           uint16_t* __restrict__ hbuf) {
-    __shared__ __attribute__((aligned(16))) uint16_t a_lds[2][BM * A_STRIDE];
-    __shared__ __attribute__((aligned(16))) float x_lds[2][BM];
+    __shared__ __attribute__((aligned(16))) uint16_t a_lds[BM * AS];
+    __shared__ __attribute__((aligned(16))) float x_lds[2][64];
+    __shared__ __attribute__((aligned(16))) uint8_t b_lds[128 * BS];
+    __shared__ __attribute__((aligned(16))) uint2 sb_lds[128];
     if ((int)blockIdx.x >= *ntiles) return;
     const Tile tl = tiles[blockIdx.x];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lg = lane >> 4, lc = lane & 15;
-    const int i_col = blockIdx.y * BN + wave * 16 + lc;  // this lane's intermediate column (weight row)
-    const int n_ms = (tl.nrows + 15) >> 4;               // active 16-row subtiles (wave-uniform)
+    const int i0 = blockIdx.y * BN;
+    const int n_ms = (tl.nrows + 15) >> 4;
 
-    // activation row of this thread's staging slot
-    const int srow = tid >> 2, sq = tid & 3;
-    const bool srow_ok = srow < tl.nrows;
-    const uint16_t* xsrc = x + (size_t)(srow_ok ? order[tl.row0 + srow] / S : 0) * H + 16 * sq;
-
+    const uint16_t* rowp[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = (tid >> 4) + 16 * j;
+        rowp[j] = row < tl.nrows ? x + (size_t)(order[tl.row0 + row] / S) * H : nullptr;
+    }
     const uint8_t* base = packed + (size_t)tl.expert * L.stride;
-    const uint8_t* gq = base + L.gate_q + (size_t)i_col * (H / 2) + 4 * lg;
-    const uint8_t* uq = base + L.up_q + (size_t)i_col * (H / 2) + 4 * lg;
-    const uint32_t* gsb = reinterpret_cast<const uint32_t*>(base + L.gate_sb) + (size_t)i_col * (H / 64);
-    const uint32_t* usb = reinterpret_cast<const uint32_t*>(base + L.up_sb) + (size_t)i_col * (H / 64);
+    const uint8_t* gq = base + L.gate_q + (size_t)i0 * (H / 2);
+    const uint8_t* uq = base + L.up_q + (size_t)i0 * (H / 2);
+    const uint32_t* gsb = reinterpret_cast<const uint32_t*>(base + L.gate_sb) + (size_t)i0 * (H / 64);
+    const uint32_t* usb = reinterpret_cast<const uint32_t*>(base + L.up_sb) + (size_t)i0 * (H / 64);
+    auto rowq = [&](int r) { return r < 64 ? gq + (size_t)r * (H / 2) : uq + (size_t)(r - 64) * (H / 2); };
+    auto rowsb = [&](int r) { return r < 64 ? gsb + (size_t)r * (H / 64) : usb + (size_t)(r - 64) * (H / 64); };
 
     f32x4_t accg[4], accu[4];
 #pragma unroll
@@ -185,78 +298,28 @@ __global__ __launch_bounds__(256) void gateup_gemm_kernel(const uint8_t* __restr
         accg[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         accu[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    const int G = H / 64;
-    uint32_t bq[PD_GU][4], bs[PD_GU][2];
-#pragma unroll
-    for (int u = 0; u < PD_GU; ++u) {
-        if (u < G) {
-            bq[u][0] = ld32(gq + 32 * u);
-            bq[u][1] = ld32(gq + 32 * u + 16);
-            bq[u][2] = ld32(uq + 32 * u);
-            bq[u][3] = ld32(uq + 32 * u + 16);
-            bs[u][0] = gsb[u];
-            bs[u][1] = usb[u];
+    const int NC = (H + KC - 1) / KC;
+    AChunk ac;
+    BChunk<128> bc;
+    load_a(rowp, 0, min(KC, H), tid, ac);
+    load_b<128>(rowq, rowsb, 0, min(KC, H), tid, bc);
+    for (int c = 0; c < NC; ++c) {
+        const int kcv = min(KC, H - c * KC);
+        store_a(a_lds, x_lds, ac, tid);
+        store_b<128>(b_lds, sb_lds, bc, tid);
+        __syncthreads();
+        if (c + 1 < NC) {
+            const int kn = min(KC, H - (c + 1) * KC);
+            load_a(rowp, c + 1, kn, tid, ac);
+            load_b<128>(rowq, rowsb, c + 1, kn, tid, bc);
         }
-    }
-    uint4 xr[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) xr[i][0] = xr[i][1] = make_uint4(0, 0, 0, 0);
-    if (srow_ok) {
-        xr[0][0] = *reinterpret_cast<const uint4*>(xsrc);
-        xr[0][1] = *reinterpret_cast<const uint4*>(xsrc + 8);
-        if (G > 1) {
-            xr[1][0] = *reinterpret_cast<const uint4*>(xsrc + 64);
-            xr[1][1] = *reinterpret_cast<const uint4*>(xsrc + 72);
+        for (int gi = 0; gi < kcv / 64; ++gi) {
+            mma_group(a_lds, x_lds, b_lds, sb_lds, wave * 16 + lc, gi, n_ms, lc, lg, accg);
+            mma_group(a_lds, x_lds, b_lds, sb_lds, 64 + wave * 16 + lc, gi, n_ms, lc, lg, accu);
         }
+        __syncthreads();
     }
-    stage_store(a_lds[0], x_lds[0], tid, xr[0][0], xr[0][1]);
-    __syncthreads();
-    for (int g0 = 0; g0 < G; g0 += PD_GU) {
-#pragma unroll
-        for (int u = 0; u < PD_GU; ++u) {
-            const int g = g0 + u;
-            if (g >= G) break;  // uniform
-            if (g + 2 < G && srow_ok) {
-                xr[u & 1][0] = *reinterpret_cast<const uint4*>(xsrc + 64 * (g + 2));
-                xr[u & 1][1] = *reinterpret_cast<const uint4*>(xsrc + 64 * (g + 2) + 8);
-            }
-            const uint4 bg0 = bfrag(bq[u][0]), bg1 = bfrag(bq[u][1]), bu0 = bfrag(bq[u][2]), bu1 = bfrag(bq[u][3]);
-            const float sg = 16.f * bf16_to_f32(bs[u][0] & 0xFFFFu), cg = bf16_to_f32(bs[u][0] >> 16) - sg;
-            const float su = 16.f * bf16_to_f32(bs[u][1] & 0xFFFFu), cu = bf16_to_f32(bs[u][1] >> 16) - su;
-            if (g + PD_GU < G) {
-                bq[u][0] = ld32(gq + 32 * (g + PD_GU));
-                bq[u][1] = ld32(gq + 32 * (g + PD_GU) + 16);
-                bq[u][2] = ld32(uq + 32 * (g + PD_GU));
-                bq[u][3] = ld32(uq + 32 * (g + PD_GU) + 16);
-                bs[u][0] = gsb[g + PD_GU];
-                bs[u][1] = usb[g + PD_GU];
-            }
-            const uint16_t* al = a_lds[u & 1];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                if (m < n_ms) {
-                    const uint4 a0 = *reinterpret_cast<const uint4*>(al + (16 * m + lc) * A_STRIDE + 8 * lg);
-                    const uint4 a1 = *reinterpret_cast<const uint4*>(al + (16 * m + lc) * A_STRIDE + 32 + 8 * lg);
-                    const float4 xs = *reinterpret_cast<const float4*>(&x_lds[u & 1][16 * m + 4 * lg]);
-                    f32x4_t pg = mfma16x16x32(a0, bg0, f32x4_t{0.f, 0.f, 0.f, 0.f});
-                    pg = mfma16x16x32(a1, bg1, pg);
-                    f32x4_t pu = mfma16x16x32(a0, bu0, f32x4_t{0.f, 0.f, 0.f, 0.f});
-                    pu = mfma16x16x32(a1, bu1, pu);
-                    accg[m][0] = fmaf(cg, xs.x, fmaf(sg, pg[0], accg[m][0]));
-                    accg[m][1] = fmaf(cg, xs.y, fmaf(sg, pg[1], accg[m][1]));
-                    accg[m][2] = fmaf(cg, xs.z, fmaf(sg, pg[2], accg[m][2]));
-                    accg[m][3] = fmaf(cg, xs.w, fmaf(sg, pg[3], accg[m][3]));
-                    accu[m][0] = fmaf(cu, xs.x, fmaf(su, pu[0], accu[m][0]));
-                    accu[m][1] = fmaf(cu, xs.y, fmaf(su, pu[1], accu[m][1]));
-                    accu[m][2] = fmaf(cu, xs.z, fmaf(su, pu[2], accu[m][2]));
-                    accu[m][3] = fmaf(cu, xs.w, fmaf(su, pu[3], accu[m][3]));
-                }
-            }
-            if (g + 1 < G) stage_store(a_lds[(u + 1) & 1], x_lds[(u + 1) & 1], tid, xr[(u + 1) & 1][0],
-                                       xr[(u + 1) & 1][1]);
-            __syncthreads();
-        }
-    }
+    const int i_col = i0 + wave * 16 + lc;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
 #pragma unroll
@@ -272,93 +335,60 @@ __global__ __launch_bounds__(256) void gateup_gemm_kernel(const uint8_t* __restr
 }
 
 // ---------------------------------------------------------------- down + scatter
-// Grid: (max_tiles, H / 64). Wavefront w computes output columns nb*64 + 16w .. +16
-// of y for the tile's rows (A = h rows, contiguous in expert-sorted order) and
-// writes y[p][n] for the row's pick p = order[row].
+// Grid: (max_tiles, H / 64). B rows are down rows nb*64 .. +64; A = h rows,
+// contiguous in expert-sorted order. Wavefront w computes output columns
+// nb*64 + 16w .. +16 and writes y[p][n] for the row's pick p = order[row].
 __global__ __launch_bounds__(256) void down_gemm_kernel(const uint8_t* __restrict__ packed, ExpertLayout L, int H,
                                                         int I, const int32_t* __restrict__ ntiles,
                                                         const Tile* __restrict__ tiles,
                                                         const int32_t* __restrict__ order,
                                                         const uint16_t* __restrict__ hbuf, float* __restrict__ y) {
-    __shared__ __attribute__((aligned(16))) uint16_t a_lds[2][BM * A_STRIDE];
-    __shared__ __attribute__((aligned(16))) float x_lds[2][BM];
+    __shared__ __attribute__((aligned(16))) uint16_t a_lds[BM * AS];
+    __shared__ __attribute__((aligned(16))) float x_lds[2][64];
+    __shared__ __attribute__((aligned(16))) uint8_t b_lds[64 * BS];
+    __shared__ __attribute__((aligned(16))) uint2 sb_lds[64];
     if ((int)blockIdx.x >= *ntiles) return;
     const Tile tl = tiles[blockIdx.x];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lg = lane >> 4, lc = lane & 15;
-    const int n_col = blockIdx.y * BN + wave * 16 + lc;
+    const int n0 = blockIdx.y * BN;
     const int n_ms = (tl.nrows + 15) >> 4;
 
-    const int srow = tid >> 2, sq = tid & 3;
-    const bool srow_ok = srow < tl.nrows;
-    const uint16_t* hsrc = hbuf + (size_t)(tl.row0 + (srow_ok ? srow : 0)) * I + 16 * sq;
-
+    const uint16_t* rowp[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = (tid >> 4) + 16 * j;
+        rowp[j] = row < tl.nrows ? hbuf + (size_t)(tl.row0 + row) * I : nullptr;
+    }
     const uint8_t* base = packed + (size_t)tl.expert * L.stride;
-    const uint8_t* dq = base + L.down_q + (size_t)n_col * (I / 2) + 4 * lg;
-    const uint32_t* dsb = reinterpret_cast<const uint32_t*>(base + L.down_sb) + (size_t)n_col * (I / 64);
+    const uint8_t* dq = base + L.down_q + (size_t)n0 * (I / 2);
+    const uint32_t* dsb = reinterpret_cast<const uint32_t*>(base + L.down_sb) + (size_t)n0 * (I / 64);
+    auto rowq = [&](int r) { return dq + (size_t)r * (I / 2); };
+    auto rowsb = [&](int r) { return dsb + (size_t)r * (I / 64); };
 
     f32x4_t acc[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int G = I / 64;
-    uint32_t bq[PD_DN][2], bs[PD_DN];
-#pragma unroll
-    for (int u = 0; u < PD_DN; ++u) {
-        if (u < G) {
-            bq[u][0] = ld32(dq + 32 * u);
-            bq[u][1] = ld32(dq + 32 * u + 16);
-            bs[u] = dsb[u];
+    const int NC = (I + KC - 1) / KC;
+    AChunk ac;
+    BChunk<64> bc;
+    load_a(rowp, 0, min(KC, I), tid, ac);
+    load_b<64>(rowq, rowsb, 0, min(KC, I), tid, bc);
+    for (int c = 0; c < NC; ++c) {
+        const int kcv = min(KC, I - c * KC);
+        store_a(a_lds, x_lds, ac, tid);
+        store_b<64>(b_lds, sb_lds, bc, tid);
+        __syncthreads();
+        if (c + 1 < NC) {
+            const int kn = min(KC, I - (c + 1) * KC);
+            load_a(rowp, c + 1, kn, tid, ac);
+            load_b<64>(rowq, rowsb, c + 1, kn, tid, bc);
         }
+        for (int gi = 0; gi < kcv / 64; ++gi)
+            mma_group(a_lds, x_lds, b_lds, sb_lds, wave * 16 + lc, gi, n_ms, lc, lg, acc);
+        __syncthreads();
     }
-    uint4 xr[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) xr[i][0] = xr[i][1] = make_uint4(0, 0, 0, 0);
-    if (srow_ok) {
-        xr[0][0] = *reinterpret_cast<const uint4*>(hsrc);
-        xr[0][1] = *reinterpret_cast<const uint4*>(hsrc + 8);
-        if (G > 1) {
-            xr[1][0] = *reinterpret_cast<const uint4*>(hsrc + 64);
-            xr[1][1] = *reinterpret_cast<const uint4*>(hsrc + 72);
-        }
-    }
-    stage_store(a_lds[0], x_lds[0], tid, xr[0][0], xr[0][1]);
-    __syncthreads();
-    for (int g0 = 0; g0 < G; g0 += PD_DN) {
-#pragma unroll
-        for (int u = 0; u < PD_DN; ++u) {
-            const int g = g0 + u;
-            if (g >= G) break;  // uniform
-            if (g + 2 < G && srow_ok) {
-                xr[u & 1][0] = *reinterpret_cast<const uint4*>(hsrc + 64 * (g + 2));
-                xr[u & 1][1] = *reinterpret_cast<const uint4*>(hsrc + 64 * (g + 2) + 8);
-            }
-            const uint4 b0 = bfrag(bq[u][0]), b1 = bfrag(bq[u][1]);
-            const float sc = 16.f * bf16_to_f32(bs[u] & 0xFFFFu), cc = bf16_to_f32(bs[u] >> 16) - sc;
-            if (g + PD_DN < G) {
-                bq[u][0] = ld32(dq + 32 * (g + PD_DN));
-                bq[u][1] = ld32(dq + 32 * (g + PD_DN) + 16);
-                bs[u] = dsb[g + PD_DN];
-            }
-            const uint16_t* al = a_lds[u & 1];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                if (m < n_ms) {
-                    const uint4 a0 = *reinterpret_cast<const uint4*>(al + (16 * m + lc) * A_STRIDE + 8 * lg);
-                    const uint4 a1 = *reinterpret_cast<const uint4*>(al + (16 * m + lc) * A_STRIDE + 32 + 8 * lg);
-                    const float4 xs = *reinterpret_cast<const float4*>(&x_lds[u & 1][16 * m + 4 * lg]);
-                    f32x4_t p = mfma16x16x32(a0, b0, f32x4_t{0.f, 0.f, 0.f, 0.f});
-                    p = mfma16x16x32(a1, b1, p);
-                    acc[m][0] = fmaf(cc, xs.x, fmaf(sc, p[0], acc[m][0]));
-                    acc[m][1] = fmaf(cc, xs.y, fmaf(sc, p[1], acc[m][1]));
-                    acc[m][2] = fmaf(cc, xs.z, fmaf(sc, p[2], acc[m][2]));
-                    acc[m][3] = fmaf(cc, xs.w, fmaf(sc, p[3], acc[m][3]));
-                }
-            }
-            if (g + 1 < G) stage_store(a_lds[(u + 1) & 1], x_lds[(u + 1) & 1], tid, xr[(u + 1) & 1][0],
-                                       xr[(u + 1) & 1][1]);
-            __syncthreads();
-        }
-    }
+    const int n_col = n0 + wave * 16 + lc;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
 #pragma unroll

@@ -66,7 +66,8 @@ def test_sizes(moe):
     sh = _big(moe)
     assert moe.moe_experts_packed_bytes(sh) == 257 * 1_769_472
     assert moe.moe_router_packed_bytes(sh) == 257 * 2048 + 257 * 32 * 4
-    assert moe.moe_decode_workspace_bytes(sh, 1) == 9216 + 256  # h rows (256-aligned) + counter word
+    # h rows (9 x 512 bf16) + control block + tagged logits (257 x 8 B, 256-aligned) + tagged h (9 x 256 x 8 B)
+    assert moe.moe_decode_workspace_bytes(sh, 1) == 9216 + 256 + 2304 + 18432
     assert moe.moe_prefill_workspace_bytes(sh, 4096) > 4096 * 9 * 512 * 2
     assert moe.moe_experts_packed_bytes(_big(moe, bits=8)) == 0
 
