@@ -111,7 +111,11 @@ moe_status moe_shape_check(const moe_shape* shape);
  *   gate q [I][H/2] | up q [I][H/2] | down q [H][I/2] |
  *   gate sb [I][H/64] | up sb [I][H/64] | down sb [H][I/64]
  * where every sb entry is a uint32 holding the group's bf16 scale in the low and
- * bf16 bias in the high half. q bytes are copied unchanged. */
+ * bf16 bias in the high half. q keeps the canonical byte order of each row, but
+ * the eight nibbles of every little-endian dword (weights k0..k7 of a row) are
+ * reordered: nibble j (bits 4j..4j+3) holds k_{2j} and nibble 4+j holds
+ * k_{2j+1}, j < 4. A shift by 4j then puts the pair (k_{2j}, k_{2j+1}) in bits 0..3
+ * and 16..19, i.e. next to each other as they sit in a bf16 activation row. */
 size_t moe_experts_packed_bytes(const moe_shape* shape);
 
 /* Packs canonical expert weights (device) into `packed` (device, packed_bytes >=

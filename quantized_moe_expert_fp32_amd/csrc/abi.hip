@@ -81,6 +81,31 @@ extern "C" size_t moe_router_packed_bytes(const moe_shape* sh) {
 }
 
 // Copies n16 16-byte units per expert from src (stride src_stride bytes) to dst.
+// Four low (or high) nibbles of a dword's bytes -> one 16-bit value, byte b's
+// nibble at bits 4b.
+__device__ __forceinline__ uint32_t gather_nibbles(uint32_t v) {
+    v &= 0x0F0F0F0Fu;
+    v = (v | (v >> 4)) & 0x00FF00FFu;
+    return (v | (v >> 8)) & 0x0000FFFFu;
+}
+
+// Canonical int4 dword (byte b = k_{2b} | k_{2b+1} << 4) -> packed order: k0, k2, k4,
+// k6 in the low and k1, k3, k5, k7 in the high 16 bits.
+__device__ __forceinline__ uint32_t pack_q_dword(uint32_t c) {
+    return gather_nibbles(c) | (gather_nibbles(c >> 4) << 16);
+}
+
+__global__ void pack_q_kernel(const uint4* __restrict__ src, size_t src_stride16, uint4* __restrict__ dst,
+                              size_t dst_stride16, size_t n16) {
+    const size_t m = blockIdx.y;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x) {
+        const uint4 v = src[m * src_stride16 + i];
+        dst[m * dst_stride16 + i] = make_uint4(pack_q_dword(v.x), pack_q_dword(v.y), pack_q_dword(v.z),
+                                               pack_q_dword(v.w));
+    }
+}
+
+// Plain 16-byte copy (router codes).
 __global__ void pack_copy_kernel(const uint4* __restrict__ src, size_t src_stride16, uint4* __restrict__ dst,
                                  size_t dst_stride16, size_t n16) {
     const size_t m = blockIdx.y;
@@ -96,12 +121,28 @@ __global__ void pack_sb_kernel(const uint16_t* __restrict__ s, const uint16_t* _
         dst[m * dst_stride4 + i] = (uint32_t)s[m * n + i] | ((uint32_t)b[m * n + i] << 16);
 }
 
-static moe_status copy_q(const void* src, size_t bytes, char* dst, size_t stride, int M, hipStream_t st) {
+static moe_status launch_q(const void* src, size_t bytes, char* dst, size_t stride, int M, hipStream_t st,
+                           bool shuffle) {
     if (!src || !aligned16(src)) return fail(MOE_ERR_INVALID_ARG, "q source NULL or not 16-byte aligned");
     size_t n16 = bytes / 16;
     dim3 grid((unsigned)((n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024), (unsigned)M);
+    if (shuffle) {
+        hipLaunchKernelGGL(pack_q_kernel, grid, dim3(256), 0, st, (const uint4*)src, n16, (uint4*)dst, stride / 16,
+                           n16);
+        return check_launch("pack_q_kernel");
+    }
     hipLaunchKernelGGL(pack_copy_kernel, grid, dim3(256), 0, st, (const uint4*)src, n16, (uint4*)dst, stride / 16, n16);
     return check_launch("pack_copy_kernel");
+}
+
+// int4 expert rows, nibbles reordered as described for moe_pack_experts.
+static moe_status copy_q(const void* src, size_t bytes, char* dst, size_t stride, int M, hipStream_t st) {
+    return launch_q(src, bytes, dst, stride, M, st, true);
+}
+
+// Router codes or fp32 router rows, unchanged.
+static moe_status copy_raw(const void* src, size_t bytes, char* dst, hipStream_t st) {
+    return launch_q(src, bytes, dst, 0, 1, st, false);
 }
 
 static moe_status copy_sb(const uint16_t* s, const uint16_t* b, size_t n, char* dst, size_t stride, int M,
@@ -146,8 +187,8 @@ extern "C" moe_status moe_pack_router(const moe_shape* sh, const void* w, const 
     hipStream_t hs = (hipStream_t)stream;
     if (sh->router_fmt == MOE_ROUTER_F32) {
         if (s || b) return fail(MOE_ERR_INVALID_ARG, "fp32 router takes no scale/bias");
-        return copy_q(w, R * H * 4, (char*)packed, 0, 1, hs);
+        return copy_raw(w, R * H * 4, (char*)packed, hs);
     }
-    if ((st = copy_q(w, R * H, (char*)packed, 0, 1, hs)) != MOE_OK) return st;
+    if ((st = copy_raw(w, R * H, (char*)packed, hs)) != MOE_OK) return st;
     return copy_sb(s, b, R * (H / 64), (char*)packed + R * H, 0, 1, hs);
 }

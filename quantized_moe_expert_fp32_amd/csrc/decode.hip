@@ -11,7 +11,8 @@
 // activations x meet the 32 nibbles q of the same group through
 //   sum x*(scale*q + bias) = 16*scale * sum x*(1 + q/16) + (bias - 16*scale) * sum x,
 // where 1 + q/16 is exactly a bf16 whose mantissa is q (one shift and one
-// and-or per two weights) and sum x*(1 + q/16) is a chain of bf16 dot2
+// and-or per two weights; the packed nibble order makes the pairs line up with
+// the activations as stored) and sum x*(1 + q/16) is a chain of bf16 dot2
 // instructions accumulating in fp32.
 #include <algorithm>
 
@@ -23,28 +24,28 @@ namespace moe {
 
 template <int CPL>
 struct XSlice {
-    uint32_t p[CPL][16];  // 32 bf16 per chunk, repacked in (0,4),(1,5),(2,6),(3,7) pairs per 8
+    uint32_t p[CPL][16];  // 32 bf16 per chunk as 16 natural-order pairs
     float s[CPL];         // plain sum of the chunk's 32 values, in element order
 };
 
-// Chunk c of this lane covers elements [32 * (lr + lpr * c), +32) of the row.
+// Chunk c of this lane covers elements [32 * (lr + lpr * c), +32) of the row. The
+// chunk sum is a chain of bf16 dot2 against (1, 1), in element order.
 template <int CPL>
 __device__ __forceinline__ void load_xslice(const uint16_t* __restrict__ row, int lr, int lpr, XSlice<CPL>& xs) {
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
         const uint4* src = reinterpret_cast<const uint4*>(row + 32 * (lr + lpr * c));
-        float sum = 0.f;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
             const uint4 v = src[q4];
-            const uint32_t in[4] = {v.x, v.y, v.z, v.w};
-            bf16x8_to_pair_order(in, &xs.p[c][4 * q4]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                sum += bf16_to_f32(in[j] & 0xFFFFu);
-                sum += bf16_to_f32(in[j] >> 16);
-            }
+            xs.p[c][4 * q4 + 0] = v.x;
+            xs.p[c][4 * q4 + 1] = v.y;
+            xs.p[c][4 * q4 + 2] = v.z;
+            xs.p[c][4 * q4 + 3] = v.w;
         }
+        float sum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sum = dot2_bf16(xs.p[c][j], 0x3F803F80u, sum);
         xs.s[c] = sum;
     }
 }
@@ -64,7 +65,7 @@ __device__ __forceinline__ ChunkLoad load_chunk(const uint8_t* __restrict__ qrow
 }
 
 // This lane's share of one row's dot product: 32 int4 weights against the
-// activation chunk xp (pair order) whose plain sum is xsum.
+// activation chunk xp (natural-order pairs) whose plain sum is xsum.
 __device__ __forceinline__ float chunk_dot(const ChunkLoad& c, const uint32_t* xp, float xsum) {
     const uint32_t qw[4] = {c.q.x, c.q.y, c.q.z, c.q.w};
     float d0 = 0.f, d1 = 0.f;
@@ -86,17 +87,51 @@ __device__ __forceinline__ float silu_f32(float g) { return g / (1.f + expf(-g))
 
 // ---------------------------------------------------------------- gate/up work item
 // 16 intermediate rows (gate row and up row each) of expert e for one token, by
-// one workgroup: wavefront w owns rows rb*16 + 4w .. +4. Writes h (bf16) at hrow.
+// one workgroup: wavefront w owns rows rb*16 + 4w .. +4.
 constexpr int GU_ROWS = 16;
 constexpr int GU_IT = 4;  // row iterations per wavefront (rows per iteration = 64 / lanes per row)
 
-// With htag (the tagged copy of the same h row, one 64-bit word per bf16 pair) the
-// rows are published there with tag `tag` instead of being stored to hrow.
+// A gate/up item's weight loads (issued by gu_load, consumed by gu_finish).
 template <int CPL>
-__device__ __forceinline__ void gateup_item(const uint8_t* __restrict__ packed, const ExpertLayout& L, int H, int I,
-                                            int e, bool valid, const uint16_t* __restrict__ xrow,
-                                            uint16_t* __restrict__ hrow, uint64_t* htag, uint32_t tag, int rb,
-                                            int wave, int lane) {
+struct GuLoads {
+    ChunkLoad g[GU_IT][CPL], u[GU_IT][CPL];
+};
+
+template <int CPL>
+__device__ __forceinline__ void gu_load(const uint8_t* __restrict__ packed, const ExpertLayout& L, int H, int e,
+                                        bool valid, int rb, int wave, int lane, GuLoads<CPL>& ld) {
+    if (!valid) return;
+    const int C = H / 32, lpr = C < 64 ? C : 64, rpw = 64 / lpr;
+    const int lr = lane % lpr, rsub = lane / lpr;
+    constexpr int per_wave = GU_ROWS / 4;
+    const int r0 = rb * GU_ROWS + wave * per_wave;
+    const uint8_t* base = packed + (size_t)e * L.stride;
+    const uint8_t* gq = base + L.gate_q;
+    const uint8_t* uq = base + L.up_q;
+    const uint32_t* gsb = reinterpret_cast<const uint32_t*>(base + L.gate_sb);
+    const uint32_t* usb = reinterpret_cast<const uint32_t*>(base + L.up_sb);
+    const size_t qstride = H / 2, sbstride = H / 64;
+#pragma unroll
+    for (int it = 0; it < GU_IT; ++it) {
+        const int rr = it * rpw + rsub;
+        const int r = r0 + (rr < per_wave ? rr : 0);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            if (rr < per_wave) {
+                ld.g[it][c] = load_chunk(gq + r * qstride, gsb + r * sbstride, lr + lpr * c);
+                ld.u[it][c] = load_chunk(uq + r * qstride, usb + r * sbstride, lr + lpr * c);
+            }
+        }
+    }
+}
+
+// Rows rb*16 + 4*wave .. +4 of h = bf16(silu(gate . x) * (up . x)), written to hrow
+// or, with htag (the tagged copy of the same h row, one 64-bit word per bf16
+// pair), published there with tag `tag`.
+template <int CPL>
+__device__ __forceinline__ void gu_finish(const GuLoads<CPL>& ld, int H, bool valid,
+                                          const uint16_t* __restrict__ xrow, uint16_t* __restrict__ hrow,
+                                          uint64_t* htag, uint32_t tag, int rb, int wave, int lane) {
     const int C = H / 32, lpr = C < 64 ? C : 64, rpw = 64 / lpr;
     const int lr = lane % lpr, rsub = lane / lpr;
     constexpr int per_wave = GU_ROWS / 4;
@@ -111,26 +146,6 @@ __device__ __forceinline__ void gateup_item(const uint8_t* __restrict__ packed, 
         }
         return;
     }
-    const uint8_t* base = packed + (size_t)e * L.stride;
-    const uint8_t* gq = base + L.gate_q;
-    const uint8_t* uq = base + L.up_q;
-    const uint32_t* gsb = reinterpret_cast<const uint32_t*>(base + L.gate_sb);
-    const uint32_t* usb = reinterpret_cast<const uint32_t*>(base + L.up_sb);
-    const size_t qstride = H / 2, sbstride = H / 64;
-
-    ChunkLoad lg[GU_IT][CPL], lu[GU_IT][CPL];
-#pragma unroll
-    for (int it = 0; it < GU_IT; ++it) {
-        const int rr = it * rpw + rsub;
-        const int r = r0 + (rr < per_wave ? rr : 0);
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            if (rr < per_wave) {
-                lg[it][c] = load_chunk(gq + r * qstride, gsb + r * sbstride, lr + lpr * c);
-                lu[it][c] = load_chunk(uq + r * qstride, usb + r * sbstride, lr + lpr * c);
-            }
-        }
-    }
     XSlice<CPL> xs;
     load_xslice(xrow, lr, lpr, xs);
     uint32_t hb[GU_IT] = {0u, 0u, 0u, 0u};  // bf16 of row it*rpw + rsub, in lanes with lr == 0
@@ -143,8 +158,8 @@ __device__ __forceinline__ void gateup_item(const uint8_t* __restrict__ packed, 
         if (act) {
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
-                g += chunk_dot(lg[it][c], xs.p[c], xs.s[c]);
-                u += chunk_dot(lu[it][c], xs.p[c], xs.s[c]);
+                g += chunk_dot(ld.g[it][c], xs.p[c], xs.s[c]);
+                u += chunk_dot(ld.u[it][c], xs.p[c], xs.s[c]);
             }
         }
         g = group_sum(g, lpr);
@@ -169,6 +184,17 @@ __device__ __forceinline__ void gateup_item(const uint8_t* __restrict__ packed, 
     }
 }
 
+// 16 intermediate rows of expert e for one token (gate and up rows each).
+template <int CPL>
+__device__ __forceinline__ void gateup_item(const uint8_t* __restrict__ packed, const ExpertLayout& L, int H, int e,
+                                            bool valid, const uint16_t* __restrict__ xrow,
+                                            uint16_t* __restrict__ hrow, uint64_t* htag, uint32_t tag, int rb,
+                                            int wave, int lane) {
+    GuLoads<CPL> ld;
+    gu_load<CPL>(packed, L, H, e, valid, rb, wave, lane, ld);
+    gu_finish<CPL>(ld, H, valid, xrow, hrow, htag, tag, rb, wave, lane);
+}
+
 // ---------------------------------------------------------------- down (+ combine) work item
 // Output rows n0 .. n0+7 of token t for every slot s (S*8 row dot products of
 // length I, I/32 lanes each) by one workgroup. Results go to LDS (ysh), then to
@@ -181,17 +207,17 @@ __device__ __forceinline__ void gateup_item(const uint8_t* __restrict__ packed, 
 constexpr int DN_ROWS = 8;
 constexpr int DN_BATCH = 5;  // 9 slots x 8 rows at I = 512: 18 iterations, 4.5 per wavefront
 
-// hsh: LDS of S * I bf16, the token's h rows of every slot, staged with one round
-// of parallel loads before the dot products. With TAGGED the rows are read from
-// their tagged copy (published in this launch), each word polled until it carries
-// `tag`; the weight loads are issued before that wait.
-template <bool TAGGED>
-__device__ __forceinline__ void down_item(const uint8_t* __restrict__ packed, const ExpertLayout& L, int H, int I,
-                                          int E, int k, int has_shared, int t, int n0,
-                                          const uint16_t* __restrict__ hbuf, const int32_t* ids_t,
-                                          const uint16_t* w_t, const uint16_t* wsh_t, float* __restrict__ y,
-                                          const uint16_t* residual, uint16_t* out, float (*ysh)[DN_ROWS],
-                                          uint32_t* hsh, const uint64_t* htag_t, uint32_t tag, unsigned* err) {
+// A down item's weight loads for one batch of DN_BATCH row iterations per
+// wavefront; they depend only on the expert ids, so a workgroup can issue the
+// first batch early (before its last gate/up item is computed).
+struct DnLoads {
+    ChunkLoad ld[DN_BATCH];
+    int slot[DN_BATCH];
+    bool ok[DN_BATCH];
+};
+
+__device__ __forceinline__ void dn_load(const uint8_t* __restrict__ packed, const ExpertLayout& L, int I, int E,
+                                        int k, int has_shared, int n0, const int32_t* ids_t, int j0, DnLoads& d) {
     const int S = k + has_shared;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int lpr = I / 32, rpw = 64 / lpr;  // I <= 2048: one chunk per lane
@@ -199,29 +225,46 @@ __device__ __forceinline__ void down_item(const uint8_t* __restrict__ packed, co
     const int n_dots = S * DN_ROWS;
     const int n_it = (n_dots + rpw - 1) / rpw;
     const size_t qstride = I / 2, sbstride = I / 64;
-    for (int j0 = 0; 4 * j0 < n_it; j0 += DN_BATCH) {
-        ChunkLoad ld[DN_BATCH];
-        int slot[DN_BATCH];
-        bool ok[DN_BATCH];
 #pragma unroll
-        for (int j = 0; j < DN_BATCH; ++j) {
-            const int it = wave + 4 * (j0 + j);
-            const int q = it * rpw + rsub;
-            ok[j] = it < n_it && q < n_dots;
-            slot[j] = ok[j] ? q / DN_ROWS : 0;
-            if (ok[j]) {
-                const int s = slot[j];
-                const int e = s < k ? ids_t[s] : E;
-                if (s < k && (e < 0 || e >= E)) {
-                    ok[j] = false;  // invalid expert id: this y row is zero
-                } else {
-                    const int n = n0 + q % DN_ROWS;
-                    const uint8_t* base = packed + (size_t)e * L.stride;
-                    ld[j] = load_chunk(base + L.down_q + n * qstride,
-                                       reinterpret_cast<const uint32_t*>(base + L.down_sb) + n * sbstride, lr);
-                }
+    for (int j = 0; j < DN_BATCH; ++j) {
+        const int it = wave + 4 * (j0 + j);
+        const int q = it * rpw + rsub;
+        d.ok[j] = it < n_it && q < n_dots;
+        d.slot[j] = d.ok[j] ? q / DN_ROWS : 0;
+        if (d.ok[j]) {
+            const int s = d.slot[j];
+            const int e = s < k ? ids_t[s] : E;
+            if (s < k && (e < 0 || e >= E)) {
+                d.ok[j] = false;  // invalid expert id: this y row is zero
+            } else {
+                const int n = n0 + q % DN_ROWS;
+                const uint8_t* base = packed + (size_t)e * L.stride;
+                d.ld[j] = load_chunk(base + L.down_q + n * qstride,
+                                     reinterpret_cast<const uint32_t*>(base + L.down_sb) + n * sbstride, lr);
             }
         }
+    }
+}
+
+// hsh: LDS of S * I bf16, the token's h rows of every slot, staged with one round
+// of parallel loads before the dot products. With TAGGED the rows are read from
+// their tagged copy (published in this launch), each word polled until it carries
+// `tag`. d holds the first batch's weight loads (dn_load with j0 = 0).
+template <bool TAGGED>
+__device__ __forceinline__ void dn_finish(DnLoads& d, const uint8_t* __restrict__ packed, const ExpertLayout& L,
+                                          int H, int I, int E, int k, int has_shared, int t, int n0,
+                                          const uint16_t* __restrict__ hbuf, const int32_t* ids_t,
+                                          const uint16_t* w_t, const uint16_t* wsh_t, float* __restrict__ y,
+                                          const uint16_t* residual, uint16_t* out, float (*ysh)[DN_ROWS],
+                                          uint32_t* hsh, const uint64_t* htag_t, uint32_t tag, unsigned* err) {
+    const int S = k + has_shared;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int lpr = I / 32, rpw = 64 / lpr;
+    const int lr = lane % lpr, rsub = lane / lpr;
+    const int n_dots = S * DN_ROWS;
+    const int n_it = (n_dots + rpw - 1) / rpw;
+    for (int j0 = 0; 4 * j0 < n_it; j0 += DN_BATCH) {
+        if (j0 > 0) dn_load(packed, L, I, E, k, has_shared, n0, ids_t, j0, d);
         if (j0 == 0) {
             const int nw = S * I / 2;
             if (TAGGED) {
@@ -245,10 +288,10 @@ __device__ __forceinline__ void down_item(const uint8_t* __restrict__ packed, co
             if (it >= n_it) break;  // wave-uniform
             const int q = it * rpw + rsub;
             float v = 0.f;
-            if (ok[j]) {
+            if (d.ok[j]) {
                 XSlice<1> hs;
-                load_xslice(reinterpret_cast<const uint16_t*>(hsh) + (size_t)slot[j] * I, lr, lpr, hs);
-                v = chunk_dot(ld[j], hs.p[0], hs.s[0]);
+                load_xslice(reinterpret_cast<const uint16_t*>(hsh) + (size_t)d.slot[j] * I, lr, lpr, hs);
+                v = chunk_dot(d.ld[j], hs.p[0], hs.s[0]);
             }
             v = group_sum(v, lpr);
             if (lr == lpr - 1 && q < n_dots) ysh[q / DN_ROWS][q % DN_ROWS] = v;
@@ -283,7 +326,7 @@ __global__ __launch_bounds__(256) void decode_gateup_kernel(const uint8_t* __res
     const int t = blockIdx.z, s = blockIdx.y, S = k + has_shared;
     const int e = s < k ? ids[(size_t)t * k + s] : E;
     const bool valid = s < k ? (e >= 0 && e < E) : true;
-    gateup_item<CPL>(packed, L, H, I, e, valid, x + (size_t)t * H, hbuf + ((size_t)t * S + s) * I, nullptr, 0u,
+    gateup_item<CPL>(packed, L, H, e, valid, x + (size_t)t * H, hbuf + ((size_t)t * S + s) * I, nullptr, 0u,
                      blockIdx.x, threadIdx.x >> 6, threadIdx.x & 63);
 }
 
@@ -298,7 +341,9 @@ __global__ __launch_bounds__(256) void decode_down_kernel(const uint8_t* __restr
     __shared__ float ysh[17][DN_ROWS];
     extern __shared__ __attribute__((aligned(16))) uint32_t hsh_dyn[];
     const int t = blockIdx.y;
-    down_item<false>(packed, L, H, I, E, k, has_shared, t, blockIdx.x * DN_ROWS, hbuf, ids + (size_t)t * k,
+    DnLoads d;
+    dn_load(packed, L, I, E, k, has_shared, blockIdx.x * DN_ROWS, ids + (size_t)t * k, 0, d);
+    dn_finish<false>(d, packed, L, H, I, E, k, has_shared, t, blockIdx.x * DN_ROWS, hbuf, ids + (size_t)t * k,
                      w ? w + (size_t)t * k : nullptr, wsh ? wsh + t : nullptr, y, residual, out, ysh, hsh_dyn,
                      nullptr, 0u, nullptr);
 }
@@ -340,8 +385,9 @@ struct LayerArgs {
 //   B: the routed gate/up items (16 rows of one token, one slot);
 //   C: down items (8 output rows of one token, all slots) with the combine.
 // Every workgroup computes the selection of the tokens it needs (DPP top-k, reading
-// the tagged logits as they arrive) into LDS before its B items. A C item issues
-// its down-weight loads, then stages its token's tagged h rows (polling each word).
+// the tagged logits as they arrive) into LDS before its B items. The first C
+// item's down-weight loads go out with the last B item's gate/up loads; a C item
+// then stages its token's tagged h rows (polling each word).
 template <int CPL, int TT, bool AFF8>
 __global__ __launch_bounds__(256) void decode_layer_kernel(LayerArgs a) {
     __shared__ int32_t s_ids[16][16];
@@ -372,7 +418,7 @@ __global__ __launch_bounds__(256) void decode_layer_kernel(LayerArgs a) {
         } else {
             const int j = item - n_router, t = j % T, rb = j / T;
             const size_t row = (size_t)t * S + k;
-            gateup_item<CPL>(a.experts, a.L, H, I, E, true, a.x + (size_t)t * H, nullptr, a.th + row * (I / 2), tag,
+            gateup_item<CPL>(a.experts, a.L, H, E, true, a.x + (size_t)t * H, nullptr, a.th + row * (I / 2), tag,
                              rb, wave, lane);
         }
     }
@@ -400,18 +446,29 @@ __global__ __launch_bounds__(256) void decode_layer_kernel(LayerArgs a) {
         if (a.has_shared && tid == 0) a.wsh[wg] = s_wsh[wg];
     }
 
-    // ---- phase B
+    // ---- phase B (the first down item's weight loads are issued with the last
+    // gate/up item's, so they overlap its arithmetic and the wait for h)
+    DnLoads dl;
+    bool dl_ready = false;
     for (int item = wg; item < n_B; item += G) {
         const int t = item % T, j = item / T, s = j / gu_per_tok, rb = j % gu_per_tok;
         const size_t row = (size_t)t * S + s;
-        gateup_item<CPL>(a.experts, a.L, H, I, s_ids[t][s], true, a.x + (size_t)t * H, nullptr, a.th + row * (I / 2),
-                         tag, rb, wave, lane);
+        GuLoads<CPL> gl;
+        gu_load<CPL>(a.experts, a.L, H, s_ids[t][s], true, rb, wave, lane, gl);
+        if (item + G >= n_B && wg < n_C) {
+            const int tc = wg % T;
+            dn_load(a.experts, a.L, I, E, k, a.has_shared, (wg / T) * DN_ROWS, s_ids[tc], 0, dl);
+            dl_ready = true;
+        }
+        gu_finish<CPL>(gl, H, true, a.x + (size_t)t * H, nullptr, a.th + row * (I / 2), tag, rb, wave, lane);
     }
 
     // ---- phase C
     for (int item = wg; item < n_C; item += G) {
         const int t = item % T, ng = item / T;
-        down_item<true>(a.experts, a.L, H, I, E, k, a.has_shared, t, ng * DN_ROWS, nullptr, s_ids[t], s_w[t],
+        if (!dl_ready) dn_load(a.experts, a.L, I, E, k, a.has_shared, ng * DN_ROWS, s_ids[t], 0, dl);
+        dl_ready = false;
+        dn_finish<true>(dl, a.experts, a.L, H, I, E, k, a.has_shared, t, ng * DN_ROWS, nullptr, s_ids[t], s_w[t],
                         &s_wsh[t], a.y, a.residual, a.out, ysh, hsh_dyn, a.th + (size_t)t * S * (I / 2), tag,
                         &ctl->error);
     }

@@ -84,24 +84,25 @@ __device__ __forceinline__ uint32_t f64_to_bf16(double d) {
     return sign | bits;
 }
 
-// Eight int4 weights of one dword (element j in bits 4j..4j+3) as four bf16 pairs
-// holding 1 + q/16 exactly, paired (0,4), (1,5), (2,6), (3,7). A dot product
-// with activations packed in the same pair order gives sum x * (1 + q/16).
-__device__ __forceinline__ void int4x8_to_bf16_pairs(uint32_t v, uint32_t out[4]) {
-    out[0] = ((v << 3) & 0x00780078u) | 0x3F803F80u;
-    out[1] = ((v >> 1) & 0x00780078u) | 0x3F803F80u;
-    out[2] = ((v >> 5) & 0x00780078u) | 0x3F803F80u;
-    out[3] = ((v >> 9) & 0x00780078u) | 0x3F803F80u;
+// (v & m) | c in one v_and_or_b32. The VOP3 encoding takes no literal and (on this
+// chip) at most one scalar operand, so the mask goes in an SGPR and the constant in
+// a VGPR.
+__device__ __forceinline__ uint32_t and_or_b32(uint32_t v, uint32_t m, uint32_t c) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "s"(m), "v"(c));
+    return r;
 }
 
-// Repacks eight consecutive bf16 values (four dwords, natural order) into the
-// pair order (0,4), (1,5), (2,6), (3,7) used by int4x8_to_bf16_pairs.
-__device__ __forceinline__ void bf16x8_to_pair_order(const uint32_t in[4], uint32_t out[4]) {
-    // in[0] = (x1:x0), in[1] = (x3:x2), in[2] = (x5:x4), in[3] = (x7:x6)
-    out[0] = __builtin_amdgcn_perm(in[2], in[0], 0x05040100u);  // (x4:x0)
-    out[1] = __builtin_amdgcn_perm(in[2], in[0], 0x07060302u);  // (x5:x1)
-    out[2] = __builtin_amdgcn_perm(in[3], in[1], 0x05040100u);  // (x6:x2)
-    out[3] = __builtin_amdgcn_perm(in[3], in[1], 0x07060302u);  // (x7:x3)
+// Eight int4 weights of one packed dword (nibble j = k_{2j}, nibble 4+j = k_{2j+1})
+// as four bf16 pairs (k0,k1), (k2,k3), (k4,k5), (k6,k7), each value 1 + q/16
+// exactly: q lands in mantissa bits 3..6 under the exponent of 1.0. A dot product
+// with activations in their natural order gives sum x * (1 + q/16).
+__device__ __forceinline__ void int4x8_to_bf16_pairs(uint32_t v, uint32_t out[4]) {
+    const uint32_t one = 0x3F803F80u;
+    out[0] = and_or_b32(v << 3, 0x00780078u, one);
+    out[1] = and_or_b32(v >> 1, 0x00780078u, one);
+    out[2] = and_or_b32(v >> 5, 0x00780078u, one);
+    out[3] = and_or_b32(v >> 9, 0x00780078u, one);
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

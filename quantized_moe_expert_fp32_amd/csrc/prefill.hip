@@ -138,11 +138,33 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const int32_t* __restric
         for (int t = tid; t < T; t += blockDim.x) order[off[E] + t] = t * S + k;
 }
 
+// ---------------------------------------------------------------- XCD-aware item mapping
+// The GEMM grids are one-dimensional over (tile, column block) items, numbered
+// tile-major so that neighbouring items share an activation tile or an expert's
+// weights. Workgroups are handed to the 8 XCDs round-robin by linear id, and each
+// XCD has its own L2, so block b takes item (b % 8) * per + b / 8: each XCD walks
+// one contiguous range of items and the sharing stays inside one L2. The grid is
+// 8 * ceil(max_tiles * nb / 8) blocks; blocks beyond the live items return.
+constexpr int N_XCD = 8;
+
+__device__ __forceinline__ bool xcd_item(int ntiles, int nb, int& tile, int& cb) {
+    const int n = ntiles * nb, per = (n + N_XCD - 1) / N_XCD;
+    const int j = (int)blockIdx.x / N_XCD, item = ((int)blockIdx.x % N_XCD) * per + j;
+    if (j >= per || item >= n) return false;
+    tile = item / nb;
+    cb = item - tile * nb;
+    return true;
+}
+
+static unsigned xcd_grid(int max_tiles, int nb) {
+    return (unsigned)((((long long)max_tiles * nb + N_XCD - 1) / N_XCD) * N_XCD);
+}
+
 // ---------------------------------------------------------------- staged GEMM core
 // Both expert GEMMs walk K in chunks of KC = 128 (two quantisation groups). Per
 // chunk a workgroup stages, with coalesced 16-byte loads:
 //   A: 64 activation rows x 128 bf16 (256 contiguous bytes per row; 16 lanes per
-//      row), stored in LDS in pair order with the per-group row sums X;
+//      row), stored in LDS as they are, with the per-group row sums X;
 //   B: NB int4 weight rows x 64 bytes (4 lanes per row) and their two (scale, bias)
 //      words.
 // The next chunk's loads are issued into registers before the current chunk is
@@ -178,9 +200,7 @@ __device__ __forceinline__ void store_a(uint16_t* __restrict__ a_lds, float (*x_
     for (int j = 0; j < 4; ++j) {
         const int row = (tid >> 4) + 16 * j;
         const uint32_t in[4] = {a.v[j].x, a.v[j].y, a.v[j].z, a.v[j].w};
-        uint32_t out[4];
-        bf16x8_to_pair_order(in, out);
-        *reinterpret_cast<uint4*>(a_lds + row * AS + 8 * c16) = make_uint4(out[0], out[1], out[2], out[3]);
+        *reinterpret_cast<uint4*>(a_lds + row * AS + 8 * c16) = a.v[j];
         float sm = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -257,8 +277,8 @@ __device__ __forceinline__ void mma_group(const uint16_t* __restrict__ a_lds, co
 }
 
 // ---------------------------------------------------------------- gate/up + SwiGLU
-// Grid: (max_tiles, I / 64). B rows 0..63 are gate rows ib*64 .., rows 64..127 the
-// matching up rows. Wavefront w computes gate and up for intermediate columns
+// Items: (tile, ib) for ib < I / 64. B rows 0..63 are gate rows ib*64 .., rows
+// 64..127 the matching up rows. Wavefront w computes gate and up for intermediate columns
 // ib*64 + 16w .. +16 over the tile's rows and writes h[row][i] = bf16(silu(gate) * up)
 // in expert-sorted row order.
 __global__ __launch_bounds__(256) void gateup_gemm_kernel(const uint8_t* __restrict__ packed, ExpertLayout L, int H,
@@ -271,11 +291,12 @@ __global__ __launch_bounds__(256) void gateup_gemm_kernel(const uint8_t* __restr
     __shared__ __attribute__((aligned(16))) float x_lds[2][64];
     __shared__ __attribute__((aligned(16))) uint8_t b_lds[128 * BS];
     __shared__ __attribute__((aligned(16))) uint2 sb_lds[128];
-    if ((int)blockIdx.x >= *ntiles) return;
-    const Tile tl = tiles[blockIdx.x];
+    int ti, ib;
+    if (!xcd_item(*ntiles, I / BN, ti, ib)) return;
+    const Tile tl = tiles[ti];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lg = lane >> 4, lc = lane & 15;
-    const int i0 = blockIdx.y * BN;
+    const int i0 = ib * BN;
     const int n_ms = (tl.nrows + 15) >> 4;
 
     const uint16_t* rowp[4];
@@ -335,7 +356,7 @@ __global__ __launch_bounds__(256) void gateup_gemm_kernel(const uint8_t* __restr
 }
 
 // ---------------------------------------------------------------- down + scatter
-// Grid: (max_tiles, H / 64). B rows are down rows nb*64 .. +64; A = h rows,
+// Items: (tile, nb) for nb < H / 64. B rows are down rows nb*64 .. +64; A = h rows,
 // contiguous in expert-sorted order. Wavefront w computes output columns
 // nb*64 + 16w .. +16 and writes y[p][n] for the row's pick p = order[row].
 __global__ __launch_bounds__(256) void down_gemm_kernel(const uint8_t* __restrict__ packed, ExpertLayout L, int H,
@@ -347,11 +368,12 @@ __global__ __launch_bounds__(256) void down_gemm_kernel(const uint8_t* __restric
     __shared__ __attribute__((aligned(16))) float x_lds[2][64];
     __shared__ __attribute__((aligned(16))) uint8_t b_lds[64 * BS];
     __shared__ __attribute__((aligned(16))) uint2 sb_lds[64];
-    if ((int)blockIdx.x >= *ntiles) return;
-    const Tile tl = tiles[blockIdx.x];
+    int ti, nbk;
+    if (!xcd_item(*ntiles, H / BN, ti, nbk)) return;
+    const Tile tl = tiles[ti];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lg = lane >> 4, lc = lane & 15;
-    const int n0 = blockIdx.y * BN;
+    const int n0 = nbk * BN;
     const int n_ms = (tl.nrows + 15) >> 4;
 
     const uint16_t* rowp[4];
@@ -447,10 +469,10 @@ extern "C" moe_status moe_experts_prefill(const moe_shape* shape, const void* ex
                        counts, offsets, ntiles, tiles, order, y);
     if ((st = check_launch("dispatch_kernel")) != MOE_OK) return st;
     const uint8_t* p = (const uint8_t*)experts_packed;
-    hipLaunchKernelGGL(gateup_gemm_kernel, dim3(W.max_tiles, I / BN), dim3(256), 0, hs, p, L, H, I, S, x, ntiles,
+    hipLaunchKernelGGL(gateup_gemm_kernel, dim3(xcd_grid(W.max_tiles, I / BN)), dim3(256), 0, hs, p, L, H, I, S, x, ntiles,
                        tiles, order, hbuf);
     if ((st = check_launch("gateup_gemm_kernel")) != MOE_OK) return st;
-    hipLaunchKernelGGL(down_gemm_kernel, dim3(W.max_tiles, H / BN), dim3(256), 0, hs, p, L, H, I, ntiles, tiles, order,
+    hipLaunchKernelGGL(down_gemm_kernel, dim3(xcd_grid(W.max_tiles, H / BN)), dim3(256), 0, hs, p, L, H, I, ntiles, tiles, order,
                        hbuf, y);
     return check_launch("down_gemm_kernel");
 }

@@ -114,6 +114,34 @@ def staged_layer_check(res, x_np, host_layer, E, has_shared=True):
 
 # ------------------------------------------------------------------ packing
 
+def packed_nibble_order(q_bytes):
+    """Canonical int4 bytes -> the packed order the header documents: per dword of
+    weights k0..k7, nibble j holds k_{2j} and nibble 4+j holds k_{2j+1}."""
+    b = np.asarray(q_bytes, dtype=np.uint8).reshape(-1, 4)
+    k = np.empty((b.shape[0], 8), np.uint32)
+    k[:, 0::2] = b & 0xF
+    k[:, 1::2] = b >> 4
+    d = np.zeros(b.shape[0], np.uint32)
+    for j in range(4):
+        d |= k[:, 2 * j] << (4 * j)
+        d |= k[:, 2 * j + 1] << (16 + 4 * j)
+    return d.astype("<u4").view(np.uint8)
+
+
+def test_packed_nibble_order_pairs():
+    """Host check of the documented order: shifting a packed dword by 4j puts
+    (k_{2j}, k_{2j+1}) in bits 0..3 and 16..19."""
+    rng = np.random.default_rng(0)
+    q = rng.integers(0, 256, 64, dtype=np.uint8)
+    d = packed_nibble_order(q).view("<u4")
+    k = np.empty(128, np.uint32)
+    k[0::2], k[1::2] = q & 0xF, q >> 4
+    for i, v in enumerate(d):
+        for j in range(4):
+            assert (int(v) >> (4 * j)) & 0xF == k[8 * i + 2 * j]
+            assert (int(v) >> (16 + 4 * j)) & 0xF == k[8 * i + 2 * j + 1]
+
+
 def test_pack_layout_matches_header(gpu):
     c = case("tiny")
     dl = dev_layer(gpu, c)
@@ -125,7 +153,7 @@ def test_pack_layout_matches_header(gpu):
         b = p[m * stride:(m + 1) * stride]
         o = 0
         for q in (L0.q_gate[m], L0.q_up[m], L0.q_down[m]):
-            assert np.array_equal(b[o:o + q.size], q.reshape(-1))
+            assert np.array_equal(b[o:o + q.size], packed_nibble_order(q.reshape(-1)))
             o += q.size
         for s, bb in ((L0.s_gate[m], L0.b_gate[m]), (L0.s_up[m], L0.b_up[m]), (L0.s_down[m], L0.b_down[m])):
             sb = b[o:o + 4 * s.size].view(np.uint32)
