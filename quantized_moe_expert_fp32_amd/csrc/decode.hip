@@ -376,101 +376,362 @@ struct LayerArgs {
     uint64_t* th;       // tagged h [T][S][I/2] (bf16 pairs)
     ExpertLayout L;
     int T, H, I, E, k, has_shared, R;
+    int stage_x;  // x and its chunk sums are staged in LDS (else read from global memory)
 };
 
-// Persistent kernel, at most one workgroup per CU, every workgroup resident.
-// Work items (token-minor numbering; item i of a phase goes to workgroup i mod G):
-//   A: router rows (4 per item) and the shared expert's gate/up items, which do
-//      not depend on routing;
-//   B: the routed gate/up items (16 rows of one token, one slot);
-//   C: down items (8 output rows of one token, all slots) with the combine.
-// Every workgroup computes the selection of the tokens it needs (DPP top-k, reading
-// the tagged logits as they arrive) into LDS before its B items. The first C
-// item's down-weight loads go out with the last B item's gate/up loads; a C item
-// then stages its token's tagged h rows (polling each word).
-template <int CPL, int TT, bool AFF8>
-__global__ __launch_bounds__(256) void decode_layer_kernel(LayerArgs a) {
+// ---- single-launch building blocks (16 wavefronts per workgroup)
+constexpr int LW = 16;        // wavefronts per workgroup
+constexpr int LTH = 64 * LW;  // threads per workgroup
+constexpr int DNB = 3;        // down row iterations per wavefront whose loads are issued together
+constexpr int MAXD = 272;     // distinct experts of one launch: at most 16 * 16 routed, plus the shared one
+
+// Gate/up row-pair task: rows 2ip and 2ip+1 of the gate and up matrices of one
+// expert. Row slot rs: 0, 1 = gate rows 2ip, 2ip+1; 2, 3 = up rows. The lane
+// layout of a row (lpr lanes, CPL chunks of 32 each) and the arithmetic are those
+// of gateup_item, so h is bit-identical between the decode entry points.
+template <int CPL>
+struct PairLoads {
+    ChunkLoad c[4][CPL];
+};
+
+template <int CPL>
+__device__ __forceinline__ void pair_load(const uint8_t* __restrict__ packed, const ExpertLayout& L, int H, int e,
+                                          int ip, int lane, PairLoads<CPL>& ld) {
+    const int C = H / 32, lpr = C < 64 ? C : 64, rpw = 64 / lpr;
+    const int lr = lane % lpr, rsub = lane / lpr;
+    const uint8_t* base = packed + (size_t)e * L.stride;
+    const size_t qstride = H / 2, sbstride = H / 64;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        if (it * rpw >= 4) break;  // wave-uniform
+        const int rs = it * rpw + rsub;
+        if (rs < 4) {
+            const size_t r = 2 * ip + (rs & 1);
+            const uint8_t* q = base + (rs < 2 ? L.gate_q : L.up_q) + r * qstride;
+            const uint32_t* sb =
+                reinterpret_cast<const uint32_t*>(base + (rs < 2 ? L.gate_sb : L.up_sb)) + r * sbstride;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) ld.c[it][c] = load_chunk(q, sb, lr + lpr * c);
+        }
+    }
+}
+
+// bf16 h of rows 2ip and 2ip+1 (low, high half) for one token's x slice.
+template <int CPL>
+__device__ __forceinline__ uint32_t pair_finish(const PairLoads<CPL>& ld, int H, const XSlice<CPL>& xs, int lane) {
+    const int C = H / 32, lpr = C < 64 ? C : 64, rpw = 64 / lpr;
+    const int rsub = lane / lpr;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        if (it * rpw >= 4) break;  // wave-uniform
+        const int rs = it * rpw + rsub;
+        float d = 0.f;
+        if (rs < 4) {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) d += chunk_dot(ld.c[it][c], xs.p[c], xs.s[c]);
+        }
+        v[it] = group_sum(d, lpr);
+    }
+    float r[4];
+#pragma unroll
+    for (int rs = 0; rs < 4; ++rs) {  // row slot rs: iteration rs / rpw, last lane of group rs % rpw
+        const int it = rs / rpw;
+        const float src = it == 0 ? v[0] : it == 1 ? v[1] : it == 2 ? v[2] : v[3];
+        r[rs] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(src), (rs % rpw) * lpr + lpr - 1));
+    }
+    const uint32_t h0 = f32_to_bf16(silu_f32(r[0]) * r[2]);
+    const uint32_t h1 = f32_to_bf16(silu_f32(r[1]) * r[3]);
+    return h0 | (h1 << 16);
+}
+
+// This lane's slice of token t's activations: from the workgroup's LDS copy
+// (values and chunk sums, staged by stage_x) or from global memory; both give the
+// values and sums of load_xslice.
+template <int CPL>
+__device__ __forceinline__ void token_xslice(bool lds, const uint16_t* s_x, const float* s_xs,
+                                             const uint16_t* __restrict__ gx, int t, int H, int lane,
+                                             XSlice<CPL>& xs) {
+    const int C = H / 32, lpr = C < 64 ? C : 64;
+    const int lr = lane % lpr;
+    if (!lds) {
+        load_xslice(gx + (size_t)t * H, lr, lpr, xs);
+        return;
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int ch = lr + lpr * c;
+        const uint4* src = reinterpret_cast<const uint4*>(s_x + (size_t)t * H + 32 * ch);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const uint4 v = src[q4];
+            xs.p[c][4 * q4 + 0] = v.x;
+            xs.p[c][4 * q4 + 1] = v.y;
+            xs.p[c][4 * q4 + 2] = v.z;
+            xs.p[c][4 * q4 + 3] = v.w;
+        }
+        xs.s[c] = s_xs[t * C + ch];
+    }
+}
+
+// Copies x [T][H] into LDS with the chunk sums of load_xslice (one chunk of 32 per
+// thread and step).
+__device__ __forceinline__ void stage_x(const uint16_t* __restrict__ gx, int T, int H, uint16_t* s_x, float* s_xs) {
+    const int C = H / 32;
+    for (int i = threadIdx.x; i < T * C; i += blockDim.x) {
+        const uint4* src = reinterpret_cast<const uint4*>(gx + (size_t)i * 32);
+        uint4* dst = reinterpret_cast<uint4*>(s_x + (size_t)i * 32);
+        uint32_t w[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const uint4 v = src[q4];
+            dst[q4] = v;
+            w[4 * q4 + 0] = v.x;
+            w[4 * q4 + 1] = v.y;
+            w[4 * q4 + 2] = v.z;
+            w[4 * q4 + 3] = v.w;
+        }
+        float sum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sum = dot2_bf16(w[j], 0x3F803F80u, sum);
+        s_xs[i] = sum;
+    }
+}
+
+// Down loads of one wavefront for one item (8 output rows, every slot): row
+// iterations wave + LW * (b0 + j), j < DNB, with the lane layout of dn_load.
+struct DnLoadsL {
+    ChunkLoad ld[DNB];
+    int slot[DNB];
+    bool ok[DNB];
+};
+
+__device__ __forceinline__ void dnl_load(const uint8_t* __restrict__ packed, const ExpertLayout& L, int I, int E,
+                                         int k, int has_shared, int n0, const int32_t* ids_t, int b0, int wave,
+                                         int lane, DnLoadsL& d) {
+    const int S = k + has_shared;
+    const int lpr = I / 32, rpw = 64 / lpr;
+    const int lr = lane % lpr, rsub = lane / lpr;
+    const int n_dots = S * DN_ROWS;
+    const int n_it = (n_dots + rpw - 1) / rpw;
+    const size_t qstride = I / 2, sbstride = I / 64;
+#pragma unroll
+    for (int j = 0; j < DNB; ++j) {
+        const int it = wave + LW * (b0 + j);
+        const int q = it * rpw + rsub;
+        d.ok[j] = it < n_it && q < n_dots;
+        d.slot[j] = d.ok[j] ? q / DN_ROWS : 0;
+        if (d.ok[j]) {
+            const int s = d.slot[j];
+            const int e = s < k ? ids_t[s] : E;
+            const int n = n0 + q % DN_ROWS;
+            const uint8_t* base = packed + (size_t)e * L.stride;
+            d.ld[j] = load_chunk(base + L.down_q + n * qstride,
+                                 reinterpret_cast<const uint32_t*>(base + L.down_sb) + n * sbstride, lr);
+        }
+    }
+}
+
+// Persistent kernel: one workgroup of 16 wavefronts per CU (every workgroup
+// resident); data moves between workgroups through epoch-tagged words.
+//   A: router rows, one wavefront per (row, token), published tagged; x is
+//      staged into LDS meanwhile.
+//   S: wavefront t selects token t (DPP top-k over the tagged logits); the
+//      workgroup then forms the distinct experts of the launch (d = 0 is the shared
+//      expert) and, per distinct expert, the (token, slot) pairs that use it.
+//   B: gate/up row-pair tasks (distinct expert, row pair), one per wavefront:
+//      the four weight rows are loaded once and applied to every token of the
+//      expert; h pairs are published tagged. Sixteen wavefronts per CU keep
+//      enough loads in flight; the shared expert's tasks are loaded before the
+//      selection.
+//   C: down items (8 output rows of one token, every slot) with the combine; a
+//      workgroup stages a token's h once (polling the tagged words) for all of its
+//      items of that token; an item's weight loads go out before that wait, and
+//      the next item's before the arithmetic.
+//
+// HC, IC, KC (when nonzero) fix hidden, inter and top_k at compile time; the
+// shape of the served model gets its own instance, with every lane layout and
+// reduction width folded.
+template <int CPL, int TT, bool AFF8, int VPL, int HC, int IC, int KC>
+__global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
     __shared__ int32_t s_ids[16][16];
     __shared__ uint16_t s_w[16][16];
     __shared__ uint16_t s_wsh[16];
+    __shared__ uint32_t s_used[32];
+    __shared__ int32_t s_upre[32];
+    __shared__ int32_t s_dexp[MAXD];
+    __shared__ int32_t s_dcnt[MAXD];
+    __shared__ uint16_t s_dtok[MAXD][16];
+    __shared__ int32_t s_nd;
     __shared__ float ysh[17][DN_ROWS];
-    extern __shared__ __attribute__((aligned(16))) uint32_t hsh_dyn[];
+    extern __shared__ __attribute__((aligned(16))) uint32_t lds_dyn[];
     const int G = gridDim.x, wg = blockIdx.x;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int T = a.T, H = a.H, I = a.I, E = a.E, k = a.k, R = a.R;
-    const int S = k + a.has_shared;
+    const int T = TT == 1 ? 1 : a.T, H = HC ? HC : a.H, I = IC ? IC : a.I, k = KC ? KC : a.k;
+    const int E = a.E, R = a.R, hs_ = a.has_shared;
+    const int S = k + hs_;
+    const int npair = I / 2;
     DecodeCtl* ctl = a.ctl;
     const uint32_t tag = load_coherent(&ctl->epoch) + 1u;
-    const int n_router = (R + 3) / 4;
-    const int gu_per_tok = I / GU_ROWS;
-    const int n_shared = a.has_shared ? T * gu_per_tok : 0;
-    const int n_A = n_router + n_shared;
-    const int n_B = T * k * gu_per_tok;
-    const int n_C = T * (H / DN_ROWS);
+    uint32_t* hsh = lds_dyn;                                                        // [S][I] bf16
+    uint16_t* s_x = reinterpret_cast<uint16_t*>(lds_dyn + (size_t)S * I / 2);      // [T][H] bf16
+    float* s_xs = reinterpret_cast<float*>(s_x + (a.stage_x ? (size_t)T * H : 0));  // [T][H/32]
+    if (tid < 32) s_used[tid] = 0u;
+    for (int i = tid; i < MAXD; i += LTH) s_dcnt[i] = 0;
 
-    // ---- phase A
-    for (int item = wg; item < n_A; item += G) {
-        if (item < n_router) {
-            const int r = item * 4 + wave;
-            if (r < R)
-                router_row<TT, AFF8>(a.router, a.logit_bias, a.x, 0, T, H, R, E, r, lane, a.logits, false, a.tlogits,
-                                     tag);
-        } else {
-            const int j = item - n_router, t = j % T, rb = j / T;
-            const size_t row = (size_t)t * S + k;
-            gateup_item<CPL>(a.experts, a.L, H, E, true, a.x + (size_t)t * H, nullptr, a.th + row * (I / 2), tag,
-                             rb, wave, lane);
-        }
+    // Wavefronts that poll must have no loads or stores of their own outstanding:
+    // the vector memory counter retires in order, so a poll's result would wait
+    // for them. Router rows and gate/up tasks are therefore numbered from the top
+    // wavefront down, and selection runs on wavefronts 0 .. T-1.
+    const int wtop = LW - 1 - wave;
+
+    // ---- A: router rows, one wavefront per (row, token); the per-lane order of the
+    // products and the reduction tree are those of router_row for any token count,
+    // so the logits equal the staged router's bit for bit
+    if (wtop < T) {
+        for (int r = wg; r < R; r += G)
+            router_row<1, AFF8>(a.router, a.logit_bias, a.x, wtop, 1, H, R, E, r, lane, a.logits, false, a.tlogits,
+                                tag);
+    }
+    if (a.stage_x) stage_x(a.x, T, H, s_x, s_xs);
+    __syncthreads();
+
+    // the shared expert's row pairs are tasks 0 .. npair-1 of phase B
+    PairLoads<CPL> cur;
+    bool have = false;
+    const int j0 = wg + G * wtop;
+    if (hs_ && j0 < npair && wave >= T) {
+        pair_load<CPL>(a.experts, a.L, H, E, j0, lane, cur);
+        have = true;
     }
 
-    // ---- selection of the tokens this workgroup needs
-    uint32_t need = 0;
-    for (int item = wg; item < n_B; item += G) need |= 1u << (item % T);
-    for (int item = wg; item < n_C; item += G) need |= 1u << (item % T);
-    if (wg < T) need |= 1u << wg;
-    for (int t = 0, c = 0; t < T; ++t) {
-        if (need >> t & 1u) {
-            if ((c & 3) == wave) {
-                const LogitSrc src{nullptr, a.tlogits + (size_t)t * R, tag, &ctl->error, false};
-                select_token_any(src, E, k, a.has_shared, lane, s_ids[t], s_w[t], &s_wsh[t]);
-            }
-            ++c;
-        }
+    // ---- S: selection, distinct experts, token lists
+    if (wave < T) {
+        const LogitSrc src{nullptr, a.tlogits + (size_t)wave * R, tag, &ctl->error, false};
+        select_token<VPL>(src, E, k, hs_, lane, s_ids[wave], s_w[wave], &s_wsh[wave]);
     }
     __syncthreads();
-    if (wg < T) {
-        if (tid < k) {
-            a.ids[(size_t)wg * k + tid] = s_ids[wg][tid];
-            a.w[(size_t)wg * k + tid] = s_w[wg][tid];
+    if (tid < T * k) {
+        const int e = s_ids[tid / k][tid % k];
+        atomicOr(&s_used[e >> 5], 1u << (e & 31));
+    }
+    if (wg == 0) {
+        if (tid < T * k) {
+            a.ids[tid] = s_ids[tid / k][tid % k];
+            a.w[tid] = s_w[tid / k][tid % k];
         }
-        if (a.has_shared && tid == 0) a.wsh[wg] = s_wsh[wg];
+        if (hs_ && tid < T) a.wsh[tid] = s_wsh[tid];
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const int nword = (E + 31) / 32;
+        const uint32_t m = lane < nword ? s_used[lane] : 0u;
+        const int c = __popc(m);
+        int incl = c;
+        for (int dd = 1; dd < 32; dd <<= 1) {
+            const int o = __shfl_up(incl, dd);
+            if (lane >= dd) incl += o;
+        }
+        int pos = hs_ + incl - c;
+        if (lane < nword) s_upre[lane] = pos;
+        for (uint32_t mm = m; mm; mm &= mm - 1) s_dexp[pos++] = 32 * lane + __builtin_ctz(mm);
+        if (lane == 31) s_nd = hs_ + incl;
+        if (lane == 0 && hs_) s_dexp[0] = E;
+    }
+    __syncthreads();
+    if (tid < T * k) {
+        const int t = tid / k, sl = tid % k, e = s_ids[t][sl];
+        const int dd = s_upre[e >> 5] + __popc(s_used[e >> 5] & ((1u << (e & 31)) - 1u));
+        const int p = atomicAdd(&s_dcnt[dd], 1);
+        s_dtok[dd][p] = (uint16_t)(t | (sl << 5));
+    }
+    if (hs_ && tid < T) {
+        s_dtok[0][tid] = (uint16_t)(tid | (k << 5));
+        if (tid == 0) s_dcnt[0] = T;
+    }
+    __syncthreads();
+
+    // ---- B: gate/up row pairs of the distinct experts
+    const int nB = s_nd * npair;
+    const int NBLK = H / DN_ROWS, nC = T * NBLK;
+    const int per = (nC + G - 1) / G, c0 = wg * per, c1 = min(nC, c0 + per);
+    DnLoadsL dcur;
+    bool dhave = false;
+    for (int j = j0; j < nB; j += G * LW) {
+        const int dd = j / npair, ip = j % npair;
+        if (!have) pair_load<CPL>(a.experts, a.L, H, s_dexp[dd], ip, lane, cur);
+        have = false;
+        const int cnt = s_dcnt[dd];
+        for (int u = 0; u < cnt; ++u) {
+            const int ent = s_dtok[dd][u], t = ent & 31, sl = ent >> 5;
+            XSlice<CPL> xs;
+            token_xslice<CPL>(a.stage_x, s_x, s_xs, a.x, t, H, lane, xs);
+            const uint32_t hp = pair_finish<CPL>(cur, H, xs, lane);
+            if (lane == 0) store_tagged(a.th + ((size_t)t * S + sl) * npair + ip, tag, hp);
+        }
     }
 
-    // ---- phase B (the first down item's weight loads are issued with the last
-    // gate/up item's, so they overlap its arithmetic and the wait for h)
-    DnLoads dl;
-    bool dl_ready = false;
-    for (int item = wg; item < n_B; item += G) {
-        const int t = item % T, j = item / T, s = j / gu_per_tok, rb = j % gu_per_tok;
-        const size_t row = (size_t)t * S + s;
-        GuLoads<CPL> gl;
-        gu_load<CPL>(a.experts, a.L, H, s_ids[t][s], true, rb, wave, lane, gl);
-        if (item + G >= n_B && wg < n_C) {
-            const int tc = wg % T;
-            dn_load(a.experts, a.L, I, E, k, a.has_shared, (wg / T) * DN_ROWS, s_ids[tc], 0, dl);
-            dl_ready = true;
+    // ---- C: down items with the combine
+    const int lpr = I / 32, rpw = 64 / lpr;
+    const int lr = lane % lpr, rsub = lane / lpr;
+    const int n_dots = S * DN_ROWS, n_it = (n_dots + rpw - 1) / rpw;
+    int staged = -1;
+    for (int c = c0; c < c1; ++c) {
+        const int t = c / NBLK, n0 = (c % NBLK) * DN_ROWS;
+        if (!dhave) dnl_load(a.experts, a.L, I, E, k, hs_, n0, s_ids[t], 0, wave, lane, dcur);
+        DnLoadsL dnxt;
+        const bool nhave = c + 1 < c1;
+        if (nhave)
+            dnl_load(a.experts, a.L, I, E, k, hs_, ((c + 1) % NBLK) * DN_ROWS, s_ids[(c + 1) / NBLK], 0, wave, lane,
+                     dnxt);
+        if (t != staged) {
+            const int nw = S * npair;
+            const uint64_t* src = a.th + (size_t)t * S * npair;
+            for (int i0 = tid; i0 < nw; i0 += LTH * 4) {
+                uint32_t v[4];
+                const int n = min(4, (nw - 1 - i0) / LTH + 1);
+                load_tagged_many<4>(src + i0, LTH, n, tag, &ctl->error, v);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (j < n) hsh[i0 + LTH * j] = v[j];
+            }
+            __syncthreads();
+            staged = t;
         }
-        gu_finish<CPL>(gl, H, true, a.x + (size_t)t * H, nullptr, a.th + row * (I / 2), tag, rb, wave, lane);
-    }
-
-    // ---- phase C
-    for (int item = wg; item < n_C; item += G) {
-        const int t = item % T, ng = item / T;
-        if (!dl_ready) dn_load(a.experts, a.L, I, E, k, a.has_shared, ng * DN_ROWS, s_ids[t], 0, dl);
-        dl_ready = false;
-        dn_finish<true>(dl, a.experts, a.L, H, I, E, k, a.has_shared, t, ng * DN_ROWS, nullptr, s_ids[t], s_w[t],
-                        &s_wsh[t], a.y, a.residual, a.out, ysh, hsh_dyn, a.th + (size_t)t * S * (I / 2), tag,
-                        &ctl->error);
+        for (int b0 = 0; LW * b0 < n_it; b0 += DNB) {
+            if (b0 > 0) dnl_load(a.experts, a.L, I, E, k, hs_, n0, s_ids[t], b0, wave, lane, dcur);
+#pragma unroll
+            for (int j = 0; j < DNB; ++j) {
+                const int it = wave + LW * (b0 + j);
+                if (it >= n_it) break;  // wave-uniform
+                const int q = it * rpw + rsub;
+                float v = 0.f;
+                if (dcur.ok[j]) {
+                    XSlice<1> hx;
+                    load_xslice(reinterpret_cast<const uint16_t*>(hsh) + (size_t)dcur.slot[j] * I, lr, lpr, hx);
+                    v = chunk_dot(dcur.ld[j], hx.p[0], hx.s[0]);
+                }
+                v = group_sum(v, lpr);
+                if (lr == lpr - 1 && q < n_dots) ysh[q / DN_ROWS][q % DN_ROWS] = v;
+            }
+        }
+        __syncthreads();
+        if (a.y) {
+            for (int i = tid; i < n_dots; i += LTH)
+                a.y[((size_t)t * S + i / DN_ROWS) * H + n0 + i % DN_ROWS] = ysh[i / DN_ROWS][i % DN_ROWS];
+        }
+        if (tid < DN_ROWS) {
+            float acc = 0.f;
+            for (int sl = 0; sl < k; ++sl) acc = fmaf(bf16_to_f32(s_w[t][sl]), ysh[sl][tid], acc);
+            if (hs_) acc = fmaf(bf16_to_f32(s_wsh[t]), ysh[k][tid], acc);
+            uint32_t bb = f32_to_bf16(acc);
+            const size_t o = (size_t)t * H + n0 + tid;
+            if (a.residual) bb = f32_to_bf16(bf16_to_f32(a.residual[o]) + bf16_to_f32(bb));
+            a.out[o] = (uint16_t)bb;
+        }
+        __syncthreads();  // ysh and hsh are reused by the next item
+        dcur = dnxt;
+        dhave = nhave;
     }
 
     // ---- exit: the last workgroup out publishes the new epoch
@@ -514,19 +775,48 @@ static int device_cus() {
 // LDS for one token's h rows of every slot.
 static size_t hsh_bytes(const moe_shape& sh) { return (size_t)n_slots(sh) * sh.inter * 2; }
 
+// LDS copy of x [T][H] with its chunk sums.
+static size_t xsh_bytes(const moe_shape& sh, int T) { return (size_t)T * sh.hidden * 2 + (size_t)T * (sh.hidden / 32) * 4; }
+
+template <int CPL, int TT, int VPL>
+static void launch_layer_v(const LayerArgs& a, bool aff8, int G, size_t lds, hipStream_t hs) {
+    if constexpr (CPL == 1 && VPL == 4) {
+        if (aff8 && a.H == 2048 && a.I == 512 && a.k == 8) {  // the served model's shape
+            hipLaunchKernelGGL((decode_layer_kernel<CPL, TT, true, VPL, 2048, 512, 8>), dim3(G), dim3(LTH), lds, hs,
+                               a);
+            return;
+        }
+    }
+    if (aff8)
+        hipLaunchKernelGGL((decode_layer_kernel<CPL, TT, true, VPL, 0, 0, 0>), dim3(G), dim3(LTH), lds, hs, a);
+    else
+        hipLaunchKernelGGL((decode_layer_kernel<CPL, TT, false, VPL, 0, 0, 0>), dim3(G), dim3(LTH), lds, hs, a);
+}
+
 template <int CPL, int TT>
 static void launch_layer_tt(const LayerArgs& a, bool aff8, int G, size_t lds, hipStream_t hs) {
-    if (aff8)
-        hipLaunchKernelGGL((decode_layer_kernel<CPL, TT, true>), dim3(G), dim3(256), lds, hs, a);
-    else
-        hipLaunchKernelGGL((decode_layer_kernel<CPL, TT, false>), dim3(G), dim3(256), lds, hs, a);
+    const int vpl = (a.E + 63) / 64;
+    if (vpl <= 1) launch_layer_v<CPL, TT, 1>(a, aff8, G, lds, hs);
+    else if (vpl <= 4) launch_layer_v<CPL, TT, 4>(a, aff8, G, lds, hs);
+    else launch_layer_v<CPL, TT, 16>(a, aff8, G, lds, hs);
 }
 
 template <int CPL>
 static void launch_layer(const LayerArgs& a, bool aff8, int G, size_t lds, hipStream_t hs) {
     if (a.T <= 1) launch_layer_tt<CPL, 1>(a, aff8, G, lds, hs);
-    else if (a.T <= 4) launch_layer_tt<CPL, 4>(a, aff8, G, lds, hs);
     else launch_layer_tt<CPL, 16>(a, aff8, G, lds, hs);
+}
+
+static int device_max_lds() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (!cache[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) return 0;
+        cache[dev] = n;
+    }
+    return cache[dev];
 }
 
 }  // namespace moe
@@ -628,12 +918,15 @@ extern "C" moe_status moe_decode_layer(const moe_shape* shape, const void* route
     a.k = sh.top_k;
     a.has_shared = sh.has_shared;
     a.R = router_rows(sh);
-    const int n_router = (a.R + 3) / 4;
-    const int n_A = n_router + (sh.has_shared ? T * (a.I / GU_ROWS) : 0);
-    const int items = std::max(std::max(n_A, T * sh.top_k * (a.I / GU_ROWS)), T * (a.H / DN_ROWS));
-    const int G = std::min(cus, items);
+    // 16 KiB covers the kernel's static LDS (selection results, distinct-expert lists)
+    const size_t lds_h = hsh_bytes(sh), lds_x = xsh_bytes(sh, T);
+    const int max_lds = device_max_lds();
+    if (max_lds <= 0) return fail(MOE_ERR_HIP, "could not query the LDS size");
+    a.stage_x = lds_h + lds_x + 16384 <= (size_t)max_lds ? 1 : 0;
+    const size_t lds = lds_h + (a.stage_x ? lds_x : 0);
+    const int G = std::min(cus, std::max(a.R, T * (a.H / DN_ROWS)));
     const bool aff8 = sh.router_fmt == MOE_ROUTER_AFFINE8;
-    if (cpl_for(sh.hidden) == 1) launch_layer<1>(a, aff8, G, hsh_bytes(sh), hs);
-    else launch_layer<2>(a, aff8, G, hsh_bytes(sh), hs);
+    if (cpl_for(sh.hidden) == 1) launch_layer<1>(a, aff8, G, lds, hs);
+    else launch_layer<2>(a, aff8, G, lds, hs);
     return check_launch("decode_layer_kernel");
 }

@@ -6,18 +6,22 @@
 
 namespace moe {
 
-// Wave-wide maximum of an unsigned value with DPP row operations (quad
-// permutations, half-row and row mirrors, then the row broadcasts 15 and 31);
-// every lane must be active. Returns the maximum in all lanes.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast15
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast31
+// Wave-wide maximum (or minimum) of an unsigned value with DPP row operations
+// (quad permutations, half-row and row mirrors, then the row broadcasts 15 and
+// 31); every lane must be active. Returns the result in all lanes.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_ext_u32(uint32_t v) {
+    auto f = [](uint32_t a, uint32_t b) { return MAX ? max(a, b) : min(a, b); };
+    const int fill = MAX ? 0 : -1;
+    v = f(v, (uint32_t)__builtin_amdgcn_update_dpp(fill, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    v = f(v, (uint32_t)__builtin_amdgcn_update_dpp(fill, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    v = f(v, (uint32_t)__builtin_amdgcn_update_dpp(fill, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+    v = f(v, (uint32_t)__builtin_amdgcn_update_dpp(fill, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+    v = f(v, (uint32_t)__builtin_amdgcn_update_dpp(fill, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast15
+    v = f(v, (uint32_t)__builtin_amdgcn_update_dpp(fill, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast31
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return wave_ext_u32<true>(v); }
 
 __device__ __forceinline__ double readlane_f64(double v, int l) {
     const uint64_t u = (uint64_t)__double_as_longlong(v);
@@ -27,78 +31,111 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
 }
 
 // Selection for one token by one full wavefront (see LogitSrc for where the
-// logits come from). Logit e lives in lane e % 64,
-// slot e / 64 as a 32-bit key: 0 once picked (or beyond E), else
-// max(ordered_logit, 1) so NaN (ordered 0) still ranks above a removed entry but
-// below every number. Each of the k rounds takes the wave maximum of the keys
-// (DPP), then the lowest expert id holding it (ballots: lowest slot, then lowest
-// lane), which realises the order (logit desc, id asc).
-// Outputs: sel_id[i] and sel_w[i] (bf16 bits) for i < k in lane i's registers are
-// written through the given pointers by lanes 0..k-1; *sel_wsh by lane 0.
+// logits come from). Expert e's logit lives in lane e % 64, slot e / 64, as a
+// 32-bit key: max(ordered_logit, 1) for e < E (so NaN, ordered 0, still ranks
+// above an absent entry but below every number), 0 beyond E. Each lane first
+// orders its own keys (descending; equal keys keep ascending slot, i.e. ascending
+// id). A round then takes the wave maximum of the lanes' leading keys (DPP); the
+// single lane holding it is the winner, and if several lanes hold it, the one
+// whose leading key has the lowest expert id (a second DPP reduction). The winner
+// drops its leading key. This realises the order (logit desc, id asc).
+// Outputs: sel_id[i] and sel_w[i] (bf16 bits) for i < k, written by lanes
+// 0..k-1; *sel_wsh by lane k, whose exp and division run beside the picks'.
 template <int VPL>
 __device__ __forceinline__ void select_token(const LogitSrc& lr, int E, int k, int has_shared, int lane,
                                              int32_t* sel_id, uint16_t* sel_w, uint16_t* sel_wsh) {
-    uint32_t key[VPL], raw[VPL];
+    uint32_t raw[VPL + 1];
     if (lr.tagged) {
-        const int n = lane < E ? (E - 1 - lane) / 64 + 1 : 0;  // this lane's logits: lane + 64 j < E
-        load_tagged_many<VPL>(lr.tagged + lane, 64, n, lr.tag, lr.err, raw);
+        // this lane's logits lane + 64 j < E, and the shared gate (index E) in the same batch
+        const int R = E + (has_shared ? 1 : 0);
+        const int n = lane < R ? (R - 1 - lane) / 64 + 1 : 0;
+        load_tagged_many<VPL + 1>(lr.tagged + lane, 64, n, lr.tag, lr.err, raw);
     } else {
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
             const int e = lane + 64 * j;
             raw[j] = e < E ? lr.get(e) : 0u;
         }
+        raw[VPL] = 0u;
     }
+    uint32_t gbits = 0u;  // the shared gate's logit, in every lane
+    if (has_shared) {
+        if (lr.tagged) {  // index E sits in lane E % 64, slot E / 64
+            uint32_t v = raw[0];
+#pragma unroll
+            for (int j = 1; j <= VPL; ++j)
+                if (j == E / 64) v = raw[j];
+            gbits = (uint32_t)__builtin_amdgcn_readlane((int)v, E % 64);
+        } else {
+            gbits = (uint32_t)__builtin_amdgcn_readfirstlane((int)(lane == 0 ? lr.get(E) : 0u));
+        }
+    }
+    uint32_t key[VPL], rv[VPL], id[VPL];
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
         const int e = lane + 64 * j;
         const uint32_t o = e < E ? ordered_logit(__uint_as_float(raw[j])) : 0u;
         key[j] = e < E ? (o > 1u ? o : 1u) : 0u;
+        rv[j] = raw[j];
+        id[j] = (uint32_t)e;
+    }
+    // stable odd-even transposition sort of this lane's keys, descending
+#pragma unroll
+    for (int pass = 0; pass < VPL; ++pass) {
+#pragma unroll
+        for (int j = pass & 1; j + 1 < VPL; j += 2) {
+            const bool sw = key[j + 1] > key[j];
+            const uint32_t k0 = key[j], r0 = rv[j], i0 = id[j];
+            key[j] = sw ? key[j + 1] : k0;
+            rv[j] = sw ? rv[j + 1] : r0;
+            id[j] = sw ? id[j + 1] : i0;
+            key[j + 1] = sw ? k0 : key[j + 1];
+            rv[j + 1] = sw ? r0 : rv[j + 1];
+            id[j + 1] = sw ? i0 : id[j + 1];
+        }
     }
     uint32_t my_id = 0, my_raw = 0;
     for (int i = 0; i < k; ++i) {
-        uint32_t m = key[0];
-#pragma unroll
-        for (int j = 1; j < VPL; ++j) m = key[j] > m ? key[j] : m;
-        m = wave_max_u32(m);
-        int wj = 0;
-        uint64_t mask = 0;
-#pragma unroll
-        for (int j = VPL - 1; j >= 0; --j) {
-            const uint64_t b = __ballot(key[j] == m);
-            if (b) {
-                wj = j;
-                mask = b;
-            }
+        const uint32_t m = wave_max_u32(key[0]);
+        const uint64_t b = __ballot(key[0] == m);
+        int wl;
+        if (__popcll(b) == 1) {
+            wl = __builtin_ctzll(b);
+        } else {  // equal leading keys in several lanes: the lowest expert id wins
+            const uint32_t mid = wave_ext_u32<false>(key[0] == m ? id[0] : 0xFFFFFFFFu);
+            wl = (int)(mid & 63u);
         }
-        const int wl = __builtin_ctzll(mask);
-        uint32_t rv = raw[0];
+        const uint32_t wid = (uint32_t)__builtin_amdgcn_readlane((int)id[0], wl);
+        const uint32_t wraw = (uint32_t)__builtin_amdgcn_readlane((int)rv[0], wl);
+        if (lane == wl) {
 #pragma unroll
-        for (int j = 1; j < VPL; ++j)
-            if (j == wj) rv = raw[j];
-        rv = (uint32_t)__builtin_amdgcn_readlane((int)rv, wl);  // the picked logit, from registers
-#pragma unroll
-        for (int j = 0; j < VPL; ++j)
-            if (j == wj && lane == wl) key[j] = 0;
+            for (int j = 0; j + 1 < VPL; ++j) {
+                key[j] = key[j + 1];
+                rv[j] = rv[j + 1];
+                id[j] = id[j + 1];
+            }
+            key[VPL - 1] = 0u;
+        }
         if (lane == i) {
-            my_id = (uint32_t)(64 * wj + wl);
-            my_raw = rv;
+            my_id = wid;
+            my_raw = wraw;
         }
     }
     my_id = my_id < (uint32_t)E ? my_id : (uint32_t)(E - 1);
     const double li = lane < k ? (double)__uint_as_float(my_raw) : 0.0;
     const double l0 = readlane_f64(li, 0);
-    const double ex = lane < k ? exp(li - l0) : 0.0;
+    // lanes < k: exp(l_i - l_top); lane k: the shared gate's exp(-g), g = bf16(gate)
+    const double g = (double)bf16_to_f32(f32_to_bf16(__uint_as_float(gbits)));
+    const double ex = exp(lane < k ? li - l0 : -g);
     double sum = 0.0;
     for (int j = 0; j < k; ++j) sum += readlane_f64(ex, j);
+    const double num = lane < k ? ex : 1.0, den = lane < k ? sum : 1.0 + ex;
+    const uint16_t wb = (uint16_t)f64_to_bf16(num / den);
     if (lane < k) {
         sel_id[lane] = (int32_t)my_id;
-        sel_w[lane] = (uint16_t)f64_to_bf16(ex / sum);
+        sel_w[lane] = wb;
     }
-    if (has_shared && lane == 0) {
-        const double g = (double)bf16_to_f32(f32_to_bf16(__uint_as_float(lr.get(E))));
-        *sel_wsh = (uint16_t)f64_to_bf16(1.0 / (1.0 + exp(-g)));
-    }
+    if (has_shared && lane == k) *sel_wsh = wb;
 }
 
 // Dispatch on the number of keys per lane.
@@ -176,31 +213,53 @@ __device__ __forceinline__ void router_row(const uint8_t* __restrict__ router, c
             const int j = j0 + 64 * c;
             if (j >= C) break;
             const int c0 = j * EPC;
-            double wv[EPC];
             const uint32_t qw[4] = {wq[c].x, wq[c].y, wq[c].z, wq[c].w};
+            double s = 0.0, b = 0.0;
             if constexpr (AFF8) {
-                const double s = (double)bf16_to_f32(wg[c] & 0xFFFFu), b = (double)bf16_to_f32(wg[c] >> 16);
-#pragma unroll
-                for (int i = 0; i < EPC; ++i) wv[i] = s * (double)((qw[i >> 2] >> (8 * (i & 3))) & 0xFFu) + b;  // exact
-            } else {
-#pragma unroll
-                for (int i = 0; i < EPC; ++i) wv[i] = (double)__uint_as_float(qw[i]);
+                s = (double)bf16_to_f32(wg[c] & 0xFFFFu);
+                b = (double)bf16_to_f32(wg[c] >> 16);
             }
+            // weight i of the chunk, exact in fp64
+            auto wt = [&](int i) -> double {
+                if constexpr (AFF8) return s * (double)((qw[i >> 2] >> (8 * (i & 3))) & 0xFFu) + b;
+                else return (double)__uint_as_float(qw[i]);
+            };
+            if constexpr (TH > 0) {
+                double wv[EPC];
 #pragma unroll
-            for (int t = 0; t < TT; ++t) {
-                if (t < nt) {
-                    uint32_t xw[XW];
-                    if constexpr (TH > 0) {
+                for (int i = 0; i < EPC; ++i) wv[i] = wt(i);
 #pragma unroll
-                        for (int i = 0; i < XW; ++i) xw[i] = xh[c][t < TH ? t : 0][i];
-                    } else {
-                        load_words<XW>(x + (size_t)(t0 + t) * H + c0, xw);
+                for (int t = 0; t < TT; ++t) {
+                    if (t < nt) {
+#pragma unroll
+                        for (int i = 0; i < EPC; ++i) {
+                            const uint32_t w = xh[c][t < TH ? t : 0][i >> 1];
+                            const uint32_t bits = (i & 1) ? (w >> 16) : (w & 0xFFFFu);
+                            acc[t] = fma((double)bf16_to_f32(bits), wv[i], acc[t]);
+                        }
                     }
+                }
+            } else {
+                // many tokens: four weights at a time, each applied to every token
+                // (per token the products still accumulate in element order); the
+                // scheduling barrier keeps the compiler from hoisting the activation
+                // reads of every group at once
 #pragma unroll
-                    for (int i = 0; i < EPC; ++i) {
-                        const uint32_t bits = (i & 1) ? (xw[i >> 1] >> 16) : (xw[i >> 1] & 0xFFFFu);
-                        acc[t] = fma((double)bf16_to_f32(bits), wv[i], acc[t]);
+                for (int g = 0; g < EPC / 4; ++g) {
+                    double w4[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) w4[i] = wt(4 * g + i);
+#pragma unroll
+                    for (int t = 0; t < TT; ++t) {
+                        if (t < nt) {
+                            const uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)(t0 + t) * H + c0 + 4 * g);
+                            acc[t] = fma((double)bf16_to_f32(xv.x & 0xFFFFu), w4[0], acc[t]);
+                            acc[t] = fma((double)bf16_to_f32(xv.x >> 16), w4[1], acc[t]);
+                            acc[t] = fma((double)bf16_to_f32(xv.y & 0xFFFFu), w4[2], acc[t]);
+                            acc[t] = fma((double)bf16_to_f32(xv.y >> 16), w4[3], acc[t]);
+                        }
                     }
+                    __builtin_amdgcn_sched_barrier(0);  // one group's activation reads in flight at a time
                 }
             }
         }
