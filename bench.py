@@ -44,7 +44,110 @@ def parse():
     ap.add_argument("--copies", type=int, default=8, help="independent weight sets for the decode workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (counter calibration) and exit")
+    ap.add_argument("--traffic-from", default=None, metavar="FETCH,WRITE,CAL_FETCH,CAL_WRITE",
+                    help="rocprofv3 --pmc output folders of FETCH_SIZE and WRITE_SIZE runs of this workload and "
+                         "of --copy-calibration; writes the scaled per-launch traffic of the workload's kernel to "
+                         "profiles/ and exits")
     return ap.parse_args()
+
+
+# ---------------------------------------------------------------- measured HBM traffic
+# Per-launch HBM bytes of the dominant kernel come from two rocprofv3 --pmc runs
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the same
+# counter reads for a plain copy of known size. The record is stored with a hash
+# of the library sources; a bench run reports it only while the hash matches.
+# kernels of the measured stage (per-launch traffic is the sum of their per-dispatch medians)
+TRAFFIC_KERNELS = {"decode": ["decode_layer_kernel"], "stack16": ["decode_layer_kernel"],
+                   "stack1": ["decode_layer_kernel"],
+                   "prefill512": ["dispatch_kernel", "gateup_gemm_kernel", "down_gemm_kernel"],
+                   "prefill4096": ["dispatch_kernel", "gateup_gemm_kernel", "down_gemm_kernel"]}
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def source_hash():
+    import hashlib
+
+    h = hashlib.sha256()
+    for sub in ("quantized_moe_expert_fp32_amd/csrc", "include"):
+        d = os.path.join(ROOT, sub)
+        for n in sorted(os.listdir(d)):
+            if n.endswith((".hip", ".h")):
+                h.update(n.encode())
+                h.update(open(os.path.join(d, n), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_path(wl):
+    return os.path.join(ROOT, "profiles", "traffic_%s.json" % wl)
+
+
+def pmc_values(folder, counter, name_part):
+    """Per-dispatch values of one counter for kernels whose name contains name_part."""
+    import csv
+
+    out = {}
+    for root, _, files in os.walk(folder):
+        for f in files:
+            if f.endswith("counter_collection.csv"):
+                for r in csv.DictReader(open(os.path.join(root, f))):
+                    if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+                        key = (r["Dispatch_Id"], r["Kernel_Name"])
+                        out[key] = out.get(key, 0.0) + float(r["Counter_Value"])
+    return list(out.values())
+
+
+def write_traffic(wl, spec):
+    fetch_dir, write_dir, cal_fetch_dir, cal_write_dir = spec.split(",")
+    kerns = TRAFFIC_KERNELS[wl]
+    f = [pmc_values(fetch_dir, "FETCH_SIZE", k) for k in kerns]
+    w = [pmc_values(write_dir, "WRITE_SIZE", k) for k in kerns]
+    cal = json.load(open(os.path.join(cal_fetch_dir, "calibration.json")))
+    known_kib = cal["bytes"] / 1024.0
+    # the copy dispatches of the calibration run (ignore small set-up kernels)
+    cf = [v for v in pmc_values(cal_fetch_dir, "FETCH_SIZE", "") if v > 0.5 * known_kib]
+    cw = [v for v in pmc_values(cal_write_dir, "WRITE_SIZE", "") if v > 0.5 * known_kib]
+    if not all(f) or not all(w) or not cf or not cw:
+        raise SystemExit("missing counter values for %s" % kerns)
+    k_fetch = known_kib / float(np.median(cf))
+    k_write = known_kib / float(np.median(cw))
+    fk = sum(float(np.median(v)) for v in f)
+    wk = sum(float(np.median(v)) for v in w)
+    rec = {"workload": wl, "kernels": kerns, "dispatches": [[len(v) for v in f], [len(v) for v in w]],
+           "fetch_kib_per_launch": fk, "write_kib_per_launch": wk,
+           "calibration_bytes": cal["bytes"], "fetch_scale": k_fetch, "write_scale": k_write,
+           "traffic_bytes_per_launch": (fk * k_fetch + wk * k_write) * 1024.0,
+           "source_hash": source_hash()}
+    os.makedirs(os.path.dirname(traffic_path(wl)), exist_ok=True)
+    json.dump(rec, open(traffic_path(wl), "w"), indent=1)
+    print(json.dumps(rec))
+
+
+def stored_traffic(wl):
+    try:
+        rec = json.load(open(traffic_path(wl)))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash():
+        log("stored traffic for %s predates the current sources: reported as null" % wl)
+        return None
+    return rec["traffic_bytes_per_launch"]
+
+
+def copy_calibration(mib):
+    import torch
+
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    rec = {"bytes": n, "copies": 5}
+    print(json.dumps(rec))
+    return rec
 
 
 def log(msg):
@@ -53,6 +156,15 @@ def log(msg):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        write_traffic(args.workload, args.traffic_from)
+        return
+    if args.copy_calibration:
+        rec = copy_calibration(args.copy_calibration)
+        out = os.environ.get("CALIBRATION_OUT")
+        if out:
+            json.dump(rec, open(out, "w"))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (expert parallelism "
               "is a design note only); run with --gpus 1", file=sys.stderr)
@@ -160,11 +272,15 @@ def main():
 
     # ---------------------------------------------------------------- timed region
     torch.cuda.synchronize()
+    ev_a, ev_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     with torch.cuda.stream(stream):
+        ev_a.record(stream)
         run_steps(K)
+        ev_b.record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    region_us = ev_a.elapsed_time(ev_b) * 1e3
     ms_per_step = elapsed * 1e3 / K
     tokens_per_step = T
     value = tokens_per_step * K / elapsed
@@ -194,6 +310,12 @@ def main():
     durs_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
     expert_us = float(np.mean(durs_ms) * 1e3)
     log("measured stage: %.2f us average over %d event-timed launches" % (expert_us, n_ev))
+    if wl == "decode":
+        # every step of the timed region is exactly one decode_layer_kernel launch:
+        # the events around the region give the kernel's average duration without
+        # the per-launch event overhead
+        expert_us = region_us / K
+        log("decode_layer_kernel: %.2f us average over the %d launches of the timed region" % (expert_us, K))
 
     # algorithmic work of one expert-stage launch
     ids_np = buf.ids.cpu().numpy()
@@ -214,7 +336,7 @@ def main():
             roof = dict(bound="hbm", achieved=alg_bytes / (expert_us * 1e-6) / 1e9, peak=HBM_PEAK_GBS,
                         unit="GB/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = stored_traffic(wl)
     roof["kernel"] = ("decode_layer_kernel (router, selection, experts, combine in one launch)" if path == "fused"
                       else "experts stage: dispatch_kernel + gateup_gemm_kernel + down_gemm_kernel")
     roof["avg_us"] = expert_us
