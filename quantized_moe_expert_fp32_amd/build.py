@@ -24,6 +24,9 @@ ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", INCLUDE, "-I", CSRC]
+# Per-source extras. The grouped GEMM applies a per-group scale to each MFMA
+# product on the VALU; MFMA results in VGPRs save a copy out of AGPRs per element.
+SOURCE_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
 
 
 def _run(cmd, verbose):
@@ -47,7 +50,7 @@ def build(verbose: bool = False) -> str:
         for src in SOURCES:
             obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
             objs.append(obj)
-            cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [HIPCC] + FLAGS + SOURCE_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
             jobs.append(ex.submit(_run, cmd, verbose))
         for j in jobs:
             j.result()

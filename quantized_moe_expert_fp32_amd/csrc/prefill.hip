@@ -13,11 +13,11 @@
 // parts below 2^-24 relative). X of the activations comes from a pre-pass, X of h
 // from the gate/up epilogue. No weight is rounded.
 //
-// Tiles: 128 expert-sorted rows x 64*NCS weight rows per workgroup of four
-// wavefronts (gate/up, NCS = 2: 64 gate + 64 up rows of the same 64 intermediate
-// columns; down, NCS = 4: 256 output columns); wavefront w owns weight rows
-// cs*64 + 16w .. (cs < NCS) over all 128 rows, with v_mfma_f32_16x16x32_bf16 in the
-// main loop, so every activation fragment read from LDS feeds NCS products.
+// Tiles: 128 expert-sorted rows x 256 weight rows per workgroup of four
+// wavefronts (gate/up: 128 gate + 128 up rows of the same 128 intermediate
+// columns; down: 256 output columns); wavefront w owns weight rows cs*64 + 16w ..
+// (cs < 4) over all 128 rows, with v_mfma_f32_16x16x32_bf16 in the main loop, so
+// every activation fragment read from LDS feeds four products.
 #include <type_traits>
 
 #include "mfma_common.h"
@@ -210,19 +210,24 @@ static unsigned xcd_grid(int max_tiles, int nb) {
 }
 
 // ---------------------------------------------------------------- grouped GEMM
-// K walks in chunks of KC = 128 (two groups). Per chunk a workgroup stages, with
-// coalesced 16-byte loads:
-//   A: 128 activation rows x 128 bf16 (256 contiguous bytes per row, 16 lanes per
-//      row; rows beyond the tile are not loaded);
-//   B: 128 int4 weight rows x 64 bytes (4 lanes per row) and their (scale, bias)
-//      words for the two groups.
-// The next chunk's loads are issued into registers before the current chunk is
-// multiplied; two barriers per chunk.
-constexpr int KC = 128;
-constexpr int AS = KC + 8;       // A row stride in LDS (bf16): 16-lane groups read distinct banks
-constexpr int BS = KC / 2 + 16;  // B row stride in LDS (bytes): the 64 fragment lanes read distinct banks
-// weight rows per workgroup: 64 * NCS, NCS = 16-column sets per wavefront (2 for
-// gate/up, 4 for down; measured)
+// A workgroup multiplies one tile (up to 128 expert-sorted rows) by a block of
+// NBR = 256 weight rows of the tile's expert over the whole K: gate/up takes 128
+// gate rows and the matching 128 up rows, down takes 256 rows. Wavefront w owns
+// the weight rows cs*64 + 16w .. +16 (cs < 4) for every tile row. K walks in
+// chunks of one quantisation group (KC = 64); per chunk, direct global-to-LDS
+// loads stage
+//   A: the tile's rows x 64 bf16 (128 B per row),
+//   B: the 256 int4 weight rows x 32 B,
+//   sb: the 256 rows' (scale, bias) words of the group,
+// into a ring of NSTAGE stages that runs NSTAGE - 1 chunks ahead of the one being
+// multiplied. Two workgroups share a CU, so one's prologue and epilogue overlap
+// the other's main loop.
+constexpr int KC = 64;
+constexpr int NBR = 256;
+constexpr int NSTAGE = 3;
+constexpr int A_BYTES = BM * KC * 2, B_BYTES = NBR * KC / 2, SB_BYTES = NBR * 4;
+constexpr int STAGE = A_BYTES + B_BYTES + SB_BYTES;  // 25 KiB
+constexpr int RING = NSTAGE * STAGE;
 
 struct GemmArgs {
     const uint8_t* packed;
@@ -241,100 +246,111 @@ struct GemmArgs {
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 
+// Direct global-to-LDS loads from base + off (base wavefront-uniform, off per lane):
+// lane l's 16 (or 4) bytes land at LDS byte address lds + 16 l (4 l); lds is
+// wavefront-uniform and goes in M0, written at least one wait state before the
+// load (the s_nop). Written as inline asm so the compiler does not treat them as
+// LDS stores (it would otherwise wait for every outstanding one before the first
+// LDS read); completion is awaited explicitly with wait_vmcnt, and the memory
+// clobber keeps LDS reads behind the barrier that follows that wait.
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t off, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void lds_dma4(const void* base, uint32_t off, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Workgroup barrier that also keeps the compiler from moving memory accesses
+// across it. This wavefront's LDS reads are complete before it (lgkmcnt 0), so a
+// stage every wavefront has passed the barrier after reading may be refilled; the
+// waits for outstanding global loads are explicit at the call sites.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited for
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// s_waitcnt with only the vector-memory count (expcnt and lgkmcnt left at their
+// maximum, i.e. not waited for); N < 64.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 __device__ __forceinline__ f32x4_t mfma16x16x16(uint2 a, uint2 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, a), __builtin_bit_cast(short4_t, b),
                                                      c, 0, 0, 0);
 }
 
-// GATEUP: B rows 0..127 are gate rows cb*128 .., rows 128..255 the matching up
+// GATEUP: weight rows 0..127 are gate rows cb*128 .., rows 128..255 the matching up
 // rows; the epilogue writes h = bf16(silu(gate) * up) and the row sums of that h
-// block (two groups of the down GEMM's K). Else (down): B rows are down rows
+// block (two groups of the down GEMM's K). Else (down): weight rows are down rows
 // cb*256 ..; the epilogue writes y[t][s][n] for the row's pick p = order[row].
-// Wavefront w owns B rows cs*64 + 16w .. +16 for cs < 4.
-template <bool GATEUP, int NCS>
+template <bool GATEUP>
 __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
-    constexpr int NBR = 64 * NCS;  // weight rows per workgroup
+    constexpr int NCS = NBR / 64;  // 16-column sets per wavefront
     constexpr int HALF = NBR / 2;  // gate/up: gate rows 0 .. HALF-1, up rows HALF .. NBR-1
-    __shared__ __attribute__((aligned(16))) uint16_t a_lds[BM * AS];
-    __shared__ __attribute__((aligned(16))) uint8_t b_lds[NBR * BS];
-    __shared__ __attribute__((aligned(16))) uint2 sb_lds[NBR];
-    __shared__ float xpart[NCS / 2][4][BM];
-    __shared__ uint32_t arow_lds[BM];  // element offset of each tile row in its source, ~0 beyond the tile
+    extern __shared__ __attribute__((aligned(16))) uint8_t ring[];  // NSTAGE stages of (A | B | sb)
+    __shared__ uint32_t arow_lds[BM];  // byte offset of each tile row in its source, ~0 beyond the tile
     const int H = a.H, I = a.I, S = a.S;
     const int K = GATEUP ? H : I;
     const int nblk = GATEUP ? (I + HALF - 1) / HALF : (H + NBR - 1) / NBR;
     int ti, cb;
     if (!xcd_item(*a.ntiles, nblk, ti, cb)) return;
     const Tile tl = a.tiles[ti];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lg = lane >> 4, lc = lane & 15;
     const int n_ms = (tl.nrows + 15) >> 4;
     const int col0 = GATEUP ? cb * HALF : cb * NBR;
 
-    // A rows: this thread stages 16-byte piece c16 of rows tid/16 + 16 j
-    const int c16 = tid & 15;
     if (tid < BM) {
         uint32_t off = 0xFFFFFFFFu;
         if (tid < tl.nrows) {
-            if constexpr (GATEUP) off = (uint32_t)((a.order[tl.row0 + tid] / S) * H);
-            else off = (uint32_t)((tl.row0 + tid) * I);
+            if constexpr (GATEUP) off = (uint32_t)(a.order[tl.row0 + tid] / S) * (uint32_t)(2 * H);
+            else off = (uint32_t)(tl.row0 + tid) * (uint32_t)(2 * I);
         }
         arow_lds[tid] = off;
     }
     __syncthreads();
-    const uint16_t* asrc = GATEUP ? a.x : a.hbuf;
-    // B rows: this thread stages 16-byte piece c4 of rows tid/4 + 64 j
+    const uint8_t* asrc = reinterpret_cast<const uint8_t*>(GATEUP ? a.x : a.hbuf);
     const uint8_t* ebase = a.packed + (size_t)tl.expert * a.L.stride;
-    auto brow_q = [&](int r) -> const uint8_t* {
-        if constexpr (GATEUP) return ebase + (r < HALF ? a.L.gate_q : a.L.up_q) + (size_t)(col0 + r % HALF) * (K / 2);
-        else return ebase + a.L.down_q + (size_t)(col0 + r) * (K / 2);
-    };
-    auto brow_sb = [&](int r) -> const uint32_t* {
-        if constexpr (GATEUP)
-            return reinterpret_cast<const uint32_t*>(ebase + (r < HALF ? a.L.gate_sb : a.L.up_sb)) +
-                   (size_t)(col0 + r % HALF) * (K / 64);
-        else return reinterpret_cast<const uint32_t*>(ebase + a.L.down_sb) + (size_t)(col0 + r) * (K / 64);
-    };
     auto brow_ok = [&](int r) -> bool { return GATEUP ? col0 + r % HALF < I : col0 + r < H; };
-    const int c4 = tid & 3;
+    // byte offsets from ebase of weight row r's q row and sb row
+    auto brow_q_off = [&](int r) -> uint32_t {
+        if constexpr (GATEUP) return (uint32_t)((r < HALF ? a.L.gate_q : a.L.up_q) + (size_t)(col0 + r % HALF) * (K / 2));
+        else return (uint32_t)(a.L.down_q + (size_t)(col0 + r) * (K / 2));
+    };
+    auto brow_sb_off = [&](int r) -> uint32_t {
+        if constexpr (GATEUP)
+            return (uint32_t)((r < HALF ? a.L.gate_sb : a.L.up_sb) + (size_t)(col0 + r % HALF) * (K / 64) * 4);
+        else return (uint32_t)(a.L.down_sb + (size_t)(col0 + r) * (K / 64) * 4);
+    };
 
-    // a chunk's staged loads (chunk c+1 loads while chunk c is multiplied)
-    struct ChunkRegs {
-        uint4 av[8], bv[NBR / 64];
-        uint2 sbv;
-    };
-    auto load_chunk_regs = [&](ChunkRegs& R, int c) {
-        const int kcv = min(KC, K - c * KC);
+    // ---- ring layout within a stage:
+    //   A: 128 rows x 128 B, the 16-byte piece p of row r at position p ^ (r & 7);
+    //   B: 256 rows x 32 B, piece p of row r at position p ^ ((r >> 2) & 1);
+    //   sb: 256 words.
+    // The XOR positions spread the fragment reads of neighbouring lanes over the
+    // banks. Rows beyond the tile or the matrix load a valid row instead (row 0),
+    // so every lane issues every load, each wavefront has exactly LPC loads per
+    // chunk in flight, and the wait for a chunk is an exact vector-memory count.
+    // Per-lane offsets are fixed for the tile; the chunk advances the uniform base.
+    const uint32_t ring_lds = lds_addr(ring);
+    uint32_t b_off[2];  // B: instruction j = 2 wave + i covers rows 32j .. 32j+31
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t off = arow_lds[(tid >> 4) + 16 * j];
-            R.av[j] = (off != 0xFFFFFFFFu && 8 * c16 < kcv)
-                          ? *reinterpret_cast<const uint4*>(asrc + off + c * KC + 8 * c16)
-                          : make_uint4(0u, 0u, 0u, 0u);
-        }
-#pragma unroll
-        for (int j = 0; j < NBR / 64; ++j) {
-            const int r = (tid >> 2) + 64 * j;
-            R.bv[j] = (brow_ok(r) && 16 * c4 < kcv / 2)
-                          ? *reinterpret_cast<const uint4*>(brow_q(r) + c * (KC / 2) + 16 * c4)
-                          : make_uint4(0u, 0u, 0u, 0u);
-        }
-        R.sbv = make_uint2(0u, 0u);
-        if (tid < NBR) {
-            const uint32_t* sp = brow_sb(tid) + c * (KC / 64);
-            R.sbv.x = brow_ok(tid) ? sp[0] : 0u;
-            R.sbv.y = (brow_ok(tid) && kcv > 64) ? sp[1] : 0u;
-        }
-    };
-    auto store_chunk = [&](const ChunkRegs& R) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            *reinterpret_cast<uint4*>(a_lds + ((tid >> 4) + 16 * j) * AS + 8 * c16) = R.av[j];
-#pragma unroll
-        for (int j = 0; j < NBR / 64; ++j)
-            *reinterpret_cast<uint4*>(b_lds + ((tid >> 2) + 64 * j) * BS + 16 * c4) = R.bv[j];
-        if (tid < NBR) sb_lds[tid] = R.sbv;
-    };
+    for (int i = 0; i < 2; ++i) {
+        const int row = 32 * (2 * wave + i) + (lane >> 1);
+        const int piece = (lane & 1) ^ ((row >> 2) & 1);
+        b_off[i] = brow_q_off(brow_ok(row) ? row : 0) + 16 * piece;
+    }
+    const int sb_row = 64 * wave + lane;  // sb: one instruction per wavefront, 64 rows
+    const uint32_t sb_off = brow_sb_off(brow_ok(sb_row) ? sb_row : 0);
 
     f32x4_t acc[8][NCS];
 #pragma unroll
@@ -342,48 +358,70 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int cs = 0; cs < NCS; ++cs) acc[m][cs] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // The K loop is instantiated for 1, 2, 4 and 8 row blocks of 16 (the tile's count
-    // rounded up), so its body is straight-line code the compiler can interleave;
-    // the rows beyond the tile are zeros in LDS.
+    // rounded up), so its body is straight-line code the compiler can interleave.
     auto kloop = [&](auto nm_tag) {
         constexpr int NM = decltype(nm_tag)::value;
-        const int NC = (K + KC - 1) / KC;
+        constexpr int NA = NM >= 2 ? NM / 2 : 1;  // A instructions (8 rows each) per wavefront
+        constexpr int LPC = NA + 3;               // loads per wavefront and chunk
+        const uint32_t arow0 = arow_lds[0];       // row 0 is always inside the tile
+        uint32_t a_off[NA];
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+            const int row = 8 * (NA * wave + i) + (lane >> 3);
+            const uint32_t off = arow_lds[row];
+            a_off[i] = (off == 0xFFFFFFFFu ? arow0 : off) + 16 * ((lane & 7) ^ (row & 7));
+        }
+        auto issue = [&](int c) {
+            const uint32_t st = ring_lds + (uint32_t)((c % NSTAGE) * STAGE);
+            const uint8_t* ab = asrc + (size_t)c * (KC * 2);
+#pragma unroll
+            for (int i = 0; i < NA; ++i) lds_dma16(ab, a_off[i], st + (NA * wave + i) * 1024);
+            const uint8_t* bb = ebase + (size_t)c * (KC / 2);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) lds_dma16(bb, b_off[i], st + A_BYTES + (2 * wave + i) * 1024);
+            lds_dma4(ebase + (size_t)c * 4, sb_off, st + A_BYTES + B_BYTES + wave * 256);
+        };
         auto compute = [&](int c) {
-            const int kcv = min(KC, K - c * KC);
-            for (int gi = 0; gi < kcv / 64; ++gi) {
-                uint4 b0[NCS], b1[NCS];
-                float s16[NCS];
+            const uint8_t* st = ring + (size_t)(c % NSTAGE) * STAGE;
+            const uint32_t* sb_st = reinterpret_cast<const uint32_t*>(st + A_BYTES + B_BYTES);
+            uint4 b0[NCS], b1[NCS];
+            float s16[NCS];
+#pragma unroll
+            for (int cs = 0; cs < NCS; ++cs) {
+                const int br = cs * 64 + 16 * wave + lc;
+                const int sw = (lc >> 2) & 1;
+                const uint8_t* bp = st + A_BYTES + br * 32 + 4 * lg;
+                b0[cs] = bfrag(*reinterpret_cast<const uint32_t*>(bp + 16 * sw));
+                b1[cs] = bfrag(*reinterpret_cast<const uint32_t*>(bp + 16 * (1 ^ sw)));
+                s16[cs] = 16.f * bf16_to_f32(sb_st[br] & 0xFFFFu);
+            }
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                const uint8_t* ar = st + (16 * m + lc) * 128;
+                const uint4 a0 = *reinterpret_cast<const uint4*>(ar + 16 * (lg ^ (lc & 7)));
+                const uint4 a1 = *reinterpret_cast<const uint4*>(ar + 16 * ((4 + lg) ^ (lc & 7)));
 #pragma unroll
                 for (int cs = 0; cs < NCS; ++cs) {
-                    const int br = cs * 64 + 16 * wave + lc;
-                    const uint8_t* bp = b_lds + br * BS + 32 * gi + 4 * lg;
-                    b0[cs] = bfrag(*reinterpret_cast<const uint32_t*>(bp));
-                    b1[cs] = bfrag(*reinterpret_cast<const uint32_t*>(bp + 16));
-                    const uint2 w = sb_lds[br];
-                    s16[cs] = 16.f * bf16_to_f32((gi ? w.y : w.x) & 0xFFFFu);
-                }
+                    f32x4_t p = mfma16x16x32(a0, b0[cs], f32x4_t{0.f, 0.f, 0.f, 0.f});
+                    p = mfma16x16x32(a1, b1[cs], p);
 #pragma unroll
-                for (int m = 0; m < NM; ++m) {
-                    const uint16_t* ar = a_lds + (16 * m + lc) * AS + 64 * gi + 8 * lg;
-                    const uint4 a0 = *reinterpret_cast<const uint4*>(ar);
-                    const uint4 a1 = *reinterpret_cast<const uint4*>(ar + 32);
-#pragma unroll
-                    for (int cs = 0; cs < NCS; ++cs) {
-                        f32x4_t p = mfma16x16x32(a0, b0[cs], f32x4_t{0.f, 0.f, 0.f, 0.f});
-                        p = mfma16x16x32(a1, b1[cs], p);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) acc[m][cs][r] = fmaf(s16[cs], p[r], acc[m][cs][r]);
-                    }
+                    for (int r = 0; r < 4; ++r) acc[m][cs][r] = fmaf(s16[cs], p[r], acc[m][cs][r]);
                 }
             }
         };
-        ChunkRegs r0;
-        load_chunk_regs(r0, 0);
+        const int NC = K / KC;
+        static_assert(NSTAGE == 3, "the wait below assumes one later chunk in flight");
+        issue(0);
+        if (NC > 1) issue(1);
         for (int c = 0; c < NC; ++c) {
-            store_chunk(r0);
-            __syncthreads();
-            if (c + 1 < NC) load_chunk_regs(r0, c + 1);
+            // this wavefront's loads of chunk c are done once only chunk c+1's are left
+            if (c + 1 < NC) wait_vmcnt<LPC>();
+            else wait_vmcnt<0>();
+            // every wavefront's loads of chunk c are in LDS, and every wavefront has
+            // finished chunk c-1, whose stage the next loads refill
+            lds_barrier();
+            if (c + 2 < NC) issue(c + 2);
             compute(c);
-            __syncthreads();
         }
     };
     if (n_ms <= 1) kloop(std::integral_constant<int, 1>{});
@@ -404,7 +442,7 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
                 const int g = 16 * kb + 4 * lg + i;
                 float cc = 0.f;
                 if (g < G && brow_ok(br)) {
-                    const uint32_t w = brow_sb(br)[g];
+                    const uint32_t w = *reinterpret_cast<const uint32_t*>(ebase + brow_sb_off(br) + 4 * g);
                     cc = bf16_to_f32(w >> 16) - 16.f * bf16_to_f32(w & 0xFFFFu);
                 }
                 split3_bf16(cc, h4[i], m4[i], l4[i]);
@@ -446,7 +484,10 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
         // h[row][i] = bf16(silu(gate) * up), i = col0 + 64 hs + 16 wave + lc (gate set
         // hs, up set NCS/2 + hs); row sums of each 64-column part hs of this block of
         // h (fp32, fixed order: 16 lanes by DPP, then the four wavefronts in order)
-        // into the down GEMM's X planes, group col0/64 + hs
+        // into the down GEMM's X planes, group col0/64 + hs. The partial sums reuse
+        // the ring's memory, free once every wavefront is past its last chunk.
+        float(*xpart)[4][BM] = reinterpret_cast<float(*)[4][BM]>(ring);
+        __syncthreads();
 #pragma unroll
         for (int hs = 0; hs < NCS / 2; ++hs) {
             const int i_col = col0 + 64 * hs + 16 * wave + lc;
@@ -539,6 +580,16 @@ extern "C" moe_status moe_experts_prefill(const moe_shape* shape, const void* ex
     if (ws_bytes < W.total) return fail(MOE_ERR_WORKSPACE, "prefill workspace too small (%zu < %zu)", ws_bytes, W.total);
     const ExpertLayout L = expert_layout(sh);
     const int S = n_slots(sh), H = sh.hidden, I = sh.inter;
+    // the GEMMs address activation rows and expert segments with 32-bit byte offsets
+    if ((size_t)T * H * 2 > 0xFFFF0000u || (size_t)T * S * I * 2 > 0xFFFF0000u || L.stride > 0xFFFF0000u)
+        return fail(MOE_ERR_UNSUPPORTED, "T = %d too large for this shape (32-bit row offsets)", T);
+    int max_lds = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+        return fail(MOE_ERR_HIP, "cannot query the device's LDS size");
+    if (max_lds < RING + 1024)
+        return fail(MOE_ERR_UNSUPPORTED, "the grouped GEMM needs %d bytes of LDS per workgroup, the device has %d",
+                    RING + 1024, max_lds);
     hipStream_t hs = (hipStream_t)stream;
     char* w = (char*)ws;
     int32_t* counts = (int32_t*)(w + W.counts);
@@ -572,11 +623,13 @@ extern "C" moe_status moe_experts_prefill(const moe_shape* shape, const void* ex
     ga.xs_a = xs_x;
     ga.xs_h = xs_h;
     ga.gs_a = W.gs_x;
-    hipLaunchKernelGGL((expert_gemm_kernel<true, 2>), dim3(xcd_grid(W.max_tiles, (I + 63) / 64)), dim3(256), 0, hs, ga);
+    hipLaunchKernelGGL((expert_gemm_kernel<true>), dim3(xcd_grid(W.max_tiles, (I + NBR / 2 - 1) / (NBR / 2))), dim3(256),
+                       RING, hs, ga);
     if ((st = check_launch("expert_gemm_kernel<gate/up>")) != MOE_OK) return st;
     ga.xs_a = xs_h;
     ga.xs_h = nullptr;
     ga.gs_a = W.gs_h;
-    hipLaunchKernelGGL((expert_gemm_kernel<false, 4>), dim3(xcd_grid(W.max_tiles, (H + 255) / 256)), dim3(256), 0, hs, ga);
+    hipLaunchKernelGGL((expert_gemm_kernel<false>), dim3(xcd_grid(W.max_tiles, (H + NBR - 1) / NBR)), dim3(256), RING, hs,
+                       ga);
     return check_launch("expert_gemm_kernel<down>");
 }
