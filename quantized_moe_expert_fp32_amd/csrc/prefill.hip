@@ -33,9 +33,12 @@ struct Tile {
 
 // Workspace layout for moe_experts_prefill.
 struct PrefillWs {
-    size_t counts, offsets, cursor, ntiles, tiles, order, h, xs_x, xs_h, total;
+    size_t counts, offsets, cursor, ntiles, tiles, order, h, xs_x, xs_h, slices, total;
     int max_tiles, gs_x, gs_h;  // group strides of the row-sum planes (multiples of 16)
+    int n_slices;               // pick slices of the parallel dispatch
 };
+
+constexpr int SLICE = 2048;  // picks per workgroup of the parallel dispatch
 
 static PrefillWs prefill_ws_layout(const moe_shape& s, int T) {
     PrefillWs w;
@@ -56,6 +59,8 @@ static PrefillWs prefill_ws_layout(const moe_shape& s, int T) {
     w.gs_h = ((s.inter / 64 + 15) / 16) * 16;
     w.xs_x = o;    o = align_up(o + 3 * 2 * (size_t)T * w.gs_x, 256);      // [3][T][gs_x] bf16
     w.xs_h = o;    o = align_up(o + 3 * 2 * (size_t)T * S * w.gs_h, 256);  // [3][T*S][gs_h] bf16
+    w.n_slices = (int)((picks + SLICE - 1) / SLICE);
+    w.slices = o;  o = align_up(o + 4 * (size_t)w.n_slices * s.n_experts, 256);  // [n_slices][E] counts, then bases
     w.total = o;
     return w;
 }
@@ -147,6 +152,119 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const int32_t* __restric
         for (int t = tid; t < T; t += blockDim.x) order[off[E] + t] = t * S + k;
 }
 
+// ---------------------------------------------------------------- parallel dispatch
+// The same result as dispatch_kernel (up to the order of rows within an expert,
+// which no later step depends on), in three launches: per-slice histograms of
+// SLICE picks, one workgroup that turns them into per-slice bases and builds the
+// offsets and the tile list, and a per-slice scatter.
+__global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __restrict__ ids, long long P, int E,
+                                                             int32_t* __restrict__ slices) {
+    __shared__ int cnt[1024];
+    const int tid = threadIdx.x;
+    for (int i = tid; i < E; i += 256) cnt[i] = 0;
+    __syncthreads();
+    const long long p0 = (long long)blockIdx.x * SLICE, p1 = min(P, p0 + SLICE);
+    for (long long p = p0 + tid; p < p1; p += 256) {
+        const int e = ids[p];
+        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+    for (int i = tid; i < E; i += 256) slices[(size_t)blockIdx.x * E + i] = cnt[i];
+}
+
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(int T, int k, int E, int has_shared, int n_slices,
+                                                             int32_t* __restrict__ slices,
+                                                             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ ntiles, Tile* __restrict__ tiles,
+                                                             int32_t* __restrict__ order) {
+    __shared__ int cnt[1025];
+    __shared__ int off[1026];
+    __shared__ int toff[1026];
+    const int M = E + has_shared, S = k + has_shared;
+    const int tid = threadIdx.x;
+    // per expert: exclusive scan over the slices (relative bases, in place)
+    for (int e = tid; e < E; e += blockDim.x) {
+        int run = 0;
+        for (int b = 0; b < n_slices; ++b) {
+            const int c = slices[(size_t)b * E + e];
+            slices[(size_t)b * E + e] = run;
+            run += c;
+        }
+        cnt[e] = run;
+    }
+    if (has_shared && tid == 0) cnt[E] = T;
+    __syncthreads();
+    if (tid < 64) {
+        const int per = (M + 63) / 64;
+        const int beg = tid * per, end = min(M, beg + per);
+        int lc = 0, lt = 0;
+        for (int i = beg; i < end; ++i) {
+            lc += cnt[i];
+            lt += (cnt[i] + BM - 1) / BM;
+        }
+        int ic = lc, it = lt;
+        for (int d = 1; d < 64; d <<= 1) {
+            const int oc = __shfl_up(ic, d), ot = __shfl_up(it, d);
+            if (tid >= d) {
+                ic += oc;
+                it += ot;
+            }
+        }
+        int rc = ic - lc, rt = it - lt;
+        for (int i = beg; i < end; ++i) {
+            off[i] = rc;
+            toff[i] = rt;
+            rc += cnt[i];
+            rt += (cnt[i] + BM - 1) / BM;
+        }
+        if (tid == 63) {
+            off[M] = ic;
+            toff[M] = it;
+            *ntiles = it;
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < M; e += blockDim.x) {
+        counts[e] = cnt[e];
+        offsets[e] = off[e];
+        const int nt = (cnt[e] + BM - 1) / BM;
+        for (int j = 0; j < nt; ++j) {
+            Tile tl;
+            tl.expert = e;
+            tl.row0 = off[e] + j * BM;
+            tl.nrows = min(BM, cnt[e] - j * BM);
+            tl.pad = 0;
+            tiles[toff[e] + j] = tl;
+        }
+    }
+    if (tid == 0) offsets[M] = off[M];
+    // absolute bases
+    for (int e = tid; e < E; e += blockDim.x)
+        for (int b = 0; b < n_slices; ++b) slices[(size_t)b * E + e] += off[e];
+    if (has_shared)
+        for (int t = tid; t < T; t += blockDim.x) order[off[E] + t] = t * S + k;
+}
+
+__global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t* __restrict__ ids, long long P, int k,
+                                                               int E, int S, int H, const int32_t* __restrict__ slices,
+                                                               int32_t* __restrict__ order, float* __restrict__ y) {
+    __shared__ int cur[1024];
+    const int tid = threadIdx.x;
+    for (int i = tid; i < E; i += 256) cur[i] = slices[(size_t)blockIdx.x * E + i];
+    __syncthreads();
+    const long long p0 = (long long)blockIdx.x * SLICE, p1 = min(P, p0 + SLICE);
+    for (long long p = p0 + tid; p < p1; p += 256) {
+        const int e = ids[p];
+        const int t = (int)(p / k), s = (int)(p % k);
+        if (e >= 0 && e < E) {
+            order[atomicAdd(&cur[e], 1)] = t * S + s;
+        } else {
+            float* yr = y + ((size_t)t * S + s) * H;
+            for (int n = 0; n < H; ++n) yr[n] = 0.f;
+        }
+    }
+}
+
 // ---------------------------------------------------------------- row sums in three bf16 parts
 // v = hi + mid + lo: hi and mid are v and the remainder truncated to bf16 (both
 // remainders exact in fp32), lo the last remainder rounded to bf16.
@@ -219,15 +337,15 @@ static unsigned xcd_grid(int max_tiles, int nb) {
 //   A: the tile's rows x 64 bf16 (128 B per row),
 //   B: the 256 int4 weight rows x 32 B,
 //   sb: the 256 rows' (scale, bias) words of the group,
-// into a ring of NSTAGE stages that runs NSTAGE - 1 chunks ahead of the one being
-// multiplied. Two workgroups share a CU, so one's prologue and epilogue overlap
-// the other's main loop.
+// into a ring of LDS stages that runs one chunk fewer than it has stages ahead of
+// the one being multiplied. A stage holds only the A rows the tile loads, so
+// tiles of up to 32 rows get five stages, 64 rows four, 128 rows three. Two
+// workgroups share a CU, so one's prologue and epilogue overlap the other's main
+// loop.
 constexpr int KC = 64;
 constexpr int NBR = 256;
-constexpr int NSTAGE = 3;
-constexpr int A_BYTES = BM * KC * 2, B_BYTES = NBR * KC / 2, SB_BYTES = NBR * 4;
-constexpr int STAGE = A_BYTES + B_BYTES + SB_BYTES;  // 25 KiB
-constexpr int RING = NSTAGE * STAGE;
+constexpr int B_BYTES = NBR * KC / 2, SB_BYTES = NBR * 4;
+constexpr int RING = 3 * (BM * KC * 2 + B_BYTES + SB_BYTES);  // 75 KiB: three stages of a full tile
 
 struct GemmArgs {
     const uint8_t* packed;
@@ -282,6 +400,17 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Wait until at most min(later, L) chunks of LPC loads each are outstanding.
+template <int LPC, int L>
+__device__ __forceinline__ void wait_chunks(int later) {
+    if constexpr (L == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (later >= L) wait_vmcnt<L * LPC>();
+        else wait_chunks<LPC, L - 1>(later);
+    }
+}
+
 __device__ __forceinline__ f32x4_t mfma16x16x16(uint2 a, uint2 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, a), __builtin_bit_cast(short4_t, b),
                                                      c, 0, 0, 0);
@@ -295,7 +424,7 @@ template <bool GATEUP>
 __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
     constexpr int NCS = NBR / 64;  // 16-column sets per wavefront
     constexpr int HALF = NBR / 2;  // gate/up: gate rows 0 .. HALF-1, up rows HALF .. NBR-1
-    extern __shared__ __attribute__((aligned(16))) uint8_t ring[];  // NSTAGE stages of (A | B | sb)
+    extern __shared__ __attribute__((aligned(16))) uint8_t ring[];  // ring of stages, each (A | B | sb)
     __shared__ uint32_t arow_lds[BM];  // byte offset of each tile row in its source, ~0 beyond the tile
     const int H = a.H, I = a.I, S = a.S;
     const int K = GATEUP ? H : I;
@@ -333,7 +462,7 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
     };
 
     // ---- ring layout within a stage:
-    //   A: 128 rows x 128 B, the 16-byte piece p of row r at position p ^ (r & 7);
+    //   A: the loaded rows x 128 B, the 16-byte piece p of row r at position p ^ (r & 7);
     //   B: 256 rows x 32 B, piece p of row r at position p ^ ((r >> 2) & 1);
     //   sb: 256 words.
     // The XOR positions spread the fragment reads of neighbouring lanes over the
@@ -363,6 +492,10 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
         constexpr int NM = decltype(nm_tag)::value;
         constexpr int NA = NM >= 2 ? NM / 2 : 1;  // A instructions (8 rows each) per wavefront
         constexpr int LPC = NA + 3;               // loads per wavefront and chunk
+        constexpr int SA = 4 * NA * 1024;         // A bytes per stage (32 NA rows)
+        constexpr int STAGE = SA + B_BYTES + SB_BYTES;
+        constexpr int NS = RING / STAGE;          // stages: 5, 4 or 3
+        static_assert(NS >= 3 && NS * STAGE <= RING && LPC * (NS - 2) < 64, "ring");
         const uint32_t arow0 = arow_lds[0];       // row 0 is always inside the tile
         uint32_t a_off[NA];
 #pragma unroll
@@ -372,25 +505,25 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
             a_off[i] = (off == 0xFFFFFFFFu ? arow0 : off) + 16 * ((lane & 7) ^ (row & 7));
         }
         auto issue = [&](int c) {
-            const uint32_t st = ring_lds + (uint32_t)((c % NSTAGE) * STAGE);
+            const uint32_t st = ring_lds + (uint32_t)((c % NS) * STAGE);
             const uint8_t* ab = asrc + (size_t)c * (KC * 2);
 #pragma unroll
             for (int i = 0; i < NA; ++i) lds_dma16(ab, a_off[i], st + (NA * wave + i) * 1024);
             const uint8_t* bb = ebase + (size_t)c * (KC / 2);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) lds_dma16(bb, b_off[i], st + A_BYTES + (2 * wave + i) * 1024);
-            lds_dma4(ebase + (size_t)c * 4, sb_off, st + A_BYTES + B_BYTES + wave * 256);
+            for (int i = 0; i < 2; ++i) lds_dma16(bb, b_off[i], st + SA + (2 * wave + i) * 1024);
+            lds_dma4(ebase + (size_t)c * 4, sb_off, st + SA + B_BYTES + wave * 256);
         };
         auto compute = [&](int c) {
-            const uint8_t* st = ring + (size_t)(c % NSTAGE) * STAGE;
-            const uint32_t* sb_st = reinterpret_cast<const uint32_t*>(st + A_BYTES + B_BYTES);
+            const uint8_t* st = ring + (size_t)(c % NS) * STAGE;
+            const uint32_t* sb_st = reinterpret_cast<const uint32_t*>(st + SA + B_BYTES);
             uint4 b0[NCS], b1[NCS];
             float s16[NCS];
 #pragma unroll
             for (int cs = 0; cs < NCS; ++cs) {
                 const int br = cs * 64 + 16 * wave + lc;
                 const int sw = (lc >> 2) & 1;
-                const uint8_t* bp = st + A_BYTES + br * 32 + 4 * lg;
+                const uint8_t* bp = st + SA + br * 32 + 4 * lg;
                 b0[cs] = bfrag(*reinterpret_cast<const uint32_t*>(bp + 16 * sw));
                 b1[cs] = bfrag(*reinterpret_cast<const uint32_t*>(bp + 16 * (1 ^ sw)));
                 s16[cs] = 16.f * bf16_to_f32(sb_st[br] & 0xFFFFu);
@@ -410,17 +543,15 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
             }
         };
         const int NC = K / KC;
-        static_assert(NSTAGE == 3, "the wait below assumes one later chunk in flight");
-        issue(0);
-        if (NC > 1) issue(1);
+        for (int c = 0; c < NS - 1 && c < NC; ++c) issue(c);
         for (int c = 0; c < NC; ++c) {
-            // this wavefront's loads of chunk c are done once only chunk c+1's are left
-            if (c + 1 < NC) wait_vmcnt<LPC>();
-            else wait_vmcnt<0>();
+            // this wavefront's loads of chunk c are done once only the later chunks'
+            // (at most NS - 2 of them) are left
+            wait_chunks<LPC, NS - 2>(NC - 1 - c);
             // every wavefront's loads of chunk c are in LDS, and every wavefront has
             // finished chunk c-1, whose stage the next loads refill
             lds_barrier();
-            if (c + 2 < NC) issue(c + 2);
+            if (c + NS - 1 < NC) issue(c + NS - 1);
             compute(c);
         }
     };
@@ -479,63 +610,95 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
         }
     }
 
-    // ---- epilogue
+    // ---- epilogue: the ring's memory is free once every wavefront is past its last chunk
+    __syncthreads();
     if constexpr (GATEUP) {
-        // h[row][i] = bf16(silu(gate) * up), i = col0 + 64 hs + 16 wave + lc (gate set
-        // hs, up set NCS/2 + hs); row sums of each 64-column part hs of this block of
-        // h (fp32, fixed order: 16 lanes by DPP, then the four wavefronts in order)
-        // into the down GEMM's X planes, group col0/64 + hs. The partial sums reuse
-        // the ring's memory, free once every wavefront is past its last chunk.
-        float(*xpart)[4][BM] = reinterpret_cast<float(*)[4][BM]>(ring);
-        __syncthreads();
+        // h = bf16(silu(gate) * up) for this block's 128 intermediate columns i =
+        // col0 + c, c = 64 hs + 16 wave + lc (gate set hs, up set 2 + hs), staged as a
+        // bf16 tile in LDS (rows beyond the tile hold zeros), then stored with 16-byte
+        // row pieces; each (row, 64-column group) sum of the stored bf16 values, in
+        // column order in fp32, goes to the down GEMM's X planes.
+        constexpr int HS = 128 + 8;  // tile row stride (bf16)
+        uint16_t* hl = reinterpret_cast<uint16_t*>(ring);
 #pragma unroll
-        for (int hs = 0; hs < NCS / 2; ++hs) {
-            const int i_col = col0 + 64 * hs + 16 * wave + lc;
+        for (int hs = 0; hs < 2; ++hs) {
+            const int c = 64 * hs + 16 * wave + lc;
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = 16 * m + 4 * lg + r;
-                    const float gv = acc[m][hs][r], uv = acc[m][NCS / 2 + hs][r];
-                    const uint32_t hb = f32_to_bf16(gv / (1.f + expf(-gv)) * uv);
-                    if (row < tl.nrows && i_col < I) a.hbuf[(size_t)(tl.row0 + row) * I + i_col] = (uint16_t)hb;
-                    const float part = group_sum(row < tl.nrows ? bf16_to_f32(hb) : 0.f, 16);
-                    if (lc == 0) xpart[hs][wave][row] = part;
+                    const float gv = acc[m][hs][r], uv = acc[m][2 + hs][r];
+                    // silu(g) = g / (1 + e^-g), e^-g = 2^(-g log2 e)
+                    const float sg = gv * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-gv * 1.44269504088896341f));
+                    const __bf16 hb = (__bf16)(sg * uv);
+                    hl[row * HS + c] = row < tl.nrows ? __builtin_bit_cast(uint16_t, hb) : (uint16_t)0;
                 }
             }
         }
         __syncthreads();
-        if (tid < (NCS / 2) * BM && (tid & (BM - 1)) < tl.nrows && col0 + 64 * (tid / BM) < I) {
-            const int row = tid & (BM - 1), hs = tid / BM, g = col0 / 64 + hs;
-            const float xs = ((xpart[hs][0][row] + xpart[hs][1][row]) + xpart[hs][2][row]) + xpart[hs][3][row];
-            uint32_t hi, mid, lo;
-            split3_bf16(xs, hi, mid, lo);
-            const size_t plane = (size_t)a.T * S * a.gs_h;
-            uint16_t* xp = a.xs_h + (size_t)(tl.row0 + row) * a.gs_h;
-            xp[g] = (uint16_t)hi;
-            xp[plane + g] = (uint16_t)mid;
-            xp[2 * plane + g] = (uint16_t)lo;
-            if (col0 == 0 && hs == 0) {  // padding groups of the planes
-                for (int gp = I / 64; gp < a.gs_h; ++gp) {
-                    xp[gp] = 0;
-                    xp[plane + gp] = 0;
-                    xp[2 * plane + gp] = 0;
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int row = 16 * it + (tid >> 4), pc = tid & 15;
+            if (row < tl.nrows && col0 + 8 * pc < I)
+                *reinterpret_cast<uint4*>(a.hbuf + (size_t)(tl.row0 + row) * I + col0 + 8 * pc) =
+                    *reinterpret_cast<const uint4*>(hl + row * HS + 8 * pc);
+        }
+        {
+            const int row = tid >> 1, hs = tid & 1, g = col0 / 64 + hs;
+            if (row < tl.nrows && col0 + 64 * hs < I) {
+                float xs = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(hl + row * HS + 64 * hs + 8 * j);
+                    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        xs += __uint_as_float(w4[q] << 16);
+                        xs += __uint_as_float(w4[q] & 0xFFFF0000u);
+                    }
+                }
+                uint32_t hi, mid, lo;
+                split3_bf16(xs, hi, mid, lo);
+                const size_t plane = (size_t)a.T * S * a.gs_h;
+                uint16_t* xp = a.xs_h + (size_t)(tl.row0 + row) * a.gs_h;
+                xp[g] = (uint16_t)hi;
+                xp[plane + g] = (uint16_t)mid;
+                xp[2 * plane + g] = (uint16_t)lo;
+                if (col0 == 0 && hs == 0) {  // padding groups of the planes
+                    for (int gp = I / 64; gp < a.gs_h; ++gp) {
+                        xp[gp] = 0;
+                        xp[plane + gp] = 0;
+                        xp[2 * plane + gp] = 0;
+                    }
                 }
             }
         }
     } else {
+        // y[order[row]][col0 + n], n < 256, staged 64 rows at a time as an fp32 tile in
+        // LDS and stored with 16-byte row pieces
+        constexpr int YS = NBR + 4;  // tile row stride (floats)
+        float* yl = reinterpret_cast<float*>(ring);
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
+        for (int half = 0; half < 2; ++half) {
+            if (64 * half < tl.nrows) {
+                if (half) __syncthreads();
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * m + 4 * lg + r;
-                if (row < tl.nrows) {
-                    float* yr = a.y + (size_t)a.order[tl.row0 + row] * H;
+                for (int mm = 0; mm < 4; ++mm) {
 #pragma unroll
-                    for (int cs = 0; cs < NCS; ++cs) {
-                        const int n = col0 + cs * 64 + 16 * wave + lc;
-                        if (n < H) yr[n] = acc[m][cs][r];
+                    for (int r = 0; r < 4; ++r) {
+                        const int rl = 16 * mm + 4 * lg + r;
+#pragma unroll
+                        for (int cs = 0; cs < NCS; ++cs) yl[rl * YS + cs * 64 + 16 * wave + lc] = acc[4 * half + mm][cs][r];
                     }
+                }
+                __syncthreads();
+#pragma unroll 4
+                for (int it = 0; it < 16; ++it) {
+                    const int rl = 4 * it + (tid >> 6), row = 64 * half + rl, pc = tid & 63;
+                    if (row < tl.nrows && col0 + 4 * pc < H)
+                        *reinterpret_cast<float4*>(a.y + (size_t)a.order[tl.row0 + row] * H + col0 + 4 * pc) =
+                            *reinterpret_cast<const float4*>(yl + rl * YS + 4 * pc);
                 }
             }
         }
@@ -598,9 +761,16 @@ extern "C" moe_status moe_experts_prefill(const moe_shape* shape, const void* ex
     Tile* tiles = (Tile*)(w + W.tiles);
     int32_t* order = (int32_t*)(w + W.order);
     uint16_t* hbuf = (uint16_t*)(w + W.h);
-    hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(1024), 0, hs, ids, T, sh.top_k, sh.n_experts, sh.has_shared, H,
-                       counts, offsets, ntiles, tiles, order, y);
-    if ((st = check_launch("dispatch_kernel")) != MOE_OK) return st;
+    int32_t* slices = (int32_t*)(w + W.slices);
+    const long long P = (long long)T * sh.top_k;
+    hipLaunchKernelGGL(dispatch_count_kernel, dim3(W.n_slices), dim3(256), 0, hs, ids, P, sh.n_experts, slices);
+    if ((st = check_launch("dispatch_count_kernel")) != MOE_OK) return st;
+    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, hs, T, sh.top_k, sh.n_experts, sh.has_shared,
+                       W.n_slices, slices, counts, offsets, ntiles, tiles, order);
+    if ((st = check_launch("dispatch_scan_kernel")) != MOE_OK) return st;
+    hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(W.n_slices), dim3(256), 0, hs, ids, P, sh.top_k, sh.n_experts, S,
+                       H, slices, order, y);
+    if ((st = check_launch("dispatch_scatter_kernel")) != MOE_OK) return st;
     GemmArgs ga;
     ga.packed = (const uint8_t*)experts_packed;
     ga.L = L;
