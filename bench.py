@@ -59,23 +59,34 @@ def parse():
 # counter reads for a plain copy of known size. The record is stored with a hash
 # of the library sources; a bench run reports it only while the hash matches.
 # kernels of the measured stage (per-launch traffic is the sum of their per-dispatch medians)
+PREFILL_KERNELS = ["dispatch_count_kernel", "dispatch_scan_kernel", "dispatch_scatter_kernel", "xsum_kernel",
+                   "expert_gemm_kernel<true>", "expert_gemm_kernel<false>"]
 TRAFFIC_KERNELS = {"decode": ["decode_layer_kernel"], "stack16": ["decode_layer_kernel"],
                    "stack1": ["decode_layer_kernel"],
-                   "prefill512": ["dispatch_kernel", "gateup_gemm_kernel", "down_gemm_kernel"],
-                   "prefill4096": ["dispatch_kernel", "gateup_gemm_kernel", "down_gemm_kernel"]}
+                   "prefill512": PREFILL_KERNELS, "prefill4096": PREFILL_KERNELS}
+# sources the measured kernels are built from: a stored traffic record holds for
+# the sources it was taken on
+DECODE_SOURCES = ["decode.hip", "route_device.h", "moe_internal.h", "abi.hip"]
+PREFILL_SOURCES = ["prefill.hip", "mfma_common.h", "moe_internal.h", "abi.hip"]
+TRAFFIC_SOURCES = {"decode": DECODE_SOURCES, "stack16": DECODE_SOURCES, "stack1": DECODE_SOURCES,
+                   "prefill512": PREFILL_SOURCES, "prefill4096": PREFILL_SOURCES}
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
-def source_hash():
+def source_hash(wl):
+    """Hash of the sources the workload's measured kernels are built from (and the headers)."""
     import hashlib
 
     h = hashlib.sha256()
-    for sub in ("quantized_moe_expert_fp32_amd/csrc", "include"):
-        d = os.path.join(ROOT, sub)
-        for n in sorted(os.listdir(d)):
-            if n.endswith((".hip", ".h")):
-                h.update(n.encode())
-                h.update(open(os.path.join(d, n), "rb").read())
+    csrc = os.path.join(ROOT, "quantized_moe_expert_fp32_amd", "csrc")
+    for n in sorted(TRAFFIC_SOURCES[wl]):
+        h.update(n.encode())
+        h.update(open(os.path.join(csrc, n), "rb").read())
+    inc = os.path.join(ROOT, "include")
+    for n in sorted(os.listdir(inc)):
+        if n.endswith(".h"):
+            h.update(n.encode())
+            h.update(open(os.path.join(inc, n), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -118,7 +129,7 @@ def write_traffic(wl, spec):
            "fetch_kib_per_launch": fk, "write_kib_per_launch": wk,
            "calibration_bytes": cal["bytes"], "fetch_scale": k_fetch, "write_scale": k_write,
            "traffic_bytes_per_launch": (fk * k_fetch + wk * k_write) * 1024.0,
-           "source_hash": source_hash()}
+           "source_hash": source_hash(wl)}
     os.makedirs(os.path.dirname(traffic_path(wl)), exist_ok=True)
     json.dump(rec, open(traffic_path(wl), "w"), indent=1)
     print(json.dumps(rec))
@@ -129,7 +140,7 @@ def stored_traffic(wl):
         rec = json.load(open(traffic_path(wl)))
     except (OSError, ValueError):
         return None
-    if rec.get("source_hash") != source_hash():
+    if rec.get("source_hash") != source_hash(wl):
         log("stored traffic for %s predates the current sources: reported as null" % wl)
         return None
     return rec["traffic_bytes_per_launch"]
@@ -338,7 +349,7 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = stored_traffic(wl)
     roof["kernel"] = ("decode_layer_kernel (router, selection, experts, combine in one launch)" if path == "fused"
-                      else "experts stage: dispatch_kernel + gateup_gemm_kernel + down_gemm_kernel")
+                      else "experts stage (moe_experts_prefill): " + " + ".join(PREFILL_KERNELS))
     roof["avg_us"] = expert_us
     roof["alg_bytes_per_launch"] = int(alg_bytes)
 
