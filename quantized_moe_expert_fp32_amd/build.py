@@ -26,7 +26,8 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-I", INCLUDE, "-I", CSRC]
 # Per-source extras. The grouped GEMM applies a per-group scale to each MFMA
 # product on the VALU; MFMA results in VGPRs save a copy out of AGPRs per element.
-SOURCE_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+SOURCE_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+                "route.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
 
 
 def _run(cmd, verbose):

@@ -54,104 +54,130 @@ __global__ __launch_bounds__(256) void router_kernel(const uint8_t* __restrict__
 
 // ---------------------------------------------------------------- logits, GEMM form (8-bit router, T > 16)
 // logits[t][r] = sum_g ( s[r][g] * sum_{k in g} x[t][k] q[r][k] + b[r][g] * sum_{k in g} x[t][k] ) (+ bias[r])
-// on the matrix cores: the int8 codes are exact bf16 operands, each 64-wide
-// group's partial comes from two v_mfma_f32_16x16x32_bf16, and scale and bias are
-// applied in fp32 per group. Grid (ceil(T / 64), ceil(R / 64)); wavefront w owns
-// router rows nb*64 + 16w .. +16 for the block's 64 tokens. Activation groups are
-// loaded two groups ahead and staged in LDS (double-buffered); weights are
-// loaded four groups ahead into a register ring.
+// on the matrix cores. A workgroup takes 32 tokens x 16 NB router rows; wavefront w
+// takes the groups [w G/4, (w+1) G/4) of K and its partial sums are added in
+// wavefront order at the end, so the result does not depend on timing. NB = 1
+// gives enough workgroups for a few hundred tokens; NB = 4 reads the activations
+// a quarter as often for thousands. Per group, 16-token block and 16 rows:
+//   * the int8 codes are exact bf16 B operands; lane (row lc, quarter lg) holds
+//     codes 16 lg .. 16 lg + 15 of its row, the first 8 for one
+//     v_mfma_f32_16x16x32_bf16 and the last 8 for the next, and the A operand
+//     carries the matching activations (any assignment of k to MFMA slots gives
+//     the same sum), so both operands are single contiguous loads;
+//   * the scale multiplies the group's partial in fp32 (one FMA per output);
+//   * the bias term b * sum x comes from two more MFMAs whose B operand is b in
+//     every slot (exact products, fp32 sums), accumulated in place.
+// Operands come straight from global memory into a ring of PD groups per
+// wavefront: no LDS and no barrier in the loop.
+constexpr int RG_TOK = 32;
+
+template <int NB>
 __global__ __launch_bounds__(256) void router_gemm_kernel(const uint8_t* __restrict__ router,
                                                           const float* __restrict__ logit_bias,
                                                           const uint16_t* __restrict__ x, int T, int H, int R, int E,
                                                           float* __restrict__ logits) {
-    __shared__ __attribute__((aligned(16))) uint16_t a_lds[2][64 * A_STRIDE];
-    __shared__ __attribute__((aligned(16))) float x_lds[2][64];
+    __shared__ float part[4][2][NB][4][64];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lg = lane >> 4, lc = lane & 15;
-    const int m0 = blockIdx.x * 64;
-    const int nrows = min(64, T - m0);
-    const int n_ms = (nrows + 15) >> 4;
-    const int r = blockIdx.y * 64 + wave * 16 + lc;
-    const bool r_ok = r < R;
-    const uint8_t* qrow = router + (size_t)(r_ok ? r : 0) * H + 8 * lg;
-    const uint32_t* sbrow = reinterpret_cast<const uint32_t*>(router + (size_t)R * H) + (size_t)(r_ok ? r : 0) * (H / 64);
-    const int srow = tid >> 2, sq = tid & 3;
-    const bool srow_ok = srow < nrows;
-    const uint16_t* xsrc = x + (size_t)(m0 + (srow_ok ? srow : 0)) * H + 16 * sq;
-
-    f32x4_t acc[4];
+    const int t0 = blockIdx.x * RG_TOK, rb = blockIdx.y * 16 * NB + lc;
+    const int G = H / 64, ga = wave * G / 4, gb = (wave + 1) * G / 4;
+    const uint8_t* qrow[NB];
+    const uint32_t* sbrow[NB];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int G = H / 64;
-    constexpr int PDR = 4;  // weight groups in flight
-    uint2 wq[PDR][2];
-    uint32_t ws[PDR];
-#pragma unroll
-    for (int u = 0; u < PDR; ++u) {
-        if (u < G) {
-            wq[u][0] = *reinterpret_cast<const uint2*>(qrow + 64 * u);
-            wq[u][1] = *reinterpret_cast<const uint2*>(qrow + 64 * u + 32);
-            ws[u] = sbrow[u];
-        }
+    for (int n = 0; n < NB; ++n) {
+        const int r = rb + 16 * n, rr = r < R ? r : 0;
+        qrow[n] = router + (size_t)rr * H + 16 * lg;
+        sbrow[n] = reinterpret_cast<const uint32_t*>(router + (size_t)R * H) + (size_t)rr * G;
     }
-    uint4 xr[2][2];
+    const uint16_t* xrow[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) xr[i][0] = xr[i][1] = make_uint4(0, 0, 0, 0);
-    if (srow_ok) {
-        xr[0][0] = *reinterpret_cast<const uint4*>(xsrc);
-        xr[0][1] = *reinterpret_cast<const uint4*>(xsrc + 8);
-        if (G > 1) {
-            xr[1][0] = *reinterpret_cast<const uint4*>(xsrc + 64);
-            xr[1][1] = *reinterpret_cast<const uint4*>(xsrc + 72);
-        }
+    for (int m = 0; m < 2; ++m) {
+        const int t = t0 + 16 * m + lc;
+        xrow[m] = x + (size_t)(t < T ? t : 0) * H + 16 * lg;
     }
-    stage_store(a_lds[0], x_lds[0], tid, xr[0][0], xr[0][1]);
-    __syncthreads();
-    for (int g0 = 0; g0 < G; g0 += PDR) {
+    f32x4_t acc[2][NB];
 #pragma unroll
-        for (int u = 0; u < PDR; ++u) {
-            const int g = g0 + u;
-            if (g >= G) break;  // uniform
-            if (g + 2 < G && srow_ok) {
-                xr[u & 1][0] = *reinterpret_cast<const uint4*>(xsrc + 64 * (g + 2));
-                xr[u & 1][1] = *reinterpret_cast<const uint4*>(xsrc + 64 * (g + 2) + 8);
-            }
-            const uint4 b0 = int8x8_to_bf16_pairs(wq[u][0].x, wq[u][0].y);
-            const uint4 b1 = int8x8_to_bf16_pairs(wq[u][1].x, wq[u][1].y);
-            const float sc = bf16_to_f32(ws[u] & 0xFFFFu), bi = bf16_to_f32(ws[u] >> 16);
-            if (g + PDR < G) {
-                wq[u][0] = *reinterpret_cast<const uint2*>(qrow + 64 * (g + PDR));
-                wq[u][1] = *reinterpret_cast<const uint2*>(qrow + 64 * (g + PDR) + 32);
-                ws[u] = sbrow[g + PDR];
-            }
-            const uint16_t* al = a_lds[u & 1];
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                if (m < n_ms) {
-                    const uint4 a0 = *reinterpret_cast<const uint4*>(al + (16 * m + lc) * A_STRIDE + 8 * lg);
-                    const uint4 a1 = *reinterpret_cast<const uint4*>(al + (16 * m + lc) * A_STRIDE + 32 + 8 * lg);
-                    const float4 xs = *reinterpret_cast<const float4*>(&x_lds[u & 1][16 * m + 4 * lg]);
-                    f32x4_t p = mfma16x16x32(a0, b0, f32x4_t{0.f, 0.f, 0.f, 0.f});
-                    p = mfma16x16x32(a1, b1, p);
-                    acc[m][0] = fmaf(bi, xs.x, fmaf(sc, p[0], acc[m][0]));
-                    acc[m][1] = fmaf(bi, xs.y, fmaf(sc, p[1], acc[m][1]));
-                    acc[m][2] = fmaf(bi, xs.z, fmaf(sc, p[2], acc[m][2]));
-                    acc[m][3] = fmaf(bi, xs.w, fmaf(sc, p[3], acc[m][3]));
+        for (int n = 0; n < NB; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    constexpr int PD = NB == 1 ? 4 : 3;  // groups in flight per wavefront
+    uint4 wq[PD][NB], xa[PD][2][2];
+    uint32_t ws[PD][NB];
+    auto load = [&](int u, int g) {
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+            wq[u][n] = *reinterpret_cast<const uint4*>(qrow[n] + 64 * g);
+            ws[u][n] = sbrow[n][g];
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            xa[u][m][0] = *reinterpret_cast<const uint4*>(xrow[m] + 64 * g);
+            xa[u][m][1] = *reinterpret_cast<const uint4*>(xrow[m] + 64 * g + 8);
+        }
+    };
+#pragma unroll
+    for (int u = 0; u < PD; ++u)
+        if (ga + u < gb) load(u, ga + u);
+    for (int g = ga; g < gb; g += PD) {
+#pragma unroll
+        for (int u = 0; u < PD; ++u) {
+            const int gg = g + u;
+            if (gg >= gb) break;  // uniform
+            uint4 b0[NB], b1[NB], bb[NB];
+            float sc[NB];
+#pragma unroll
+            for (int n = 0; n < NB; ++n) {
+                b0[n] = int8x8_to_bf16_pairs(wq[u][n].x, wq[u][n].y);
+                b1[n] = int8x8_to_bf16_pairs(wq[u][n].z, wq[u][n].w);
+                sc[n] = bf16_to_f32(ws[u][n] & 0xFFFFu);
+                const uint32_t bp = (ws[u][n] >> 16) | (ws[u][n] & 0xFFFF0000u);
+                bb[n] = make_uint4(bp, bp, bp, bp);
+            }
+            uint4 a[2][2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                a[m][0] = xa[u][m][0];
+                a[m][1] = xa[u][m][1];
+            }
+            if (gg + PD < gb) load(u, gg + PD);
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+#pragma unroll
+                for (int n = 0; n < NB; ++n) {
+                    f32x4_t p = mfma16x16x32(a[m][0], b0[n], f32x4_t{0.f, 0.f, 0.f, 0.f});
+                    p = mfma16x16x32(a[m][1], b1[n], p);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[m][n][i] = fmaf(sc[n], p[i], acc[m][n][i]);
+                    acc[m][n] = mfma16x16x32(a[m][0], bb[n], acc[m][n]);
+                    acc[m][n] = mfma16x16x32(a[m][1], bb[n], acc[m][n]);
                 }
             }
-            if (g + 1 < G) stage_store(a_lds[(u + 1) & 1], x_lds[(u + 1) & 1], tid, xr[(u + 1) & 1][0],
-                                       xr[(u + 1) & 1][1]);
-            __syncthreads();
         }
     }
-    if (!r_ok) return;
-    const float bias = (r < E && logit_bias) ? logit_bias[r] : 0.f;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 16 * m + 4 * lg + i;
-            if (row < nrows) logits[(size_t)(m0 + row) * R + r] = acc[m][i] + bias;
+        for (int n = 0; n < NB; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) part[wave][m][n][i][lane] = acc[m][n][i];
+    __syncthreads();
+    // the reduction and stores are spread over the four wavefronts (one n-block
+    // each for NB = 4, wavefront 0 for NB = 1)
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+        if (NB == 1 ? wave != 0 : wave != n) continue;
+        const int r = rb + 16 * n;
+        if (r >= R) continue;
+        const float bias = (r < E && logit_bias) ? logit_bias[r] : 0.f;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = t0 + 16 * m + 4 * lg + i;
+                const float v = ((part[0][m][n][i][lane] + part[1][m][n][i][lane]) + part[2][m][n][i][lane]) +
+                                part[3][m][n][i][lane];
+                if (t < T) logits[(size_t)t * R + r] = v + bias;
+            }
         }
     }
 }
@@ -229,8 +255,14 @@ extern "C" moe_status moe_route(const moe_shape* shape, const void* router_packe
     hipStream_t hs = (hipStream_t)stream;
     if (T > 16 && shape->router_fmt == MOE_ROUTER_AFFINE8) {
         const int R = router_rows(*shape);
-        hipLaunchKernelGGL(router_gemm_kernel, dim3((T + 63) / 64, (R + 63) / 64), dim3(256), 0, hs,
-                           (const uint8_t*)router_packed, logit_bias, x, T, shape->hidden, R, shape->n_experts, logits);
+        if (T <= 1024)
+            hipLaunchKernelGGL(router_gemm_kernel<1>, dim3((T + RG_TOK - 1) / RG_TOK, (R + 15) / 16), dim3(256), 0, hs,
+                               (const uint8_t*)router_packed, logit_bias, x, T, shape->hidden, R, shape->n_experts,
+                               logits);
+        else
+            hipLaunchKernelGGL(router_gemm_kernel<4>, dim3((T + RG_TOK - 1) / RG_TOK, (R + 63) / 64), dim3(256), 0, hs,
+                               (const uint8_t*)router_packed, logit_bias, x, T, shape->hidden, R, shape->n_experts,
+                               logits);
         if ((st = check_launch("router_gemm_kernel")) != MOE_OK) return st;
     } else {
         launch_router<false>(*shape, (const uint8_t*)router_packed, logit_bias, x, T, logits, nullptr, ids, w,

@@ -368,7 +368,7 @@ def test_prefill_full_size(gpu, name):
     print(name, stats)
 
 
-@pytest.mark.parametrize("T", [1, 2, 17, 63, 64, 65, 130, 1000])
+@pytest.mark.parametrize("T", [1, 2, 17, 63, 64, 65, 130, 1000, 1100])
 def test_prefill_ragged_T(gpu, T):
     c = case("decode")
     dl = dev_layer(gpu, c)
