@@ -179,9 +179,11 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int T, int k, int E
                                                              int32_t* __restrict__ order) {
     __shared__ int cnt[1025];
     __shared__ int off[1026];
-    __shared__ int toff[1026];
+    __shared__ int foff[1026];  // full-tile offsets
+    __shared__ int bucket[9];   // partial tiles by row-block count (8 - n blocks)
     const int M = E + has_shared, S = k + has_shared;
     const int tid = threadIdx.x;
+    if (tid < 9) bucket[tid] = 0;
     // per expert: exclusive scan over the slices (relative bases, in place)
     for (int e = tid; e < E; e += blockDim.x) {
         int run = 0;
@@ -194,13 +196,17 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int T, int k, int E
     }
     if (has_shared && tid == 0) cnt[E] = T;
     __syncthreads();
+    for (int e = tid; e < M; e += blockDim.x) {
+        const int rem = cnt[e] % BM;
+        if (rem) atomicAdd(&bucket[8 - (rem + 15) / 16], 1);
+    }
     if (tid < 64) {
         const int per = (M + 63) / 64;
         const int beg = tid * per, end = min(M, beg + per);
         int lc = 0, lt = 0;
         for (int i = beg; i < end; ++i) {
             lc += cnt[i];
-            lt += (cnt[i] + BM - 1) / BM;
+            lt += cnt[i] / BM;
         }
         int ic = lc, it = lt;
         for (int d = 1; d < 64; d <<= 1) {
@@ -213,28 +219,48 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int T, int k, int E
         int rc = ic - lc, rt = it - lt;
         for (int i = beg; i < end; ++i) {
             off[i] = rc;
-            toff[i] = rt;
+            foff[i] = rt;
             rc += cnt[i];
-            rt += (cnt[i] + BM - 1) / BM;
+            rt += cnt[i] / BM;
         }
         if (tid == 63) {
             off[M] = ic;
-            toff[M] = it;
-            *ntiles = it;
+            foff[M] = it;
         }
+    }
+    __syncthreads();
+    // Tile list: every full tile first (expert order), then the partial tiles with
+    // the most row blocks first, so the items that start last are the cheapest.
+    // Order within a bucket is arbitrary.
+    if (tid == 0) {
+        int run = foff[M];
+        for (int b = 0; b < 9; ++b) {
+            const int c = bucket[b];
+            bucket[b] = run;
+            run += c;
+        }
+        *ntiles = run;
     }
     __syncthreads();
     for (int e = tid; e < M; e += blockDim.x) {
         counts[e] = cnt[e];
         offsets[e] = off[e];
-        const int nt = (cnt[e] + BM - 1) / BM;
-        for (int j = 0; j < nt; ++j) {
+        const int nfull = cnt[e] / BM, rem = cnt[e] % BM;
+        for (int j = 0; j < nfull; ++j) {
             Tile tl;
             tl.expert = e;
             tl.row0 = off[e] + j * BM;
-            tl.nrows = min(BM, cnt[e] - j * BM);
+            tl.nrows = BM;
             tl.pad = 0;
-            tiles[toff[e] + j] = tl;
+            tiles[foff[e] + j] = tl;
+        }
+        if (rem) {
+            Tile tl;
+            tl.expert = e;
+            tl.row0 = off[e] + nfull * BM;
+            tl.nrows = rem;
+            tl.pad = 0;
+            tiles[atomicAdd(&bucket[8 - (rem + 15) / 16], 1)] = tl;
         }
     }
     if (tid == 0) offsets[M] = off[M];
@@ -306,25 +332,29 @@ __global__ __launch_bounds__(256) void xsum_kernel(const uint16_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------- XCD-aware item mapping
-// The GEMM grids are one-dimensional over (tile, column block) items, numbered
-// tile-major so that neighbouring items share an activation tile or an expert's
-// weights. Workgroups are handed to the 8 XCDs round-robin by linear id, and each
-// XCD has its own L2, so block b takes item (b % 8) * per + b / 8: each XCD walks
-// one contiguous range of items and the sharing stays inside one L2. The grid is
-// 8 * ceil(max_tiles * nb / 8) blocks; blocks beyond the live items return.
-constexpr int N_XCD = 8;
+// The GEMM grids are one-dimensional over (tile, column block) items. Workgroups
+// are handed to the 8 XCDs round-robin by linear id, and each XCD has its own L2.
+// Block b runs on XCD x = b % 8 as that XCD's j-th block, j = b / 8. Tiles are
+// dealt to the XCDs in runs of XCD_RUN consecutive tiles, and an XCD takes its
+// tiles in order, all column blocks of a tile in a row: the workgroups that share
+// a tile's activations share one L2, and a tile list sorted by cost stays balanced
+// across the XCDs. Runs of one tile measured best on the 512-token and skewed
+// 4096-token workloads: longer runs keep an expert's consecutive tiles in one L2
+// but put the few heavy tiles at the head of the list on one XCD. Blocks beyond
+// the live tiles return.
+constexpr int N_XCD = 8, XCD_RUN = 1;
 
 __device__ __forceinline__ bool xcd_item(int ntiles, int nb, int& tile, int& cb) {
-    const int n = ntiles * nb, per = (n + N_XCD - 1) / N_XCD;
-    const int j = (int)blockIdx.x / N_XCD, item = ((int)blockIdx.x % N_XCD) * per + j;
-    if (j >= per || item >= n) return false;
-    tile = item / nb;
-    cb = item - tile * nb;
-    return true;
+    const int x = (int)blockIdx.x % N_XCD, j = (int)blockIdx.x / N_XCD;
+    const int lt = j / nb;  // this XCD's lt-th tile
+    tile = (lt / XCD_RUN) * (N_XCD * XCD_RUN) + x * XCD_RUN + lt % XCD_RUN;
+    cb = j % nb;
+    return tile < ntiles;
 }
 
 static unsigned xcd_grid(int max_tiles, int nb) {
-    return (unsigned)((((long long)max_tiles * nb + N_XCD - 1) / N_XCD) * N_XCD);
+    const int runs = (max_tiles + N_XCD * XCD_RUN - 1) / (N_XCD * XCD_RUN);
+    return (unsigned)(runs * XCD_RUN * N_XCD * nb);
 }
 
 // ---------------------------------------------------------------- grouped GEMM
