@@ -108,14 +108,19 @@ moe_status moe_shape_check(const moe_shape* shape);
 /* ---------------------------------------------------------------- weight packing
  * The kernels read one packed buffer per layer. Per expert m (stride
  * moe_experts_packed_bytes / M), in this order:
- *   gate q [I][H/2] | up q [I][H/2] | down q [H][I/2] |
- *   gate sb [I][H/64] | up sb [I][H/64] | down sb [H][I/64]
- * where every sb entry is a uint32 holding the group's bf16 scale in the low and
- * bf16 bias in the high half. q keeps the canonical byte order of each row, but
- * the eight nibbles of every little-endian dword (weights k0..k7 of a row) are
- * reordered: nibble j (bits 4j..4j+3) holds k_{2j} and nibble 4+j holds
- * k_{2j+1}, j < 4. A shift by 4j then puts the pair (k_{2j}, k_{2j+1}) in bits 0..3
- * and 16..19, i.e. next to each other as they sit in a bf16 activation row. */
+ *   gate/up q [I/2][H/64][4][32 B] | down q [H/4][I/64][4][32 B] |
+ *   gate/up sb [I/2][H/64][4] | down sb [H/4][I/64][4]
+ * Rows come in blocks of four: gate/up block b holds gate rows 2b, 2b+1 and up
+ * rows 2b, 2b+1 (in that slot order), down block b holds down rows 4b .. 4b+3.
+ * For each block and 64-wide group g, the four rows' 32 bytes of that group
+ * (their weights 64g .. 64g+63, canonical byte order) follow one another, so one
+ * 128-byte line holds one group of a whole block. Every sb entry is a uint32
+ * holding the group's bf16 scale in the low and bf16 bias in the high half, in
+ * the same block, group, slot order. Within every little-endian dword (weights
+ * k0..k7 of a row) the eight nibbles are reordered: nibble j (bits 4j..4j+3)
+ * holds k_{2j} and nibble 4+j holds k_{2j+1}, j < 4. A shift by 4j then puts the
+ * pair (k_{2j}, k_{2j+1}) in bits 0..3 and 16..19, i.e. next to each other as
+ * they sit in a bf16 activation row. */
 size_t moe_experts_packed_bytes(const moe_shape* shape);
 
 /* Packs canonical expert weights (device) into `packed` (device, packed_bytes >=

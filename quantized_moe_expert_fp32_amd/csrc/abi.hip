@@ -95,12 +95,20 @@ __device__ __forceinline__ uint32_t pack_q_dword(uint32_t c) {
     return gather_nibbles(c) | (gather_nibbles(c >> 4) << 16);
 }
 
-__global__ void pack_q_kernel(const uint4* __restrict__ src, size_t src_stride16, uint4* __restrict__ dst,
-                              size_t dst_stride16, size_t n16) {
+// One canonical int4 matrix [N][K/2] per expert into the blocked layout (see
+// ExpertLayout): row r goes to block r / spb, slot slot0 + r % spb, and its 16-byte
+// piece c (weights 32c .. 32c+31) to ((block * K/64 + c/2) * 4 + slot) * 2 + c % 2
+// in 16-byte units; nibbles reordered within each dword.
+__global__ void pack_q_kernel(const uint4* __restrict__ src, size_t n16, int K, int spb, int slot0,
+                              uint4* __restrict__ dst, size_t dst_stride16) {
     const size_t m = blockIdx.y;
+    const size_t cpr = (size_t)K / 32, gpr = (size_t)K / 64;  // pieces and groups per row
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x) {
-        const uint4 v = src[m * src_stride16 + i];
-        dst[m * dst_stride16 + i] = make_uint4(pack_q_dword(v.x), pack_q_dword(v.y), pack_q_dword(v.z),
+        const uint4 v = src[m * n16 + i];
+        const size_t r = i / cpr, c = i % cpr;
+        const size_t blk = r / spb, slot = slot0 + r % spb;
+        const size_t o = ((blk * gpr + c / 2) * 4 + slot) * 2 + c % 2;
+        dst[m * dst_stride16 + o] = make_uint4(pack_q_dword(v.x), pack_q_dword(v.y), pack_q_dword(v.z),
                                                pack_q_dword(v.w));
     }
 }
@@ -113,43 +121,52 @@ __global__ void pack_copy_kernel(const uint4* __restrict__ src, size_t src_strid
         dst[m * dst_stride16 + i] = src[m * src_stride16 + i];
 }
 
-// sb[m][i] = scale | bias << 16 for n entries per expert.
-__global__ void pack_sb_kernel(const uint16_t* __restrict__ s, const uint16_t* __restrict__ b, size_t n,
-                               uint32_t* __restrict__ dst, size_t dst_stride4) {
+// sb = scale | bias << 16 for n entries per expert. gpr > 0: the entries are
+// [N][gpr] (row, group) of an expert matrix, placed like the q rows of
+// pack_q_kernel at (block * gpr + g) * 4 + slot; gpr == 0: copied in order.
+__global__ void pack_sb_kernel(const uint16_t* __restrict__ s, const uint16_t* __restrict__ b, size_t n, int gpr,
+                               int spb, int slot0, uint32_t* __restrict__ dst, size_t dst_stride4) {
     const size_t m = blockIdx.y;
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-        dst[m * dst_stride4 + i] = (uint32_t)s[m * n + i] | ((uint32_t)b[m * n + i] << 16);
-}
-
-static moe_status launch_q(const void* src, size_t bytes, char* dst, size_t stride, int M, hipStream_t st,
-                           bool shuffle) {
-    if (!src || !aligned16(src)) return fail(MOE_ERR_INVALID_ARG, "q source NULL or not 16-byte aligned");
-    size_t n16 = bytes / 16;
-    dim3 grid((unsigned)((n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024), (unsigned)M);
-    if (shuffle) {
-        hipLaunchKernelGGL(pack_q_kernel, grid, dim3(256), 0, st, (const uint4*)src, n16, (uint4*)dst, stride / 16,
-                           n16);
-        return check_launch("pack_q_kernel");
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+        size_t o = i;
+        if (gpr > 0) {
+            const size_t r = i / gpr, g = i % gpr;
+            o = ((r / spb) * gpr + g) * 4 + slot0 + r % spb;
+        }
+        dst[m * dst_stride4 + o] = (uint32_t)s[m * n + i] | ((uint32_t)b[m * n + i] << 16);
     }
-    hipLaunchKernelGGL(pack_copy_kernel, grid, dim3(256), 0, st, (const uint4*)src, n16, (uint4*)dst, stride / 16, n16);
-    return check_launch("pack_copy_kernel");
 }
 
-// int4 expert rows, nibbles reordered as described for moe_pack_experts.
-static moe_status copy_q(const void* src, size_t bytes, char* dst, size_t stride, int M, hipStream_t st) {
-    return launch_q(src, bytes, dst, stride, M, st, true);
+static dim3 pack_grid(size_t n, int M) {
+    return dim3((unsigned)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024), (unsigned)M);
+}
+
+// int4 expert matrix [N][K/2] per expert (canonical), into the blocked layout with
+// spb rows per block from slot slot0 (gate 2, 0; up 2, 2; down 4, 0).
+static moe_status copy_q(const void* src, size_t N, int K, int spb, int slot0, char* dst, size_t stride, int M,
+                         hipStream_t st) {
+    if (!src || !aligned16(src)) return fail(MOE_ERR_INVALID_ARG, "q source NULL or not 16-byte aligned");
+    const size_t n16 = N * (size_t)K / 32;
+    hipLaunchKernelGGL(pack_q_kernel, pack_grid(n16, M), dim3(256), 0, st, (const uint4*)src, n16, K, spb, slot0,
+                       (uint4*)dst, stride / 16);
+    return check_launch("pack_q_kernel");
 }
 
 // Router codes or fp32 router rows, unchanged.
 static moe_status copy_raw(const void* src, size_t bytes, char* dst, hipStream_t st) {
-    return launch_q(src, bytes, dst, 0, 1, st, false);
+    if (!src || !aligned16(src)) return fail(MOE_ERR_INVALID_ARG, "source NULL or not 16-byte aligned");
+    const size_t n16 = bytes / 16;
+    hipLaunchKernelGGL(pack_copy_kernel, pack_grid(n16, 1), dim3(256), 0, st, (const uint4*)src, n16, (uint4*)dst,
+                       (size_t)0, n16);
+    return check_launch("pack_copy_kernel");
 }
 
-static moe_status copy_sb(const uint16_t* s, const uint16_t* b, size_t n, char* dst, size_t stride, int M,
-                          hipStream_t st) {
+// (scale, bias) words: n entries per expert, blocked like copy_q when gpr > 0.
+static moe_status copy_sb(const uint16_t* s, const uint16_t* b, size_t n, int gpr, int spb, int slot0, char* dst,
+                          size_t stride, int M, hipStream_t st) {
     if (!s || !b) return fail(MOE_ERR_INVALID_ARG, "scale/bias source NULL");
-    dim3 grid((unsigned)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024), (unsigned)M);
-    hipLaunchKernelGGL(pack_sb_kernel, grid, dim3(256), 0, st, s, b, n, (uint32_t*)dst, stride / 4);
+    hipLaunchKernelGGL(pack_sb_kernel, pack_grid(n, M), dim3(256), 0, st, s, b, n, gpr, spb, slot0, (uint32_t*)dst,
+                       stride / 4);
     return check_launch("pack_sb_kernel");
 }
 
@@ -165,12 +182,17 @@ extern "C" moe_status moe_pack_experts(const moe_shape* sh, const moe_expert_can
     const size_t H = sh->hidden, I = sh->inter;
     hipStream_t s = (hipStream_t)stream;
     char* d = (char*)packed;
-    if ((st = copy_q(src->q_gate, I * H / 2, d + L.gate_q, L.stride, M, s)) != MOE_OK) return st;
-    if ((st = copy_q(src->q_up, I * H / 2, d + L.up_q, L.stride, M, s)) != MOE_OK) return st;
-    if ((st = copy_q(src->q_down, H * I / 2, d + L.down_q, L.stride, M, s)) != MOE_OK) return st;
-    if ((st = copy_sb(src->s_gate, src->b_gate, I * (H / 64), d + L.gate_sb, L.stride, M, s)) != MOE_OK) return st;
-    if ((st = copy_sb(src->s_up, src->b_up, I * (H / 64), d + L.up_sb, L.stride, M, s)) != MOE_OK) return st;
-    if ((st = copy_sb(src->s_down, src->b_down, H * (I / 64), d + L.down_sb, L.stride, M, s)) != MOE_OK) return st;
+    const int Hi = (int)H, Ii = (int)I;
+    if ((st = copy_q(src->q_gate, I, Hi, 2, 0, d + L.gu_q, L.stride, M, s)) != MOE_OK) return st;
+    if ((st = copy_q(src->q_up, I, Hi, 2, 2, d + L.gu_q, L.stride, M, s)) != MOE_OK) return st;
+    if ((st = copy_q(src->q_down, H, Ii, 4, 0, d + L.down_q, L.stride, M, s)) != MOE_OK) return st;
+    if ((st = copy_sb(src->s_gate, src->b_gate, I * (H / 64), Hi / 64, 2, 0, d + L.gu_sb, L.stride, M, s)) != MOE_OK)
+        return st;
+    if ((st = copy_sb(src->s_up, src->b_up, I * (H / 64), Hi / 64, 2, 2, d + L.gu_sb, L.stride, M, s)) != MOE_OK)
+        return st;
+    if ((st = copy_sb(src->s_down, src->b_down, H * (I / 64), Ii / 64, 4, 0, d + L.down_sb, L.stride, M, s)) !=
+        MOE_OK)
+        return st;
     return MOE_OK;
 }
 
@@ -190,5 +212,5 @@ extern "C" moe_status moe_pack_router(const moe_shape* sh, const void* w, const 
         return copy_raw(w, R * H * 4, (char*)packed, hs);
     }
     if ((st = copy_raw(w, R * H, (char*)packed, hs)) != MOE_OK) return st;
-    return copy_sb(s, b, R * (H / 64), (char*)packed + R * H, 0, 1, hs);
+    return copy_sb(s, b, R * (H / 64), 0, 1, 0, (char*)packed + R * H, 0, 1, hs);
 }

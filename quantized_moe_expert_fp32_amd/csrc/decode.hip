@@ -56,11 +56,13 @@ struct ChunkLoad {
     uint32_t sb;
 };
 
+// qrow, sbrow: a row's bases in the blocked packed layout (gu_row_q / gu_row_sb,
+// dn_row_q / dn_row_sb); chunk = 16-byte piece of 32 weights.
 __device__ __forceinline__ ChunkLoad load_chunk(const uint8_t* __restrict__ qrow, const uint32_t* __restrict__ sbrow,
                                                 int chunk) {
     ChunkLoad c;
-    c.q = *reinterpret_cast<const uint4*>(qrow + 16 * chunk);
-    c.sb = sbrow[chunk >> 1];
+    c.q = *reinterpret_cast<const uint4*>(qrow + piece_off(chunk));
+    c.sb = sbrow[4 * (chunk >> 1)];
     return c;
 }
 
@@ -106,11 +108,6 @@ __device__ __forceinline__ void gu_load(const uint8_t* __restrict__ packed, cons
     constexpr int per_wave = GU_ROWS / 4;
     const int r0 = rb * GU_ROWS + wave * per_wave;
     const uint8_t* base = packed + (size_t)e * L.stride;
-    const uint8_t* gq = base + L.gate_q;
-    const uint8_t* uq = base + L.up_q;
-    const uint32_t* gsb = reinterpret_cast<const uint32_t*>(base + L.gate_sb);
-    const uint32_t* usb = reinterpret_cast<const uint32_t*>(base + L.up_sb);
-    const size_t qstride = H / 2, sbstride = H / 64;
 #pragma unroll
     for (int it = 0; it < GU_IT; ++it) {
         const int rr = it * rpw + rsub;
@@ -118,8 +115,10 @@ __device__ __forceinline__ void gu_load(const uint8_t* __restrict__ packed, cons
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             if (rr < per_wave) {
-                ld.g[it][c] = load_chunk(gq + r * qstride, gsb + r * sbstride, lr + lpr * c);
-                ld.u[it][c] = load_chunk(uq + r * qstride, usb + r * sbstride, lr + lpr * c);
+                ld.g[it][c] = load_chunk(base + gu_row_q(L, H, 0, r),
+                                         reinterpret_cast<const uint32_t*>(base + gu_row_sb(L, H, 0, r)), lr + lpr * c);
+                ld.u[it][c] = load_chunk(base + gu_row_q(L, H, 1, r),
+                                         reinterpret_cast<const uint32_t*>(base + gu_row_sb(L, H, 1, r)), lr + lpr * c);
             }
         }
     }
@@ -224,7 +223,6 @@ __device__ __forceinline__ void dn_load(const uint8_t* __restrict__ packed, cons
     const int lr = lane % lpr, rsub = lane / lpr;
     const int n_dots = S * DN_ROWS;
     const int n_it = (n_dots + rpw - 1) / rpw;
-    const size_t qstride = I / 2, sbstride = I / 64;
 #pragma unroll
     for (int j = 0; j < DN_BATCH; ++j) {
         const int it = wave + 4 * (j0 + j);
@@ -239,8 +237,8 @@ __device__ __forceinline__ void dn_load(const uint8_t* __restrict__ packed, cons
             } else {
                 const int n = n0 + q % DN_ROWS;
                 const uint8_t* base = packed + (size_t)e * L.stride;
-                d.ld[j] = load_chunk(base + L.down_q + n * qstride,
-                                     reinterpret_cast<const uint32_t*>(base + L.down_sb) + n * sbstride, lr);
+                d.ld[j] = load_chunk(base + dn_row_q(L, I, n),
+                                     reinterpret_cast<const uint32_t*>(base + dn_row_sb(L, I, n)), lr);
             }
         }
     }
@@ -400,16 +398,14 @@ __device__ __forceinline__ void pair_load(const uint8_t* __restrict__ packed, co
     const int C = H / 32, lpr = C < 64 ? C : 64, rpw = 64 / lpr;
     const int lr = lane % lpr, rsub = lane / lpr;
     const uint8_t* base = packed + (size_t)e * L.stride;
-    const size_t qstride = H / 2, sbstride = H / 64;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         if (it * rpw >= 4) break;  // wave-uniform
         const int rs = it * rpw + rsub;
         if (rs < 4) {
-            const size_t r = 2 * ip + (rs & 1);
-            const uint8_t* q = base + (rs < 2 ? L.gate_q : L.up_q) + r * qstride;
-            const uint32_t* sb =
-                reinterpret_cast<const uint32_t*>(base + (rs < 2 ? L.gate_sb : L.up_sb)) + r * sbstride;
+            const int r = 2 * ip + (rs & 1);
+            const uint8_t* q = base + gu_row_q(L, H, rs >= 2, r);
+            const uint32_t* sb = reinterpret_cast<const uint32_t*>(base + gu_row_sb(L, H, rs >= 2, r));
 #pragma unroll
             for (int c = 0; c < CPL; ++c) ld.c[it][c] = load_chunk(q, sb, lr + lpr * c);
         }
@@ -514,7 +510,6 @@ __device__ __forceinline__ void dnl_load(const uint8_t* __restrict__ packed, con
     const int lr = lane % lpr, rsub = lane / lpr;
     const int n_dots = S * DN_ROWS;
     const int n_it = (n_dots + rpw - 1) / rpw;
-    const size_t qstride = I / 2, sbstride = I / 64;
 #pragma unroll
     for (int j = 0; j < DNB; ++j) {
         const int it = wave + LW * (b0 + j);
@@ -526,8 +521,8 @@ __device__ __forceinline__ void dnl_load(const uint8_t* __restrict__ packed, con
             const int e = s < k ? ids_t[s] : E;
             const int n = n0 + q % DN_ROWS;
             const uint8_t* base = packed + (size_t)e * L.stride;
-            d.ld[j] = load_chunk(base + L.down_q + n * qstride,
-                                 reinterpret_cast<const uint32_t*>(base + L.down_sb) + n * sbstride, lr);
+            d.ld[j] = load_chunk(base + dn_row_q(L, I, n), reinterpret_cast<const uint32_t*>(base + dn_row_sb(L, I, n)),
+                                 lr);
         }
     }
 }

@@ -22,23 +22,46 @@ inline int32_t n_mats(const moe_shape& s) { return s.n_experts + (s.has_shared ?
 inline int32_t n_slots(const moe_shape& s) { return s.top_k + (s.has_shared ? 1 : 0); }
 inline int32_t router_rows(const moe_shape& s) { return s.n_experts + (s.has_shared ? 1 : 0); }
 
-// Byte offsets of one expert's segments inside the packed buffer.
+// Byte offsets of one expert's segments inside the packed buffer. Weight rows are
+// stored in blocks of four rows per quantisation group: each 128-byte line holds
+// the 32 bytes (64 int4 weights) of one group for four rows, so a grouped GEMM
+// that walks K one group at a time reads whole lines, and a wavefront that
+// streams the four rows of a block back to back reads the same lines.
+//   gu_q    [I/2][H/64][4][32 B]: block b holds gate rows 2b, 2b+1 and up rows 2b, 2b+1
+//   down_q  [H/4][I/64][4][32 B]: block b holds down rows 4b .. 4b+3
+//   gu_sb   [I/2][H/64][4] and down_sb [H/4][I/64][4]: the (scale | bias << 16) words
+//           of the same rows and groups, in the same order
 struct ExpertLayout {
-    size_t gate_q, up_q, down_q, gate_sb, up_sb, down_sb, stride;
+    size_t gu_q, down_q, gu_sb, down_sb, stride;
 };
 
 inline ExpertLayout expert_layout(const moe_shape& s) {
     const size_t H = (size_t)s.hidden, I = (size_t)s.inter, G = 64;
     ExpertLayout L;
-    L.gate_q = 0;
-    L.up_q = L.gate_q + I * H / 2;
-    L.down_q = L.up_q + I * H / 2;
-    L.gate_sb = L.down_q + H * I / 2;
-    L.up_sb = L.gate_sb + I * (H / G) * 4;
-    L.down_sb = L.up_sb + I * (H / G) * 4;
+    L.gu_q = 0;
+    L.down_q = L.gu_q + I * H;
+    L.gu_sb = L.down_q + H * I / 2;
+    L.down_sb = L.gu_sb + 2 * I * (H / G) * 4;
     L.stride = L.down_sb + H * (I / G) * 4;
     return L;
 }
+
+// Row bases inside one expert (byte offsets). The 16-byte piece ch (weights
+// 32 ch .. 32 ch + 31) of a row is at base + (ch / 2) * 128 + (ch % 2) * 16; the
+// word of group g of a row's sb is at sb base + 16 g.
+__host__ __device__ inline size_t gu_row_q(const ExpertLayout& L, int H, int up, int i) {
+    return L.gu_q + (size_t)(i >> 1) * (size_t)(H / 64) * 128 + (size_t)((up ? 2 : 0) + (i & 1)) * 32;
+}
+__host__ __device__ inline size_t gu_row_sb(const ExpertLayout& L, int H, int up, int i) {
+    return L.gu_sb + (size_t)(i >> 1) * (size_t)(H / 64) * 16 + (size_t)((up ? 2 : 0) + (i & 1)) * 4;
+}
+__host__ __device__ inline size_t dn_row_q(const ExpertLayout& L, int I, int n) {
+    return L.down_q + (size_t)(n >> 2) * (size_t)(I / 64) * 128 + (size_t)(n & 3) * 32;
+}
+__host__ __device__ inline size_t dn_row_sb(const ExpertLayout& L, int I, int n) {
+    return L.down_sb + (size_t)(n >> 2) * (size_t)(I / 64) * 16 + (size_t)(n & 3) * 4;
+}
+__host__ __device__ inline size_t piece_off(int ch) { return (size_t)(ch >> 1) * 128 + (size_t)(ch & 1) * 16; }
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 

@@ -480,36 +480,55 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
     const uint8_t* asrc = reinterpret_cast<const uint8_t*>(GATEUP ? a.x : a.hbuf);
     const uint8_t* ebase = a.packed + (size_t)tl.expert * a.L.stride;
     auto brow_ok = [&](int r) -> bool { return GATEUP ? col0 + r % HALF < I : col0 + r < H; };
-    // byte offsets from ebase of weight row r's q row and sb row
-    auto brow_q_off = [&](int r) -> uint32_t {
-        if constexpr (GATEUP) return (uint32_t)((r < HALF ? a.L.gate_q : a.L.up_q) + (size_t)(col0 + r % HALF) * (K / 2));
-        else return (uint32_t)(a.L.down_q + (size_t)(col0 + r) * (K / 2));
+    // The workgroup's 256 weight rows are 64 four-row blocks of the packed layout
+    // (gate/up: block col0/2 + jb holds gate and up rows col0 + 2jb, col0 + 2jb + 1;
+    // down: block col0/4 + jb holds rows col0 + 4jb .. +3). Weight row br (gate
+    // column br, up column br - 128, or down row br) sits in block jb at slot:
+    auto brow_block = [&](int br, int& jb, int& slot) {
+        if constexpr (GATEUP) {
+            const int i = br % HALF;
+            jb = i >> 1;
+            slot = (br >= HALF ? 2 : 0) + (i & 1);
+        } else {
+            jb = br >> 2;
+            slot = br & 3;
+        }
     };
-    auto brow_sb_off = [&](int r) -> uint32_t {
-        if constexpr (GATEUP)
-            return (uint32_t)((r < HALF ? a.L.gate_sb : a.L.up_sb) + (size_t)(col0 + r % HALF) * (K / 64) * 4);
-        else return (uint32_t)(a.L.down_sb + (size_t)(col0 + r) * (K / 64) * 4);
+    // global block of the workgroup's block jb; blocks beyond the matrix read block 0
+    const int nblk_mat = GATEUP ? I / 2 : H / 4;
+    const int blk0 = GATEUP ? col0 / 2 : col0 / 4;
+    auto gblock = [&](int jb) -> int { return blk0 + jb < nblk_mat ? blk0 + jb : blk0; };
+    const size_t q_region = GATEUP ? a.L.gu_q : a.L.down_q, sb_region = GATEUP ? a.L.gu_sb : a.L.down_sb;
+    const int G = K / 64;
+    // byte offset from ebase of the (scale, bias) word of weight row br, group g
+    auto brow_sb_word = [&](int br, int g) -> size_t {
+        int jb, slot;
+        brow_block(br, jb, slot);
+        return sb_region + ((size_t)gblock(jb) * G + g) * 16 + 4 * slot;
     };
 
     // ---- ring layout within a stage:
     //   A: the loaded rows x 128 B, the 16-byte piece p of row r at position p ^ (r & 7);
-    //   B: 256 rows x 32 B, piece p of row r at position p ^ ((r >> 2) & 1);
-    //   sb: 256 words.
+    //   B: 64 blocks x 128 B (the group's line of each block: slot s, 16-byte half h
+    //      is piece 2s + h), piece p of block jb at position p ^ bsw(jb);
+    //   sb: 64 blocks x 4 words.
     // The XOR positions spread the fragment reads of neighbouring lanes over the
-    // banks. Rows beyond the tile or the matrix load a valid row instead (row 0),
-    // so every lane issues every load, each wavefront has exactly LPC loads per
-    // chunk in flight, and the wait for a chunk is an exact vector-memory count.
-    // Per-lane offsets are fixed for the tile; the chunk advances the uniform base.
+    // banks. Rows beyond the tile or the matrix load a valid row instead, so every
+    // lane issues every load, each wavefront has exactly LPC loads per chunk in
+    // flight, and the wait for a chunk is an exact vector-memory count. Per-lane
+    // offsets are fixed for the tile; the chunk advances the uniform base by one
+    // line (q) or 16 bytes (sb).
+    auto bsw = [](int jb) -> int { return ((jb >> 1) & 3) << 1; };  // even: keeps a slot's two halves adjacent
     const uint32_t ring_lds = lds_addr(ring);
-    uint32_t b_off[2];  // B: instruction j = 2 wave + i covers rows 32j .. 32j+31
+    uint32_t b_off[2];  // B: instruction j = 2 wave + i covers blocks 8j .. 8j+7
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const int row = 32 * (2 * wave + i) + (lane >> 1);
-        const int piece = (lane & 1) ^ ((row >> 2) & 1);
-        b_off[i] = brow_q_off(brow_ok(row) ? row : 0) + 16 * piece;
+        const int jb = 8 * (2 * wave + i) + (lane >> 3);
+        const int piece = (lane & 7) ^ bsw(jb);
+        b_off[i] = (uint32_t)(q_region + (size_t)gblock(jb) * G * 128 + 16 * piece);
     }
-    const int sb_row = 64 * wave + lane;  // sb: one instruction per wavefront, 64 rows
-    const uint32_t sb_off = brow_sb_off(brow_ok(sb_row) ? sb_row : 0);
+    // sb: one instruction per wavefront, blocks 16 wave .. +16, four words each
+    const uint32_t sb_off = (uint32_t)(sb_region + (size_t)gblock(16 * wave + (lane >> 2)) * G * 16 + 4 * (lane & 3));
 
     f32x4_t acc[8][NCS];
 #pragma unroll
@@ -539,10 +558,10 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
             const uint8_t* ab = asrc + (size_t)c * (KC * 2);
 #pragma unroll
             for (int i = 0; i < NA; ++i) lds_dma16(ab, a_off[i], st + (NA * wave + i) * 1024);
-            const uint8_t* bb = ebase + (size_t)c * (KC / 2);
+            const uint8_t* bb = ebase + (size_t)c * 128;
 #pragma unroll
             for (int i = 0; i < 2; ++i) lds_dma16(bb, b_off[i], st + SA + (2 * wave + i) * 1024);
-            lds_dma4(ebase + (size_t)c * 4, sb_off, st + SA + B_BYTES + wave * 256);
+            lds_dma4(ebase + (size_t)c * 16, sb_off, st + SA + B_BYTES + wave * 256);
         };
         auto compute = [&](int c) {
             const uint8_t* st = ring + (size_t)(c % NS) * STAGE;
@@ -551,12 +570,12 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
             float s16[NCS];
 #pragma unroll
             for (int cs = 0; cs < NCS; ++cs) {
-                const int br = cs * 64 + 16 * wave + lc;
-                const int sw = (lc >> 2) & 1;
-                const uint8_t* bp = st + SA + br * 32 + 4 * lg;
-                b0[cs] = bfrag(*reinterpret_cast<const uint32_t*>(bp + 16 * sw));
-                b1[cs] = bfrag(*reinterpret_cast<const uint32_t*>(bp + 16 * (1 ^ sw)));
-                s16[cs] = 16.f * bf16_to_f32(sb_st[br] & 0xFFFFu);
+                int jb, slot;
+                brow_block(cs * 64 + 16 * wave + lc, jb, slot);
+                const uint8_t* bp = st + SA + jb * 128 + 16 * ((2 * slot) ^ bsw(jb)) + 4 * lg;
+                b0[cs] = bfrag(*reinterpret_cast<const uint32_t*>(bp));
+                b1[cs] = bfrag(*reinterpret_cast<const uint32_t*>(bp + 16));
+                s16[cs] = 16.f * bf16_to_f32(sb_st[4 * jb + slot] & 0xFFFFu);
             }
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
@@ -591,7 +610,6 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
     else kloop(std::integral_constant<int, 8>{});
 
     // ---- bias term: sum over groups of X[row][g] * (bias - 16 scale)[col][g], 16 groups per MFMA
-    const int G = K / 64;
     for (int kb = 0; kb < (G + 15) / 16; ++kb) {
         uint2 ch[NCS], cm[NCS], cl[NCS];
 #pragma unroll
@@ -603,7 +621,7 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
                 const int g = 16 * kb + 4 * lg + i;
                 float cc = 0.f;
                 if (g < G && brow_ok(br)) {
-                    const uint32_t w = *reinterpret_cast<const uint32_t*>(ebase + brow_sb_off(br) + 4 * g);
+                    const uint32_t w = *reinterpret_cast<const uint32_t*>(ebase + brow_sb_word(br, g));
                     cc = bf16_to_f32(w >> 16) - 16.f * bf16_to_f32(w & 0xFFFFu);
                 }
                 split3_bf16(cc, h4[i], m4[i], l4[i]);

@@ -143,22 +143,42 @@ def test_packed_nibble_order_pairs():
 
 
 def test_pack_layout_matches_header(gpu):
+    """Packed experts follow the blocked layout documented in include/moe.h."""
     c = case("tiny")
     dl = dev_layer(gpu, c)
     L0 = c.layers[0]
     p = dl.experts.cpu().numpy()
     H, I, M = 256, 64, 17
+    G, Gd = H // 64, I // 64
     stride = p.size // M
+
+    def words(sv, bv):
+        return sv.reshape(-1).astype(np.uint32) | (bv.reshape(-1).astype(np.uint32) << 16)
+
     for m in (0, 5, 16):
         b = p[m * stride:(m + 1) * stride]
-        o = 0
-        for q in (L0.q_gate[m], L0.q_up[m], L0.q_down[m]):
-            assert np.array_equal(b[o:o + q.size], packed_nibble_order(q.reshape(-1)))
-            o += q.size
-        for s, bb in ((L0.s_gate[m], L0.b_gate[m]), (L0.s_up[m], L0.b_up[m]), (L0.s_down[m], L0.b_down[m])):
-            sb = b[o:o + 4 * s.size].view(np.uint32)
-            assert np.array_equal(sb, s.reshape(-1).astype(np.uint32) | (bb.reshape(-1).astype(np.uint32) << 16))
-            o += 4 * s.size
+        gu = b[:I * H].reshape(I // 2, G, 4, 32)
+        for q, slot0 in ((L0.q_gate[m], 0), (L0.q_up[m], 2)):
+            rows = packed_nibble_order(q.reshape(-1)).reshape(I, G, 32)
+            for s in (0, 1):
+                assert np.array_equal(gu[:, :, slot0 + s, :], rows[s::2])
+        o = I * H
+        dn = b[o:o + H * I // 2].reshape(H // 4, Gd, 4, 32)
+        rows = packed_nibble_order(L0.q_down[m].reshape(-1)).reshape(H, Gd, 32)
+        for s in range(4):
+            assert np.array_equal(dn[:, :, s, :], rows[s::4])
+        o += H * I // 2
+        gsb = b[o:o + 2 * I * G * 4].view(np.uint32).reshape(I // 2, G, 4)
+        for sv, bv, slot0 in ((L0.s_gate[m], L0.b_gate[m], 0), (L0.s_up[m], L0.b_up[m], 2)):
+            w = words(sv, bv).reshape(I, G)
+            for s in (0, 1):
+                assert np.array_equal(gsb[:, :, slot0 + s], w[s::2])
+        o += 2 * I * G * 4
+        dsb = b[o:o + H * Gd * 4].view(np.uint32).reshape(H // 4, Gd, 4)
+        w = words(L0.s_down[m], L0.b_down[m]).reshape(H, Gd)
+        for s in range(4):
+            assert np.array_equal(dsb[:, :, s], w[s::4])
+        o += H * Gd * 4
         assert o == stride
     r = dl.router.cpu().numpy().view(np.float32).reshape(17, H)
     assert np.array_equal(r, L0.router_f32)
