@@ -34,7 +34,7 @@ struct Tile {
 // Workspace layout for moe_experts_prefill.
 struct PrefillWs {
     size_t counts, offsets, cursor, ntiles, tiles, order, h, xs_x, xs_h, slices, total;
-    int max_tiles, gs_x, gs_h;  // group strides of the row-sum planes (multiples of 16)
+    int max_tiles, gs_x, gs_h;  // group strides of the row-sum planes (x: multiple of 32, h: of 16)
     int n_slices;               // pick slices of the parallel dispatch
 };
 
@@ -55,7 +55,7 @@ static PrefillWs prefill_ws_layout(const moe_shape& s, int T) {
     w.tiles = o;   o = align_up(o + sizeof(Tile) * (size_t)w.max_tiles, 256);
     w.order = o;   o = align_up(o + 4 * (size_t)T * S, 256);
     w.h = o;       o = align_up(o + 2 * (size_t)T * S * s.inter, 256);
-    w.gs_x = ((s.hidden / 64 + 15) / 16) * 16;
+    w.gs_x = ((s.hidden / 64 + 31) / 32) * 32;
     w.gs_h = ((s.inter / 64 + 15) / 16) * 16;
     w.xs_x = o;    o = align_up(o + 3 * 2 * (size_t)T * w.gs_x, 256);      // [3][T][gs_x] bf16
     w.xs_h = o;    o = align_up(o + 3 * 2 * (size_t)T * S * w.gs_h, 256);  // [3][T*S][gs_h] bf16
@@ -456,6 +456,7 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
     constexpr int HALF = NBR / 2;  // gate/up: gate rows 0 .. HALF-1, up rows HALF .. NBR-1
     extern __shared__ __attribute__((aligned(16))) uint8_t ring[];  // ring of stages, each (A | B | sb)
     __shared__ uint32_t arow_lds[BM];  // byte offset of each tile row in its source, ~0 beyond the tile
+    __shared__ int32_t asrc_lds[BM];   // row of each tile row in its row-sum planes
     const int H = a.H, I = a.I, S = a.S;
     const int K = GATEUP ? H : I;
     const int nblk = GATEUP ? (I + HALF - 1) / HALF : (H + NBR - 1) / NBR;
@@ -470,11 +471,14 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
 
     if (tid < BM) {
         uint32_t off = 0xFFFFFFFFu;
+        int src = 0;
         if (tid < tl.nrows) {
-            if constexpr (GATEUP) off = (uint32_t)(a.order[tl.row0 + tid] / S) * (uint32_t)(2 * H);
-            else off = (uint32_t)(tl.row0 + tid) * (uint32_t)(2 * I);
+            if constexpr (GATEUP) src = a.order[tl.row0 + tid] / S;
+            else src = tl.row0 + tid;
+            off = (uint32_t)src * (uint32_t)(2 * K);
         }
         arow_lds[tid] = off;
+        asrc_lds[tid] = src;
     }
     __syncthreads();
     const uint8_t* asrc = reinterpret_cast<const uint8_t*>(GATEUP ? a.x : a.hbuf);
@@ -535,9 +539,104 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
     for (int m = 0; m < 8; ++m)
 #pragma unroll
         for (int cs = 0; cs < NCS; ++cs) acc[m][cs] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // ---- bias term: sum over groups of X[row][g] * (bias - 16 scale)[col][g] on the
+    // matrix cores, KG groups per MFMA (gate/up: 32 with v_mfma_f32_16x16x32_bf16; down,
+    // whose K has few groups: 16 with v_mfma_f32_16x16x16_bf16), computed first: its
+    // loads go out while the ring fills, and the accumulators start from it. When one
+    // step covers every group, the tile rows' X planes arrive by direct loads in the
+    // ring's last stage (free until the loop's first refill) at xs_st, plane stride
+    // xs_ps bytes, row stride 2 KG bytes; else (and for later steps) from memory.
+    constexpr int KG = GATEUP ? 32 : 16;
+    constexpr int GPL = KG / 4;  // groups per lane and MFMA
+    using frag_t = typename std::conditional<GATEUP, uint4, uint2>::type;
+    auto bmfma = [](const frag_t& x, const frag_t& c, f32x4_t v) -> f32x4_t {
+        if constexpr (GATEUP) return mfma16x16x32(x, c, v);
+        else return mfma16x16x16(x, c, v);
+    };
+    auto pack_frag = [](const uint32_t* v) -> frag_t {  // GPL bf16 values -> fragment
+        if constexpr (GATEUP)
+            return make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
+        else return make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
+    };
+    auto bias_term = [&](auto nm_tag, const uint8_t* xs_st, int xs_ps) __attribute__((always_inline)) {
+        constexpr int NM = decltype(nm_tag)::value;
+        const size_t plane = (size_t)(GATEUP ? a.T : a.T * S) * a.gs_a;
+        for (int kb = 0; kb < (G + KG - 1) / KG; ++kb) {
+            uint32_t w[NCS][GPL];
+#pragma unroll
+            for (int cs = 0; cs < NCS; ++cs) {
+                const int br = cs * 64 + 16 * wave + lc;
+#pragma unroll
+                for (int i = 0; i < GPL; ++i) {
+                    const int g = KG * kb + GPL * lg + i;
+                    w[cs][i] = (g < G && brow_ok(br)) ? *reinterpret_cast<const uint32_t*>(ebase + brow_sb_word(br, g))
+                                                      : 0u;  // scale 0, bias 0: c = 0
+                }
+            }
+            frag_t ch[NCS], cm[NCS], cl[NCS];
+#pragma unroll
+            for (int cs = 0; cs < NCS; ++cs) {
+                uint32_t h[GPL], md[GPL], l[GPL];
+#pragma unroll
+                for (int i = 0; i < GPL; ++i) {
+                    const float cc = bf16_to_f32(w[cs][i] >> 16) - 16.f * bf16_to_f32(w[cs][i] & 0xFFFFu);
+                    split3_bf16(cc, h[i], md[i], l[i]);
+                }
+                ch[cs] = pack_frag(h);
+                cm[cs] = pack_frag(md);
+                cl[cs] = pack_frag(l);
+            }
+            const bool xlds = xs_st != nullptr && kb == 0;
+            if (xlds) {  // every wavefront's X loads are in LDS
+                wait_vmcnt<0>();
+                lds_barrier();
+            }
+            // row blocks in batches (their X loads together), to bound registers
+            constexpr int MBMAX = 2;
+            constexpr int MB = NM < MBMAX ? NM : MBMAX;
+#pragma unroll
+            for (int m0 = 0; m0 < NM; m0 += MB) {
+                frag_t xv[MB][3];
+#pragma unroll
+                for (int mm = 0; mm < MB; ++mm) {
+                    const int row = 16 * (m0 + mm) + lc;
+                    const frag_t z{};
+                    xv[mm][0] = xv[mm][1] = xv[mm][2] = z;
+                    if (xlds) {
+                        const uint8_t* xp = xs_st + row * (2 * KG) + 2 * GPL * lg;
+                        xv[mm][0] = *reinterpret_cast<const frag_t*>(xp);
+                        xv[mm][1] = *reinterpret_cast<const frag_t*>(xp + xs_ps);
+                        xv[mm][2] = *reinterpret_cast<const frag_t*>(xp + 2 * xs_ps);
+                    } else if (row < tl.nrows) {
+                        const uint16_t* xp = a.xs_a + (size_t)asrc_lds[row] * a.gs_a + KG * kb + GPL * lg;
+                        xv[mm][0] = *reinterpret_cast<const frag_t*>(xp);
+                        xv[mm][1] = *reinterpret_cast<const frag_t*>(xp + plane);
+                        xv[mm][2] = *reinterpret_cast<const frag_t*>(xp + 2 * plane);
+                    }
+                }
+#pragma unroll
+                for (int mm = 0; mm < MB; ++mm) {
+#pragma unroll
+                    for (int cs = 0; cs < NCS; ++cs) {
+                        f32x4_t v = acc[m0 + mm][cs];
+                        v = bmfma(xv[mm][0], ch[cs], v);
+                        v = bmfma(xv[mm][0], cm[cs], v);
+                        v = bmfma(xv[mm][1], ch[cs], v);
+                        v = bmfma(xv[mm][0], cl[cs], v);
+                        v = bmfma(xv[mm][2], ch[cs], v);
+                        v = bmfma(xv[mm][1], cm[cs], v);
+                        acc[m0 + mm][cs] = v;
+                    }
+                }
+                if constexpr (MB < NM)
+                    if (!xlds) __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+
     // The K loop is instantiated for 1, 2, 4 and 8 row blocks of 16 (the tile's count
     // rounded up), so its body is straight-line code the compiler can interleave.
-    auto kloop = [&](auto nm_tag) {
+    auto kloop = [&](auto nm_tag) __attribute__((always_inline)) {
         constexpr int NM = decltype(nm_tag)::value;
         constexpr int NA = NM >= 2 ? NM / 2 : 1;  // A instructions (8 rows each) per wavefront
         constexpr int LPC = NA + 3;               // loads per wavefront and chunk
@@ -553,7 +652,7 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
             const uint32_t off = arow_lds[row];
             a_off[i] = (off == 0xFFFFFFFFu ? arow0 : off) + 16 * ((lane & 7) ^ (row & 7));
         }
-        auto issue = [&](int c) {
+        auto issue = [&](int c) __attribute__((always_inline)) {
             const uint32_t st = ring_lds + (uint32_t)((c % NS) * STAGE);
             const uint8_t* ab = asrc + (size_t)c * (KC * 2);
 #pragma unroll
@@ -563,7 +662,7 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
             for (int i = 0; i < 2; ++i) lds_dma16(bb, b_off[i], st + SA + (2 * wave + i) * 1024);
             lds_dma4(ebase + (size_t)c * 16, sb_off, st + SA + B_BYTES + wave * 256);
         };
-        auto compute = [&](int c) {
+        auto compute = [&](int c) __attribute__((always_inline)) {
             const uint8_t* st = ring + (size_t)(c % NS) * STAGE;
             const uint32_t* sb_st = reinterpret_cast<const uint32_t*>(st + SA + B_BYTES);
             uint4 b0[NCS], b1[NCS];
@@ -593,6 +692,23 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
         };
         const int NC = K / KC;
         for (int c = 0; c < NS - 1 && c < NC; ++c) issue(c);
+        if (G <= KG) {
+            // the X planes of the tile's 32 NA staged rows (rows beyond the tile read row 0)
+            // into the last stage: plane p, row r at p * XR * 2KG + r * 2KG
+            constexpr int XROW = 2 * KG, RPI = 1024 / XROW, LPX = XROW / 16;
+            constexpr int XR = 32 * NA, NIX = 3 * XR / RPI;
+            static_assert(3 * XR * XROW <= STAGE, "X planes fit in a stage");
+            const uint32_t xl = ring_lds + (uint32_t)((NS - 1) * STAGE);
+            const size_t plane_b = (size_t)(GATEUP ? a.T : a.T * S) * a.gs_a * 2;
+            for (int j = wave; j < NIX; j += 4) {
+                const int p = j / (XR / RPI), r = (j % (XR / RPI)) * RPI + lane / LPX;
+                const uint32_t off = (uint32_t)((size_t)asrc_lds[r] * a.gs_a * 2 + 16 * (lane % LPX));
+                lds_dma16(reinterpret_cast<const uint8_t*>(a.xs_a) + p * plane_b, off, xl + j * 1024);
+            }
+            bias_term(nm_tag, ring + (size_t)(NS - 1) * STAGE, XR * XROW);
+        } else {
+            bias_term(nm_tag, nullptr, 0);
+        }
         for (int c = 0; c < NC; ++c) {
             // this wavefront's loads of chunk c are done once only the later chunks'
             // (at most NS - 2 of them) are left
@@ -608,55 +724,6 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
     else if (n_ms <= 2) kloop(std::integral_constant<int, 2>{});
     else if (n_ms <= 4) kloop(std::integral_constant<int, 4>{});
     else kloop(std::integral_constant<int, 8>{});
-
-    // ---- bias term: sum over groups of X[row][g] * (bias - 16 scale)[col][g], 16 groups per MFMA
-    for (int kb = 0; kb < (G + 15) / 16; ++kb) {
-        uint2 ch[NCS], cm[NCS], cl[NCS];
-#pragma unroll
-        for (int cs = 0; cs < NCS; ++cs) {
-            const int br = cs * 64 + 16 * wave + lc;
-            uint32_t h4[4], m4[4], l4[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int g = 16 * kb + 4 * lg + i;
-                float cc = 0.f;
-                if (g < G && brow_ok(br)) {
-                    const uint32_t w = *reinterpret_cast<const uint32_t*>(ebase + brow_sb_word(br, g));
-                    cc = bf16_to_f32(w >> 16) - 16.f * bf16_to_f32(w & 0xFFFFu);
-                }
-                split3_bf16(cc, h4[i], m4[i], l4[i]);
-            }
-            ch[cs] = make_uint2(h4[0] | (h4[1] << 16), h4[2] | (h4[3] << 16));
-            cm[cs] = make_uint2(m4[0] | (m4[1] << 16), m4[2] | (m4[3] << 16));
-            cl[cs] = make_uint2(l4[0] | (l4[1] << 16), l4[2] | (l4[3] << 16));
-        }
-        const size_t plane = (size_t)(GATEUP ? a.T : a.T * S) * a.gs_a;
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            if (m < n_ms) {
-                const int row = 16 * m + lc;
-                uint2 xh = make_uint2(0u, 0u), xm = xh, xl = xh;
-                if (row < tl.nrows) {
-                    const int src = GATEUP ? a.order[tl.row0 + row] / S : tl.row0 + row;
-                    const uint16_t* xp = a.xs_a + (size_t)src * a.gs_a + 16 * kb + 4 * lg;
-                    xh = *reinterpret_cast<const uint2*>(xp);
-                    xm = *reinterpret_cast<const uint2*>(xp + plane);
-                    xl = *reinterpret_cast<const uint2*>(xp + 2 * plane);
-                }
-#pragma unroll
-                for (int cs = 0; cs < NCS; ++cs) {
-                    f32x4_t v = acc[m][cs];
-                    v = mfma16x16x16(xh, ch[cs], v);
-                    v = mfma16x16x16(xh, cm[cs], v);
-                    v = mfma16x16x16(xm, ch[cs], v);
-                    v = mfma16x16x16(xh, cl[cs], v);
-                    v = mfma16x16x16(xl, ch[cs], v);
-                    v = mfma16x16x16(xm, cm[cs], v);
-                    acc[m][cs] = v;
-                }
-            }
-        }
-    }
 
     // ---- epilogue: the ring's memory is free once every wavefront is past its last chunk
     __syncthreads();
