@@ -457,6 +457,7 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t ring[];  // ring of stages, each (A | B | sb)
     __shared__ uint32_t arow_lds[BM];  // byte offset of each tile row in its source, ~0 beyond the tile
     __shared__ int32_t asrc_lds[BM];   // row of each tile row in its row-sum planes
+    __shared__ int32_t pick_lds[BM];   // down: pick p = order[row] of each tile row (its y row)
     const int H = a.H, I = a.I, S = a.S;
     const int K = GATEUP ? H : I;
     const int nblk = GATEUP ? (I + HALF - 1) / HALF : (H + NBR - 1) / NBR;
@@ -479,6 +480,7 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
         }
         arow_lds[tid] = off;
         asrc_lds[tid] = src;
+        if constexpr (!GATEUP) pick_lds[tid] = tid < tl.nrows ? a.order[tl.row0 + tid] : 0;
     }
     __syncthreads();
     const uint8_t* asrc = reinterpret_cast<const uint8_t*>(GATEUP ? a.x : a.hbuf);
@@ -812,7 +814,7 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
                 for (int it = 0; it < 16; ++it) {
                     const int rl = 4 * it + (tid >> 6), row = 64 * half + rl, pc = tid & 63;
                     if (row < tl.nrows && col0 + 4 * pc < H)
-                        *reinterpret_cast<float4*>(a.y + (size_t)a.order[tl.row0 + row] * H + col0 + 4 * pc) =
+                        *reinterpret_cast<float4*>(a.y + (size_t)pick_lds[row] * H + col0 + 4 * pc) =
                             *reinterpret_cast<const float4*>(yl + rl * YS + 4 * pc);
                 }
             }
@@ -865,9 +867,9 @@ extern "C" moe_status moe_experts_prefill(const moe_shape* shape, const void* ex
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
         return fail(MOE_ERR_HIP, "cannot query the device's LDS size");
-    if (max_lds < RING + 1024)
+    if (max_lds < RING + 2048)
         return fail(MOE_ERR_UNSUPPORTED, "the grouped GEMM needs %d bytes of LDS per workgroup, the device has %d",
-                    RING + 1024, max_lds);
+                    RING + 2048, max_lds);
     hipStream_t hs = (hipStream_t)stream;
     char* w = (char*)ws;
     int32_t* counts = (int32_t*)(w + W.counts);
