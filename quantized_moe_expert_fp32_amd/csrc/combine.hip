@@ -4,9 +4,11 @@
 #include "moe_internal.h"
 
 namespace moe {
+typedef float f4_t __attribute__((ext_vector_type(4)));
 
 // One thread per four consecutive outputs of a token; slots are summed in slot
-// order (0..k-1, then the shared slot) with fp32 fused multiply-adds.
+// order (0..k-1, then the shared slot) with fp32 fused multiply-adds. y is read
+// once, with non-temporal loads, so it does not displace other data in the caches.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const uint16_t* __restrict__ w,
                                                       const uint16_t* __restrict__ wsh, int T, int H, int k, int S,
                                                       const uint16_t* residual, uint16_t* out) {
@@ -18,7 +20,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
     for (int s = 0; s < k; ++s) {
         const float ws = bf16_to_f32(w[t * k + s]);
-        const float4 v = *reinterpret_cast<const float4*>(yt + (size_t)s * H);
+        const f4_t v = __builtin_nontemporal_load(reinterpret_cast<const f4_t*>(yt + (size_t)s * H));
         a0 = fmaf(ws, v.x, a0);
         a1 = fmaf(ws, v.y, a1);
         a2 = fmaf(ws, v.z, a2);
@@ -26,7 +28,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     }
     if (wsh) {
         const float ws = bf16_to_f32(wsh[t]);
-        const float4 v = *reinterpret_cast<const float4*>(yt + (size_t)k * H);
+        const f4_t v = __builtin_nontemporal_load(reinterpret_cast<const f4_t*>(yt + (size_t)k * H));
         a0 = fmaf(ws, v.x, a0);
         a1 = fmaf(ws, v.y, a1);
         a2 = fmaf(ws, v.z, a2);
@@ -78,7 +80,8 @@ extern "C" moe_status moe_combine(const moe_shape* shape, const float* y, const 
     moe_status st = validate_shape(shape);
     if (st != MOE_OK) return st;
     if (T < 1) return fail(MOE_ERR_INVALID_ARG, "T = %d, need T >= 1", T);
-    if (!y || !w || !out || !aligned16(y)) return fail(MOE_ERR_INVALID_ARG, "NULL or unaligned pointer");
+    if (!y || !w || !out || !aligned16(y) || !aligned16(out) || (residual && !aligned16(residual)))
+        return fail(MOE_ERR_INVALID_ARG, "NULL or unaligned pointer");
     if (shape->has_shared != (w_shared != nullptr))
         return fail(MOE_ERR_INVALID_ARG, "w_shared must be given iff the layer has a shared expert");
     const int H = shape->hidden;

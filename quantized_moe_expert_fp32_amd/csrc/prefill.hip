@@ -793,7 +793,9 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
         }
     } else {
         // y[order[row]][col0 + n], n < 256, staged 64 rows at a time as an fp32 tile in
-        // LDS and stored with 16-byte row pieces
+        // LDS and stored with 16-byte row pieces. The stores are non-temporal: y is read
+        // once, by the combine, and would otherwise evict weight lines and activation
+        // tiles that later workgroups read again.
         constexpr int YS = NBR + 4;  // tile row stride (floats)
         float* yl = reinterpret_cast<float*>(ring);
 #pragma unroll
@@ -814,8 +816,8 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
                 for (int it = 0; it < 16; ++it) {
                     const int rl = 4 * it + (tid >> 6), row = 64 * half + rl, pc = tid & 63;
                     if (row < tl.nrows && col0 + 4 * pc < H)
-                        *reinterpret_cast<float4*>(a.y + (size_t)pick_lds[row] * H + col0 + 4 * pc) =
-                            *reinterpret_cast<const float4*>(yl + rl * YS + 4 * pc);
+                        __builtin_nontemporal_store(*reinterpret_cast<const f32x4_t*>(yl + rl * YS + 4 * pc),
+                                                    reinterpret_cast<f32x4_t*>(a.y + (size_t)pick_lds[row] * H + col0 + 4 * pc));
                 }
             }
         }
