@@ -646,6 +646,11 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
         constexpr int STAGE = SA + B_BYTES + SB_BYTES;
         constexpr int NS = RING / STAGE;          // stages: 5, 4 or 3
         static_assert(NS >= 3 && NS * STAGE <= RING && LPC * (NS - 2) < 64, "ring");
+        // Tiles of up to 32 rows stream weights faster than they use the VALU, so they
+        // add the bias term chunk by chunk instead of before the loop: the chunk's row
+        // sums X come from two more MFMAs against ones, and c = bias - 16 scale from the
+        // (scale, bias) word the chunk already holds; one more fp32 FMA per output.
+        constexpr bool INB = NM <= 2;
         const uint32_t arow0 = arow_lds[0];       // row 0 is always inside the tile
         uint32_t a_off[NA];
 #pragma unroll
@@ -668,7 +673,7 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
             const uint8_t* st = ring + (size_t)(c % NS) * STAGE;
             const uint32_t* sb_st = reinterpret_cast<const uint32_t*>(st + SA + B_BYTES);
             uint4 b0[NCS], b1[NCS];
-            float s16[NCS];
+            float s16[NCS], cb16[NCS];
 #pragma unroll
             for (int cs = 0; cs < NCS; ++cs) {
                 int jb, slot;
@@ -676,25 +681,37 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
                 const uint8_t* bp = st + SA + jb * 128 + 16 * ((2 * slot) ^ bsw(jb)) + 4 * lg;
                 b0[cs] = bfrag(*reinterpret_cast<const uint32_t*>(bp));
                 b1[cs] = bfrag(*reinterpret_cast<const uint32_t*>(bp + 16));
-                s16[cs] = 16.f * bf16_to_f32(sb_st[4 * jb + slot] & 0xFFFFu);
+                const uint32_t w = sb_st[4 * jb + slot];
+                s16[cs] = 16.f * bf16_to_f32(w & 0xFFFFu);
+                if constexpr (INB) cb16[cs] = brow_ok(cs * 64 + 16 * wave + lc) ? bf16_to_f32(w >> 16) - s16[cs] : 0.f;
             }
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
                 const uint8_t* ar = st + (16 * m + lc) * 128;
                 const uint4 a0 = *reinterpret_cast<const uint4*>(ar + 16 * (lg ^ (lc & 7)));
                 const uint4 a1 = *reinterpret_cast<const uint4*>(ar + 16 * ((4 + lg) ^ (lc & 7)));
+                f32x4_t xs{0.f, 0.f, 0.f, 0.f};  // INB: the chunk's row sums (every column alike)
+                if constexpr (INB) {
+                    const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+                    xs = mfma16x16x32(a0, ones, xs);
+                    xs = mfma16x16x32(a1, ones, xs);
+                }
 #pragma unroll
                 for (int cs = 0; cs < NCS; ++cs) {
                     f32x4_t p = mfma16x16x32(a0, b0[cs], f32x4_t{0.f, 0.f, 0.f, 0.f});
                     p = mfma16x16x32(a1, b1[cs], p);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[m][cs][r] = fmaf(s16[cs], p[r], acc[m][cs][r]);
+                    for (int r = 0; r < 4; ++r) {
+                        if constexpr (INB) acc[m][cs][r] = fmaf(xs[r], cb16[cs], fmaf(s16[cs], p[r], acc[m][cs][r]));
+                        else acc[m][cs][r] = fmaf(s16[cs], p[r], acc[m][cs][r]);
+                    }
                 }
             }
         };
         const int NC = K / KC;
         for (int c = 0; c < NS - 1 && c < NC; ++c) issue(c);
-        if (G <= KG) {
+        if constexpr (INB) {
+        } else if (G <= KG) {
             // the X planes of the tile's 32 NA staged rows (rows beyond the tile read row 0)
             // into the last stage: plane p, row r at p * XR * 2KG + r * 2KG
             constexpr int XROW = 2 * KG, RPI = 1024 / XROW, LPX = XROW / 16;
