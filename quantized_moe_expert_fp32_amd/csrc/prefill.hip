@@ -306,11 +306,14 @@ __device__ __forceinline__ void split3_bf16(float v, uint32_t& hi, uint32_t& mid
 
 // X[t][g] = sum of x[t][64g .. 64g+63] (a chain of bf16 dot2 against (1, 1)) for
 // g < H/64, zero for the padding groups up to gs; stored as three bf16 planes.
+// Within each block of 32 groups, group 4j + q sits at position 8q + j: the order
+// of the gate/up GEMM's bias operands (see bias_term there).
 __global__ __launch_bounds__(256) void xsum_kernel(const uint16_t* __restrict__ x, int T, int H, int gs,
                                                    uint16_t* __restrict__ planes) {
     const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= (long long)T * gs) return;
-    const int t = (int)(idx / gs), g = (int)(idx % gs);
+    const int t = (int)(idx / gs), pos = (int)(idx % gs);
+    const int g = (pos & ~31) | ((pos & 7) << 2) | ((pos & 31) >> 3);
     float sum = 0.f;
     if (g < H / 64) {
         const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)t * H + 64 * g);
@@ -570,7 +573,11 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
                 const int br = cs * 64 + 16 * wave + lc;
 #pragma unroll
                 for (int i = 0; i < GPL; ++i) {
-                    const int g = KG * kb + GPL * lg + i;
+                    // k slot 8 lg + i of the step: group 4i + lg for gate/up (whose x row
+                    // sums are stored in that order), so the 16 lanes of a row block read
+                    // the four consecutive groups' words of their blocks, 64-byte runs;
+                    // group 4 lg + i for down
+                    const int g = GATEUP ? KG * kb + 4 * i + lg : KG * kb + GPL * lg + i;
                     w[cs][i] = (g < G && brow_ok(br)) ? *reinterpret_cast<const uint32_t*>(ebase + brow_sb_word(br, g))
                                                       : 0u;  // scale 0, bias 0: c = 0
                 }
@@ -646,11 +653,11 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
         constexpr int STAGE = SA + B_BYTES + SB_BYTES;
         constexpr int NS = RING / STAGE;          // stages: 5, 4 or 3
         static_assert(NS >= 3 && NS * STAGE <= RING && LPC * (NS - 2) < 64, "ring");
-        // Tiles of up to 32 rows stream weights faster than they use the VALU, so they
+        // Tiles of up to 64 rows stream weights faster than they use the VALU, so they
         // add the bias term chunk by chunk instead of before the loop: the chunk's row
         // sums X come from two more MFMAs against ones, and c = bias - 16 scale from the
         // (scale, bias) word the chunk already holds; one more fp32 FMA per output.
-        constexpr bool INB = NM <= 2;
+        constexpr bool INB = NM <= 4;
         const uint32_t arow0 = arow_lds[0];       // row 0 is always inside the tile
         uint32_t a_off[NA];
 #pragma unroll
