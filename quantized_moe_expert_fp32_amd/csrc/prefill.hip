@@ -33,12 +33,9 @@ struct Tile {
 
 // Workspace layout for moe_experts_prefill.
 struct PrefillWs {
-    size_t counts, offsets, cursor, ntiles, tiles, order, h, xs_x, xs_h, slices, total;
+    size_t counts, offsets, cursor, ntiles, tiles, order, h, xs_x, xs_h, total;
     int max_tiles, gs_x, gs_h;  // group strides of the row-sum planes (x: multiple of 32, h: of 16)
-    int n_slices;               // pick slices of the parallel dispatch
 };
-
-constexpr int SLICE = 2048;  // picks per workgroup of the parallel dispatch
 
 static PrefillWs prefill_ws_layout(const moe_shape& s, int T) {
     PrefillWs w;
@@ -59,8 +56,6 @@ static PrefillWs prefill_ws_layout(const moe_shape& s, int T) {
     w.gs_h = ((s.inter / 64 + 15) / 16) * 16;
     w.xs_x = o;    o = align_up(o + 3 * 2 * (size_t)T * w.gs_x, 256);      // [3][T][gs_x] bf16
     w.xs_h = o;    o = align_up(o + 3 * 2 * (size_t)T * S * w.gs_h, 256);  // [3][T*S][gs_h] bf16
-    w.n_slices = (int)((picks + SLICE - 1) / SLICE);
-    w.slices = o;  o = align_up(o + 4 * (size_t)w.n_slices * s.n_experts, 256);  // [n_slices][E] counts, then bases
     w.total = o;
     return w;
 }
@@ -152,55 +147,114 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const int32_t* __restric
         for (int t = tid; t < T; t += blockDim.x) order[off[E] + t] = t * S + k;
 }
 
-// ---------------------------------------------------------------- parallel dispatch
-// The same result as dispatch_kernel (up to the order of rows within an expert,
-// which no later step depends on), in three launches: per-slice histograms of
-// SLICE picks, one workgroup that turns them into per-slice bases and builds the
-// offsets and the tile list, and a per-slice scatter.
-__global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __restrict__ ids, long long P, int E,
-                                                             int32_t* __restrict__ slices) {
-    __shared__ int cnt[1024];
-    const int tid = threadIdx.x;
-    for (int i = tid; i < E; i += 256) cnt[i] = 0;
-    __syncthreads();
-    const long long p0 = (long long)blockIdx.x * SLICE, p1 = min(P, p0 + SLICE);
-    for (long long p = p0 + tid; p < p1; p += 256) {
-        const int e = ids[p];
-        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
-    }
-    __syncthreads();
-    for (int i = tid; i < E; i += 256) slices[(size_t)blockIdx.x * E + i] = cnt[i];
+// ---------------------------------------------------------------- row sums in three bf16 parts
+// v = hi + mid + lo: hi and mid are v and the remainder truncated to bf16 (both
+// remainders exact in fp32), lo the last remainder rounded to bf16.
+__device__ __forceinline__ void split3_bf16(float v, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+    const uint32_t h = __float_as_uint(v) & 0xFFFF0000u;
+    const float r1 = v - __uint_as_float(h);
+    const uint32_t m = __float_as_uint(r1) & 0xFFFF0000u;
+    const float r2 = r1 - __uint_as_float(m);
+    hi = h >> 16;
+    mid = m >> 16;
+    lo = f32_to_bf16(r2);
 }
 
-__global__ __launch_bounds__(1024) void dispatch_scan_kernel(int T, int k, int E, int has_shared, int n_slices,
-                                                             int32_t* __restrict__ slices,
-                                                             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                                             int32_t* __restrict__ ntiles, Tile* __restrict__ tiles,
-                                                             int32_t* __restrict__ order) {
-    __shared__ int cnt[1025];
-    __shared__ int off[1026];
-    __shared__ int foff[1026];  // full-tile offsets
-    __shared__ int bucket[9];   // partial tiles by row-block count (8 - n blocks)
+// X[t][g] = sum of x[t][64g .. 64g+63] (a chain of bf16 dot2 against (1, 1)) for
+// g < H/64, zero for the padding groups up to gs; stored as three bf16 planes.
+// Within each block of 32 groups, group 4j + q sits at position 8q + j: the order
+// of the gate/up GEMM's bias operands (see bias_term there).
+__device__ __forceinline__ void xsum_entry(const uint16_t* __restrict__ x, int T, int H, int gs,
+                                           uint16_t* __restrict__ planes, long long idx) {
+    if (idx >= (long long)T * gs) return;
+    const int t = (int)(idx / gs), pos = (int)(idx % gs);
+    const int g = (pos & ~31) | ((pos & 7) << 2) | ((pos & 31) >> 3);
+    float sum = 0.f;
+    if (g < H / 64) {
+        const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)t * H + 64 * g);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const uint4 v = src[q];
+            sum = dot2_bf16(v.x, 0x3F803F80u, sum);
+            sum = dot2_bf16(v.y, 0x3F803F80u, sum);
+            sum = dot2_bf16(v.z, 0x3F803F80u, sum);
+            sum = dot2_bf16(v.w, 0x3F803F80u, sum);
+        }
+    }
+    uint32_t hi, mid, lo;
+    split3_bf16(sum, hi, mid, lo);
+    const size_t plane = (size_t)T * gs;
+    planes[idx] = (uint16_t)hi;
+    planes[plane + idx] = (uint16_t)mid;
+    planes[2 * plane + idx] = (uint16_t)lo;
+}
+
+// ---------------------------------------------------------------- set-up: dispatch and row sums
+// One launch before the GEMMs. Workgroup 0 turns the picks into the expert-sorted
+// pick order and the tile list; the other workgroups compute the row sums of x,
+// one (token, group) each. The dispatch walks the picks p = t*k + s in batches of
+// eight per thread (consecutive p across the lanes, all loads in flight before the
+// first count); pick p goes to wavefront (p mod 1024)/64, which counts it in its own
+// LDS histogram (fewer lanes contend for a hot expert's counter). A scan over the
+// wavefronts and then over the experts gives every (wavefront, expert) its base in
+// the order, and the same walk scatters the picks. The shared expert takes every token. Picks with an id
+// outside [0, E) are skipped and their y rows zeroed. The tile list holds every full
+// tile first (expert order), then the partial tiles with the most row blocks first,
+// so the items that start last are the cheapest; order within a size class and of
+// rows within an expert are arbitrary (no later step depends on them).
+constexpr int SETUP_THREADS = 1024, SETUP_WAVES = SETUP_THREADS / 64, SETUP_EMAX = 1024;
+
+__global__ __launch_bounds__(SETUP_THREADS) void prefill_setup_kernel(
+    const int32_t* __restrict__ ids, int T, int k, int E, int has_shared, int H, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ ntiles, Tile* __restrict__ tiles,
+    int32_t* __restrict__ order, float* __restrict__ y, const uint16_t* __restrict__ x, int gs,
+    uint16_t* __restrict__ planes) {
+    if (blockIdx.x > 0) {
+        xsum_entry(x, T, H, gs, planes, (long long)(blockIdx.x - 1) * SETUP_THREADS + threadIdx.x);
+        return;
+    }
+    __shared__ int hist[SETUP_WAVES][SETUP_EMAX];  // per-wavefront counts, then bases, then cursors
+    __shared__ int cnt[SETUP_EMAX + 1];
+    __shared__ int off[SETUP_EMAX + 2];
+    __shared__ int foff[SETUP_EMAX + 2];  // full-tile offsets
+    __shared__ int bucket[9];             // partial tiles by row-block count (8 - n blocks)
     const int M = E + has_shared, S = k + has_shared;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, wave = tid >> 6;
+    for (int i = tid; i < SETUP_WAVES * SETUP_EMAX; i += SETUP_THREADS) (&hist[0][0])[i] = 0;
     if (tid < 9) bucket[tid] = 0;
-    // per expert: exclusive scan over the slices (relative bases, in place)
-    for (int e = tid; e < E; e += blockDim.x) {
+    __syncthreads();
+    constexpr int PB = 8;  // picks per thread and batch
+    const long long P = (long long)T * k;
+    for (long long p0 = 0; p0 < P; p0 += (long long)SETUP_THREADS * PB) {
+        int ev[PB];
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+            const long long p = p0 + j * SETUP_THREADS + tid;
+            ev[j] = p < P ? ids[p] : -1;
+        }
+#pragma unroll
+        for (int j = 0; j < PB; ++j)
+            if (ev[j] >= 0 && ev[j] < E) atomicAdd(&hist[wave][ev[j]], 1);
+    }
+    __syncthreads();
+    // per expert: exclusive scan over the wavefronts (in place) and the total
+    for (int e = tid; e < E; e += SETUP_THREADS) {
         int run = 0;
-        for (int b = 0; b < n_slices; ++b) {
-            const int c = slices[(size_t)b * E + e];
-            slices[(size_t)b * E + e] = run;
+#pragma unroll
+        for (int w = 0; w < SETUP_WAVES; ++w) {
+            const int c = hist[w][e];
+            hist[w][e] = run;
             run += c;
         }
         cnt[e] = run;
     }
     if (has_shared && tid == 0) cnt[E] = T;
     __syncthreads();
-    for (int e = tid; e < M; e += blockDim.x) {
+    for (int e = tid; e < M; e += SETUP_THREADS) {
         const int rem = cnt[e] % BM;
         if (rem) atomicAdd(&bucket[8 - (rem + 15) / 16], 1);
     }
-    if (tid < 64) {
+    if (tid < 64) {  // exclusive scans of the rows and the full tiles over the experts
         const int per = (M + 63) / 64;
         const int beg = tid * per, end = min(M, beg + per);
         int lc = 0, lt = 0;
@@ -229,9 +283,6 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int T, int k, int E
         }
     }
     __syncthreads();
-    // Tile list: every full tile first (expert order), then the partial tiles with
-    // the most row blocks first, so the items that start last are the cheapest.
-    // Order within a bucket is arbitrary.
     if (tid == 0) {
         int run = foff[M];
         for (int b = 0; b < 9; ++b) {
@@ -240,9 +291,10 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int T, int k, int E
             run += c;
         }
         *ntiles = run;
+        offsets[M] = off[M];
     }
     __syncthreads();
-    for (int e = tid; e < M; e += blockDim.x) {
+    for (int e = tid; e < M; e += SETUP_THREADS) {
         counts[e] = cnt[e];
         offsets[e] = off[e];
         const int nfull = cnt[e] / BM, rem = cnt[e] % BM;
@@ -262,76 +314,39 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int T, int k, int E
             tl.pad = 0;
             tiles[atomicAdd(&bucket[8 - (rem + 15) / 16], 1)] = tl;
         }
-    }
-    if (tid == 0) offsets[M] = off[M];
-    // absolute bases
-    for (int e = tid; e < E; e += blockDim.x)
-        for (int b = 0; b < n_slices; ++b) slices[(size_t)b * E + e] += off[e];
-    if (has_shared)
-        for (int t = tid; t < T; t += blockDim.x) order[off[E] + t] = t * S + k;
-}
-
-__global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t* __restrict__ ids, long long P, int k,
-                                                               int E, int S, int H, const int32_t* __restrict__ slices,
-                                                               int32_t* __restrict__ order, float* __restrict__ y) {
-    __shared__ int cur[1024];
-    const int tid = threadIdx.x;
-    for (int i = tid; i < E; i += 256) cur[i] = slices[(size_t)blockIdx.x * E + i];
-    __syncthreads();
-    const long long p0 = (long long)blockIdx.x * SLICE, p1 = min(P, p0 + SLICE);
-    for (long long p = p0 + tid; p < p1; p += 256) {
-        const int e = ids[p];
-        const int t = (int)(p / k), s = (int)(p % k);
-        if (e >= 0 && e < E) {
-            order[atomicAdd(&cur[e], 1)] = t * S + s;
-        } else {
-            float* yr = y + ((size_t)t * S + s) * H;
-            for (int n = 0; n < H; ++n) yr[n] = 0.f;
-        }
-    }
-}
-
-// ---------------------------------------------------------------- row sums in three bf16 parts
-// v = hi + mid + lo: hi and mid are v and the remainder truncated to bf16 (both
-// remainders exact in fp32), lo the last remainder rounded to bf16.
-__device__ __forceinline__ void split3_bf16(float v, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
-    const uint32_t h = __float_as_uint(v) & 0xFFFF0000u;
-    const float r1 = v - __uint_as_float(h);
-    const uint32_t m = __float_as_uint(r1) & 0xFFFF0000u;
-    const float r2 = r1 - __uint_as_float(m);
-    hi = h >> 16;
-    mid = m >> 16;
-    lo = f32_to_bf16(r2);
-}
-
-// X[t][g] = sum of x[t][64g .. 64g+63] (a chain of bf16 dot2 against (1, 1)) for
-// g < H/64, zero for the padding groups up to gs; stored as three bf16 planes.
-// Within each block of 32 groups, group 4j + q sits at position 8q + j: the order
-// of the gate/up GEMM's bias operands (see bias_term there).
-__global__ __launch_bounds__(256) void xsum_kernel(const uint16_t* __restrict__ x, int T, int H, int gs,
-                                                   uint16_t* __restrict__ planes) {
-    const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= (long long)T * gs) return;
-    const int t = (int)(idx / gs), pos = (int)(idx % gs);
-    const int g = (pos & ~31) | ((pos & 7) << 2) | ((pos & 31) >> 3);
-    float sum = 0.f;
-    if (g < H / 64) {
-        const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)t * H + 64 * g);
+        if (e < E) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const uint4 v = src[q];
-            sum = dot2_bf16(v.x, 0x3F803F80u, sum);
-            sum = dot2_bf16(v.y, 0x3F803F80u, sum);
-            sum = dot2_bf16(v.z, 0x3F803F80u, sum);
-            sum = dot2_bf16(v.w, 0x3F803F80u, sum);
+            for (int w = 0; w < SETUP_WAVES; ++w) hist[w][e] += off[e];  // cursors
         }
     }
-    uint32_t hi, mid, lo;
-    split3_bf16(sum, hi, mid, lo);
-    const size_t plane = (size_t)T * gs;
-    planes[idx] = (uint16_t)hi;
-    planes[plane + idx] = (uint16_t)mid;
-    planes[2 * plane + idx] = (uint16_t)lo;
+    if (has_shared)
+        for (int t = tid; t < T; t += SETUP_THREADS) order[off[E] + t] = t * S + k;
+    __syncthreads();
+    for (long long p0 = 0; p0 < P; p0 += (long long)SETUP_THREADS * PB) {
+        int ev[PB];
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+            const long long p = p0 + j * SETUP_THREADS + tid;
+            ev[j] = p < P ? ids[p] : 0;
+        }
+        // token and slot of pick p0 + tid; when k divides the block size, each later
+        // pick of the batch is SETUP_THREADS / k tokens further at the same slot
+        const bool even = SETUP_THREADS % k == 0;
+        const int tb = (int)((p0 + tid) / k), sb = (int)((p0 + tid) % k);
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+            const long long p = p0 + j * SETUP_THREADS + tid;
+            if (p >= P) continue;
+            const int t = even ? tb + j * (SETUP_THREADS / k) : (int)(p / k);
+            const int sl = even ? sb : (int)(p % k), e = ev[j];
+            if (e >= 0 && e < E) {
+                order[atomicAdd(&hist[wave][e], 1)] = t * S + sl;
+            } else {
+                float* yr = y + ((size_t)t * S + sl) * H;
+                for (int n = 0; n < H; ++n) yr[n] = 0.f;
+            }
+        }
+    }
 }
 
 // ---------------------------------------------------------------- XCD-aware item mapping
@@ -904,16 +919,13 @@ extern "C" moe_status moe_experts_prefill(const moe_shape* shape, const void* ex
     Tile* tiles = (Tile*)(w + W.tiles);
     int32_t* order = (int32_t*)(w + W.order);
     uint16_t* hbuf = (uint16_t*)(w + W.h);
-    int32_t* slices = (int32_t*)(w + W.slices);
-    const long long P = (long long)T * sh.top_k;
-    hipLaunchKernelGGL(dispatch_count_kernel, dim3(W.n_slices), dim3(256), 0, hs, ids, P, sh.n_experts, slices);
-    if ((st = check_launch("dispatch_count_kernel")) != MOE_OK) return st;
-    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, hs, T, sh.top_k, sh.n_experts, sh.has_shared,
-                       W.n_slices, slices, counts, offsets, ntiles, tiles, order);
-    if ((st = check_launch("dispatch_scan_kernel")) != MOE_OK) return st;
-    hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(W.n_slices), dim3(256), 0, hs, ids, P, sh.top_k, sh.n_experts, S,
-                       H, slices, order, y);
-    if ((st = check_launch("dispatch_scatter_kernel")) != MOE_OK) return st;
+    uint16_t* xs_x = (uint16_t*)(w + W.xs_x);
+    uint16_t* xs_h = (uint16_t*)(w + W.xs_h);
+    const long long nsum = (long long)T * W.gs_x;
+    hipLaunchKernelGGL(prefill_setup_kernel, dim3((unsigned)(1 + (nsum + SETUP_THREADS - 1) / SETUP_THREADS)),
+                       dim3(SETUP_THREADS), 0, hs, ids, T, sh.top_k, sh.n_experts, sh.has_shared, H, counts, offsets,
+                       ntiles, tiles, order, y, x, W.gs_x, xs_x);
+    if ((st = check_launch("prefill_setup_kernel")) != MOE_OK) return st;
     GemmArgs ga;
     ga.packed = (const uint8_t*)experts_packed;
     ga.L = L;
@@ -928,11 +940,6 @@ extern "C" moe_status moe_experts_prefill(const moe_shape* shape, const void* ex
     ga.y = y;
     ga.T = T;
     ga.gs_h = W.gs_h;
-    uint16_t* xs_x = (uint16_t*)(w + W.xs_x);
-    uint16_t* xs_h = (uint16_t*)(w + W.xs_h);
-    const long long nsum = (long long)T * W.gs_x;
-    hipLaunchKernelGGL(xsum_kernel, dim3((unsigned)((nsum + 255) / 256)), dim3(256), 0, hs, x, T, H, W.gs_x, xs_x);
-    if ((st = check_launch("xsum_kernel")) != MOE_OK) return st;
     ga.xs_a = xs_x;
     ga.xs_h = xs_h;
     ga.gs_a = W.gs_x;
