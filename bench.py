@@ -59,7 +59,8 @@ def parse():
 # counter reads for a plain copy of known size. The record is stored with a hash
 # of the library sources; a bench run reports it only while the hash matches.
 # kernels of the measured stage (per-launch traffic is the sum of their per-dispatch medians)
-PREFILL_KERNELS = ["prefill_setup_kernel", "expert_gemm_kernel<true>", "expert_gemm_kernel<false>"]
+PREFILL_KERNELS = ["prefill_count_kernel", "prefill_scatter_kernel", "expert_gemm_kernel<true>",
+                   "expert_gemm_kernel<false>"]
 TRAFFIC_KERNELS = {"decode": ["decode_layer_kernel"], "stack16": ["decode_layer_kernel"],
                    "stack1": ["decode_layer_kernel"],
                    "prefill512": PREFILL_KERNELS, "prefill4096": PREFILL_KERNELS}

@@ -33,9 +33,12 @@ struct Tile {
 
 // Workspace layout for moe_experts_prefill.
 struct PrefillWs {
-    size_t counts, offsets, cursor, ntiles, tiles, order, h, xs_x, xs_h, total;
+    size_t counts, offsets, cursor, ntiles, tiles, order, h, xs_x, xs_h, slices, total;
     int max_tiles, gs_x, gs_h;  // group strides of the row-sum planes (x: multiple of 32, h: of 16)
+    int n_slices;               // pick slices of the dispatch
 };
+
+constexpr int SLICE = 2048;  // picks per slice (one workgroup of the dispatch each)
 
 static PrefillWs prefill_ws_layout(const moe_shape& s, int T) {
     PrefillWs w;
@@ -56,6 +59,8 @@ static PrefillWs prefill_ws_layout(const moe_shape& s, int T) {
     w.gs_h = ((s.inter / 64 + 15) / 16) * 16;
     w.xs_x = o;    o = align_up(o + 3 * 2 * (size_t)T * w.gs_x, 256);      // [3][T][gs_x] bf16
     w.xs_h = o;    o = align_up(o + 3 * 2 * (size_t)T * S * w.gs_h, 256);  // [3][T*S][gs_h] bf16
+    w.n_slices = (int)((picks + SLICE - 1) / SLICE);
+    w.slices = o;  o = align_up(o + 4 * (size_t)w.n_slices * s.n_experts, 256);  // [n_slices][E] counts
     w.total = o;
     return w;
 }
@@ -190,77 +195,88 @@ __device__ __forceinline__ void xsum_entry(const uint16_t* __restrict__ x, int T
 }
 
 // ---------------------------------------------------------------- set-up: dispatch and row sums
-// One launch before the GEMMs. Workgroup 0 turns the picks into the expert-sorted
-// pick order and the tile list; the other workgroups compute the row sums of x,
-// one (token, group) each. The dispatch walks the picks p = t*k + s in batches of
-// eight per thread (consecutive p across the lanes, all loads in flight before the
-// first count); pick p goes to wavefront (p mod 1024)/64, which counts it in its own
-// LDS histogram (fewer lanes contend for a hot expert's counter). A scan over the
-// wavefronts and then over the experts gives every (wavefront, expert) its base in
-// the order, and the same walk scatters the picks. The shared expert takes every token. Picks with an id
-// outside [0, E) are skipped and their y rows zeroed. The tile list holds every full
-// tile first (expert order), then the partial tiles with the most row blocks first,
-// so the items that start last are the cheapest; order within a size class and of
-// rows within an expert are arbitrary (no later step depends on them).
-constexpr int SETUP_THREADS = 1024, SETUP_WAVES = SETUP_THREADS / 64, SETUP_EMAX = 1024;
+// Two launches before the GEMMs. The picks p = t*k + s are cut into slices of SLICE
+// consecutive picks, one workgroup each.
+//   count: each slice's per-expert counts (an LDS histogram) go to slices[b][e]; the
+//     workgroups after the slices compute the row sums of x, one (token, group) per
+//     thread.
+//   scatter: every slice's workgroup reads the whole count matrix (n_slices x E) and
+//     derives the experts' totals, their offsets in the expert-sorted order and its
+//     own base within each expert (the sum over the earlier slices), then scatters
+//     its picks through LDS cursors. Workgroup 0 also writes the counts, the offsets,
+//     the shared expert's rows (it takes every token) and the tile list: every full
+//     tile first (expert order), then the partial tiles with the most row blocks
+//     first, so the items that start last are the cheapest.
+// The order of rows within an expert and of tiles within a size class are arbitrary;
+// no later step depends on them. Picks with an id outside [0, E) are skipped and
+// their y rows zeroed. A slice's picks are loaded before any is counted or placed.
+constexpr int DT = 256, DPT = SLICE / DT;  // threads per workgroup, picks per thread
 
-__global__ __launch_bounds__(SETUP_THREADS) void prefill_setup_kernel(
-    const int32_t* __restrict__ ids, int T, int k, int E, int has_shared, int H, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ ntiles, Tile* __restrict__ tiles,
-    int32_t* __restrict__ order, float* __restrict__ y, const uint16_t* __restrict__ x, int gs,
-    uint16_t* __restrict__ planes) {
-    if (blockIdx.x > 0) {
-        xsum_entry(x, T, H, gs, planes, (long long)(blockIdx.x - 1) * SETUP_THREADS + threadIdx.x);
+__global__ __launch_bounds__(DT) void prefill_count_kernel(const int32_t* __restrict__ ids, long long P, int E,
+                                                           int n_slices, int32_t* __restrict__ slices,
+                                                           const uint16_t* __restrict__ x, int T, int H, int gs,
+                                                           uint16_t* __restrict__ planes) {
+    if ((int)blockIdx.x >= n_slices) {
+        xsum_entry(x, T, H, gs, planes, (long long)(blockIdx.x - n_slices) * DT + threadIdx.x);
         return;
     }
-    __shared__ int hist[SETUP_WAVES][SETUP_EMAX];  // per-wavefront counts, then bases, then cursors
-    __shared__ int cnt[SETUP_EMAX + 1];
-    __shared__ int off[SETUP_EMAX + 2];
-    __shared__ int foff[SETUP_EMAX + 2];  // full-tile offsets
-    __shared__ int bucket[9];             // partial tiles by row-block count (8 - n blocks)
-    const int M = E + has_shared, S = k + has_shared;
-    const int tid = threadIdx.x, wave = tid >> 6;
-    for (int i = tid; i < SETUP_WAVES * SETUP_EMAX; i += SETUP_THREADS) (&hist[0][0])[i] = 0;
-    if (tid < 9) bucket[tid] = 0;
+    __shared__ int cnt[1024];
+    const int tid = threadIdx.x;
+    for (int i = tid; i < E; i += DT) cnt[i] = 0;
     __syncthreads();
-    constexpr int PB = 8;  // picks per thread and batch
-    const long long P = (long long)T * k;
-    for (long long p0 = 0; p0 < P; p0 += (long long)SETUP_THREADS * PB) {
-        int ev[PB];
+    const long long p0 = (long long)blockIdx.x * SLICE;
+    int ev[DPT];
 #pragma unroll
-        for (int j = 0; j < PB; ++j) {
-            const long long p = p0 + j * SETUP_THREADS + tid;
-            ev[j] = p < P ? ids[p] : -1;
-        }
-#pragma unroll
-        for (int j = 0; j < PB; ++j)
-            if (ev[j] >= 0 && ev[j] < E) atomicAdd(&hist[wave][ev[j]], 1);
+    for (int j = 0; j < DPT; ++j) {
+        const long long p = p0 + j * DT + tid;
+        ev[j] = p < P ? ids[p] : -1;
     }
-    __syncthreads();
-    // per expert: exclusive scan over the wavefronts (in place) and the total
-    for (int e = tid; e < E; e += SETUP_THREADS) {
-        int run = 0;
 #pragma unroll
-        for (int w = 0; w < SETUP_WAVES; ++w) {
-            const int c = hist[w][e];
-            hist[w][e] = run;
-            run += c;
+    for (int j = 0; j < DPT; ++j)
+        if (ev[j] >= 0 && ev[j] < E) atomicAdd(&cnt[ev[j]], 1);
+    __syncthreads();
+    for (int i = tid; i < E; i += DT) slices[(size_t)blockIdx.x * E + i] = cnt[i];
+}
+
+__global__ __launch_bounds__(DT) void prefill_scatter_kernel(
+    const int32_t* __restrict__ ids, int T, int k, int E, int has_shared, int H, int n_slices,
+    const int32_t* __restrict__ slices, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ ntiles, Tile* __restrict__ tiles, int32_t* __restrict__ order, float* __restrict__ y) {
+    __shared__ int cnt[1025];   // the experts' totals
+    __shared__ int off[1026];   // their offsets in the order
+    __shared__ int foff[1026];  // their full tiles' offsets in the tile list
+    __shared__ int cur[1024];   // this slice's cursors
+    __shared__ int bucket[9];   // partial tiles by row-block count (8 - n blocks)
+    const int M = E + has_shared, S = k + has_shared;
+    const int tid = threadIdx.x, b = blockIdx.x;
+    if (tid < 9) bucket[tid] = 0;
+    const long long P = (long long)T * k, p0 = (long long)b * SLICE;
+    int ev[DPT];
+#pragma unroll
+    for (int j = 0; j < DPT; ++j) {
+        const long long p = p0 + j * DT + tid;
+        ev[j] = p < P ? ids[p] : -1;
+    }
+    for (int e = tid; e < E; e += DT) {
+        int tot = 0, base = 0;
+#pragma unroll 8
+        for (int s2 = 0; s2 < n_slices; ++s2) {
+            const int c = slices[(size_t)s2 * E + e];
+            base += s2 < b ? c : 0;
+            tot += c;
         }
-        cnt[e] = run;
+        cnt[e] = tot;
+        cur[e] = base;
     }
     if (has_shared && tid == 0) cnt[E] = T;
     __syncthreads();
-    for (int e = tid; e < M; e += SETUP_THREADS) {
-        const int rem = cnt[e] % BM;
-        if (rem) atomicAdd(&bucket[8 - (rem + 15) / 16], 1);
-    }
     if (tid < 64) {  // exclusive scans of the rows and the full tiles over the experts
         const int per = (M + 63) / 64;
         const int beg = tid * per, end = min(M, beg + per);
         int lc = 0, lt = 0;
-        for (int i = beg; i < end; ++i) {
-            lc += cnt[i];
-            lt += cnt[i] / BM;
+        for (int i2 = beg; i2 < end; ++i2) {
+            lc += cnt[i2];
+            lt += cnt[i2] / BM;
         }
         int ic = lc, it = lt;
         for (int d = 1; d < 64; d <<= 1) {
@@ -271,11 +287,11 @@ __global__ __launch_bounds__(SETUP_THREADS) void prefill_setup_kernel(
             }
         }
         int rc = ic - lc, rt = it - lt;
-        for (int i = beg; i < end; ++i) {
-            off[i] = rc;
-            foff[i] = rt;
-            rc += cnt[i];
-            rt += cnt[i] / BM;
+        for (int i2 = beg; i2 < end; ++i2) {
+            off[i2] = rc;
+            foff[i2] = rt;
+            rc += cnt[i2];
+            rt += cnt[i2] / BM;
         }
         if (tid == 63) {
             off[M] = ic;
@@ -283,68 +299,64 @@ __global__ __launch_bounds__(SETUP_THREADS) void prefill_setup_kernel(
         }
     }
     __syncthreads();
-    if (tid == 0) {
-        int run = foff[M];
-        for (int b = 0; b < 9; ++b) {
-            const int c = bucket[b];
-            bucket[b] = run;
-            run += c;
+    for (int e = tid; e < E; e += DT) cur[e] += off[e];
+    if (b == 0) {
+        for (int e = tid; e < M; e += DT) {
+            const int rem = cnt[e] % BM;
+            if (rem) atomicAdd(&bucket[8 - (rem + 15) / 16], 1);
         }
-        *ntiles = run;
-        offsets[M] = off[M];
-    }
-    __syncthreads();
-    for (int e = tid; e < M; e += SETUP_THREADS) {
-        counts[e] = cnt[e];
-        offsets[e] = off[e];
-        const int nfull = cnt[e] / BM, rem = cnt[e] % BM;
-        for (int j = 0; j < nfull; ++j) {
-            Tile tl;
-            tl.expert = e;
-            tl.row0 = off[e] + j * BM;
-            tl.nrows = BM;
-            tl.pad = 0;
-            tiles[foff[e] + j] = tl;
-        }
-        if (rem) {
-            Tile tl;
-            tl.expert = e;
-            tl.row0 = off[e] + nfull * BM;
-            tl.nrows = rem;
-            tl.pad = 0;
-            tiles[atomicAdd(&bucket[8 - (rem + 15) / 16], 1)] = tl;
-        }
-        if (e < E) {
-#pragma unroll
-            for (int w = 0; w < SETUP_WAVES; ++w) hist[w][e] += off[e];  // cursors
-        }
-    }
-    if (has_shared)
-        for (int t = tid; t < T; t += SETUP_THREADS) order[off[E] + t] = t * S + k;
-    __syncthreads();
-    for (long long p0 = 0; p0 < P; p0 += (long long)SETUP_THREADS * PB) {
-        int ev[PB];
-#pragma unroll
-        for (int j = 0; j < PB; ++j) {
-            const long long p = p0 + j * SETUP_THREADS + tid;
-            ev[j] = p < P ? ids[p] : 0;
-        }
-        // token and slot of pick p0 + tid; when k divides the block size, each later
-        // pick of the batch is SETUP_THREADS / k tokens further at the same slot
-        const bool even = SETUP_THREADS % k == 0;
-        const int tb = (int)((p0 + tid) / k), sb = (int)((p0 + tid) % k);
-#pragma unroll
-        for (int j = 0; j < PB; ++j) {
-            const long long p = p0 + j * SETUP_THREADS + tid;
-            if (p >= P) continue;
-            const int t = even ? tb + j * (SETUP_THREADS / k) : (int)(p / k);
-            const int sl = even ? sb : (int)(p % k), e = ev[j];
-            if (e >= 0 && e < E) {
-                order[atomicAdd(&hist[wave][e], 1)] = t * S + sl;
-            } else {
-                float* yr = y + ((size_t)t * S + sl) * H;
-                for (int n = 0; n < H; ++n) yr[n] = 0.f;
+        __syncthreads();
+        if (tid == 0) {
+            int run = foff[M];
+            for (int q = 0; q < 9; ++q) {
+                const int c = bucket[q];
+                bucket[q] = run;
+                run += c;
             }
+            *ntiles = run;
+            offsets[M] = off[M];
+        }
+        __syncthreads();
+        for (int e = tid; e < M; e += DT) {
+            counts[e] = cnt[e];
+            offsets[e] = off[e];
+            const int nfull = cnt[e] / BM, rem = cnt[e] % BM;
+            for (int q = 0; q < nfull; ++q) {
+                Tile tl;
+                tl.expert = e;
+                tl.row0 = off[e] + q * BM;
+                tl.nrows = BM;
+                tl.pad = 0;
+                tiles[foff[e] + q] = tl;
+            }
+            if (rem) {
+                Tile tl;
+                tl.expert = e;
+                tl.row0 = off[e] + nfull * BM;
+                tl.nrows = rem;
+                tl.pad = 0;
+                tiles[atomicAdd(&bucket[8 - (rem + 15) / 16], 1)] = tl;
+            }
+        }
+        if (has_shared)
+            for (int t = tid; t < T; t += DT) order[off[E] + t] = t * S + k;
+    }
+    __syncthreads();
+    // token and slot of pick p0 + tid; when k divides DT, each later pick of this
+    // thread is DT / k tokens further at the same slot
+    const bool even = DT % k == 0;
+    const int tb = (int)((p0 + tid) / k), sb = (int)((p0 + tid) % k);
+#pragma unroll
+    for (int j = 0; j < DPT; ++j) {
+        const long long p = p0 + j * DT + tid;
+        if (p >= P) continue;
+        const int t = even ? tb + j * (DT / k) : (int)(p / k);
+        const int sl = even ? sb : (int)(p % k), e = ev[j];
+        if (e >= 0 && e < E) {
+            order[atomicAdd(&cur[e], 1)] = t * S + sl;
+        } else {
+            float* yr = y + ((size_t)t * S + sl) * H;
+            for (int n = 0; n < H; ++n) yr[n] = 0.f;
         }
     }
 }
@@ -922,10 +934,14 @@ extern "C" moe_status moe_experts_prefill(const moe_shape* shape, const void* ex
     uint16_t* xs_x = (uint16_t*)(w + W.xs_x);
     uint16_t* xs_h = (uint16_t*)(w + W.xs_h);
     const long long nsum = (long long)T * W.gs_x;
-    hipLaunchKernelGGL(prefill_setup_kernel, dim3((unsigned)(1 + (nsum + SETUP_THREADS - 1) / SETUP_THREADS)),
-                       dim3(SETUP_THREADS), 0, hs, ids, T, sh.top_k, sh.n_experts, sh.has_shared, H, counts, offsets,
-                       ntiles, tiles, order, y, x, W.gs_x, xs_x);
-    if ((st = check_launch("prefill_setup_kernel")) != MOE_OK) return st;
+    int32_t* slices = (int32_t*)(w + W.slices);
+    const long long P = (long long)T * sh.top_k;
+    hipLaunchKernelGGL(prefill_count_kernel, dim3((unsigned)(W.n_slices + (nsum + DT - 1) / DT)), dim3(DT), 0, hs, ids,
+                       P, sh.n_experts, W.n_slices, slices, x, T, H, W.gs_x, xs_x);
+    if ((st = check_launch("prefill_count_kernel")) != MOE_OK) return st;
+    hipLaunchKernelGGL(prefill_scatter_kernel, dim3((unsigned)W.n_slices), dim3(DT), 0, hs, ids, T, sh.top_k,
+                       sh.n_experts, sh.has_shared, H, W.n_slices, slices, counts, offsets, ntiles, tiles, order, y);
+    if ((st = check_launch("prefill_scatter_kernel")) != MOE_OK) return st;
     GemmArgs ga;
     ga.packed = (const uint8_t*)experts_packed;
     ga.L = L;
