@@ -594,19 +594,35 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
         constexpr int NM = decltype(nm_tag)::value;
         const size_t plane = (size_t)(GATEUP ? a.T : a.T * S) * a.gs_a;
         for (int kb = 0; kb < (G + KG - 1) / KG; ++kb) {
+            // k slot 8 lg + i of the step: group 4i + lg for gate/up (whose x row sums are
+            // stored in that order), so the 16 lanes of a row block read the four
+            // consecutive groups' words of their blocks, 64-byte runs; group 4 lg + i for
+            // down. Every lane loads a valid word (groups past G read the last group,
+            // blocks past the matrix block 0) and zeroes afterwards what it must not use
+            // (scale 0, bias 0: c = 0). The empty asm statements keep the loads ahead of
+            // that test: a load the compiler moves under it gets a branch of its own and
+            // a wait for every outstanding load, so the loads would go out one at a time.
             uint32_t w[NCS][GPL];
 #pragma unroll
             for (int cs = 0; cs < NCS; ++cs) {
                 const int br = cs * 64 + 16 * wave + lc;
 #pragma unroll
                 for (int i = 0; i < GPL; ++i) {
-                    // k slot 8 lg + i of the step: group 4i + lg for gate/up (whose x row
-                    // sums are stored in that order), so the 16 lanes of a row block read
-                    // the four consecutive groups' words of their blocks, 64-byte runs;
-                    // group 4 lg + i for down
                     const int g = GATEUP ? KG * kb + 4 * i + lg : KG * kb + GPL * lg + i;
-                    w[cs][i] = (g < G && brow_ok(br)) ? *reinterpret_cast<const uint32_t*>(ebase + brow_sb_word(br, g))
-                                                      : 0u;  // scale 0, bias 0: c = 0
+                    w[cs][i] = *reinterpret_cast<const uint32_t*>(ebase + brow_sb_word(br, g < G ? g : G - 1));
+                }
+            }
+#pragma unroll
+            for (int cs = 0; cs < NCS; ++cs)
+#pragma unroll
+                for (int i = 0; i < GPL; ++i) asm volatile("" : "+v"(w[cs][i]));
+#pragma unroll
+            for (int cs = 0; cs < NCS; ++cs) {
+                const bool ok = brow_ok(cs * 64 + 16 * wave + lc);
+#pragma unroll
+                for (int i = 0; i < GPL; ++i) {
+                    const int g = GATEUP ? KG * kb + 4 * i + lg : KG * kb + GPL * lg + i;
+                    if (!(ok && g < G)) w[cs][i] = 0u;
                 }
             }
             frag_t ch[NCS], cm[NCS], cl[NCS];
