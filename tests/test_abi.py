@@ -97,6 +97,11 @@ def test_host_argument_checks_launch_nothing(moe):
     assert st == moe.ERR_INVALID_ARG
     st = moe.raw_call("moe_combine", byref(sh), v(P), v(P), None, 1, None, v(P), None)
     assert st == moe.ERR_INVALID_ARG
+    # combine: out and residual must be 16-byte aligned like every device pointer
+    st = moe.raw_call("moe_combine", byref(sh), v(P), v(P), v(P), 1, None, v(P + 8), None)
+    assert st == moe.ERR_INVALID_ARG
+    st = moe.raw_call("moe_combine", byref(sh), v(P), v(P), v(P), 1, v(P + 2), v(P), None)
+    assert st == moe.ERR_INVALID_ARG
     # refused formats never reach a kernel
     st = moe.raw_call("moe_route", byref(_big(moe, bits=8)), v(P), None, v(P), 1, v(P), v(P), v(P), v(P), None)
     assert st == moe.ERR_UNSUPPORTED
