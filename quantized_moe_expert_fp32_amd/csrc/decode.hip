@@ -347,12 +347,14 @@ __global__ __launch_bounds__(256) void decode_down_kernel(const uint8_t* __restr
 }
 
 // ---------------------------------------------------------------- single-launch decode layer
-// Control words in the workspace. A launch publishes with tag epoch + 1; the last
-// workgroup to leave stores the new epoch, so stale words of earlier launches never
-// carry the current tag and nothing has to be cleared between launches.
+// Control words in the workspace. A launch publishes with tag epoch + 1. Each
+// workgroup counts itself in once all of its wavefronts have read the epoch; the
+// one that counts last stores the new epoch as it leaves, so stale words of earlier
+// launches never carry the current tag and nothing has to be cleared between
+// launches.
 struct DecodeCtl {
     unsigned epoch;       // tag of the last completed launch
-    unsigned exit_count;  // workgroups finished (back to zero after each launch)
+    unsigned exit_count;  // workgroups that have read the epoch (back to zero after each launch)
     unsigned error;       // a bounded poll timed out (sticky)
     unsigned pad;
 };
@@ -590,7 +592,6 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
     }
     if (a.stage_x) stage_x(a.x, T, H, s_x, s_xs);
     __syncthreads();
-
     // the shared expert's row pairs are tasks 0 .. npair-1 of phase B
     PairLoads<CPL> cur;
     bool have = false;
@@ -599,6 +600,16 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
         pair_load<CPL>(a.experts, a.L, H, E, j0, lane, cur);
         have = true;
     }
+    // Every wavefront of this workgroup has read the epoch (the barrier above waited
+    // for its loads), so the workgroup may count itself in now. With fewer tokens
+    // than wavefronts the top wavefront selects nothing and does it here, after its
+    // first task's loads: the count's round trip then overlaps the work rather than
+    // a wavefront's next wait (the memory counter retires in order). Otherwise the
+    // count waits for the exit. The workgroup that counted last publishes the next
+    // epoch on its way out.
+    const bool count_early = T < LW;
+    unsigned counted = 0u;
+    if (count_early && tid == LTH - 64) counted = atomicAdd(&ctl->exit_count, 1u);
 
     // ---- S: selection, distinct experts, token lists
     if (wave < T) {
@@ -729,10 +740,11 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
         dhave = nhave;
     }
 
-    // ---- exit: the last workgroup out publishes the new epoch
+    // ---- exit: the workgroup that counted itself in last publishes the new epoch
     __syncthreads();
-    if (tid == 0) {
-        if (atomicAdd(&ctl->exit_count, 1u) == (unsigned)G - 1) {
+    if (tid == LTH - 64) {
+        if (!count_early) counted = atomicAdd(&ctl->exit_count, 1u);
+        if (counted == (unsigned)G - 1) {
             atomicExch(&ctl->exit_count, 0u);
             atomicExch(&ctl->epoch, tag);
         }
