@@ -613,7 +613,9 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
 
     // ---- S: selection, distinct experts, token lists
     if (wave < T) {
-        const LogitSrc src{nullptr, a.tlogits + (size_t)wave * R, tag, &ctl->error, false};
+        // up to four tokens: all of a lane's logit words reloaded together in each
+        // polling round (few wavefronts poll); more: only the stale ones
+        const LogitSrc src{nullptr, a.tlogits + (size_t)wave * R, tag, &ctl->error, false, T <= 4};
         select_token<VPL>(src, E, k, hs_, lane, s_ids[wave], s_w[wave], &s_wsh[wave]);
     }
     __syncthreads();

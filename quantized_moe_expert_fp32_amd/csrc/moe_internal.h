@@ -202,6 +202,40 @@ __device__ __forceinline__ void load_tagged_many(const uint64_t* p, int stride, 
     for (int j = 0; j < N; ++j) out[j] = (uint32_t)v[j];
 }
 
+// As load_tagged_many, but every round reloads all n words together (0 <= n <= N;
+// p[0] must be readable even when n = 0; out[j] = 0 for j >= n). A word that
+// carries the launch's tag never changes again within the launch, so reloading it
+// is harmless. The loads are unconditional and the empty asm statements keep them
+// together; with a per-word test the compiler gives each reload a branch and a
+// wait of its own, one round trip per stale word. For short lists of words that
+// few wavefronts wait on: the decode layer's selection with few tokens. With many
+// polling wavefronts the extra loads in flight slow the producers more than the
+// serial re-polls cost (measured at 16 tokens per launch).
+template <int N>
+__device__ __forceinline__ void load_tagged_batch(const uint64_t* p, int stride, int n, uint32_t tag, unsigned* err,
+                                                  uint32_t* out) {
+    uint64_t v[N];
+    for (unsigned it = 0;; ++it) {
+#pragma unroll
+        for (int j = 0; j < N; ++j)
+            v[j] = __hip_atomic_load(const_cast<uint64_t*>(p + (size_t)(j < n ? j : 0) * stride), __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int j = 0; j < N; ++j) asm volatile("" : "+v"(v[j]));
+        bool ok = true;
+#pragma unroll
+        for (int j = 0; j < N; ++j) ok = ok && (j >= n || (uint32_t)(v[j] >> 32) == tag);
+        if (ok) break;
+        if (it >= SPIN_LIMIT) {
+            atomicOr(err, 1u);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+#pragma unroll
+    for (int j = 0; j < N; ++j) out[j] = j < n ? (uint32_t)v[j] : 0u;
+}
+
 // DPP move of a 32-bit value (every lane must be active).
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
@@ -251,6 +285,7 @@ struct LogitSrc {
     uint32_t tag;
     unsigned* err;
     bool coherent;
+    bool batch;  // tagged: reload every word in each polling round (load_tagged_batch)
     __device__ __forceinline__ uint32_t get(int i) const {
         if (tagged) return load_tagged_wait(tagged + i, tag, err);
         if (coherent) return load_coherent(reinterpret_cast<const uint32_t*>(plain) + i);

@@ -49,7 +49,10 @@ __device__ __forceinline__ void select_token(const LogitSrc& lr, int E, int k, i
         // this lane's logits lane + 64 j < E, and the shared gate (index E) in the same batch
         const int R = E + (has_shared ? 1 : 0);
         const int n = lane < R ? (R - 1 - lane) / 64 + 1 : 0;
-        load_tagged_many<VPL + 1>(lr.tagged + lane, 64, n, lr.tag, lr.err, raw);
+        if (lr.batch)
+            load_tagged_batch<VPL + 1>(lr.tagged + (lane < R ? lane : 0), 64, n, lr.tag, lr.err, raw);
+        else
+            load_tagged_many<VPL + 1>(lr.tagged + lane, 64, n, lr.tag, lr.err, raw);
     } else {
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
