@@ -665,6 +665,19 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
     const int per = (nC + G - 1) / G, c0 = wg * per, c1 = min(nC, c0 + per);
     DnLoadsL dcur;
     bool dhave = false;
+    // One token: there are fewer gate/up tasks than wavefronts (9 * 256 of 16 * 256
+    // at hidden 2048, inter 512, top-8 plus shared), and the wavefronts without a task would put their down loads and h polls ahead of the
+    // others' task loads in the CU's memory pipeline. So every wavefront issues its
+    // first task's loads before any wavefront of the workgroup goes on to phase C;
+    // the barrier waits for the issue only, not for the data. With more tokens every
+    // wavefront has a task and the barrier measured slower.
+    if constexpr (TT == 1) {
+        if (!have && j0 < nB) {
+            pair_load<CPL>(a.experts, a.L, H, s_dexp[j0 / npair], j0 % npair, lane, cur);
+            have = true;
+        }
+        __builtin_amdgcn_s_barrier();
+    }
     for (int j = j0; j < nB; j += G * LW) {
         const int dd = j / npair, ip = j % npair;
         if (!have) pair_load<CPL>(a.experts, a.L, H, s_dexp[dd], ip, lane, cur);
