@@ -554,6 +554,8 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
     __shared__ int32_t s_ids[16][16];
     __shared__ uint16_t s_w[16][16];
     __shared__ uint16_t s_wsh[16];
+    __shared__ uint32_t s_raw[16][16];  // the picks' fp32 logit bits, per token
+    __shared__ uint32_t s_gbits[16];    // the shared gate's fp32 logit bits, per token
     __shared__ uint32_t s_used[32];
     __shared__ int32_t s_upre[32];
     __shared__ int32_t s_dexp[MAXD];
@@ -605,59 +607,77 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
     // than wavefronts the top wavefront selects nothing and does it here, after its
     // first task's loads: the count's round trip then overlaps the work rather than
     // a wavefront's next wait (the memory counter retires in order). Otherwise the
-    // count waits for the exit. The workgroup that counted last publishes the next
-    // epoch on its way out.
+    // count waits for the exit. The workgroup that counted last resets the count and
+    // publishes the next epoch: every workgroup has read the epoch by then, and the
+    // next launch starts only after this one ends. An early count is settled after
+    // phase B, when its round trip is long over.
     const bool count_early = T < LW;
     unsigned counted = 0u;
     if (count_early && tid == LTH - 64) counted = atomicAdd(&ctl->exit_count, 1u);
 
-    // ---- S: selection, distinct experts, token lists
+    // ---- S: selection (the ids; the weights follow the first gate/up loads),
+    // distinct experts, token lists
     if (wave < T) {
         // up to four tokens: all of a lane's logit words reloaded together in each
         // polling round (few wavefronts poll); more: only the stale ones
         const LogitSrc src{nullptr, a.tlogits + (size_t)wave * R, tag, &ctl->error, false, T <= 4};
-        select_token<VPL>(src, E, k, hs_, lane, s_ids[wave], s_w[wave], &s_wsh[wave]);
+        const SelState sel = select_ids<VPL>(src, E, k, hs_, lane, s_ids[wave]);
+        if (lane < k) s_raw[wave][lane] = sel.raw;
+        if (lane == 0) s_gbits[wave] = sel.gbits;
+        if (wg == 0 && lane < k) a.ids[wave * k + lane] = (int32_t)sel.id;
+        if constexpr (TT == 1) {
+            // one token: its k picks are k distinct experts (k <= E), listed in pick
+            // order after the shared expert
+            if (lane < k) {
+                s_dexp[hs_ + lane] = (int32_t)sel.id;
+                s_dcnt[hs_ + lane] = 1;
+                s_dtok[hs_ + lane][0] = (uint16_t)(lane << 5);
+            }
+            if (lane == 0) {
+                if (hs_) {
+                    s_dexp[0] = E;
+                    s_dcnt[0] = 1;
+                    s_dtok[0][0] = (uint16_t)(k << 5);
+                }
+                s_nd = hs_ + k;
+            }
+        }
     }
     __syncthreads();
-    if (tid < T * k) {
-        const int e = s_ids[tid / k][tid % k];
-        atomicOr(&s_used[e >> 5], 1u << (e & 31));
-    }
-    if (wg == 0) {
+    if constexpr (TT != 1) {
         if (tid < T * k) {
-            a.ids[tid] = s_ids[tid / k][tid % k];
-            a.w[tid] = s_w[tid / k][tid % k];
+            const int e = s_ids[tid / k][tid % k];
+            atomicOr(&s_used[e >> 5], 1u << (e & 31));
         }
-        if (hs_ && tid < T) a.wsh[tid] = s_wsh[tid];
-    }
-    __syncthreads();
-    if (wave == 0) {
-        const int nword = (E + 31) / 32;
-        const uint32_t m = lane < nword ? s_used[lane] : 0u;
-        const int c = __popc(m);
-        int incl = c;
-        for (int dd = 1; dd < 32; dd <<= 1) {
-            const int o = __shfl_up(incl, dd);
-            if (lane >= dd) incl += o;
+        __syncthreads();
+        if (wave == 0) {
+            const int nword = (E + 31) / 32;
+            const uint32_t m = lane < nword ? s_used[lane] : 0u;
+            const int c = __popc(m);
+            int incl = c;
+            for (int dd = 1; dd < 32; dd <<= 1) {
+                const int o = __shfl_up(incl, dd);
+                if (lane >= dd) incl += o;
+            }
+            int pos = hs_ + incl - c;
+            if (lane < nword) s_upre[lane] = pos;
+            for (uint32_t mm = m; mm; mm &= mm - 1) s_dexp[pos++] = 32 * lane + __builtin_ctz(mm);
+            if (lane == 31) s_nd = hs_ + incl;
+            if (lane == 0 && hs_) s_dexp[0] = E;
         }
-        int pos = hs_ + incl - c;
-        if (lane < nword) s_upre[lane] = pos;
-        for (uint32_t mm = m; mm; mm &= mm - 1) s_dexp[pos++] = 32 * lane + __builtin_ctz(mm);
-        if (lane == 31) s_nd = hs_ + incl;
-        if (lane == 0 && hs_) s_dexp[0] = E;
+        __syncthreads();
+        if (tid < T * k) {
+            const int t = tid / k, sl = tid % k, e = s_ids[t][sl];
+            const int dd = s_upre[e >> 5] + __popc(s_used[e >> 5] & ((1u << (e & 31)) - 1u));
+            const int p = atomicAdd(&s_dcnt[dd], 1);
+            s_dtok[dd][p] = (uint16_t)(t | (sl << 5));
+        }
+        if (hs_ && tid < T) {
+            s_dtok[0][tid] = (uint16_t)(tid | (k << 5));
+            if (tid == 0) s_dcnt[0] = T;
+        }
+        __syncthreads();
     }
-    __syncthreads();
-    if (tid < T * k) {
-        const int t = tid / k, sl = tid % k, e = s_ids[t][sl];
-        const int dd = s_upre[e >> 5] + __popc(s_used[e >> 5] & ((1u << (e & 31)) - 1u));
-        const int p = atomicAdd(&s_dcnt[dd], 1);
-        s_dtok[dd][p] = (uint16_t)(t | (sl << 5));
-    }
-    if (hs_ && tid < T) {
-        s_dtok[0][tid] = (uint16_t)(tid | (k << 5));
-        if (tid == 0) s_dcnt[0] = T;
-    }
-    __syncthreads();
 
     // ---- B: gate/up row pairs of the distinct experts
     const int nB = s_nd * npair;
@@ -665,18 +685,32 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
     const int per = (nC + G - 1) / G, c0 = wg * per, c1 = min(nC, c0 + per);
     DnLoadsL dcur;
     bool dhave = false;
-    // One token: there are fewer gate/up tasks than wavefronts (9 * 256 of 16 * 256
-    // at hidden 2048, inter 512, top-8 plus shared), and the wavefronts without a task would put their down loads and h polls ahead of the
-    // others' task loads in the CU's memory pipeline. So every wavefront issues its
-    // first task's loads before any wavefront of the workgroup goes on to phase C;
-    // the barrier waits for the issue only, not for the data. With more tokens every
+    // Every wavefront with a task issues its first task's loads here. With one token
+    // there are fewer tasks than wavefronts (9 * 256 of 16 * 256 at hidden 2048,
+    // inter 512, top-8 plus shared), and the wavefronts without one would put their
+    // down loads and h polls ahead of the others' task loads in the CU's memory
+    // pipeline; so no wavefront goes on to phase C before all have issued (the
+    // barrier waits for the issue only, not for the data). With more tokens every
     // wavefront has a task and the barrier measured slower.
-    if constexpr (TT == 1) {
-        if (!have && j0 < nB) {
-            pair_load<CPL>(a.experts, a.L, H, s_dexp[j0 / npair], j0 % npair, lane, cur);
-            have = true;
+    if (!have && j0 < nB) {
+        pair_load<CPL>(a.experts, a.L, H, s_dexp[j0 / npair], j0 % npair, lane, cur);
+        have = true;
+    }
+    if constexpr (TT == 1) __builtin_amdgcn_s_barrier();
+    // The pick weights are read only by the combine, after phase C's first barrier;
+    // the selecting wavefronts compute them while their first task's loads are out
+    // (their inputs wait in LDS, not in registers, across the issue).
+    if (wave < T) {
+        const SelState sel{0u, lane < k ? s_raw[wave][lane] : 0u, s_gbits[wave]};
+        const uint16_t wb = select_weights(sel, k, lane);
+        if (lane < k) {
+            s_w[wave][lane] = wb;
+            if (wg == 0) a.w[wave * k + lane] = wb;
         }
-        __builtin_amdgcn_s_barrier();
+        if (hs_ && lane == k) {
+            s_wsh[wave] = wb;
+            if (wg == 0) a.wsh[wave] = wb;
+        }
     }
     for (int j = j0; j < nB; j += G * LW) {
         const int dd = j / npair, ip = j % npair;
@@ -690,6 +724,11 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
             const uint32_t hp = pair_finish<CPL>(cur, H, xs, lane);
             if (lane == 0) store_tagged(a.th + ((size_t)t * S + sl) * npair + ip, tag, hp);
         }
+    }
+
+    if (count_early && tid == LTH - 64 && counted == (unsigned)G - 1) {
+        atomicExch(&ctl->exit_count, 0u);
+        atomicExch(&ctl->epoch, tag);
     }
 
     // ---- C: down items with the combine
@@ -755,11 +794,11 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
         dhave = nhave;
     }
 
-    // ---- exit: the workgroup that counted itself in last publishes the new epoch
-    __syncthreads();
-    if (tid == LTH - 64) {
-        if (!count_early) counted = atomicAdd(&ctl->exit_count, 1u);
-        if (counted == (unsigned)G - 1) {
+    // ---- exit: a workgroup that did not count itself in early does it now; the one
+    // that counted last publishes the new epoch
+    if (!count_early) {
+        __syncthreads();
+        if (tid == LTH - 64 && atomicAdd(&ctl->exit_count, 1u) == (unsigned)G - 1) {
             atomicExch(&ctl->exit_count, 0u);
             atomicExch(&ctl->epoch, tag);
         }

@@ -39,11 +39,21 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
 // single lane holding it is the winner, and if several lanes hold it, the one
 // whose leading key has the lowest expert id (a second DPP reduction). The winner
 // drops its leading key. This realises the order (logit desc, id asc).
-// Outputs: sel_id[i] and sel_w[i] (bf16 bits) for i < k, written by lanes
-// 0..k-1; *sel_wsh by lane k, whose exp and division run beside the picks'.
+// select_ids writes sel_id[i] for i < k (lanes 0..k-1) and returns what the
+// weights need; select_weights then gives lane i < k the bf16 bits of pick i's
+// weight and lane k the shared weight's (its exp and division run beside the
+// picks'). The weights are needed only by the combine, so a caller may compute
+// them later than the ids. select_token does both and stores sel_w[i] (i < k)
+// and *sel_wsh.
+struct SelState {
+    uint32_t id;     // lane i < k: pick i's expert id
+    uint32_t raw;    // lane i < k: pick i's fp32 logit bits
+    uint32_t gbits;  // every lane: the shared gate's fp32 logit bits
+};
+
 template <int VPL>
-__device__ __forceinline__ void select_token(const LogitSrc& lr, int E, int k, int has_shared, int lane,
-                                             int32_t* sel_id, uint16_t* sel_w, uint16_t* sel_wsh) {
+__device__ __forceinline__ SelState select_ids(const LogitSrc& lr, int E, int k, int has_shared, int lane,
+                                               int32_t* sel_id) {
     uint32_t raw[VPL + 1];
     if (lr.tagged) {
         // this lane's logits lane + 64 j < E, and the shared gate (index E) in the same batch
@@ -125,19 +135,28 @@ __device__ __forceinline__ void select_token(const LogitSrc& lr, int E, int k, i
         }
     }
     my_id = my_id < (uint32_t)E ? my_id : (uint32_t)(E - 1);
-    const double li = lane < k ? (double)__uint_as_float(my_raw) : 0.0;
+    if (lane < k) sel_id[lane] = (int32_t)my_id;
+    return SelState{my_id, my_raw, gbits};
+}
+
+__device__ __forceinline__ uint16_t select_weights(const SelState& st, int k, int lane) {
+    const double li = lane < k ? (double)__uint_as_float(st.raw) : 0.0;
     const double l0 = readlane_f64(li, 0);
     // lanes < k: exp(l_i - l_top); lane k: the shared gate's exp(-g), g = bf16(gate)
-    const double g = (double)bf16_to_f32(f32_to_bf16(__uint_as_float(gbits)));
+    const double g = (double)bf16_to_f32(f32_to_bf16(__uint_as_float(st.gbits)));
     const double ex = exp(lane < k ? li - l0 : -g);
     double sum = 0.0;
     for (int j = 0; j < k; ++j) sum += readlane_f64(ex, j);
     const double num = lane < k ? ex : 1.0, den = lane < k ? sum : 1.0 + ex;
-    const uint16_t wb = (uint16_t)f64_to_bf16(num / den);
-    if (lane < k) {
-        sel_id[lane] = (int32_t)my_id;
-        sel_w[lane] = wb;
-    }
+    return (uint16_t)f64_to_bf16(num / den);
+}
+
+template <int VPL>
+__device__ __forceinline__ void select_token(const LogitSrc& lr, int E, int k, int has_shared, int lane,
+                                             int32_t* sel_id, uint16_t* sel_w, uint16_t* sel_wsh) {
+    const SelState st = select_ids<VPL>(lr, E, k, has_shared, lane, sel_id);
+    const uint16_t wb = select_weights(st, k, lane);
+    if (lane < k) sel_w[lane] = wb;
     if (has_shared && lane == k) *sel_wsh = wb;
 }
 
