@@ -587,7 +587,18 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
     // ---- A: router rows, one wavefront per (row, token); the per-lane order of the
     // products and the reduction tree are those of router_row for any token count,
     // so the logits equal the staged router's bit for bit
-    if (wtop < T) {
+    // Rows beyond the first G (the shared gate's at 256 experts) go to further
+    // wavefronts when they fit above the selecting ones, so that no wavefront
+    // computes two rows one after the other.
+    const int nrw = (R + G - 1) / G;
+    if ((nrw + 1) * T <= LW) {
+        if (wtop < nrw * T) {
+            const int r = wg + G * (wtop / T);
+            if (r < R)
+                router_row<1, AFF8>(a.router, a.logit_bias, a.x, wtop % T, 1, H, R, E, r, lane, a.logits, false,
+                                    a.tlogits, tag);
+        }
+    } else if (wtop < T) {
         for (int r = wg; r < R; r += G)
             router_row<1, AFF8>(a.router, a.logit_bias, a.x, wtop, 1, H, R, E, r, lane, a.logits, false, a.tlogits,
                                 tag);
