@@ -166,7 +166,8 @@ moe_status moe_route_from_logits(const moe_shape* shape, const float* logits, in
  *   h = bf16(silu(x Wg_e^T) * (x Wu_e^T))   (SwiGLU; the bf16 rounding is a reading)
  *   y[t][s][:] = h Wd_e^T                   (fp32, not rounded to bf16: [P3-build])
  * ws: device scratch of moe_decode_workspace_bytes(shape, T) bytes (holds h and,
- * for moe_decode_layer, one counter word). Each row's result does not depend on T
+ * for moe_decode_layer, its control words and the tagged logit and h words it
+ * hands between workgroups). Each row's result does not depend on T
  * or on the other rows. Expert ids outside [0, E) give zero y rows. */
 size_t moe_decode_workspace_bytes(const moe_shape* shape, int32_t T);
 moe_status moe_experts_decode(const moe_shape* shape, const void* experts_packed,

@@ -65,6 +65,14 @@ __host__ __device__ inline size_t piece_off(int ch) { return (size_t)(ch >> 1) *
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// The XCD (accelerator complex die) this wavefront runs on, 0..7 on MI355X, from
+// the XCC_ID hardware register.
+__device__ __forceinline__ unsigned xcd_id() {
+    unsigned v;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+    return v & 0xFu;
+}
+
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // ------------------------------------------------------------------ device side

@@ -192,11 +192,13 @@ __device__ __forceinline__ void load_words(const uint16_t* p, uint32_t* out) {
 // exact in fp64 and accumulate in fp64 in a fixed order (lane-sequential, then a
 // butterfly), so a token's logits do not depend on T or on the other tokens.
 // The logit of token t is written to logits[t][r] (coherently when `coherent`)
-// and, when `tagged` is given, published to tagged[t][r] with tag `tag`.
+// and, when `tagged` is given, published with tag `tag` to the two copies
+// tagged[t * tstride + r] and tagged[t * tstride + tcopy + r].
 template <int TT, bool AFF8>
 __device__ __forceinline__ void router_row(const uint8_t* __restrict__ router, const float* __restrict__ logit_bias,
                                            const uint16_t* __restrict__ x, int t0, int nt, int H, int R, int E, int r,
-                                           int lane, float* logits, bool coherent, uint64_t* tagged, uint32_t tag) {
+                                           int lane, float* logits, bool coherent, uint64_t* tagged, uint32_t tag,
+                                           size_t tstride = 0, size_t tcopy = 0) {
     double acc[TT];
 #pragma unroll
     for (int t = 0; t < TT; ++t) acc[t] = 0.0;
@@ -299,7 +301,11 @@ __device__ __forceinline__ void router_row(const uint8_t* __restrict__ router, c
                     store_coherent(reinterpret_cast<uint32_t*>(logits) + o, v);
                 else
                     reinterpret_cast<uint32_t*>(logits)[o] = v;
-                if (tagged) store_tagged(tagged + o, tag, v);
+                if (tagged) {
+                    uint64_t* p = tagged + (size_t)(t0 + t) * tstride + r;
+                    store_tagged(p, tag, v);
+                    store_tagged(p + tcopy, tag, v);
+                }
             }
     }
 }
