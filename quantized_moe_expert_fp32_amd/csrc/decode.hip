@@ -557,6 +557,7 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
     __shared__ uint16_t s_wsh[16];
     __shared__ uint32_t s_raw[16][16];  // the picks' fp32 logit bits, per token
     __shared__ uint32_t s_gbits[16];    // the shared gate's fp32 logit bits, per token
+    __shared__ int s_race[16];          // per token: the wavefront that won its polling race
     __shared__ uint32_t s_used[32];
     __shared__ int32_t s_upre[32];
     __shared__ int32_t s_dexp[MAXD];
@@ -577,13 +578,21 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
     uint16_t* s_x = reinterpret_cast<uint16_t*>(lds_dyn + (size_t)S * I / 2);      // [T][H] bf16
     float* s_xs = reinterpret_cast<float*>(s_x + (a.stage_x ? (size_t)T * H : 0));  // [T][H/32]
     if (tid < 32) s_used[tid] = 0u;
+    if (tid < 16) s_race[tid] = -1;
     for (int i = tid; i < MAXD; i += LTH) s_dcnt[i] = 0;
 
     // Wavefronts that poll must have no loads or stores of their own outstanding:
     // the vector memory counter retires in order, so a poll's result would wait
     // for them. Router rows and gate/up tasks are therefore numbered from the top
-    // wavefront down, and selection runs on wavefronts 0 .. T-1.
+    // wavefront down, and selection polls on wavefronts 0 .. npoll-1.
     const int wtop = LW - 1 - wave;
+    // Up to four tokens, two wavefronts poll each token's logits, one per copy
+    // (the tagged logits are published twice, 8 KiB apart, and device memory
+    // alternates between the chip's two halves in 8 KiB blocks, by physical
+    // address): the first to see them all selects, which is in effect the copy on
+    // this XCD's half. More tokens: one wavefront per token, on copy 0.
+    const bool race = T <= 4;
+    const int npoll = race ? 2 * T : T;
 
     // ---- A: router rows, one wavefront per (row, token); the per-lane order of the
     // products and the reduction tree are those of router_row for any token count,
@@ -592,7 +601,7 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
     // wavefronts when they fit above the selecting ones, so that no wavefront
     // computes two rows one after the other.
     const int nrw = (R + G - 1) / G;
-    if ((nrw + 1) * T <= LW) {
+    if (nrw * T + npoll <= LW) {
         if (wtop < nrw * T) {
             const int r = wg + G * (wtop / T);
             if (r < R)
@@ -610,7 +619,7 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
     PairLoads<CPL> cur;
     bool have = false;
     const int j0 = wg + G * wtop;
-    if (hs_ && j0 < npair && wave >= T) {
+    if (hs_ && j0 < npair && wave >= npoll) {
         pair_load<CPL>(a.experts, a.L, H, E, j0, lane, cur);
         have = true;
     }
@@ -629,31 +638,33 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
 
     // ---- S: selection (the ids; the weights follow the first gate/up loads),
     // distinct experts, token lists
-    if (wave < T) {
+    if (wave < npoll) {
         // up to four tokens: all of a lane's logit words reloaded together in each
         // polling round (few wavefronts poll); more: only the stale ones
-        // the copy in the 8 KiB half-blocks nearer this XCD (see the workspace layout)
-        const LogitSrc src{nullptr, a.tlogits + (size_t)wave * a.tl_stride + (xcd_id() >= 4 ? a.tl_copy : 0), tag,
-                           &ctl->error, false, T <= 4};
-        const SelState sel = select_ids<VPL>(src, E, k, hs_, lane, s_ids[wave]);
-        if (lane < k) s_raw[wave][lane] = sel.raw;
-        if (lane == 0) s_gbits[wave] = sel.gbits;
-        if (wg == 0 && lane < k) a.ids[wave * k + lane] = (int32_t)sel.id;
-        if constexpr (TT == 1) {
-            // one token: its k picks are k distinct experts (k <= E), listed in pick
-            // order after the shared expert
-            if (lane < k) {
-                s_dexp[hs_ + lane] = (int32_t)sel.id;
-                s_dcnt[hs_ + lane] = 1;
-                s_dtok[hs_ + lane][0] = (uint16_t)(lane << 5);
-            }
-            if (lane == 0) {
-                if (hs_) {
-                    s_dexp[0] = E;
-                    s_dcnt[0] = 1;
-                    s_dtok[0][0] = (uint16_t)(k << 5);
+        const int t = wave < T ? wave : wave - T;
+        const LogitSrc src{nullptr, a.tlogits + (size_t)t * a.tl_stride + (wave >= T ? a.tl_copy : 0), tag,
+                           &ctl->error, false, race, race ? &s_race[t] : nullptr, wave};
+        const SelState sel = select_ids<VPL>(src, E, k, hs_, lane, s_ids[t]);
+        if (sel.won) {
+            if (lane < k) s_raw[t][lane] = sel.raw;
+            if (lane == 0) s_gbits[t] = sel.gbits;
+            if (wg == 0 && lane < k) a.ids[t * k + lane] = (int32_t)sel.id;
+            if constexpr (TT == 1) {
+                // one token: its k picks are k distinct experts (k <= E), listed in
+                // pick order after the shared expert
+                if (lane < k) {
+                    s_dexp[hs_ + lane] = (int32_t)sel.id;
+                    s_dcnt[hs_ + lane] = 1;
+                    s_dtok[hs_ + lane][0] = (uint16_t)(lane << 5);
                 }
-                s_nd = hs_ + k;
+                if (lane == 0) {
+                    if (hs_) {
+                        s_dexp[0] = E;
+                        s_dcnt[0] = 1;
+                        s_dtok[0][0] = (uint16_t)(k << 5);
+                    }
+                    s_nd = hs_ + k;
+                }
             }
         }
     }
@@ -909,12 +920,13 @@ static size_t hbuf_bytes(const moe_shape& sh, int T) { return align_up((size_t)T
 //
 // Tagged logits: every selecting wavefront polls all of its token's logits, from
 // every XCD. Device memory alternates between the two halves of the chip in
-// 8 KiB blocks (address bit 13; measured on MI355X: a coherent load from an XCD
-// of the other half takes the longer path), so a small buffer sits on one half.
-// The router therefore publishes every logit twice, in two copies 8 KiB apart
-// (one on each half, whatever the mapping), and a wavefront polls the copy for
-// its own XCD: bit 13 clear for XCDs 0-3, set for 4-7. The region starts on a
-// 16 KiB boundary of the device address; a token takes 2 * tl_half bytes.
+// 8 KiB blocks (measured on MI355X: a coherent load from an XCD of the other half
+// takes the longer path; which half a block is on depends on address bit 13 and
+// on bits of the physical page), so a small buffer sits on one half. The router
+// therefore publishes every logit twice, in two copies 8 KiB apart, one on each
+// half, and with up to four tokens two wavefronts race, one per copy. The region
+// starts on a 16 KiB boundary of the device address; a token takes 2 * tl_half
+// bytes.
 static size_t tl_half(const moe_shape& sh) { return align_up((size_t)router_rows(sh) * 8, 8192); }
 
 struct DecodeWs {

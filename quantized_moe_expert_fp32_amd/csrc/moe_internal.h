@@ -65,14 +65,6 @@ __host__ __device__ inline size_t piece_off(int ch) { return (size_t)(ch >> 1) *
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// The XCD (accelerator complex die) this wavefront runs on, 0..7 on MI355X, from
-// the XCC_ID hardware register.
-__device__ __forceinline__ unsigned xcd_id() {
-    unsigned v;
-    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
-    return v & 0xFu;
-}
-
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // ------------------------------------------------------------------ device side
@@ -219,6 +211,40 @@ __device__ __forceinline__ void load_tagged_many(const uint64_t* p, int stride, 
 // few wavefronts wait on: the decode layer's selection with few tokens. With many
 // polling wavefronts the extra loads in flight slow the producers more than the
 // serial re-polls cost (measured at 16 tokens per launch).
+// As load_tagged_batch, for a race between wavefronts that poll copies of the
+// same words: *owner (LDS, -1 before the race) takes the id `me` of the first
+// wavefront whose words all carry the tag, or that gives up after SPIN_LIMIT
+// rounds (the error word is then set); the others stop at their next round.
+// Returns whether this wavefront won; only the winner's out[] is meaningful.
+template <int N>
+__device__ __forceinline__ bool load_tagged_race(const uint64_t* p, int stride, int n, uint32_t tag, unsigned* err,
+                                                 int* owner, int me, uint32_t* out) {
+    uint64_t v[N];
+    for (unsigned it = 0;; ++it) {
+#pragma unroll
+        for (int j = 0; j < N; ++j)
+            v[j] = __hip_atomic_load(const_cast<uint64_t*>(p + (size_t)(j < n ? j : 0) * stride), __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int j = 0; j < N; ++j) asm volatile("" : "+v"(v[j]));
+        bool ok = true;
+#pragma unroll
+        for (int j = 0; j < N; ++j) ok = ok && (j >= n || (uint32_t)(v[j] >> 32) == tag);
+        const bool give_up = it >= SPIN_LIMIT;
+        if (__ballot(ok) == __ballot(true) || give_up) {
+            if (give_up) atomicOr(err, 1u);
+            int prev = 0;
+            if ((threadIdx.x & 63) == 0) prev = atomicCAS(owner, -1, me);
+            prev = __shfl(prev, 0);
+#pragma unroll
+            for (int j = 0; j < N; ++j) out[j] = j < n ? (uint32_t)v[j] : 0u;
+            return prev == -1;
+        }
+        if (*reinterpret_cast<volatile int*>(owner) != -1) return false;
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
 template <int N>
 __device__ __forceinline__ void load_tagged_batch(const uint64_t* p, int stride, int n, uint32_t tag, unsigned* err,
                                                   uint32_t* out) {
@@ -294,6 +320,8 @@ struct LogitSrc {
     unsigned* err;
     bool coherent;
     bool batch;  // tagged: reload every word in each polling round (load_tagged_batch)
+    int* race = nullptr;  // tagged, batch: LDS word of a polling race (load_tagged_race)
+    int me = 0;           // this wavefront's entry in that race
     __device__ __forceinline__ uint32_t get(int i) const {
         if (tagged) return load_tagged_wait(tagged + i, tag, err);
         if (coherent) return load_coherent(reinterpret_cast<const uint32_t*>(plain) + i);
