@@ -597,11 +597,25 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
     // ---- A: router rows, one wavefront per (row, token); the per-lane order of the
     // products and the reduction tree are those of router_row for any token count,
     // so the logits equal the staged router's bit for bit
-    // Rows beyond the first G (the shared gate's at 256 experts) go to further
-    // wavefronts when they fit above the selecting ones, so that no wavefront
-    // computes two rows one after the other.
+    // One token: the router rows go to the workgroups with wg % 8 < 4, up to three
+    // rows each on separate wavefronts. Workgroups are dealt to the XCDs in turn,
+    // and XCDs 4-7 start about 0.6 us after XCDs 0-3; every selection waits for the
+    // last logit, so the rows are best computed where the launch starts first (if
+    // the dealing differs, only the speed changes). More tokens: rows beyond the
+    // first G (the shared gate's at 256 experts) go to further wavefronts when
+    // they fit above the selecting ones, so that no wavefront computes two rows
+    // one after the other.
     const int nrw = (R + G - 1) / G;
-    if (nrw * T + npoll <= LW) {
+    const int GE = G / 2;                  // workgroups with wg % 8 < 4
+    const int mE = (R * T + GE - 1) / GE;  // router rows per such workgroup
+    if (TT == 1 && G % 8 == 0 && mE + npoll <= LW) {
+        if ((wg & 7) < 4 && wtop < mE) {
+            const int r = (wg >> 3) * 4 + (wg & 7) + GE * wtop;
+            if (r < R)
+                router_row<1, AFF8>(a.router, a.logit_bias, a.x, 0, 1, H, R, E, r, lane, a.logits, false, a.tlogits,
+                                    tag, a.tl_stride, a.tl_copy);
+        }
+    } else if (nrw * T + npoll <= LW) {
         if (wtop < nrw * T) {
             const int r = wg + G * (wtop / T);
             if (r < R)
