@@ -354,9 +354,13 @@ __global__ __launch_bounds__(256) void decode_down_kernel(const uint8_t* __restr
 // launches.
 struct DecodeCtl {
     unsigned epoch;       // tag of the last completed launch
-    unsigned exit_count;  // workgroups that have read the epoch (back to zero after each launch)
+    unsigned exit_count;  // groups of workgroups that have all read the epoch (back to zero after each launch)
     unsigned error;       // a bounded poll timed out (sticky)
-    unsigned pad;
+    unsigned pad[29];
+    struct {
+        unsigned count;  // workgroups wg with wg % 8 == g that have read the epoch
+        unsigned pad[31];
+    } group[8];
 };
 
 struct LayerArgs {
@@ -646,9 +650,18 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
     // publishes the next epoch: every workgroup has read the epoch by then, and the
     // next launch starts only after this one ends. An early count is settled after
     // phase B, when its round trip is long over.
+    // The early count has two levels: one counter per group of workgroups
+    // (wg % 8), each on its own 128-byte line, and the last of a group counts the
+    // group in at the top. Atomics on one word are performed one after another, and
+    // with a single counter the workgroups at the back of 256 waited so long for
+    // the return that the logit polls queued behind it in the CU were late
+    // (T=1 13.8 -> 12.3 us). At the exit a second level is one more round trip at
+    // the very end, so the count there stays single.
     const bool count_early = T < LW;
+    const int grp = wg & 7;
+    const unsigned gsize = (unsigned)((G - grp + 7) / 8), ngrp = (unsigned)min(G, 8);
     unsigned counted = 0u;
-    if (count_early && tid == LTH - 64) counted = atomicAdd(&ctl->exit_count, 1u);
+    if (count_early && tid == LTH - 64) counted = atomicAdd(&ctl->group[grp].count, 1u);
 
     // ---- S: selection (the ids; the weights follow the first gate/up loads),
     // distinct experts, token lists
@@ -770,9 +783,12 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
     // first would otherwise share the memory system with the task loads still out
     // across the chip and slow them (T=1 17.5 -> 14.5 us, T=2 23.0 -> 19.5 us).
     __syncthreads();
-    if (count_early && tid == LTH - 64 && counted == (unsigned)G - 1) {
-        atomicExch(&ctl->exit_count, 0u);
-        atomicExch(&ctl->epoch, tag);
+    if (count_early && tid == LTH - 64 && counted == gsize - 1) {
+        atomicExch(&ctl->group[grp].count, 0u);
+        if (atomicAdd(&ctl->exit_count, 1u) == ngrp - 1) {
+            atomicExch(&ctl->exit_count, 0u);
+            atomicExch(&ctl->epoch, tag);
+        }
     }
 
     // ---- C: down items with the combine
@@ -950,7 +966,7 @@ struct DecodeWs {
 static DecodeWs decode_ws_layout(const moe_shape& sh, int T) {
     DecodeWs w;
     w.ctl = hbuf_bytes(sh, T);
-    w.tlogits = w.ctl + 256;
+    w.tlogits = w.ctl + align_up(sizeof(DecodeCtl), 256);
     w.th = w.tlogits + 16384 + (size_t)T * 2 * tl_half(sh);
     w.total = w.th + align_up((size_t)T * n_slots(sh) * (sh.inter / 2) * 8, 256);
     return w;
