@@ -54,7 +54,8 @@ typedef enum moe_status {
     MOE_ERR_INVALID_ARG = -1, /* bad pointer, size or shape field                */
     MOE_ERR_UNSUPPORTED = -2, /* well-formed but not served (bit width, group ...) */
     MOE_ERR_WORKSPACE = -3,   /* caller buffer smaller than the documented size   */
-    MOE_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed        */
+    MOE_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed        */
+    MOE_ERR_TIMEOUT = -5      /* a bounded in-kernel wait timed out (moe_decode_layer_check) */
 } moe_status;
 
 enum { MOE_ROUTER_F32 = 0, MOE_ROUTER_AFFINE8 = 1 };
@@ -181,17 +182,26 @@ moe_status moe_experts_decode(const moe_shape* shape, const void* experts_packed
  * or NULL; out [T][H] bf16 (bf16(residual + out) if residual != NULL; residual
  * may alias out). One persistent launch (at most one workgroup per compute unit,
  * all resident): workgroups hand data to each other through words of ws tagged
- * with a per-launch epoch. ws must be zero-filled before its first use with this
- * call and is then ready for every later call without clearing; calls that share
- * a ws must not overlap in time, and the launch must not share the GPU with work
+ * with a per-launch epoch. ws belongs to one (shape, T): it must be zero-filled
+ * before its first use with this call (and again before it is used with another
+ * T) and is then ready for every later call without clearing; calls that share a
+ * ws must not overlap in time, and the launch must not share the GPU with work
  * that keeps its workgroups from being resident (its waits are bounded: on a
- * timeout it sets an error word in ws and its outputs are undefined).
- * [P3-build], [P1-phase]. */
+ * timeout it sets an error word in ws and its outputs are undefined; see
+ * moe_decode_layer_check). [P3-build], [P1-phase]. */
 moe_status moe_decode_layer(const moe_shape* shape, const void* router_packed,
                             const float* logit_bias, const void* experts_packed,
                             const uint16_t* x, int32_t T, void* ws, size_t ws_bytes,
                             float* logits, int32_t* ids, uint16_t* w, uint16_t* w_shared,
                             float* y, const uint16_t* residual, uint16_t* out, void* stream);
+
+/* Waits for `stream`, then reads and clears the error word that moe_decode_layer
+ * sets in ws (same shape and T) when one of its bounded waits times out. Returns
+ * MOE_OK if no call since the last check timed out, MOE_ERR_TIMEOUT if one did
+ * (the outputs of the calls since then are undefined), MOE_ERR_INVALID_ARG /
+ * MOE_ERR_WORKSPACE for bad arguments, MOE_ERR_HIP if a runtime call fails. */
+moe_status moe_decode_layer_check(const moe_shape* shape, int32_t T, void* ws, size_t ws_bytes,
+                                  void* stream);
 
 /* ---------------------------------------------------------------- a3: dispatch
  * Histogram and expert-sorted order of the T*S picks ([P1-phase] Phase 9b:

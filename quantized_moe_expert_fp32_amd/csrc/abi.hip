@@ -58,6 +58,7 @@ extern "C" const char* moe_status_str(int32_t st) {
         case MOE_ERR_UNSUPPORTED: return "unsupported shape or format";
         case MOE_ERR_WORKSPACE: return "buffer too small";
         case MOE_ERR_HIP: return "HIP runtime error";
+        case MOE_ERR_TIMEOUT: return "a bounded in-kernel wait timed out";
         default: return "unknown status";
     }
 }

@@ -1065,3 +1065,22 @@ extern "C" moe_status moe_decode_layer(const moe_shape* shape, const void* route
     else launch_layer<2>(a, aff8, G, lds, hs);
     return check_launch("decode_layer_kernel");
 }
+
+extern "C" moe_status moe_decode_layer_check(const moe_shape* shape, int32_t T, void* ws, size_t ws_bytes,
+                                             void* stream) {
+    clear_error();
+    moe_status st = validate_shape(shape);
+    if (st != MOE_OK) return st;
+    if (T < 1 || T > 16) return fail(MOE_ERR_INVALID_ARG, "decode path takes 1..16 rows, got T = %d", T);
+    if (!ws || !aligned16(ws)) return fail(MOE_ERR_INVALID_ARG, "NULL or unaligned workspace");
+    if (ws_bytes < moe_decode_workspace_bytes(shape, T)) return fail(MOE_ERR_WORKSPACE, "decode workspace too small");
+    unsigned* err = &reinterpret_cast<DecodeCtl*>((char*)ws + decode_ws_layout(*shape, T).ctl)->error;
+    unsigned v = 0;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess ||
+        hipMemcpy(&v, err, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess)
+        return fail(MOE_ERR_HIP, "could not read the decode error word");
+    if (v == 0) return MOE_OK;
+    if (hipMemset(err, 0, sizeof(v)) != hipSuccess) return fail(MOE_ERR_HIP, "could not clear the decode error word");
+    return fail(MOE_ERR_TIMEOUT, "a bounded wait of moe_decode_layer timed out; outputs since the last check are "
+                                 "undefined");
+}

@@ -22,7 +22,7 @@ _lib = ctypes.CDLL(_LIB_PATH)
 ROUTER_F32 = 0
 ROUTER_AFFINE8 = 1
 
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_TIMEOUT = 0, -1, -2, -3, -4, -5
 
 
 class MoeError(RuntimeError):
@@ -83,6 +83,8 @@ _lib.moe_experts_decode.restype = _I32
 _lib.moe_experts_decode.argtypes = [_S, _P, _P, _I32, _P, _P, _SZ, _P, _P]
 _lib.moe_decode_layer.restype = _I32
 _lib.moe_decode_layer.argtypes = [_S, _P, _P, _P, _P, _I32, _P, _SZ, _P, _P, _P, _P, _P, _P, _P, _P]
+_lib.moe_decode_layer_check.restype = _I32
+_lib.moe_decode_layer_check.argtypes = [_S, _I32, _P, _SZ, _P]
 _lib.moe_dispatch.restype = _I32
 _lib.moe_dispatch.argtypes = [_S, _P, _I32, _P, _P, _P, _P]
 _lib.moe_prefill_workspace_bytes.restype = _SZ
@@ -97,7 +99,7 @@ _lib.moe_rmsnorm.argtypes = [_I32, _P, _I32, ctypes.c_float, _P, _P]
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_last_error", "moe_shape_check",
            "moe_experts_packed_bytes", "moe_pack_experts", "moe_router_packed_bytes", "moe_pack_router",
            "moe_route", "moe_route_from_logits", "moe_decode_workspace_bytes", "moe_experts_decode", "moe_decode_layer",
-           "moe_dispatch", "moe_prefill_workspace_bytes", "moe_experts_prefill", "moe_combine", "moe_rmsnorm")
+           "moe_decode_layer_check", "moe_dispatch", "moe_prefill_workspace_bytes", "moe_experts_prefill", "moe_combine", "moe_rmsnorm")
 
 
 def library_path() -> str:
@@ -187,6 +189,16 @@ def moe_decode_layer(shape, router_packed, logit_bias, experts_packed, x, T, ws,
                                  _ptr(x), T, _ptr(ws), _nbytes(ws), _ptr(logits), _ptr(ids), _ptr(w),
                                  _ptr(w_shared), _ptr(y), _ptr(residual), _ptr(out), _stream(stream)),
            "moe_decode_layer")
+
+
+def moe_decode_layer_check(shape, T, ws, stream=None):
+    """True if no moe_decode_layer call on ws since the last check timed out in a
+    bounded wait; False if one did (the word is cleared). Raises on bad arguments."""
+    st = _lib.moe_decode_layer_check(ctypes.byref(shape), T, _ptr(ws), _nbytes(ws), _stream(stream))
+    if st == ERR_TIMEOUT:
+        return False
+    _check(st, "moe_decode_layer_check")
+    return True
 
 
 def moe_dispatch(shape, ids, T, counts, offsets, order, stream=None):

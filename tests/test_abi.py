@@ -40,6 +40,7 @@ def test_abi_version_and_strings(moe):
     lib.moe_status_str.restype = ctypes.c_char_p
     assert lib.moe_status_str(0) == b"ok"
     assert lib.moe_status_str(-2) == b"unsupported shape or format"
+    assert lib.moe_status_str(moe.ERR_TIMEOUT) == b"a bounded in-kernel wait timed out"
 
 
 def _big(moe, **kw):
@@ -110,6 +111,13 @@ def test_host_argument_checks_launch_nothing(moe):
     assert st == moe.ERR_UNSUPPORTED
     # rmsnorm aliasing is refused
     st = moe.raw_call("moe_rmsnorm", 2048, v(P), 1, ctypes.c_float(1e-6), v(P), None)
+    assert st == moe.ERR_INVALID_ARG
+    # the decode error check validates before it touches the workspace
+    st = moe.raw_call("moe_decode_layer_check", byref(sh), 17, v(P), 1 << 20, None)
+    assert st == moe.ERR_INVALID_ARG
+    st = moe.raw_call("moe_decode_layer_check", byref(sh), 1, v(P), 64, None)
+    assert st == moe.ERR_WORKSPACE
+    st = moe.raw_call("moe_decode_layer_check", byref(sh), 1, v(P + 4), 1 << 20, None)
     assert st == moe.ERR_INVALID_ARG
 
 

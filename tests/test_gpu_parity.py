@@ -331,15 +331,39 @@ def test_fused_decode_layer_matches_staged_calls(gpu, T):
         outs.append(dict(logits=buf.logits.cpu().numpy(), ids=buf.ids.cpu().numpy(), w=L.bits_to_numpy(buf.w),
                          wsh=L.bits_to_numpy(buf.wsh), y=buf.y.cpu().numpy(), out=L.bits_to_numpy(buf.out)))
     off = (T * 9 * 512 * 2 + 255) // 256 * 256  # control words follow the bf16 h rows
-    ctl = buf.ws.cpu().numpy()[off:off + 16].view(np.uint32)
+    ctl = buf.ws.cpu().numpy()[off:off + 1152].view(np.uint32)
     assert ctl[2] == 0, "a bounded poll timed out"
     assert ctl[1] == 0 and ctl[0] == 3  # exit counter back at zero; one epoch per launch
+    assert all(ctl[32 * (1 + g)] == 0 for g in range(8))  # the group counters too
+    from quantized_moe_expert_fp32_amd import moe
+
+    assert moe.moe_decode_layer_check(dl.shape, T, buf.ws)
     b, b2 = outs[0], outs[2]
     for key in ("logits", "ids", "w", "wsh", "y", "out"):
         assert np.array_equal(a[key], b[key]), key
         assert np.array_equal(b[key], b2[key]), key
     staged_route_check(gpu, b, 256, 8)
     staged_layer_check(b, x, c.layers[0], 256)
+
+
+def test_decode_layer_check_reports_and_clears(gpu):
+    """moe_decode_layer_check reports the error word that a timed-out bounded wait
+    leaves in the workspace, and clears it. The word is set from the host: no
+    kernel is made to time out."""
+    from quantized_moe_expert_fp32_amd import moe
+
+    L = _L()
+    c = case("decode")
+    dl = dev_layer(gpu, c)
+    buf = L.alloc_buffers(dl.shape, 1, "fused")
+    L.layer_step(dl, L.to_device(synth.random_x(500, 1, 2048)), buf, "fused")
+    assert moe.moe_decode_layer_check(dl.shape, 1, buf.ws)
+    err = (1 * 9 * 512 * 2 + 255) // 256 * 256 + 8  # third word of the control block
+    buf.ws[err:err + 4].fill_(1)
+    assert not moe.moe_decode_layer_check(dl.shape, 1, buf.ws)
+    assert moe.moe_decode_layer_check(dl.shape, 1, buf.ws)
+    with pytest.raises(moe.MoeError):
+        moe.moe_decode_layer_check(dl.shape, 17, buf.ws)
 
 
 def test_fused_decode_residual_alias(gpu):
