@@ -568,7 +568,7 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
     __shared__ int32_t s_dcnt[MAXD];
     __shared__ uint16_t s_dtok[MAXD][16];
     __shared__ int32_t s_nd;
-    __shared__ float ysh[17][DN_ROWS];
+    __shared__ float ysh2[2][17][DN_ROWS];  // down results, alternating between items
     extern __shared__ __attribute__((aligned(16))) uint32_t lds_dyn[];
     const int G = gridDim.x, wg = blockIdx.x;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -579,7 +579,8 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
     DecodeCtl* ctl = a.ctl;
     const uint32_t tag = load_coherent(&ctl->epoch) + 1u;
     uint32_t* hsh = lds_dyn;                                                        // [S][I] bf16
-    uint16_t* s_x = reinterpret_cast<uint16_t*>(lds_dyn + (size_t)S * I / 2);      // [T][H] bf16
+    float* s_hs = reinterpret_cast<float*>(lds_dyn + (size_t)S * I / 2);           // [S][I/32] h chunk sums
+    uint16_t* s_x = reinterpret_cast<uint16_t*>(s_hs + (size_t)S * (I / 32));      // [T][H] bf16
     float* s_xs = reinterpret_cast<float*>(s_x + (a.stage_x ? (size_t)T * H : 0));  // [T][H/32]
     if (tid < 32) s_used[tid] = 0u;
     if (tid < 16) s_race[tid] = -1;
@@ -804,6 +805,7 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
     int staged = -1;
     for (int c = c0; c < c1; ++c) {
         const int t = c / NBLK, n0 = (c % NBLK) * DN_ROWS;
+        float(*ysh)[DN_ROWS] = ysh2[TT == 1 ? 0 : (c - c0) & 1];
         if (!dhave) dnl_load(a.experts, a.L, I, E, k, hs_, n0, s_ids[t], 0, wave, lane, dcur);
         DnLoadsL dnxt;
         const bool nhave = c + 1 < c1;
@@ -822,6 +824,16 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
                     if (j < n) hsh[i0 + LTH * j] = v[j];
             }
             __syncthreads();
+            if constexpr (TT != 1) {
+                // the chunk sums of h, once per token (load_xslice's arithmetic, so
+                // bit-identical to computing them per row)
+                if (tid < S * lpr) {
+                    XSlice<1> hx;
+                    load_xslice(reinterpret_cast<const uint16_t*>(hsh) + (size_t)(tid / lpr) * I, tid % lpr, lpr, hx);
+                    s_hs[tid] = hx.s[0];
+                }
+                __syncthreads();
+            }
             staged = t;
         }
         for (int b0 = 0; LW * b0 < n_it; b0 += DNB) {
@@ -834,7 +846,21 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
                 float v = 0.f;
                 if (dcur.ok[j]) {
                     XSlice<1> hx;
-                    load_xslice(reinterpret_cast<const uint16_t*>(hsh) + (size_t)dcur.slot[j] * I, lr, lpr, hx);
+                    if constexpr (TT != 1) {
+                        const uint4* src = reinterpret_cast<const uint4*>(
+                            reinterpret_cast<const uint16_t*>(hsh) + (size_t)dcur.slot[j] * I + 32 * lr);
+#pragma unroll
+                        for (int q4 = 0; q4 < 4; ++q4) {
+                            const uint4 hv = src[q4];
+                            hx.p[0][4 * q4 + 0] = hv.x;
+                            hx.p[0][4 * q4 + 1] = hv.y;
+                            hx.p[0][4 * q4 + 2] = hv.z;
+                            hx.p[0][4 * q4 + 3] = hv.w;
+                        }
+                        hx.s[0] = s_hs[dcur.slot[j] * lpr + lr];
+                    } else {
+                        load_xslice(reinterpret_cast<const uint16_t*>(hsh) + (size_t)dcur.slot[j] * I, lr, lpr, hx);
+                    }
                     v = chunk_dot(dcur.ld[j], hx.p[0], hx.s[0]);
                 }
                 v = group_sum(v, lpr);
@@ -855,7 +881,11 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
             if (a.residual) bb = f32_to_bf16(bf16_to_f32(a.residual[o]) + bf16_to_f32(bb));
             a.out[o] = (uint16_t)bb;
         }
-        __syncthreads();  // ysh and hsh are reused by the next item
+        // More tokens: no barrier here. The next item writes the other ysh buffer, hsh
+        // is not read after the barrier above, and this buffer is written again only
+        // after the next item's barrier, which every wavefront reaches after its reads
+        // here. One token (one item per workgroup) keeps the barrier.
+        if constexpr (TT == 1) __syncthreads();
         dcur = dnxt;
         dhave = nhave;
     }
@@ -1060,7 +1090,8 @@ extern "C" moe_status moe_decode_layer(const moe_shape* shape, const void* route
     a.has_shared = sh.has_shared;
     a.R = router_rows(sh);
     // 16 KiB covers the kernel's static LDS (selection results, distinct-expert lists)
-    const size_t lds_h = hsh_bytes(sh), lds_x = xsh_bytes(sh, T);
+    // h rows and their chunk sums, then (when staged) x and its chunk sums
+    const size_t lds_h = hsh_bytes(sh) + (size_t)n_slots(sh) * (sh.inter / 32) * 4, lds_x = xsh_bytes(sh, T);
     const int max_lds = device_max_lds();
     if (max_lds <= 0) return fail(MOE_ERR_HIP, "could not query the LDS size");
     a.stage_x = lds_h + lds_x + 16384 <= (size_t)max_lds ? 1 : 0;
