@@ -501,7 +501,7 @@ __device__ __forceinline__ void stage_x(const uint16_t* __restrict__ gx, int T, 
     }
 }
 
-// Down loads of one wavefront for one item (8 output rows, every slot): row
+// Down loads of one wavefront for one item (DR output rows, every slot): row
 // iterations wave + LW * (b0 + j), j < DNB, with the lane layout of dn_load.
 struct DnLoadsL {
     ChunkLoad ld[DNB];
@@ -537,20 +537,23 @@ __device__ __forceinline__ void dnl_load(const uint8_t* __restrict__ packed, con
 
 // Persistent kernel: one workgroup of 16 wavefronts per CU (every workgroup
 // resident); data moves between workgroups through epoch-tagged words.
-//   A: router rows, one wavefront per (row, token), published tagged; x is
-//      staged into LDS meanwhile.
-//   S: wavefront t selects token t (DPP top-k over the tagged logits); the
-//      workgroup then forms the distinct experts of the launch (d = 0 is the shared
-//      expert) and, per distinct expert, the (token, slot) pairs that use it.
+//   A: router rows, one wavefront per (row, token), published tagged (twice, on
+//      the chip's two halves); x is staged into LDS meanwhile.
+//   S: token t is selected by wavefront t, or with up to four tokens by the
+//      winner of a race between wavefronts t and T + t on the two logit copies
+//      (DPP top-k). The workgroup then forms the distinct experts of the launch
+//      (the shared expert first) and, per distinct expert, the (token, slot)
+//      pairs that use it; the pick weights follow once the gate/up loads are out.
 //   B: gate/up row-pair tasks (distinct expert, row pair), one per wavefront:
 //      the four weight rows are loaded once and applied to every token of the
 //      expert; h pairs are published tagged. Sixteen wavefronts per CU keep
 //      enough loads in flight; the shared expert's tasks are loaded before the
 //      selection.
-//   C: down items (8 output rows of one token, every slot) with the combine; a
-//      workgroup stages a token's h once (polling the tagged words) for all of its
-//      items of that token; an item's weight loads go out before that wait, and
-//      the next item's before the arithmetic.
+//   C: down items (8 output rows with one token, 16 with more, every slot) with
+//      the combine; a workgroup enters C when its own gate/up tasks are done and
+//      stages a token's h once (polling the tagged words) for all of its items of
+//      that token; an item's weight loads go out before that wait, and the next
+//      item's before the arithmetic.
 //
 // HC, IC, KC (when nonzero) fix hidden, inter and top_k at compile time; the
 // shape of the served model gets its own instance, with every lane layout and
