@@ -893,8 +893,11 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
         // More tokens: no barrier here. The next item writes the other ysh buffer, hsh
         // is not read after the barrier above, and this buffer is written again only
         // after the next item's barrier, which every wavefront reaches after its reads
-        // here. One token (one item per workgroup) keeps the barrier.
-        if constexpr (TT == 1) __syncthreads();
+        // here. One token reuses the single buffer, so it waits here when another item
+        // of its workgroup follows.
+        if constexpr (TT == 1) {
+            if (c + 1 < c1) __syncthreads();
+        }
         dcur = dnxt;
         dhave = nhave;
     }
