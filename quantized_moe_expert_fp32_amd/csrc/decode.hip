@@ -755,10 +755,11 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
     bool dhave = false;
     // Every wavefront with a task issues its first task's loads here. With one token
     // there are fewer tasks than wavefronts (9 * 256 of 16 * 256 at hidden 2048,
-    // inter 512, top-8 plus shared), and the wavefronts without one would put their
-    // down loads and h polls ahead of the others' task loads in the CU's memory
-    // pipeline; so no wavefront goes on to phase C before all have issued (the
-    // barrier waits for the issue only, not for the data). With more tokens every
+    // inter 512, top-8 plus shared), and a barrier on the issue (not on the data)
+    // lets every task's loads out before the selecting wavefront's fp64 weight
+    // arithmetic and the idle wavefronts go on. It was first measured against idle
+    // wavefronts' down loads and h polls (T=1 20.1 -> 18.0 us); with the barrier
+    // before phase C in place it still saves 0.25 us. With more tokens every
     // wavefront has a task and the barrier measured slower.
     if (!have && j0 < nB) {
         pair_load<CPL>(a.experts, a.L, H, s_dexp[j0 / npair], j0 % npair, lane, cur);
