@@ -313,7 +313,7 @@ def test_decode_batch_invariance(gpu):
         assert np.array_equal(part["out"], full["out"][:T])
 
 
-@pytest.mark.parametrize("T", [1, 5, 16])
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 16])
 def test_fused_decode_layer_matches_staged_calls(gpu, T):
     """moe_decode_layer (three launches) gives bit-identical outputs to moe_route +
     moe_experts_decode + moe_combine, and the oracle bar end to end."""
