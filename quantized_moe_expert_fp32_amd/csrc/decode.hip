@@ -378,11 +378,16 @@ struct LayerArgs {
     DecodeCtl* ctl;
     uint64_t* tlogits;  // tagged logits: token t's copy c at tlogits + t * tl_stride + c * tl_copy
     size_t tl_stride, tl_copy;  // in words
-    uint64_t* th;       // tagged h [T][S][I/2] (bf16 pairs)
+    uint64_t* th;       // tagged h [T][S][I/2] (bf16 pairs); one token: two copies, th_word
     ExpertLayout L;
     int T, H, I, E, k, has_shared, R;
     int stage_x;  // x and its chunk sums are staged in LDS (else read from global memory)
 };
+
+// Tagged h of one token: word w in copy c (0, 1) sits at th_word(w, c). Blocks of
+// 1024 words (8 KiB) alternate between the copies, so with a 16 KiB-aligned base
+// the two copies of a word are 8 KiB apart, on the chip's two halves.
+__device__ __forceinline__ size_t th_word(size_t w, int c) { return (w >> 10) * 2048 + (size_t)c * 1024 + (w & 1023); }
 
 // ---- single-launch building blocks (16 wavefronts per workgroup)
 constexpr int LW = 16;        // wavefronts per workgroup
@@ -791,7 +796,15 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
             XSlice<CPL> xs;
             token_xslice<CPL>(a.stage_x, s_x, s_xs, a.x, t, H, lane, xs);
             const uint32_t hp = pair_finish<CPL>(cur, H, xs, lane);
-            if (lane == 0) store_tagged(a.th + ((size_t)t * S + sl) * npair + ip, tag, hp);
+            if (lane == 0) {
+                const size_t w = ((size_t)t * S + sl) * npair + ip;
+                if constexpr (TT == 1) {
+                    store_tagged(a.th + th_word(w, 0), tag, hp);
+                    store_tagged(a.th + th_word(w, 1), tag, hp);
+                } else {
+                    store_tagged(a.th + w, tag, hp);
+                }
+            }
         }
     }
 
@@ -824,11 +837,18 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
                          dnxt);
         if (t != staged) {
             const int nw = S * npair;
-            const uint64_t* src = a.th + (size_t)t * S * npair;
+            // one token: h from the copy that won this workgroup's logit race (the
+            // copy on its half of the chip when both regions sit in one 2 MiB page)
+            static_assert(LTH == 1024, "staging steps one 1024-word block at a time");
+            const int hc = s_race[0] >= T ? 1 : 0;
+            const uint64_t* src = TT == 1 ? a.th + th_word(0, hc) : a.th + (size_t)t * S * npair;
             for (int i0 = tid; i0 < nw; i0 += LTH * 4) {
                 uint32_t v[4];
                 const int n = min(4, (nw - 1 - i0) / LTH + 1);
-                load_tagged_many<4>(src + i0, LTH, n, tag, &ctl->error, v);
+                if constexpr (TT == 1)
+                    load_tagged_many<4>(src + i0, 2 * LTH, n, tag, &ctl->error, v);
+                else
+                    load_tagged_many<4>(src + i0, LTH, n, tag, &ctl->error, v);
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     if (j < n) hsh[i0 + LTH * j] = v[j];
@@ -1017,7 +1037,10 @@ static DecodeWs decode_ws_layout(const moe_shape& sh, int T) {
     w.ctl = hbuf_bytes(sh, T);
     w.tlogits = w.ctl + align_up(sizeof(DecodeCtl), 256);
     w.th = w.tlogits + 16384 + (size_t)T * 2 * tl_half(sh);
-    w.total = w.th + align_up((size_t)T * n_slots(sh) * (sh.inter / 2) * 8, 256);
+    // tagged h; one token: 16 KiB of alignment slack, then blocks of 16 KiB (8 KiB
+    // per copy)
+    const size_t nh = (size_t)T * n_slots(sh) * (sh.inter / 2);
+    w.total = w.th + (T == 1 ? 16384 + (nh + 1023) / 1024 * 16384 : align_up(nh * 8, 256));
     return w;
 }
 
@@ -1093,7 +1116,7 @@ extern "C" moe_status moe_decode_layer(const moe_shape* shape, const void* route
     a.tlogits = (uint64_t*)align_up((size_t)((char*)ws + W.tlogits), 16384);
     a.tl_stride = 2 * tl_half(sh) / 8;
     a.tl_copy = tl_half(sh) / 8;
-    a.th = (uint64_t*)((char*)ws + W.th);
+    a.th = (uint64_t*)(T == 1 ? align_up((size_t)((char*)ws + W.th), 16384) : (size_t)((char*)ws + W.th));
     a.L = expert_layout(sh);
     a.T = T;
     a.H = sh.hidden;

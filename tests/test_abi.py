@@ -69,8 +69,8 @@ def test_sizes(moe):
     assert moe.moe_router_packed_bytes(sh) == 257 * 2048 + 257 * 32 * 4
     # h rows (9 x 512 bf16) + control block (a 128-byte line of words, then eight 128-byte group counters,
     # padded to 256) + tagged logits (16 KiB of alignment slack, then two 8 KiB copies per token: 257 x 8 B
-    # each) + tagged h (9 x 256 x 8 B)
-    assert moe.moe_decode_workspace_bytes(sh, 1) == 9216 + 1280 + 16384 + 2 * 8192 + 18432
+    # each) + tagged h (9 x 256 x 8 B; one token: two copies in 16 KiB blocks after 16 KiB of slack)
+    assert moe.moe_decode_workspace_bytes(sh, 1) == 9216 + 1280 + 16384 + 2 * 8192 + 16384 + 3 * 16384
     assert moe.moe_decode_workspace_bytes(sh, 16) == 16 * 9216 + 1280 + 16384 + 16 * 2 * 8192 + 16 * 18432
     assert moe.moe_prefill_workspace_bytes(sh, 4096) > 4096 * 9 * 512 * 2
     assert moe.moe_experts_packed_bytes(_big(moe, bits=8)) == 0
