@@ -11,10 +11,15 @@ batch of synthetic input already resident in HBM:
   prefill512   T=512 tokens through one layer;
   prefill4096  T=4096 tokens, Zipf(1.1) logit bias (skewed expert loads);
   stack1/16    one decode step of T=1 / T=16 tokens through 40 stacked layers.
-The timed region replays HIP graphs of the step sequence (captured once).
-Rank 0 prints one JSON line; `roofline` covers the expert stage (the kernels
-launched by moe_experts_decode / moe_experts_prefill), timed with HIP events
-on the launch stream; `cpu_baseline` times the FP64 oracle on a bounded sample.
+The timed region replays HIP graphs of the step sequence (captured once): one
+graph of min(K, 64) steps replayed K // that times, and one of the remaining steps.
+The process prints one JSON line. Its headline is the chosen workload (decode by
+default); "workloads" holds a record of the same form for each other workload
+(skipped with --only), timed with the same step counts capped by that
+workload's default. `roofline` covers the dominant stage: decode_layer_kernel for
+T <= 16, the experts stage (moe_experts_prefill) for prefill, timed with HIP events
+on the launch stream. `cpu_baseline` times the FP64 oracle on a bounded sample
+(`cores`: BLAS threads it ran with; `host_cores`: the host's core count).
 """
 
 from __future__ import annotations
@@ -43,6 +48,7 @@ def parse():
                     choices=["decode", "prefill512", "prefill4096", "stack1", "stack16"])
     ap.add_argument("--copies", type=int, default=8, help="independent weight sets for the decode workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", action="store_true", help="measure the chosen workload alone (no sub-records)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (counter calibration) and exit")
@@ -165,6 +171,207 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
+WORKLOADS = ("decode", "prefill512", "prefill4096", "stack1", "stack16")
+METRIC = "MoE-layer tokens/s (decode bs1, prefill 512/4096) + % HBM/MFMA roofline"
+
+
+class Inputs:
+    """Device-resident layers and activations of one workload (the 40 stack layers
+    are shared by stack1 and stack16)."""
+
+    def __init__(self, wl, copies, cache):
+        from quantized_moe_expert_fp32_amd import layer as L
+        from quantized_moe_expert_fp32_amd import synth
+
+        t0 = time.time()
+        if wl == "decode":
+            base = synth.make_case("decode")
+            self.hosts = [base.layers[0]] + [synth.make_layer(base.shape, base.seed, c) for c in range(1, copies)]
+            self.x_host = np.concatenate([base.x, synth.random_x(base.seed, 63, 2048)], axis=0)
+            self.T = 1
+        elif wl in ("prefill512", "prefill4096"):
+            base = synth.make_case(wl)
+            self.hosts = [base.layers[0]]
+            self.x_host = base.x
+            self.T = base.T
+        else:
+            self.T = 1 if wl == "stack1" else 16
+            base = synth.make_case("stack", T=self.T, n_layers=1)
+            if "stack_hosts" not in cache:
+                cache["stack_hosts"] = [base.layers[0]] + [synth.make_layer(base.shape, base.seed, l)
+                                                           for l in range(1, 40)]
+            self.hosts = cache["stack_hosts"]
+            self.x_host = base.x
+        self.shape = L.make_shape(base.shape)
+        key = "stack_layers" if wl.startswith("stack") else wl + "_layers"
+        if key not in cache:
+            cache[key] = [L.DeviceLayer(self.shape, h) for h in self.hosts]
+        self.layers = cache[key]
+        self.x = L.to_device(self.x_host)
+        # SHA-256 (first 16 hex digits) of the first layer's arrays and the activations
+        self.sha256 = {k: v[:16] for k, v in self.hosts[0].sha256().items()}
+        import hashlib
+
+        self.sha256["x"] = hashlib.sha256(np.ascontiguousarray(self.x_host).tobytes()).hexdigest()[:16]
+        self.setup_s = time.time() - t0
+
+
+def run_workload(wl, K, W, inp, no_cpu, cpu_seconds):
+    """Times K steps of one workload (graph replays) and its dominant stage; returns
+    the record of the bench line for it."""
+    import torch
+
+    from quantized_moe_expert_fp32_amd import layer as L
+    from quantized_moe_expert_fp32_amd import moe
+
+    T, shape, layers, xs = inp.T, inp.shape, inp.layers, inp.x
+    path = L.pick_path(T)
+    buf = L.alloc_buffers(shape, T, path)
+    S = shape.slots
+    log("%s: %d weight sets, set-up %.1f s" % (wl, len(layers), inp.setup_s))
+
+    # ---------------------------------------------------------------- the step sequence
+    if wl.startswith("stack"):
+        x_state = xs.clone()
+        xn = torch.empty_like(x_state)
+        period = 1
+
+        def step(j):
+            L.stack_step(layers, x_state, xn, buf, path=path)
+    elif wl == "decode":
+        period = xs.shape[0]  # 64 consecutive steps cover every token and every weight copy
+
+        def step(j):
+            dl = layers[j % len(layers)]
+            r = j % period
+            L.layer_step(dl, xs[r:r + 1], buf, path)
+    else:
+        period = 1
+
+        def step(j):
+            L.layer_step(layers[0], xs, buf, path)
+
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for j in range(min(max(W, 1), 3)):
+            step(j)
+    torch.cuda.synchronize()
+
+    # graphs: one of n_cap consecutive steps (n_cap = min(K, 64, a multiple of the
+    # period)), replayed K // n_cap times, and one of the remaining K % n_cap steps
+    n_cap = min(K, 64)
+    if period > 1 and n_cap >= period:
+        n_cap -= n_cap % period
+
+    def capture(n, start):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for j in range(n):
+                step(start + j)
+        return g
+
+    g_main = capture(n_cap, 0)
+    rem = K % n_cap
+    g_rem = capture(rem, (K // n_cap) * n_cap) if rem else None
+    torch.cuda.synchronize()
+
+    def run_steps(n):
+        for _ in range(n // n_cap):
+            g_main.replay()
+        if n % n_cap:
+            if n % n_cap == rem:
+                g_rem.replay()
+            else:
+                with torch.cuda.stream(stream):
+                    for j in range(n % n_cap):
+                        step(j)
+
+    with torch.cuda.stream(stream):
+        run_steps(W)
+    torch.cuda.synchronize()
+
+    # ---------------------------------------------------------------- timed region
+    ev_a, ev_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        ev_a.record(stream)
+        run_steps(K)
+        ev_b.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    region_us = ev_a.elapsed_time(ev_b) * 1e3
+    value = T * K / elapsed
+    log("%s: timed region %d steps in %.4f s (%.2f us per step on the stream)" % (wl, K, elapsed, region_us / K))
+
+    # ---------------------------------------------------------------- dominant stage (HIP events on its stream)
+    n_ev = min(max(K, 8), 512 if not wl.startswith("stack") else 200)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(200_000_000)  # keep the GPU busy while the host queues the measured launches
+        for j in range(n_ev):
+            dl = layers[j % len(layers)]
+            xin = xs[(j % xs.shape[0]):(j % xs.shape[0]) + 1] if wl == "decode" else xs
+            if path == "fused":
+                starts[j].record(stream)
+                moe.moe_decode_layer(shape, dl.router, dl.logit_bias, dl.experts, xin, T, buf.ws, buf.logits,
+                                     buf.ids, buf.w, buf.wsh, buf.y, None, buf.out)
+                ends[j].record(stream)
+            else:
+                moe.moe_route(shape, dl.router, dl.logit_bias, xin, T, buf.logits, buf.ids, buf.w, buf.wsh)
+                starts[j].record(stream)
+                moe.moe_experts_prefill(shape, dl.experts, xin, T, buf.ids, buf.ws, buf.y)
+                ends[j].record(stream)
+    torch.cuda.synchronize()
+    durs_ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    stage_us = float(np.mean(durs_ms) * 1e3)
+    log("%s: dominant stage %.2f us average over %d event-timed launches" % (wl, stage_us, n_ev))
+    if wl == "decode":
+        # every step of the timed region is one decode_layer_kernel launch: the
+        # events around the region give its average per-launch duration without
+        # the per-launch event overhead
+        stage_us = region_us / K
+        log("decode: decode_layer_kernel %.2f us per launch over the timed region" % stage_us)
+
+    # algorithmic work of one launch of the dominant stage: the weights of every
+    # distinct expert it touches (read once) plus the activations; the fp32 slot
+    # buffer and the bf16 intermediate are not counted
+    ids_np = buf.ids.cpu().numpy()
+    distinct = len(set(ids_np.reshape(-1).tolist())) + shape.has_shared
+    alg_bytes = distinct * EXPERT_BYTES + T * 2048 * 2
+    flops = T * S * 3 * 2 * 2048 * 512
+    if path == "fused":
+        alg_bytes += ROUTER_BYTES  # the launch also streams the router
+    if wl == "prefill4096":
+        roof = dict(bound="mfma", achieved=flops / (stage_us * 1e-6) / 1e12, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s")
+    else:
+        roof = dict(bound="hbm", achieved=alg_bytes / (stage_us * 1e-6) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = stored_traffic(wl)
+    roof["kernel"] = ("decode_layer_kernel (router, selection, experts, combine in one launch)" if path == "fused"
+                      else "experts stage (moe_experts_prefill): " + " + ".join(PREFILL_KERNELS))
+    roof["avg_us"] = stage_us
+    roof["alg_bytes_per_launch"] = int(alg_bytes)
+    roof["alg_flops_per_launch"] = int(flops)
+
+    cpu = None
+    if not no_cpu:
+        cpu = cpu_baseline(wl, inp.hosts, inp.x_host, T, shape, cpu_seconds)
+    unit = "layer-tokens/s" if not wl.startswith("stack") else "tokens/s"
+    return {
+        "value": value, "unit": unit, "steps": K, "warmup": W, "ms_per_step": elapsed * 1e3 / K,
+        "us_per_step_stream": region_us / K,
+        "config": {"workload": wl, "T": T, "hidden": 2048, "n_experts": 256, "top_k": 8, "shared": 1,
+                   "inter": 512, "weights": "int4 affine g64", "router": "8-bit affine g64",
+                   "layers": len(layers) if wl.startswith("stack") else 1,
+                   "weight_copies": len(layers) if wl == "decode" else 1, "path": path,
+                   "graph_steps": n_cap},
+        "roofline": roof, "cpu_baseline": cpu, "inputs_sha256": inp.sha256, "setup_s": inp.setup_s,
+    }
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -183,194 +390,37 @@ def main():
 
     import torch
 
-    from quantized_moe_expert_fp32_amd import layer as L
-    from quantized_moe_expert_fp32_amd import moe, synth
-
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    wl = args.workload
+    torch.cuda.set_device(torch.device("cuda:0"))
+    head = args.workload
     defaults = {"decode": (2048, 256), "prefill512": (200, 20), "prefill4096": (50, 5),
                 "stack1": (50, 5), "stack16": (50, 5)}
-    K = args.steps if args.steps is not None else defaults[wl][0]
-    W = args.warmup if args.warmup is not None else defaults[wl][1]
-
-    # ---------------------------------------------------------------- inputs
-    t_setup = time.time()
-    if wl == "decode":
-        base = synth.make_case("decode")
-        shape = L.make_shape(base.shape)
-        hosts = [base.layers[0]] + [synth.make_layer(base.shape, base.seed, c) for c in range(1, args.copies)]
-        layers = [L.DeviceLayer(shape, h) for h in hosts]
-        NX = 64
-        xs_host = np.concatenate([base.x, synth.random_x(base.seed, NX - 1, 2048)], axis=0)
-        T = 1
-    elif wl in ("prefill512", "prefill4096"):
-        base = synth.make_case(wl)
-        shape = L.make_shape(base.shape)
-        hosts = [base.layers[0]]
-        layers = [L.DeviceLayer(shape, hosts[0])]
-        xs_host = base.x
-        T = base.T
-    else:
-        T = 1 if wl == "stack1" else 16
-        base = synth.make_case("stack", T=T, n_layers=1)
-        shape = L.make_shape(base.shape)
-        hosts = [base.layers[0]]
-        layers = [L.DeviceLayer(shape, hosts[0])]
-        for l in range(1, 40):
-            layers.append(L.DeviceLayer(shape, synth.make_layer(base.shape, base.seed, l)))
-        xs_host = base.x
-    setup_s = time.time() - t_setup
-    log("setup done in %.1f s (%s, %d weight sets)" % (setup_s, wl, len(layers)))
-    path = L.pick_path(T)
-    xs = L.to_device(xs_host)
-    buf = L.alloc_buffers(shape, T, path)
-    S = shape.slots
-
-    # ---------------------------------------------------------------- the step sequence
-    if wl.startswith("stack"):
-        x_state = xs.clone()
-        xn = torch.empty_like(x_state)
-        seq_len = 1
-
-        def step(j):
-            L.stack_step(layers, x_state, xn, buf, path=path)
-    elif wl == "decode":
-        seq_len = NX  # one graph covers 64 consecutive steps (every token, every copy)
-
-        def step(j):
-            dl = layers[j % len(layers)]
-            r = j % NX
-            L.layer_step(dl, xs[r:r + 1], buf, path)
-    else:
-        seq_len = 1
-
-        def step(j):
-            L.layer_step(layers[0], xs, buf, path)
-
-    stream = torch.cuda.Stream()
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        for j in range(min(W, 3)):
-            step(j)
-    torch.cuda.synchronize()
-
-    # graphs of seq_len consecutive steps; replay g covers steps g*seq_len .. +seq_len
-    graphs = []
-    for gi in range(1):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for j in range(seq_len):
-                step(gi * seq_len + j)
-        graphs.append(g)
-    torch.cuda.synchronize()
-
-    def run_steps(n, start=0):
-        done = 0
-        gi = 0
-        while done + seq_len <= n:
-            graphs[gi % len(graphs)].replay()
-            gi += 1
-            done += seq_len
-        if done < n:
-            with torch.cuda.stream(stream):
-                for j in range(done, n):
-                    step(start + j)
-
-    with torch.cuda.stream(stream):
-        run_steps(W)
-    torch.cuda.synchronize()
-
-    # ---------------------------------------------------------------- timed region
-    torch.cuda.synchronize()
-    ev_a, ev_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        ev_a.record(stream)
-        run_steps(K)
-        ev_b.record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    region_us = ev_a.elapsed_time(ev_b) * 1e3
-    ms_per_step = elapsed * 1e3 / K
-    tokens_per_step = T
-    value = tokens_per_step * K / elapsed
-    log("timed region: %d steps in %.3f s" % (K, elapsed))
-
-    # ---------------------------------------------------------------- expert-stage timing (HIP events)
-    n_ev = min(K, 512)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-    with torch.cuda.stream(stream):
-        torch.cuda._sleep(200_000_000)  # keep the GPU busy while the host queues the measured launches
-        for j in range(n_ev):
-            dl = layers[j % len(layers)]
-            xin = xs[(j % xs.shape[0]):(j % xs.shape[0]) + 1] if wl == "decode" else xs
-            if path == "fused":
-                # the whole decode layer is one kernel (decode_layer_kernel)
-                starts[j].record(stream)
-                moe.moe_decode_layer(shape, dl.router, dl.logit_bias, dl.experts, xin, T, buf.ws, buf.logits, buf.ids,
-                                     buf.w, buf.wsh, buf.y, None, buf.out)
-                ends[j].record(stream)
-            else:
-                moe.moe_route(shape, dl.router, dl.logit_bias, xin, T, buf.logits, buf.ids, buf.w, buf.wsh)
-                starts[j].record(stream)
-                moe.moe_experts_prefill(shape, dl.experts, xin, T, buf.ids, buf.ws, buf.y)
-                ends[j].record(stream)
-    torch.cuda.synchronize()
-    durs_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
-    expert_us = float(np.mean(durs_ms) * 1e3)
-    log("measured stage: %.2f us average over %d event-timed launches" % (expert_us, n_ev))
-    if wl == "decode":
-        # every step of the timed region is exactly one decode_layer_kernel launch:
-        # the events around the region give the kernel's average duration without
-        # the per-launch event overhead
-        expert_us = region_us / K
-        log("decode_layer_kernel: %.2f us average over the %d launches of the timed region" % (expert_us, K))
-
-    # algorithmic work of one expert-stage launch
-    ids_np = buf.ids.cpu().numpy()
-    # (weights of every distinct expert the launch touches, read once, plus the activations;
-    # the fp32 slot buffer and the bf16 intermediate are not counted)
-    distinct = len(set(ids_np.reshape(-1).tolist())) + shape.has_shared
-    alg_bytes = distinct * EXPERT_BYTES + T * 2048 * 2
-    flops = T * S * 3 * 2 * 2048 * 512
-    if path == "fused":
-        alg_bytes += ROUTER_BYTES  # the launch also streams the router
-    if path in ("decode", "fused"):
-        roof = dict(bound="hbm", achieved=alg_bytes / (expert_us * 1e-6) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
-    else:
-        if wl == "prefill4096":
-            roof = dict(bound="mfma", achieved=flops / (expert_us * 1e-6) / 1e12, peak=BF16_PEAK_TFLOPS,
-                        unit="TFLOP/s")
-        else:
-            roof = dict(bound="hbm", achieved=alg_bytes / (expert_us * 1e-6) / 1e9, peak=HBM_PEAK_GBS,
-                        unit="GB/s")
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = stored_traffic(wl)
-    roof["kernel"] = ("decode_layer_kernel (router, selection, experts, combine in one launch)" if path == "fused"
-                      else "experts stage (moe_experts_prefill): " + " + ".join(PREFILL_KERNELS))
-    roof["avg_us"] = expert_us
-    roof["alg_bytes_per_launch"] = int(alg_bytes)
-
-    # ---------------------------------------------------------------- CPU baseline (oracle)
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, hosts, xs_host, T, shape, args.cpu_seconds)
-
-    unit = "layer-tokens/s" if not wl.startswith("stack") else "tokens/s"
-    metric = "MoE-layer tokens/s (decode bs1, prefill 512/4096) + % HBM/MFMA roofline"
+    K = args.steps if args.steps is not None else defaults[head][0]
+    W = args.warmup if args.warmup is not None else defaults[head][1]
+    cache = {}
+    rec = run_workload(head, K, W, Inputs(head, args.copies, cache), args.no_cpu_baseline, args.cpu_seconds)
+    others = {}
+    if not args.only:
+        # the other configurations of the metric, each with its own roofline; the
+        # step and warm-up counts are the headline's, capped by the workload's default
+        for wl in WORKLOADS:
+            if wl == head:
+                continue
+            k2 = min(K, defaults[wl][0])
+            w2 = min(W, defaults[wl][1])
+            r = run_workload(wl, k2, w2, Inputs(wl, args.copies, cache), args.no_cpu_baseline,
+                             min(args.cpu_seconds, 5.0))
+            for drop in ("setup_s",):
+                r.pop(drop, None)
+            others[wl] = r
+            if wl == "prefill4096":
+                cache.pop("prefill4096_layers", None)
     line = {
-        "metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": K, "warmup": W,
-        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "metric": METRIC, "value": rec["value"], "unit": rec["unit"], "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": rec["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16 activations, int4 weights, fp32/fp64 accumulation", "data": "synthetic",
-        "config": {"workload": wl, "T": T, "hidden": 2048, "n_experts": 256, "top_k": 8, "shared": 1,
-                   "inter": 512, "weights": "int4 affine g64", "router": "8-bit affine g64",
-                   "layers": len(layers) if wl.startswith("stack") else 1,
-                   "weight_copies": len(layers) if wl == "decode" else 1, "path": path},
-        "roofline": roof,
-        "cpu_baseline": cpu,
-        "setup_s": setup_s,
+        "config": rec["config"], "roofline": rec["roofline"], "cpu_baseline": rec["cpu_baseline"],
+        "inputs_sha256": rec["inputs_sha256"], "us_per_step_stream": rec["us_per_step_stream"],
+        "setup_s": rec["setup_s"], "workloads": others,
     }
     print(json.dumps(line), flush=True)
 
@@ -396,7 +446,6 @@ def cpu_baseline(wl, hosts, xs_host, T, shape, budget_s):
             done_tokens += 1
             j += 1
         sample = "%d single-token layer passes over the rotating copies/tokens" % done_tokens
-        unit = "layer-tokens/s"
     elif wl.startswith("prefill"):
         n = min(T, 64)
         while time.perf_counter() - t0 < budget_s and layer_passes < 4:
@@ -404,19 +453,19 @@ def cpu_baseline(wl, hosts, xs_host, T, shape, budget_s):
             done_tokens += n
             layer_passes += 1
         sample = "%d passes of the first %d tokens through the layer" % (layer_passes, n)
-        unit = "layer-tokens/s"
     else:
         n = xs_host.shape[0]
         x = xs_host
         for l in range(len(hosts)):
+            if layer_passes and time.perf_counter() - t0 >= budget_s:
+                break
             x = O.residual_bf16(x, O.layer_forward(O.rmsnorm_bf16(x), hosts[l], k)["out"])
             layer_passes += 1
         done_tokens = n * layer_passes
-        sample = "%d tokens through %d of the 40 layers (layer-tokens)" % (n, layer_passes)
-        unit = "layer-tokens/s"
+        sample = "%d tokens through the first %d of the 40 layers (layer-tokens)" % (n, layer_passes)
     el = time.perf_counter() - t0
-    return {"value": done_tokens / el, "unit": unit, "cores": cores, "kind": "oracle", "sample": sample,
-            "seconds": el}
+    return {"value": done_tokens / el, "unit": "layer-tokens/s", "cores": cores, "host_cores": os.cpu_count(),
+            "kind": "oracle", "sample": sample, "seconds": el}
 
 
 if __name__ == "__main__":

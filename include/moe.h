@@ -219,6 +219,25 @@ moe_status moe_dispatch(const moe_shape* shape, const int32_t* ids, int32_t T, i
  * with the SwiGLU epilogue, then the down GEMM scattering rows back to y[t][s].
  * ws: device scratch of moe_prefill_workspace_bytes(shape, T) bytes. */
 size_t moe_prefill_workspace_bytes(const moe_shape* shape, int32_t T);
+
+/* Where moe_experts_prefill leaves its dispatch inside ws for a call with this
+ * shape and T (byte offsets from ws; written to *view_host, host memory):
+ *   counts [M] int32 (counts[E] = T for the shared expert), offsets [M+1] int32
+ *   (exclusive prefix sums), ntiles one int32, tiles [max_tiles] of four int32
+ *   {expert, row0, nrows, 0} (the first ntiles are the work list: a tile covers
+ *   rows row0 .. row0+nrows-1 of the expert-sorted order, at most 128, all of one
+ *   expert), order [T*S] int32 (pick indices t*S + s grouped by ascending expert,
+ *   and within an expert by ascending pick index).
+ * For checks of the dispatch and for callers that reuse the expert-sorted order
+ * ([P1-phase] Phase 9b: lookup-table dispatch). MOE_ERR_INVALID_ARG for a bad
+ * shape, T < 1 or NULL view_host. */
+typedef struct moe_prefill_dispatch_view {
+    size_t counts, offsets, ntiles, tiles, order;
+    int32_t max_tiles;
+    int32_t pad;
+} moe_prefill_dispatch_view;
+moe_status moe_prefill_dispatch_layout(const moe_shape* shape, int32_t T, moe_prefill_dispatch_view* view_host);
+
 moe_status moe_experts_prefill(const moe_shape* shape, const void* experts_packed,
                                const uint16_t* x, int32_t T, const int32_t* ids, void* ws,
                                size_t ws_bytes, float* y, void* stream);

@@ -102,6 +102,21 @@ def dequant_int8(q, scale_bits, bias_bits) -> np.ndarray:
     return s * q + b
 
 
+def dequant_expert(q, scale_bits, bias_bits, bits: int) -> np.ndarray:
+    """An expert matrix in its storage format: affine 4-bit (two weights per byte,
+    dequant_int4) or affine 8-bit (one weight per byte, dequant_int8), groups of 64.
+
+    TensorFold #931, "What I'd build": experts are affine 4-bit in groups of 64,
+    and the 8-bit experts (a second checkpoint of the same layout) store one code
+    per byte with the same groups; w = scale * q + bias either way.
+    """
+    if bits == 4:
+        return dequant_int4(q, scale_bits, bias_bits)
+    if bits == 8:
+        return dequant_int8(q, scale_bits, bias_bits)
+    raise ValueError("expert bit width %d" % bits)
+
+
 def router_matrix(layer) -> np.ndarray:
     """Router [E(+1), H] in float64: fp32 rows, or dequantised 8-bit affine rows."""
     if getattr(layer, "router_f32", None) is not None:
@@ -225,7 +240,7 @@ def silu64(z) -> np.ndarray:
         return z / (1.0 + np.exp(-z))
 
 
-def expert_ffn(x64, q_gate, s_gate, b_gate, q_up, s_up, b_up, q_down, s_down, b_down):
+def expert_ffn(x64, q_gate, s_gate, b_gate, q_up, s_up, b_up, q_down, s_down, b_down, bits: int = 4):
     """One expert on rows x64 [n, H]: returns (h bf16 bits [n, I], y float64 [n, H]).
 
     gate/up pair then down (TensorFold #931, "Gate": "the expert gate/up pair,
@@ -233,14 +248,21 @@ def expert_ffn(x64, q_gate, s_gate, b_gate, q_up, s_up, b_up, q_down, s_down, b_
     bf16 (the model's activation type) before the down projection; y is kept in
     float64 because the contract rounds only the weighted sum.
     """
-    Wg = dequant_int4(q_gate, s_gate, b_gate)
-    Wu = dequant_int4(q_up, s_up, b_up)
-    Wd = dequant_int4(q_down, s_down, b_down)
+    Wg = dequant_expert(q_gate, s_gate, b_gate, bits)
+    Wu = dequant_expert(q_up, s_up, b_up, bits)
+    Wd = dequant_expert(q_down, s_down, b_down, bits)
     g = x64 @ Wg.T
     u = x64 @ Wu.T
     h = round_bf16(silu64(g) * u)
     y = bf16_to_f64(h) @ Wd.T
     return h, y
+
+
+def expert_bits(layer) -> int:
+    """Bit width of a layer's expert codes, from its storage: 4-bit matrices hold
+    two codes per byte along the input dimension ([.., I, H/2] for gate), 8-bit
+    one ([.., I, H])."""
+    return 8 if layer.q_gate.shape[-1] == layer.q_down.shape[-2] else 4
 
 
 def expert_outputs(x_bits, ids, layer, n_experts: int, has_shared: bool):
@@ -255,6 +277,7 @@ def expert_outputs(x_bits, ids, layer, n_experts: int, has_shared: bool):
     S = k + (1 if has_shared else 0)
     H = x.shape[1]
     I = layer.q_gate.shape[1]
+    bits = expert_bits(layer)
     y = np.zeros((T, S, H), dtype=np.float64)
     h = np.zeros((T, S, I), dtype=np.uint16)
     experts = sorted(set(int(e) for e in ids.reshape(-1)))
@@ -268,7 +291,7 @@ def expert_outputs(x_bits, ids, layer, n_experts: int, has_shared: bool):
             rows_t, rows_s = np.nonzero(ids == e)
         he, ye = expert_ffn(x[rows_t], layer.q_gate[e], layer.s_gate[e], layer.b_gate[e],
                             layer.q_up[e], layer.s_up[e], layer.b_up[e],
-                            layer.q_down[e], layer.s_down[e], layer.b_down[e])
+                            layer.q_down[e], layer.s_down[e], layer.b_down[e], bits)
         y[rows_t, rows_s] = ye
         h[rows_t, rows_s] = he
     return y, h
@@ -326,26 +349,57 @@ def layer_forward(x_bits, layer, top_k: int, has_shared: bool = True):
     return {"logits": logits, "ids": ids, "w": w, "wsh": wsh, "h": h, "y": y, "out": out}
 
 
-def stack_forward(x_bits, layers, top_k: int, has_shared: bool = True, eps: float = 1e-6):
-    """x_{l+1} = bf16(x_l + MoE_l(bf16(RMSNorm(x_l)))) over the given layers."""
-    xs = [np.asarray(x_bits, dtype=np.uint16)]
-    for L in layers:
-        xn = rmsnorm_bf16(xs[-1], eps)
-        st = layer_forward(xn, L, top_k, has_shared)
-        xs.append(residual_bf16(xs[-1], st["out"]))
-    return xs
-
+# ---------------------------------------------------------------- comparison helpers (test bars)
 
 def bf16_ulp(v) -> np.ndarray:
-    """Spacing of bf16 values at |v| (float64), 2^-133 below the normal range."""
+    """Spacing of the bf16 values around |v| (float64): 2^(e-8) for |v| in [2^(e-1), 2^e),
+    and 2^-133 (the least subnormal step) below the normal range and at zero.
+
+    bf16 keeps 8 significant bits, so the spacing inside the binade [2^(e-1), 2^e)
+    is 2^(e-1) * 2^-7 = 2^(e-8); the normal range ends at 2^-126, under which the
+    values are multiples of 2^-133.
+    """
     a = np.abs(np.asarray(v, dtype=np.float64))
     _, e = np.frexp(a)
+    e = np.where(a == 0.0, -200, e)
     return np.ldexp(1.0, np.maximum(e - 8, -133))
 
 
 def near_tie_tokens(logits_routed, k: int, gap: float = 1e-5) -> np.ndarray:
-    """Tokens whose top k+1 logits hold an adjacent gap below `gap` (boolean [T])."""
+    """Tokens whose k-th and (k+1)-th largest routed logits lie less than `gap` apart.
+
+    These are the tokens whose set of picks may change when the logits move by
+    less than `gap`: the exemption that the pick bar grants (boolean [T]). Ranks
+    are by value; equal values count as a gap of zero.
+    """
     l = np.sort(np.asarray(logits_routed, dtype=np.float64), axis=1)[:, ::-1]
-    m = min(k + 1, l.shape[1])
-    d = l[:, :m - 1] - l[:, 1:m]
-    return (d < gap).any(axis=1)
+    if l.shape[1] <= k:
+        return np.zeros(l.shape[0], dtype=bool)
+    return (l[:, k - 1] - l[:, k]) < gap
+
+
+def picks_within_ties(ids, ref_logits_routed, k: int, gap: float = 1e-5):
+    """Compares ordered picks `ids` [T, k] with the oracle's picks on ref logits.
+
+    A token passes when, slot by slot, each pick is the oracle's pick or an expert
+    whose oracle logit lies within `gap` of that pick's. So a pick may differ from
+    the oracle's only across a near tie: at the k-th/(k+1)-th boundary (the set
+    changes; near_tie_tokens) or between two ranks inside the top k (the order
+    changes). The picks of a token must be k distinct ids in [0, E).
+    Returns (ok [T] bool, set_exempt [T] bool, order_exempt [T] bool): the last two
+    mark passing tokens that differ from the oracle's picks, with a different set
+    or with the same set in another order.
+    """
+    ids = np.asarray(ids, dtype=np.int64)
+    l = np.asarray(ref_logits_routed, dtype=np.float64)
+    T, E = l.shape
+    ref = topk(ref_logits_routed, k).astype(np.int64)
+    valid = ((ids >= 0) & (ids < E)).all(axis=1)
+    distinct = np.array([len(set(r.tolist())) == k for r in ids])
+    safe = np.clip(ids, 0, E - 1)
+    rows = np.arange(T)[:, None]
+    close = (ids == ref) | (np.abs(l[rows, safe] - l[rows, ref]) < gap)
+    ok = valid & distinct & close.all(axis=1)
+    differ = (ids != ref).any(axis=1)
+    same_set = np.array([set(a.tolist()) == set(b.tolist()) for a, b in zip(ids, ref)])
+    return ok, ok & differ & ~same_set, ok & differ & same_set

@@ -15,6 +15,8 @@
 // the activations as stored) and sum x*(1 + q/16) is a chain of bf16 dot2
 // instructions accumulating in fp32.
 #include <algorithm>
+#include <map>
+#include <mutex>
 
 #include "moe_internal.h"
 #include "route_device.h"
@@ -577,6 +579,7 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
     __shared__ int32_t s_dcnt[MAXD];
     __shared__ uint16_t s_dtok[MAXD][16];
     __shared__ int32_t s_nd;
+    __shared__ int s_bad;  // a bounded wait of this workgroup timed out: its h and outputs become NaN
     // rows per down item: one token has one item per workgroup; more tokens run
     // items one after another, and items of 16 rows keep more loads in flight per
     // wavefront (T=16 69.4 -> 60.3 us, T=8 39.8 -> 35.6; 32 rows measured no better
@@ -598,6 +601,7 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
     float* s_xs = reinterpret_cast<float*>(s_x + (a.stage_x ? (size_t)T * H : 0));  // [T][H/32]
     if (tid < 32) s_used[tid] = 0u;
     if (tid < 16) s_race[tid] = -1;
+    if (tid == 0) s_bad = 0;
     for (int i = tid; i < MAXD; i += LTH) s_dcnt[i] = 0;
 
     // Wavefronts that poll must have no loads or stores of their own outstanding:
@@ -688,6 +692,7 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
                            &ctl->error, false, race, race ? &s_race[t] : nullptr, wave};
         const SelState sel = select_ids<VPL>(src, E, k, hs_, lane, s_ids[t]);
         if (sel.won) {
+            if (sel.timeout && lane == 0) s_bad = 1;
             if (lane < k) s_raw[t][lane] = sel.raw;
             if (lane == 0) s_gbits[t] = sel.gbits;
             if (wg == 0 && lane < k) a.ids[t * k + lane] = (int32_t)sel.id;
@@ -795,7 +800,10 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
             const int ent = s_dtok[dd][u], t = ent & 31, sl = ent >> 5;
             XSlice<CPL> xs;
             token_xslice<CPL>(a.stage_x, s_x, s_xs, a.x, t, H, lane, xs);
-            const uint32_t hp = pair_finish<CPL>(cur, H, xs, lane);
+            uint32_t hp = pair_finish<CPL>(cur, H, xs, lane);
+            // after a timed-out wait in this workgroup its h pairs are NaN, so the
+            // outputs of every token they reach are NaN rather than silently stale
+            if (s_bad) hp = 0x7FC07FC0u;
             if (lane == 0) {
                 const size_t w = ((size_t)t * S + sl) * npair + ip;
                 if constexpr (TT == 1) {
@@ -840,19 +848,21 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
             // one token: h from the copy that won this workgroup's logit race (the
             // copy on its half of the chip when both regions sit in one 2 MiB page)
             static_assert(LTH == 1024, "staging steps one 1024-word block at a time");
+            // (i0 = tid + 4 LTH m, so words i0 + LTH j, j < 4, sit at th_word(i0) + 2 LTH j)
             const int hc = s_race[0] >= T ? 1 : 0;
-            const uint64_t* src = TT == 1 ? a.th + th_word(0, hc) : a.th + (size_t)t * S * npair;
+            bool tmo = false;
             for (int i0 = tid; i0 < nw; i0 += LTH * 4) {
                 uint32_t v[4];
                 const int n = min(4, (nw - 1 - i0) / LTH + 1);
                 if constexpr (TT == 1)
-                    load_tagged_many<4>(src + i0, 2 * LTH, n, tag, &ctl->error, v);
+                    tmo |= load_tagged_many<4>(a.th + th_word(i0, hc), 2 * LTH, n, tag, &ctl->error, v);
                 else
-                    load_tagged_many<4>(src + i0, LTH, n, tag, &ctl->error, v);
+                    tmo |= load_tagged_many<4>(a.th + (size_t)t * S * npair + i0, LTH, n, tag, &ctl->error, v);
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     if (j < n) hsh[i0 + LTH * j] = v[j];
             }
+            if (tmo) s_bad = 1;
             __syncthreads();
             if constexpr (TT != 1) {
                 // the chunk sums of h, once per token (load_xslice's arithmetic, so
@@ -898,9 +908,11 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
             }
         }
         __syncthreads();
+        const bool bad = s_bad != 0;  // a timed-out wait here: y and out are NaN
         if (a.y) {
             for (int i = tid; i < n_dots; i += LTH)
-                a.y[((size_t)t * S + i / DR) * H + n0 + i % DR] = ysh[i / DR][i % DR];
+                a.y[((size_t)t * S + i / DR) * H + n0 + i % DR] = bad ? __uint_as_float(0x7FC00000u)
+                                                                      : ysh[i / DR][i % DR];
         }
         if (tid < DR) {
             float acc = 0.f;
@@ -909,7 +921,7 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
             uint32_t bb = f32_to_bf16(acc);
             const size_t o = (size_t)t * H + n0 + tid;
             if (a.residual) bb = f32_to_bf16(bf16_to_f32(a.residual[o]) + bf16_to_f32(bb));
-            a.out[o] = (uint16_t)bb;
+            a.out[o] = bad ? (uint16_t)0x7FC0u : (uint16_t)bb;
         }
         // More tokens: no barrier here. The next item writes the other ysh buffer, hsh
         // is not read after the barrier above, and this buffer is written again only
@@ -968,33 +980,45 @@ static size_t hsh_bytes(const moe_shape& sh) { return (size_t)n_slots(sh) * sh.i
 // LDS copy of x [T][H] with its chunk sums.
 static size_t xsh_bytes(const moe_shape& sh, int T) { return (size_t)T * sh.hidden * 2 + (size_t)T * (sh.hidden / 32) * 4; }
 
+typedef void (*LayerKernel)(LayerArgs);
+
 template <int CPL, int TT, int VPL>
-static void launch_layer_v(const LayerArgs& a, bool aff8, int G, size_t lds, hipStream_t hs) {
+static LayerKernel pick_layer_v(const LayerArgs& a, bool aff8) {
     if constexpr (CPL == 1 && VPL == 4) {
-        if (aff8 && a.H == 2048 && a.I == 512 && a.k == 8) {  // the served model's shape
-            hipLaunchKernelGGL((decode_layer_kernel<CPL, TT, true, VPL, 2048, 512, 8>), dim3(G), dim3(LTH), lds, hs,
-                               a);
-            return;
-        }
+        if (aff8 && a.H == 2048 && a.I == 512 && a.k == 8)  // the served model's shape
+            return decode_layer_kernel<CPL, TT, true, VPL, 2048, 512, 8>;
     }
-    if (aff8)
-        hipLaunchKernelGGL((decode_layer_kernel<CPL, TT, true, VPL, 0, 0, 0>), dim3(G), dim3(LTH), lds, hs, a);
-    else
-        hipLaunchKernelGGL((decode_layer_kernel<CPL, TT, false, VPL, 0, 0, 0>), dim3(G), dim3(LTH), lds, hs, a);
+    return aff8 ? decode_layer_kernel<CPL, TT, true, VPL, 0, 0, 0> : decode_layer_kernel<CPL, TT, false, VPL, 0, 0, 0>;
 }
 
 template <int CPL, int TT>
-static void launch_layer_tt(const LayerArgs& a, bool aff8, int G, size_t lds, hipStream_t hs) {
+static LayerKernel pick_layer_tt(const LayerArgs& a, bool aff8) {
     const int vpl = (a.E + 63) / 64;
-    if (vpl <= 1) launch_layer_v<CPL, TT, 1>(a, aff8, G, lds, hs);
-    else if (vpl <= 4) launch_layer_v<CPL, TT, 4>(a, aff8, G, lds, hs);
-    else launch_layer_v<CPL, TT, 16>(a, aff8, G, lds, hs);
+    if (vpl <= 1) return pick_layer_v<CPL, TT, 1>(a, aff8);
+    if (vpl <= 4) return pick_layer_v<CPL, TT, 4>(a, aff8);
+    return pick_layer_v<CPL, TT, 16>(a, aff8);
 }
 
-template <int CPL>
-static void launch_layer(const LayerArgs& a, bool aff8, int G, size_t lds, hipStream_t hs) {
-    if (a.T <= 1) launch_layer_tt<CPL, 1>(a, aff8, G, lds, hs);
-    else launch_layer_tt<CPL, 16>(a, aff8, G, lds, hs);
+// The kernel instance for a launch: hidden (chunks per lane), one token or more,
+// keys per lane of the selection, router format, and the served shape.
+static LayerKernel pick_layer(const LayerArgs& a, bool aff8) {
+    if (cpl_for(a.H) == 1) return a.T <= 1 ? pick_layer_tt<1, 1>(a, aff8) : pick_layer_tt<1, 16>(a, aff8);
+    return a.T <= 1 ? pick_layer_tt<2, 1>(a, aff8) : pick_layer_tt<2, 16>(a, aff8);
+}
+
+// Workgroups of kernel f (LTH threads, lds bytes of dynamic LDS) that one compute
+// unit can hold at once, cached per (instance, LDS size); 0 if the query fails.
+static int layer_blocks_per_cu(LayerKernel f, size_t lds) {
+    static std::mutex mu;
+    static std::map<std::pair<const void*, size_t>, int> cache;
+    std::lock_guard<std::mutex> lock(mu);
+    const auto key = std::make_pair(reinterpret_cast<const void*>(f), lds);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, f, LTH, lds) != hipSuccess) return 0;
+    cache[key] = nb;
+    return nb;
 }
 
 static int device_max_lds() {
@@ -1133,9 +1157,15 @@ extern "C" moe_status moe_decode_layer(const moe_shape* shape, const void* route
     a.stage_x = lds_h + lds_x + 16384 <= (size_t)max_lds ? 1 : 0;
     const size_t lds = lds_h + (a.stage_x ? lds_x : 0);
     const int G = std::min(cus, std::max(a.R, T * (a.H / DN_ROWS)));
-    const bool aff8 = sh.router_fmt == MOE_ROUTER_AFFINE8;
-    if (cpl_for(sh.hidden) == 1) launch_layer<1>(a, aff8, G, lds, hs);
-    else launch_layer<2>(a, aff8, G, lds, hs);
+    const LayerKernel f = pick_layer(a, sh.router_fmt == MOE_ROUTER_AFFINE8);
+    // the workgroups wait for each other, so all G must be resident at once
+    const int nb = layer_blocks_per_cu(f, lds);
+    if (nb <= 0 || (long long)nb * cus < G)
+        return fail(MOE_ERR_UNSUPPORTED, "decode layer: %d workgroups of %d threads with %zu bytes of LDS cannot all be "
+                    "resident (%d per compute unit, %d compute units)", G, LTH, lds, nb, cus);
+    void* args[] = {&a};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(f), dim3(G), dim3(LTH), args, lds, hs);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "decode_layer_kernel: %s", hipGetErrorString(e));
     return check_launch("decode_layer_kernel");
 }
 

@@ -172,9 +172,10 @@ __device__ __forceinline__ uint32_t load_tagged_wait(const uint64_t* p, uint32_t
 }
 
 // N tagged words at p[0], p[stride], ...: all loads issued at once, then only the
-// stale ones are polled again (bounded).
+// stale ones are polled again (bounded). Returns true if the wait timed out (the
+// error word is then set and out[] may hold stale values).
 template <int N>
-__device__ __forceinline__ void load_tagged_many(const uint64_t* p, int stride, int n, uint32_t tag, unsigned* err,
+__device__ __forceinline__ bool load_tagged_many(const uint64_t* p, int stride, int n, uint32_t tag, unsigned* err,
                                                  uint32_t* out) {
     uint64_t v[N];
 #pragma unroll
@@ -182,6 +183,7 @@ __device__ __forceinline__ void load_tagged_many(const uint64_t* p, int stride, 
         v[j] = j < n ? __hip_atomic_load(const_cast<uint64_t*>(p + (size_t)j * stride), __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT)
                      : ((uint64_t)tag << 32);
+    bool timed_out = false;
     for (unsigned it = 0;; ++it) {
         bool ok = true;
 #pragma unroll
@@ -189,6 +191,7 @@ __device__ __forceinline__ void load_tagged_many(const uint64_t* p, int stride, 
         if (ok) break;
         if (it >= SPIN_LIMIT) {
             atomicOr(err, 1u);
+            timed_out = true;
             break;
         }
         __builtin_amdgcn_s_sleep(1);
@@ -200,6 +203,7 @@ __device__ __forceinline__ void load_tagged_many(const uint64_t* p, int stride, 
     }
 #pragma unroll
     for (int j = 0; j < N; ++j) out[j] = (uint32_t)v[j];
+    return timed_out;
 }
 
 // As load_tagged_many, but every round reloads all n words together (0 <= n <= N;
@@ -210,16 +214,47 @@ __device__ __forceinline__ void load_tagged_many(const uint64_t* p, int stride, 
 // wait of its own, one round trip per stale word. For short lists of words that
 // few wavefronts wait on: the decode layer's selection with few tokens. With many
 // polling wavefronts the extra loads in flight slow the producers more than the
-// serial re-polls cost (measured at 16 tokens per launch).
+// serial re-polls cost (measured at 16 tokens per launch). Returns true if the
+// wait timed out.
+template <int N>
+__device__ __forceinline__ bool load_tagged_batch(const uint64_t* p, int stride, int n, uint32_t tag, unsigned* err,
+                                                  uint32_t* out) {
+    uint64_t v[N];
+    bool timed_out = false;
+    for (unsigned it = 0;; ++it) {
+#pragma unroll
+        for (int j = 0; j < N; ++j)
+            v[j] = __hip_atomic_load(const_cast<uint64_t*>(p + (size_t)(j < n ? j : 0) * stride), __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int j = 0; j < N; ++j) asm volatile("" : "+v"(v[j]));
+        bool ok = true;
+#pragma unroll
+        for (int j = 0; j < N; ++j) ok = ok && (j >= n || (uint32_t)(v[j] >> 32) == tag);
+        if (ok) break;
+        if (it >= SPIN_LIMIT) {
+            atomicOr(err, 1u);
+            timed_out = true;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+#pragma unroll
+    for (int j = 0; j < N; ++j) out[j] = j < n ? (uint32_t)v[j] : 0u;
+    return timed_out;
+}
+
 // As load_tagged_batch, for a race between wavefronts that poll copies of the
 // same words: *owner (LDS, -1 before the race) takes the id `me` of the first
 // wavefront whose words all carry the tag, or that gives up after SPIN_LIMIT
 // rounds (the error word is then set); the others stop at their next round.
-// Returns whether this wavefront won; only the winner's out[] is meaningful.
+// Returns whether this wavefront won; only the winner's out[] is meaningful, and
+// gave_up tells the winner that its words may be stale (it timed out).
 template <int N>
 __device__ __forceinline__ bool load_tagged_race(const uint64_t* p, int stride, int n, uint32_t tag, unsigned* err,
-                                                 int* owner, int me, uint32_t* out) {
+                                                 int* owner, int me, uint32_t* out, bool& gave_up) {
     uint64_t v[N];
+    gave_up = false;
     for (unsigned it = 0;; ++it) {
 #pragma unroll
         for (int j = 0; j < N; ++j)
@@ -233,6 +268,7 @@ __device__ __forceinline__ bool load_tagged_race(const uint64_t* p, int stride, 
         const bool give_up = it >= SPIN_LIMIT;
         if (__ballot(ok) == __ballot(true) || give_up) {
             if (give_up) atomicOr(err, 1u);
+            gave_up = give_up;
             int prev = 0;
             if ((threadIdx.x & 63) == 0) prev = atomicCAS(owner, -1, me);
             prev = __shfl(prev, 0);
@@ -243,31 +279,6 @@ __device__ __forceinline__ bool load_tagged_race(const uint64_t* p, int stride, 
         if (*reinterpret_cast<volatile int*>(owner) != -1) return false;
         __builtin_amdgcn_s_sleep(1);
     }
-}
-
-template <int N>
-__device__ __forceinline__ void load_tagged_batch(const uint64_t* p, int stride, int n, uint32_t tag, unsigned* err,
-                                                  uint32_t* out) {
-    uint64_t v[N];
-    for (unsigned it = 0;; ++it) {
-#pragma unroll
-        for (int j = 0; j < N; ++j)
-            v[j] = __hip_atomic_load(const_cast<uint64_t*>(p + (size_t)(j < n ? j : 0) * stride), __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-        for (int j = 0; j < N; ++j) asm volatile("" : "+v"(v[j]));
-        bool ok = true;
-#pragma unroll
-        for (int j = 0; j < N; ++j) ok = ok && (j >= n || (uint32_t)(v[j] >> 32) == tag);
-        if (ok) break;
-        if (it >= SPIN_LIMIT) {
-            atomicOr(err, 1u);
-            break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-    }
-#pragma unroll
-    for (int j = 0; j < N; ++j) out[j] = j < n ? (uint32_t)v[j] : 0u;
 }
 
 // DPP move of a 32-bit value (every lane must be active).

@@ -4,22 +4,17 @@
 //
 // GEMM operands (exact): activations enter as bf16; each int4 weight q enters the
 // MFMA as the bf16 value 1 + q/16 (exact), so one 64-wide group's MFMA partial is
-// P = sum x*(1 + q/16). With X = sum x over the same group the group's
-// contribution is 16*scale*P + (bias - 16*scale)*X. The first term is applied per
-// group on the accumulator (one fp32 FMA per output); the second, summed over the
-// groups, is itself a small product of row sums X[row][g] and column terms
-// c[col][g] = bias - 16*scale, done at the end of the tile on the matrix cores
-// with X and c each split into three bf16 parts (products exact, the neglected
-// parts below 2^-24 relative). X of the activations comes from a pre-pass, X of h
-// from the gate/up epilogue. No weight is rounded.
+// P = sum x*(1 + q/16). With X = sum x over the same group (two more MFMAs against
+// ones) the group's contribution is 16*scale*P + (bias - 16*scale)*X, added to the
+// accumulator group by group with two fp32 FMAs per output. No weight is rounded,
+// and every output's arithmetic depends only on its own activation row and weight
+// row: a row's result is the same in any tile, at any token count, run to run.
 //
 // Tiles: 128 expert-sorted rows x 256 weight rows per workgroup of four
 // wavefronts (gate/up: 128 gate + 128 up rows of the same 128 intermediate
 // columns; down: 256 output columns); wavefront w owns weight rows cs*64 + 16w ..
 // (cs < 4) over all 128 rows, with v_mfma_f32_16x16x32_bf16 in the main loop, so
 // every activation fragment read from LDS feeds four products.
-#include <type_traits>
-
 #include "mfma_common.h"
 #include "moe_internal.h"
 
@@ -33,9 +28,9 @@ struct Tile {
 
 // Workspace layout for moe_experts_prefill.
 struct PrefillWs {
-    size_t counts, offsets, cursor, ntiles, tiles, order, h, xs_x, xs_h, slices, total;
-    int max_tiles, gs_x, gs_h;  // group strides of the row-sum planes (x: multiple of 32, h: of 16)
-    int n_slices;               // pick slices of the dispatch
+    size_t counts, offsets, cursor, ntiles, tiles, order, h, slices, total;
+    int max_tiles;
+    int n_slices;  // pick slices of the dispatch
 };
 
 constexpr int SLICE = 2048;  // picks per slice (one workgroup of the dispatch each)
@@ -55,10 +50,6 @@ static PrefillWs prefill_ws_layout(const moe_shape& s, int T) {
     w.tiles = o;   o = align_up(o + sizeof(Tile) * (size_t)w.max_tiles, 256);
     w.order = o;   o = align_up(o + 4 * (size_t)T * S, 256);
     w.h = o;       o = align_up(o + 2 * (size_t)T * S * s.inter, 256);
-    w.gs_x = ((s.hidden / 64 + 31) / 32) * 32;
-    w.gs_h = ((s.inter / 64 + 15) / 16) * 16;
-    w.xs_x = o;    o = align_up(o + 3 * 2 * (size_t)T * w.gs_x, 256);      // [3][T][gs_x] bf16
-    w.xs_h = o;    o = align_up(o + 3 * 2 * (size_t)T * S * w.gs_h, 256);  // [3][T*S][gs_h] bf16
     w.n_slices = (int)((picks + SLICE - 1) / SLICE);
     w.slices = o;  o = align_up(o + 4 * (size_t)w.n_slices * s.n_experts, 256);  // [n_slices][E] counts
     w.total = o;
@@ -152,74 +143,27 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const int32_t* __restric
         for (int t = tid; t < T; t += blockDim.x) order[off[E] + t] = t * S + k;
 }
 
-// ---------------------------------------------------------------- row sums in three bf16 parts
-// v = hi + mid + lo: hi and mid are v and the remainder truncated to bf16 (both
-// remainders exact in fp32), lo the last remainder rounded to bf16.
-__device__ __forceinline__ void split3_bf16(float v, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
-    const uint32_t h = __float_as_uint(v) & 0xFFFF0000u;
-    const float r1 = v - __uint_as_float(h);
-    const uint32_t m = __float_as_uint(r1) & 0xFFFF0000u;
-    const float r2 = r1 - __uint_as_float(m);
-    hi = h >> 16;
-    mid = m >> 16;
-    lo = f32_to_bf16(r2);
-}
-
-// X[t][g] = sum of x[t][64g .. 64g+63] (a chain of bf16 dot2 against (1, 1)) for
-// g < H/64, zero for the padding groups up to gs; stored as three bf16 planes.
-// Within each block of 32 groups, group 4j + q sits at position 8q + j: the order
-// of the gate/up GEMM's bias operands (see bias_term there).
-__device__ __forceinline__ void xsum_entry(const uint16_t* __restrict__ x, int T, int H, int gs,
-                                           uint16_t* __restrict__ planes, long long idx) {
-    if (idx >= (long long)T * gs) return;
-    const int t = (int)(idx / gs), pos = (int)(idx % gs);
-    const int g = (pos & ~31) | ((pos & 7) << 2) | ((pos & 31) >> 3);
-    float sum = 0.f;
-    if (g < H / 64) {
-        const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)t * H + 64 * g);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const uint4 v = src[q];
-            sum = dot2_bf16(v.x, 0x3F803F80u, sum);
-            sum = dot2_bf16(v.y, 0x3F803F80u, sum);
-            sum = dot2_bf16(v.z, 0x3F803F80u, sum);
-            sum = dot2_bf16(v.w, 0x3F803F80u, sum);
-        }
-    }
-    uint32_t hi, mid, lo;
-    split3_bf16(sum, hi, mid, lo);
-    const size_t plane = (size_t)T * gs;
-    planes[idx] = (uint16_t)hi;
-    planes[plane + idx] = (uint16_t)mid;
-    planes[2 * plane + idx] = (uint16_t)lo;
-}
-
-// ---------------------------------------------------------------- set-up: dispatch and row sums
+// ---------------------------------------------------------------- set-up: dispatch
 // Two launches before the GEMMs. The picks p = t*k + s are cut into slices of SLICE
 // consecutive picks, one workgroup each.
-//   count: each slice's per-expert counts (an LDS histogram) go to slices[b][e]; the
-//     workgroups after the slices compute the row sums of x, one (token, group) per
-//     thread.
+//   count: each slice's per-expert counts (an LDS histogram) go to slices[b][e].
 //   scatter: every slice's workgroup reads the whole count matrix (n_slices x E) and
 //     derives the experts' totals, their offsets in the expert-sorted order and its
-//     own base within each expert (the sum over the earlier slices), then scatters
-//     its picks through LDS cursors. Workgroup 0 also writes the counts, the offsets,
-//     the shared expert's rows (it takes every token) and the tile list: every full
-//     tile first (expert order), then the partial tiles with the most row blocks
-//     first, so the items that start last are the cheapest.
-// The order of rows within an expert and of tiles within a size class are arbitrary;
-// no later step depends on them. Picks with an id outside [0, E) are skipped and
-// their y rows zeroed. A slice's picks are loaded before any is counted or placed.
+//     own base within each expert (the sum over the earlier slices), then places its
+//     picks in ascending pick order, 256 at a time: each wavefront ranks its 64 picks
+//     among the lower lanes holding the same id (one ballot per id bit), and the
+//     counts of the lower wavefronts come through LDS. Workgroup 0 also writes the
+//     counts, the offsets, the shared expert's rows (it takes every token) and the
+//     tile list: every full tile first (expert order), then the partial tiles with
+//     the most row blocks first (expert order within a size), so the items that
+//     start last are the cheapest.
+// Everything the two launches write is a function of the ids alone. Picks with an
+// id outside [0, E) are skipped and their y rows zeroed. A slice's picks are loaded
+// before any is counted or placed.
 constexpr int DT = 256, DPT = SLICE / DT;  // threads per workgroup, picks per thread
 
 __global__ __launch_bounds__(DT) void prefill_count_kernel(const int32_t* __restrict__ ids, long long P, int E,
-                                                           int n_slices, int32_t* __restrict__ slices,
-                                                           const uint16_t* __restrict__ x, int T, int H, int gs,
-                                                           uint16_t* __restrict__ planes) {
-    if ((int)blockIdx.x >= n_slices) {
-        xsum_entry(x, T, H, gs, planes, (long long)(blockIdx.x - n_slices) * DT + threadIdx.x);
-        return;
-    }
+                                                           int32_t* __restrict__ slices) {
     __shared__ int cnt[1024];
     const int tid = threadIdx.x;
     for (int i = tid; i < E; i += DT) cnt[i] = 0;
@@ -238,18 +182,30 @@ __global__ __launch_bounds__(DT) void prefill_count_kernel(const int32_t* __rest
     for (int i = tid; i < E; i += DT) slices[(size_t)blockIdx.x * E + i] = cnt[i];
 }
 
+// Lanes of this wavefront whose key equals this lane's (keys below 2^11), from one
+// ballot per key bit; every lane must be active.
+__device__ __forceinline__ uint64_t equal_key_lanes(uint32_t key) {
+    uint64_t m = ~0ull;
+#pragma unroll
+    for (int b = 0; b < 11; ++b) {
+        const uint64_t v = __ballot((key >> b) & 1u);
+        m &= ((key >> b) & 1u) ? v : ~v;
+    }
+    return m;
+}
+
 __global__ __launch_bounds__(DT) void prefill_scatter_kernel(
     const int32_t* __restrict__ ids, int T, int k, int E, int has_shared, int H, int n_slices,
     const int32_t* __restrict__ slices, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ ntiles, Tile* __restrict__ tiles, int32_t* __restrict__ order, float* __restrict__ y) {
-    __shared__ int cnt[1025];   // the experts' totals
-    __shared__ int off[1026];   // their offsets in the order
-    __shared__ int foff[1026];  // their full tiles' offsets in the tile list
-    __shared__ int cur[1024];   // this slice's cursors
-    __shared__ int bucket[9];   // partial tiles by row-block count (8 - n blocks)
+    __shared__ int cnt[1025];             // the experts' totals
+    __shared__ int off[1026];             // their offsets in the order
+    __shared__ int foff[1026];            // their full tiles' offsets in the tile list
+    __shared__ int cur[1024];             // this slice's next position per expert
+    __shared__ int wcnt[DT / 64][1024];   // picks per (wavefront, expert) among the current 256
     const int M = E + has_shared, S = k + has_shared;
-    const int tid = threadIdx.x, b = blockIdx.x;
-    if (tid < 9) bucket[tid] = 0;
+    const int tid = threadIdx.x, b = blockIdx.x, wave = tid >> 6, lane = tid & 63;
+    for (int i = tid; i < (DT / 64) * 1024; i += DT) (&wcnt[0][0])[i] = 0;
     const long long P = (long long)T * k, p0 = (long long)b * SLICE;
     int ev[DPT];
 #pragma unroll
@@ -302,25 +258,9 @@ __global__ __launch_bounds__(DT) void prefill_scatter_kernel(
     for (int e = tid; e < E; e += DT) cur[e] += off[e];
     if (b == 0) {
         for (int e = tid; e < M; e += DT) {
-            const int rem = cnt[e] % BM;
-            if (rem) atomicAdd(&bucket[8 - (rem + 15) / 16], 1);
-        }
-        __syncthreads();
-        if (tid == 0) {
-            int run = foff[M];
-            for (int q = 0; q < 9; ++q) {
-                const int c = bucket[q];
-                bucket[q] = run;
-                run += c;
-            }
-            *ntiles = run;
-            offsets[M] = off[M];
-        }
-        __syncthreads();
-        for (int e = tid; e < M; e += DT) {
             counts[e] = cnt[e];
             offsets[e] = off[e];
-            const int nfull = cnt[e] / BM, rem = cnt[e] % BM;
+            const int nfull = cnt[e] / BM;
             for (int q = 0; q < nfull; ++q) {
                 Tile tl;
                 tl.expert = e;
@@ -329,34 +269,75 @@ __global__ __launch_bounds__(DT) void prefill_scatter_kernel(
                 tl.pad = 0;
                 tiles[foff[e] + q] = tl;
             }
-            if (rem) {
-                Tile tl;
-                tl.expert = e;
-                tl.row0 = off[e] + nfull * BM;
-                tl.nrows = rem;
-                tl.pad = 0;
-                tiles[atomicAdd(&bucket[8 - (rem + 15) / 16], 1)] = tl;
-            }
         }
         if (has_shared)
             for (int t = tid; t < T; t += DT) order[off[E] + t] = t * S + k;
+        if (tid < 64) {
+            // partial tiles by size class q = 8 - (row blocks), in expert order within a
+            // class: count the classes, then place each tile at its class base plus its
+            // rank among the lower experts of the class
+            int tot[9], run[9];
+#pragma unroll
+            for (int q = 0; q < 9; ++q) tot[q] = 0;
+            for (int e0 = 0; e0 < M; e0 += 64) {
+                const int e = e0 + tid, rem = e < M ? cnt[e] % BM : 0;
+                const int cls = rem ? 8 - (rem + 15) / 16 : -1;
+#pragma unroll
+                for (int q = 0; q < 9; ++q) tot[q] += __popcll(__ballot(cls == q));
+            }
+            int acc = foff[M];
+#pragma unroll
+            for (int q = 0; q < 9; ++q) {
+                run[q] = acc;
+                acc += tot[q];
+            }
+            if (tid == 0) {
+                *ntiles = acc;
+                offsets[M] = off[M];
+            }
+            const uint64_t below = (1ull << tid) - 1ull;
+            for (int e0 = 0; e0 < M; e0 += 64) {
+                const int e = e0 + tid, rem = e < M ? cnt[e] % BM : 0;
+                const int cls = rem ? 8 - (rem + 15) / 16 : -1;
+#pragma unroll
+                for (int q = 0; q < 9; ++q) {
+                    const uint64_t m = __ballot(cls == q);
+                    if (cls == q) {
+                        Tile tl;
+                        tl.expert = e;
+                        tl.row0 = off[e] + (cnt[e] / BM) * BM;
+                        tl.nrows = rem;
+                        tl.pad = 0;
+                        tiles[run[q] + __popcll(m & below)] = tl;
+                    }
+                    run[q] += __popcll(m);
+                }
+            }
+        }
     }
     __syncthreads();
-    // token and slot of pick p0 + tid; when k divides DT, each later pick of this
-    // thread is DT / k tokens further at the same slot
-    const bool even = DT % k == 0;
-    const int tb = (int)((p0 + tid) / k), sb = (int)((p0 + tid) % k);
+    const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
     for (int j = 0; j < DPT; ++j) {
         const long long p = p0 + j * DT + tid;
-        if (p >= P) continue;
-        const int t = even ? tb + j * (DT / k) : (int)(p / k);
-        const int sl = even ? sb : (int)(p % k), e = ev[j];
-        if (e >= 0 && e < E) {
-            order[atomicAdd(&cur[e], 1)] = t * S + sl;
-        } else {
-            float* yr = y + ((size_t)t * S + sl) * H;
+        const int e = ev[j];
+        const bool ok = p < P && e >= 0 && e < E;
+        const uint64_t peers = equal_key_lanes(ok ? (uint32_t)e : 2047u);
+        const int rank = __popcll(peers & below);
+        if (ok && rank == 0) wcnt[wave][e] = __popcll(peers);
+        __syncthreads();
+        if (ok) {
+            int pos = cur[e] + rank;
+            for (int w2 = 0; w2 < wave; ++w2) pos += wcnt[w2][e];
+            order[pos] = (int)(p / k) * S + (int)(p % k);
+        } else if (p < P) {
+            float* yr = y + ((size_t)(p / k) * S + (size_t)(p % k)) * H;
             for (int n = 0; n < H; ++n) yr[n] = 0.f;
+        }
+        __syncthreads();
+        if (ok && rank == 0) {  // every lane has read cur and the counts: advance, clear
+            atomicAdd(&cur[e], __popcll(peers));
+            wcnt[wave][e] = 0;
         }
     }
 }
@@ -417,12 +398,9 @@ struct GemmArgs {
     const int32_t* order;
     uint16_t* hbuf;             // h [T*S][I] bf16, expert-sorted rows (written by gate/up, read by down)
     float* y;                   // down: [T][S][H]
-    const uint16_t* xs_a;       // row-sum planes of this GEMM's A rows
-    uint16_t* xs_h;             // gate/up: row-sum planes of h (written)
-    int T, gs_a, gs_h;
+    int T;
 };
 
-typedef short short4_t __attribute__((ext_vector_type(4)));
 
 // Direct global-to-LDS loads from base + off (base wavefront-uniform, off per lane):
 // lane l's 16 (or 4) bytes land at LDS byte address lds + 16 l (4 l); lds is
@@ -471,22 +449,15 @@ __device__ __forceinline__ void wait_chunks(int later) {
     }
 }
 
-__device__ __forceinline__ f32x4_t mfma16x16x16(uint2 a, uint2 b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, a), __builtin_bit_cast(short4_t, b),
-                                                     c, 0, 0, 0);
-}
-
 // GATEUP: weight rows 0..127 are gate rows cb*128 .., rows 128..255 the matching up
-// rows; the epilogue writes h = bf16(silu(gate) * up) and the row sums of that h
-// block (two groups of the down GEMM's K). Else (down): weight rows are down rows
-// cb*256 ..; the epilogue writes y[t][s][n] for the row's pick p = order[row].
+// rows; the epilogue writes h = bf16(silu(gate) * up). Else (down): weight rows are
+// down rows cb*256 ..; the epilogue writes y[t][s][n] for the row's pick p = order[row].
 template <bool GATEUP>
 __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
     constexpr int NCS = NBR / 64;  // 16-column sets per wavefront
     constexpr int HALF = NBR / 2;  // gate/up: gate rows 0 .. HALF-1, up rows HALF .. NBR-1
     extern __shared__ __attribute__((aligned(16))) uint8_t ring[];  // ring of stages, each (A | B | sb)
     __shared__ uint32_t arow_lds[BM];  // byte offset of each tile row in its source, ~0 beyond the tile
-    __shared__ int32_t asrc_lds[BM];   // row of each tile row in its row-sum planes
     __shared__ int32_t pick_lds[BM];   // down: pick p = order[row] of each tile row (its y row)
     const int H = a.H, I = a.I, S = a.S;
     const int K = GATEUP ? H : I;
@@ -509,7 +480,6 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
             off = (uint32_t)src * (uint32_t)(2 * K);
         }
         arow_lds[tid] = off;
-        asrc_lds[tid] = src;
         if constexpr (!GATEUP) pick_lds[tid] = tid < tl.nrows ? a.order[tl.row0 + tid] : 0;
     }
     __syncthreads();
@@ -536,12 +506,6 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
     auto gblock = [&](int jb) -> int { return blk0 + jb < nblk_mat ? blk0 + jb : blk0; };
     const size_t q_region = GATEUP ? a.L.gu_q : a.L.down_q, sb_region = GATEUP ? a.L.gu_sb : a.L.down_sb;
     const int G = K / 64;
-    // byte offset from ebase of the (scale, bias) word of weight row br, group g
-    auto brow_sb_word = [&](int br, int g) -> size_t {
-        int jb, slot;
-        brow_block(br, jb, slot);
-        return sb_region + ((size_t)gblock(jb) * G + g) * 16 + 4 * slot;
-    };
 
     // ---- ring layout within a stage:
     //   A: the loaded rows x 128 B, the 16-byte piece p of row r at position p ^ (r & 7);
@@ -571,121 +535,6 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
     for (int m = 0; m < 8; ++m)
 #pragma unroll
         for (int cs = 0; cs < NCS; ++cs) acc[m][cs] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // ---- bias term: sum over groups of X[row][g] * (bias - 16 scale)[col][g] on the
-    // matrix cores, KG groups per MFMA (gate/up: 32 with v_mfma_f32_16x16x32_bf16; down,
-    // whose K has few groups: 16 with v_mfma_f32_16x16x16_bf16), computed first: its
-    // loads go out while the ring fills, and the accumulators start from it. When one
-    // step covers every group, the tile rows' X planes arrive by direct loads in the
-    // ring's last stage (free until the loop's first refill) at xs_st, plane stride
-    // xs_ps bytes, row stride 2 KG bytes; else (and for later steps) from memory.
-    constexpr int KG = GATEUP ? 32 : 16;
-    constexpr int GPL = KG / 4;  // groups per lane and MFMA
-    using frag_t = typename std::conditional<GATEUP, uint4, uint2>::type;
-    auto bmfma = [](const frag_t& x, const frag_t& c, f32x4_t v) -> f32x4_t {
-        if constexpr (GATEUP) return mfma16x16x32(x, c, v);
-        else return mfma16x16x16(x, c, v);
-    };
-    auto pack_frag = [](const uint32_t* v) -> frag_t {  // GPL bf16 values -> fragment
-        if constexpr (GATEUP)
-            return make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
-        else return make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
-    };
-    auto bias_term = [&](auto nm_tag, const uint8_t* xs_st, int xs_ps) __attribute__((always_inline)) {
-        constexpr int NM = decltype(nm_tag)::value;
-        const size_t plane = (size_t)(GATEUP ? a.T : a.T * S) * a.gs_a;
-        for (int kb = 0; kb < (G + KG - 1) / KG; ++kb) {
-            // k slot 8 lg + i of the step: group 4i + lg for gate/up (whose x row sums are
-            // stored in that order), so the 16 lanes of a row block read the four
-            // consecutive groups' words of their blocks, 64-byte runs; group 4 lg + i for
-            // down. Every lane loads a valid word (groups past G read the last group,
-            // blocks past the matrix block 0) and zeroes afterwards what it must not use
-            // (scale 0, bias 0: c = 0). The empty asm statements keep the loads ahead of
-            // that test: a load the compiler moves under it gets a branch of its own and
-            // a wait for every outstanding load, so the loads would go out one at a time.
-            uint32_t w[NCS][GPL];
-#pragma unroll
-            for (int cs = 0; cs < NCS; ++cs) {
-                const int br = cs * 64 + 16 * wave + lc;
-#pragma unroll
-                for (int i = 0; i < GPL; ++i) {
-                    const int g = GATEUP ? KG * kb + 4 * i + lg : KG * kb + GPL * lg + i;
-                    w[cs][i] = *reinterpret_cast<const uint32_t*>(ebase + brow_sb_word(br, g < G ? g : G - 1));
-                }
-            }
-#pragma unroll
-            for (int cs = 0; cs < NCS; ++cs)
-#pragma unroll
-                for (int i = 0; i < GPL; ++i) asm volatile("" : "+v"(w[cs][i]));
-#pragma unroll
-            for (int cs = 0; cs < NCS; ++cs) {
-                const bool ok = brow_ok(cs * 64 + 16 * wave + lc);
-#pragma unroll
-                for (int i = 0; i < GPL; ++i) {
-                    const int g = GATEUP ? KG * kb + 4 * i + lg : KG * kb + GPL * lg + i;
-                    if (!(ok && g < G)) w[cs][i] = 0u;
-                }
-            }
-            frag_t ch[NCS], cm[NCS], cl[NCS];
-#pragma unroll
-            for (int cs = 0; cs < NCS; ++cs) {
-                uint32_t h[GPL], md[GPL], l[GPL];
-#pragma unroll
-                for (int i = 0; i < GPL; ++i) {
-                    const float cc = bf16_to_f32(w[cs][i] >> 16) - 16.f * bf16_to_f32(w[cs][i] & 0xFFFFu);
-                    split3_bf16(cc, h[i], md[i], l[i]);
-                }
-                ch[cs] = pack_frag(h);
-                cm[cs] = pack_frag(md);
-                cl[cs] = pack_frag(l);
-            }
-            const bool xlds = xs_st != nullptr && kb == 0;
-            if (xlds) {  // every wavefront's X loads are in LDS
-                wait_vmcnt<0>();
-                lds_barrier();
-            }
-            // row blocks in batches (their X loads together), to bound registers
-            constexpr int MBMAX = 2;
-            constexpr int MB = NM < MBMAX ? NM : MBMAX;
-#pragma unroll
-            for (int m0 = 0; m0 < NM; m0 += MB) {
-                frag_t xv[MB][3];
-#pragma unroll
-                for (int mm = 0; mm < MB; ++mm) {
-                    const int row = 16 * (m0 + mm) + lc;
-                    const frag_t z{};
-                    xv[mm][0] = xv[mm][1] = xv[mm][2] = z;
-                    if (xlds) {
-                        const uint8_t* xp = xs_st + row * (2 * KG) + 2 * GPL * lg;
-                        xv[mm][0] = *reinterpret_cast<const frag_t*>(xp);
-                        xv[mm][1] = *reinterpret_cast<const frag_t*>(xp + xs_ps);
-                        xv[mm][2] = *reinterpret_cast<const frag_t*>(xp + 2 * xs_ps);
-                    } else if (row < tl.nrows) {
-                        const uint16_t* xp = a.xs_a + (size_t)asrc_lds[row] * a.gs_a + KG * kb + GPL * lg;
-                        xv[mm][0] = *reinterpret_cast<const frag_t*>(xp);
-                        xv[mm][1] = *reinterpret_cast<const frag_t*>(xp + plane);
-                        xv[mm][2] = *reinterpret_cast<const frag_t*>(xp + 2 * plane);
-                    }
-                }
-#pragma unroll
-                for (int mm = 0; mm < MB; ++mm) {
-#pragma unroll
-                    for (int cs = 0; cs < NCS; ++cs) {
-                        f32x4_t v = acc[m0 + mm][cs];
-                        v = bmfma(xv[mm][0], ch[cs], v);
-                        v = bmfma(xv[mm][0], cm[cs], v);
-                        v = bmfma(xv[mm][1], ch[cs], v);
-                        v = bmfma(xv[mm][0], cl[cs], v);
-                        v = bmfma(xv[mm][2], ch[cs], v);
-                        v = bmfma(xv[mm][1], cm[cs], v);
-                        acc[m0 + mm][cs] = v;
-                    }
-                }
-                if constexpr (MB < NM)
-                    if (!xlds) __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-    };
-
     // The K loop is instantiated for 1, 2, 4 and 8 row blocks of 16 (the tile's count
     // rounded up), so its body is straight-line code the compiler can interleave.
     auto kloop = [&](auto nm_tag) __attribute__((always_inline)) {
@@ -696,11 +545,6 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
         constexpr int STAGE = SA + B_BYTES + SB_BYTES;
         constexpr int NS = RING / STAGE;          // stages: 5, 4 or 3
         static_assert(NS >= 3 && NS * STAGE <= RING && LPC * (NS - 2) < 64, "ring");
-        // Tiles of up to 64 rows stream weights faster than they use the VALU, so they
-        // add the bias term chunk by chunk instead of before the loop: the chunk's row
-        // sums X come from two more MFMAs against ones, and c = bias - 16 scale from the
-        // (scale, bias) word the chunk already holds; one more fp32 FMA per output.
-        constexpr bool INB = NM <= 4;
         const uint32_t arow0 = arow_lds[0];       // row 0 is always inside the tile
         uint32_t a_off[NA];
 #pragma unroll
@@ -733,51 +577,28 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
                 b1[cs] = bfrag(*reinterpret_cast<const uint32_t*>(bp + 16));
                 const uint32_t w = sb_st[4 * jb + slot];
                 s16[cs] = 16.f * bf16_to_f32(w & 0xFFFFu);
-                if constexpr (INB) cb16[cs] = brow_ok(cs * 64 + 16 * wave + lc) ? bf16_to_f32(w >> 16) - s16[cs] : 0.f;
+                cb16[cs] = brow_ok(cs * 64 + 16 * wave + lc) ? bf16_to_f32(w >> 16) - s16[cs] : 0.f;
             }
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
                 const uint8_t* ar = st + (16 * m + lc) * 128;
                 const uint4 a0 = *reinterpret_cast<const uint4*>(ar + 16 * (lg ^ (lc & 7)));
                 const uint4 a1 = *reinterpret_cast<const uint4*>(ar + 16 * ((4 + lg) ^ (lc & 7)));
-                f32x4_t xs{0.f, 0.f, 0.f, 0.f};  // INB: the chunk's row sums (every column alike)
-                if constexpr (INB) {
-                    const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
-                    xs = mfma16x16x32(a0, ones, xs);
-                    xs = mfma16x16x32(a1, ones, xs);
-                }
+                // the chunk's row sums X (every column alike)
+                const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+                f32x4_t xs = mfma16x16x32(a0, ones, f32x4_t{0.f, 0.f, 0.f, 0.f});
+                xs = mfma16x16x32(a1, ones, xs);
 #pragma unroll
                 for (int cs = 0; cs < NCS; ++cs) {
                     f32x4_t p = mfma16x16x32(a0, b0[cs], f32x4_t{0.f, 0.f, 0.f, 0.f});
                     p = mfma16x16x32(a1, b1[cs], p);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        if constexpr (INB) acc[m][cs][r] = fmaf(xs[r], cb16[cs], fmaf(s16[cs], p[r], acc[m][cs][r]));
-                        else acc[m][cs][r] = fmaf(s16[cs], p[r], acc[m][cs][r]);
-                    }
+                    for (int r = 0; r < 4; ++r) acc[m][cs][r] = fmaf(xs[r], cb16[cs], fmaf(s16[cs], p[r], acc[m][cs][r]));
                 }
             }
         };
         const int NC = K / KC;
         for (int c = 0; c < NS - 1 && c < NC; ++c) issue(c);
-        if constexpr (INB) {
-        } else if (G <= KG) {
-            // the X planes of the tile's 32 NA staged rows (rows beyond the tile read row 0)
-            // into the last stage: plane p, row r at p * XR * 2KG + r * 2KG
-            constexpr int XROW = 2 * KG, RPI = 1024 / XROW, LPX = XROW / 16;
-            constexpr int XR = 32 * NA, NIX = 3 * XR / RPI;
-            static_assert(3 * XR * XROW <= STAGE, "X planes fit in a stage");
-            const uint32_t xl = ring_lds + (uint32_t)((NS - 1) * STAGE);
-            const size_t plane_b = (size_t)(GATEUP ? a.T : a.T * S) * a.gs_a * 2;
-            for (int j = wave; j < NIX; j += 4) {
-                const int p = j / (XR / RPI), r = (j % (XR / RPI)) * RPI + lane / LPX;
-                const uint32_t off = (uint32_t)((size_t)asrc_lds[r] * a.gs_a * 2 + 16 * (lane % LPX));
-                lds_dma16(reinterpret_cast<const uint8_t*>(a.xs_a) + p * plane_b, off, xl + j * 1024);
-            }
-            bias_term(nm_tag, ring + (size_t)(NS - 1) * STAGE, XR * XROW);
-        } else {
-            bias_term(nm_tag, nullptr, 0);
-        }
         for (int c = 0; c < NC; ++c) {
             // this wavefront's loads of chunk c are done once only the later chunks'
             // (at most NS - 2 of them) are left
@@ -800,8 +621,7 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
         // h = bf16(silu(gate) * up) for this block's 128 intermediate columns i =
         // col0 + c, c = 64 hs + 16 wave + lc (gate set hs, up set 2 + hs), staged as a
         // bf16 tile in LDS (rows beyond the tile hold zeros), then stored with 16-byte
-        // row pieces; each (row, 64-column group) sum of the stored bf16 values, in
-        // column order in fp32, goes to the down GEMM's X planes.
+        // row pieces.
         constexpr int HS = 128 + 8;  // tile row stride (bf16)
         uint16_t* hl = reinterpret_cast<uint16_t*>(ring);
 #pragma unroll
@@ -827,36 +647,6 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
             if (row < tl.nrows && col0 + 8 * pc < I)
                 *reinterpret_cast<uint4*>(a.hbuf + (size_t)(tl.row0 + row) * I + col0 + 8 * pc) =
                     *reinterpret_cast<const uint4*>(hl + row * HS + 8 * pc);
-        }
-        {
-            const int row = tid >> 1, hs = tid & 1, g = col0 / 64 + hs;
-            if (row < tl.nrows && col0 + 64 * hs < I) {
-                float xs = 0.f;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(hl + row * HS + 64 * hs + 8 * j);
-                    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        xs += __uint_as_float(w4[q] << 16);
-                        xs += __uint_as_float(w4[q] & 0xFFFF0000u);
-                    }
-                }
-                uint32_t hi, mid, lo;
-                split3_bf16(xs, hi, mid, lo);
-                const size_t plane = (size_t)a.T * S * a.gs_h;
-                uint16_t* xp = a.xs_h + (size_t)(tl.row0 + row) * a.gs_h;
-                xp[g] = (uint16_t)hi;
-                xp[plane + g] = (uint16_t)mid;
-                xp[2 * plane + g] = (uint16_t)lo;
-                if (col0 == 0 && hs == 0) {  // padding groups of the planes
-                    for (int gp = I / 64; gp < a.gs_h; ++gp) {
-                        xp[gp] = 0;
-                        xp[plane + gp] = 0;
-                        xp[2 * plane + gp] = 0;
-                    }
-                }
-            }
         }
     } else {
         // y[order[row]][col0 + n], n < 256, staged 64 rows at a time as an fp32 tile in
@@ -900,6 +690,22 @@ using namespace moe;
 extern "C" size_t moe_prefill_workspace_bytes(const moe_shape* shape, int32_t T) {
     if (validate_shape(shape) != MOE_OK || T < 1) return 0;
     return prefill_ws_layout(*shape, T).total;
+}
+
+extern "C" moe_status moe_prefill_dispatch_layout(const moe_shape* shape, int32_t T, moe_prefill_dispatch_view* v) {
+    clear_error();
+    moe_status st = validate_shape(shape);
+    if (st != MOE_OK) return st;
+    if (T < 1 || !v) return fail(MOE_ERR_INVALID_ARG, "T = %d or NULL view", T);
+    const PrefillWs W = prefill_ws_layout(*shape, T);
+    v->counts = W.counts;
+    v->offsets = W.offsets;
+    v->ntiles = W.ntiles;
+    v->tiles = W.tiles;
+    v->order = W.order;
+    v->max_tiles = W.max_tiles;
+    v->pad = 0;
+    return MOE_OK;
 }
 
 extern "C" moe_status moe_dispatch(const moe_shape* shape, const int32_t* ids, int32_t T, int32_t* counts,
@@ -947,13 +753,9 @@ extern "C" moe_status moe_experts_prefill(const moe_shape* shape, const void* ex
     Tile* tiles = (Tile*)(w + W.tiles);
     int32_t* order = (int32_t*)(w + W.order);
     uint16_t* hbuf = (uint16_t*)(w + W.h);
-    uint16_t* xs_x = (uint16_t*)(w + W.xs_x);
-    uint16_t* xs_h = (uint16_t*)(w + W.xs_h);
-    const long long nsum = (long long)T * W.gs_x;
     int32_t* slices = (int32_t*)(w + W.slices);
     const long long P = (long long)T * sh.top_k;
-    hipLaunchKernelGGL(prefill_count_kernel, dim3((unsigned)(W.n_slices + (nsum + DT - 1) / DT)), dim3(DT), 0, hs, ids,
-                       P, sh.n_experts, W.n_slices, slices, x, T, H, W.gs_x, xs_x);
+    hipLaunchKernelGGL(prefill_count_kernel, dim3((unsigned)W.n_slices), dim3(DT), 0, hs, ids, P, sh.n_experts, slices);
     if ((st = check_launch("prefill_count_kernel")) != MOE_OK) return st;
     hipLaunchKernelGGL(prefill_scatter_kernel, dim3((unsigned)W.n_slices), dim3(DT), 0, hs, ids, T, sh.top_k,
                        sh.n_experts, sh.has_shared, H, W.n_slices, slices, counts, offsets, ntiles, tiles, order, y);
@@ -971,16 +773,9 @@ extern "C" moe_status moe_experts_prefill(const moe_shape* shape, const void* ex
     ga.hbuf = hbuf;
     ga.y = y;
     ga.T = T;
-    ga.gs_h = W.gs_h;
-    ga.xs_a = xs_x;
-    ga.xs_h = xs_h;
-    ga.gs_a = W.gs_x;
     hipLaunchKernelGGL((expert_gemm_kernel<true>), dim3(xcd_grid(W.max_tiles, (I + NBR / 2 - 1) / (NBR / 2))), dim3(256),
                        RING, hs, ga);
     if ((st = check_launch("expert_gemm_kernel<gate/up>")) != MOE_OK) return st;
-    ga.xs_a = xs_h;
-    ga.xs_h = nullptr;
-    ga.gs_a = W.gs_h;
     hipLaunchKernelGGL((expert_gemm_kernel<false>), dim3(xcd_grid(W.max_tiles, (H + NBR - 1) / NBR)), dim3(256), RING, hs,
                        ga);
     return check_launch("expert_gemm_kernel<down>");

@@ -50,24 +50,27 @@ struct SelState {
     uint32_t raw;    // lane i < k: pick i's fp32 logit bits
     uint32_t gbits;  // every lane: the shared gate's fp32 logit bits
     bool won;        // false: another wavefront of a polling race selects this token (nothing written)
+    bool timeout;    // a bounded wait for tagged logits timed out: the picks come from stale words
 };
 
 template <int VPL>
 __device__ __forceinline__ SelState select_ids(const LogitSrc& lr, int E, int k, int has_shared, int lane,
                                                int32_t* sel_id) {
     uint32_t raw[VPL + 1];
+    bool tmo = false;
     if (lr.tagged) {
         // this lane's logits lane + 64 j < E, and the shared gate (index E) in the same batch
         const int R = E + (has_shared ? 1 : 0);
         const int n = lane < R ? (R - 1 - lane) / 64 + 1 : 0;
         if (lr.race) {
             if (!load_tagged_race<VPL + 1>(lr.tagged + (lane < R ? lane : 0), 64, n, lr.tag, lr.err, lr.race, lr.me,
-                                           raw))
-                return SelState{0u, 0u, 0u, false};
+                                           raw, tmo))
+                return SelState{0u, 0u, 0u, false, false};
         } else if (lr.batch)
-            load_tagged_batch<VPL + 1>(lr.tagged + (lane < R ? lane : 0), 64, n, lr.tag, lr.err, raw);
+            tmo = load_tagged_batch<VPL + 1>(lr.tagged + (lane < R ? lane : 0), 64, n, lr.tag, lr.err, raw);
         else
-            load_tagged_many<VPL + 1>(lr.tagged + lane, 64, n, lr.tag, lr.err, raw);
+            tmo = load_tagged_many<VPL + 1>(lr.tagged + lane, 64, n, lr.tag, lr.err, raw);
+        tmo = __ballot(tmo) != 0;
     } else {
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
@@ -141,7 +144,7 @@ __device__ __forceinline__ SelState select_ids(const LogitSrc& lr, int E, int k,
     }
     my_id = my_id < (uint32_t)E ? my_id : (uint32_t)(E - 1);
     if (lane < k) sel_id[lane] = (int32_t)my_id;
-    return SelState{my_id, my_raw, gbits, true};
+    return SelState{my_id, my_raw, gbits, true, tmo};
 }
 
 __device__ __forceinline__ uint16_t select_weights(const SelState& st, int k, int lane) {

@@ -97,7 +97,7 @@ def pick_path(T: int) -> str:
 
 def layer_step(layer: DeviceLayer, x: torch.Tensor, buf: StepBuffers, path: Optional[str] = None,
                residual: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None, stream=None):
-    """One layer on one stream. path "fused" (T <= 16): moe_decode_layer (three launches);
+    """One layer on one stream. path "fused" (T <= 16): moe_decode_layer (one launch);
     "decode" / "prefill": moe_route, then moe_experts_decode or moe_experts_prefill, then
     moe_combine."""
     sh, T = layer.shape, buf.T
@@ -118,11 +118,14 @@ def layer_step(layer: DeviceLayer, x: torch.Tensor, buf: StepBuffers, path: Opti
 
 def stack_step(layers, x: torch.Tensor, xn: torch.Tensor, buf: StepBuffers, eps: float = 1e-6,
                path: Optional[str] = None, stream=None, keep: Optional[list] = None):
-    """x <- bf16(x + MoE(bf16(RMSNorm(x)))) for every layer, in place on x."""
+    """x <- bf16(x + MoE(bf16(RMSNorm(x)))) for every layer, in place on x. With
+    `keep`, a copy of every layer's output state, normalised input and picks is
+    appended to it as (x, xn, ids) (device copies, made on the stream; under graph capture they live in
+    the graph's memory and hold the last replay's values)."""
     sh = layers[0].shape
     for L in layers:
         moe.moe_rmsnorm(sh.hidden, x, buf.T, eps, xn, stream)
         layer_step(L, xn, buf, path, residual=x, out=x, stream=stream)
         if keep is not None:
-            keep.append(x.clone())
+            keep.append((x.clone(), xn.clone(), buf.ids.clone()))
     return x

@@ -49,6 +49,12 @@ class Shape(ctypes.Structure):
         return self.n_experts + self.has_shared
 
 
+class PrefillDispatchView(ctypes.Structure):
+    _fields_ = [("counts", ctypes.c_size_t), ("offsets", ctypes.c_size_t), ("ntiles", ctypes.c_size_t),
+                ("tiles", ctypes.c_size_t), ("order", ctypes.c_size_t), ("max_tiles", ctypes.c_int32),
+                ("pad", ctypes.c_int32)]
+
+
 class ExpertCanon(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("q_gate", "s_gate", "b_gate", "q_up", "s_up", "b_up", "q_down", "s_down", "b_down")]
@@ -89,6 +95,8 @@ _lib.moe_dispatch.restype = _I32
 _lib.moe_dispatch.argtypes = [_S, _P, _I32, _P, _P, _P, _P]
 _lib.moe_prefill_workspace_bytes.restype = _SZ
 _lib.moe_prefill_workspace_bytes.argtypes = [_S, _I32]
+_lib.moe_prefill_dispatch_layout.restype = _I32
+_lib.moe_prefill_dispatch_layout.argtypes = [_S, _I32, ctypes.POINTER(PrefillDispatchView)]
 _lib.moe_experts_prefill.restype = _I32
 _lib.moe_experts_prefill.argtypes = [_S, _P, _P, _I32, _P, _P, _SZ, _P, _P]
 _lib.moe_combine.restype = _I32
@@ -99,7 +107,8 @@ _lib.moe_rmsnorm.argtypes = [_I32, _P, _I32, ctypes.c_float, _P, _P]
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_last_error", "moe_shape_check",
            "moe_experts_packed_bytes", "moe_pack_experts", "moe_router_packed_bytes", "moe_pack_router",
            "moe_route", "moe_route_from_logits", "moe_decode_workspace_bytes", "moe_experts_decode", "moe_decode_layer",
-           "moe_decode_layer_check", "moe_dispatch", "moe_prefill_workspace_bytes", "moe_experts_prefill", "moe_combine", "moe_rmsnorm")
+           "moe_decode_layer_check", "moe_dispatch", "moe_prefill_workspace_bytes", "moe_prefill_dispatch_layout",
+           "moe_experts_prefill", "moe_combine", "moe_rmsnorm")
 
 
 def library_path() -> str:
@@ -204,6 +213,12 @@ def moe_decode_layer_check(shape, T, ws, stream=None):
 def moe_dispatch(shape, ids, T, counts, offsets, order, stream=None):
     _check(_lib.moe_dispatch(ctypes.byref(shape), _ptr(ids), T, _ptr(counts), _ptr(offsets), _ptr(order),
                              _stream(stream)), "moe_dispatch")
+
+
+def moe_prefill_dispatch_layout(shape, T) -> PrefillDispatchView:
+    v = PrefillDispatchView()
+    _check(_lib.moe_prefill_dispatch_layout(ctypes.byref(shape), T, ctypes.byref(v)), "moe_prefill_dispatch_layout")
+    return v
 
 
 def moe_experts_prefill(shape, experts_packed, x, T, ids, ws, y, stream=None):

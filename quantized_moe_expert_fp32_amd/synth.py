@@ -21,6 +21,8 @@ Storage formats (the "canonical" layout every consumer reads):
   * int4 matrix [rows, cols]: uint8 [rows, cols/2], element 2j in the low
     nibble of byte j, element 2j+1 in the high nibble. Values q in 0..15.
     scale and bias are bf16 [rows, cols/64]; the weight is scale*q + bias.
+  * int8 expert matrix [rows, cols] (8-bit experts): uint8 [rows, cols], q in
+    0..255, scale and bias as above.
   * int8 router [E+1, H]: uint8 q in 0..255, scale and bias bf16 [E+1, H/64].
   * fp32 router [E+1, H]: float32.
   * Experts are stacked [E+1, ...]; index E is the shared expert. Router row E
@@ -33,6 +35,9 @@ Draw order for one layer, rng = numpy.random.default_rng([seed, 1000 + layer]):
        packed nibbles  rng.integers(0, 256, rows*cols/2, uint8)
        scale           rng.uniform(0.002, 0.02, rows*cols/64) -> fp32 -> bf16
        bias            -8 * scale (exact in bf16)
+     (8-bit experts, shape.bits == 8: codes rng.integers(0, 256, rows*cols, uint8),
+     scale rng.uniform(0.002, 0.02, rows*cols/64) / 16 -> fp32 -> bf16, bias
+     -128 * scale: the same weight range as the 4-bit matrices)
 Activations: numpy.random.default_rng([seed, 1]).standard_normal((T, H)) -> fp32 -> bf16.
 
 bf16 values are produced from fp32 draws by torch's round-to-nearest-even cast
@@ -170,6 +175,16 @@ def _int4_matrix(rng: np.random.Generator, n: int, rows: int, cols: int):
     return q, s_bits, b_bits
 
 
+def _int8_matrix(rng: np.random.Generator, n: int, rows: int, cols: int):
+    """8-bit affine codes with the int4 matrices' weight range: q uniform 0..255,
+    scale bf16(U(0.002, 0.02) / 16), bias -128 * scale (exact in bf16)."""
+    q = rng.integers(0, 256, size=(n, rows, cols), dtype=np.uint8)
+    scale32 = (rng.uniform(0.002, 0.02, size=(n, rows, cols // GROUP)) / 16.0).astype(np.float32)
+    s_bits = _to_bf16_bits(scale32)
+    b_bits = _to_bf16_bits(np.float32(-128.0) * bf16_bits_to_f32(s_bits))
+    return q, s_bits, b_bits
+
+
 def make_layer(shape: Shape, seed: int, layer: int = 0, zipf: bool = False) -> Layer:
     rng = np.random.default_rng([seed, 1000 + layer])
     H, I, E = shape.hidden, shape.inter, shape.n_experts
@@ -184,9 +199,10 @@ def make_layer(shape: Shape, seed: int, layer: int = 0, zipf: bool = False) -> L
     if zipf:
         r = rng.permutation(E) + 1
         L.logit_bias = (-1.1 * np.log(r.astype(np.float64))).astype(np.float32)
-    L.q_gate, L.s_gate, L.b_gate = _int4_matrix(rng, M, I, H)
-    L.q_up, L.s_up, L.b_up = _int4_matrix(rng, M, I, H)
-    L.q_down, L.s_down, L.b_down = _int4_matrix(rng, M, H, I)
+    mat = _int8_matrix if shape.bits == 8 else _int4_matrix
+    L.q_gate, L.s_gate, L.b_gate = mat(rng, M, I, H)
+    L.q_up, L.s_up, L.b_up = mat(rng, M, I, H)
+    L.q_down, L.s_down, L.b_down = mat(rng, M, H, I)
     return L
 
 

@@ -1,16 +1,6 @@
 """GPU parity: every stage of the HIP path (called through the C ABI) against the
-FP64 oracle on the same seeded inputs.
+FP64 oracle on the same seeded inputs. The bars are stated in tests/_parity.py."""
 
-Bars (routing contract of TensorFold issue #931, "What I'd build"; staged
-reference per projection class from its "Gate" section):
-  * integer work (picks, dispatch) bit-exact; end-to-end picks exempt a token whose
-    top k+1 oracle logits hold an adjacent gap below 1e-5 (counted);
-  * pick and shared weights bit-exact when computed from the same fp32 logits;
-  * logits within 1 fp32 ulp of the oracle's fp32 rounding of the fp64 sum;
-  * layer outputs: |gpu - ref| <= max(2 bf16 ulp(ref), 1e-2 |ref|, 1e-2 rms(ref row)).
-"""
-
-import functools
 import itertools
 
 import numpy as np
@@ -19,97 +9,10 @@ import torch
 
 from oracle import moe_oracle as O
 from quantized_moe_expert_fp32_amd import synth
+from tests._parity import (_L, case, check_logits, check_picks, dev_layer, out_tolerance_check, record_stats,
+                           run_path, staged_layer_check, staged_route_check)
 
 pytestmark = pytest.mark.gpu
-
-
-# ------------------------------------------------------------------ helpers
-
-@functools.lru_cache(maxsize=None)
-def case(name, T=None):
-    return synth.make_case(name, T=T)
-
-
-def _L():
-    from quantized_moe_expert_fp32_amd import layer as L
-
-    return L
-
-
-def dev_layer(gpu, c, idx=0, shape=None):
-    L = _L()
-    sh = shape or L.make_shape(c.shape)
-    return L.DeviceLayer(sh, c.layers[idx])
-
-
-def run_path(gpu, dl, x_np, path):
-    """route -> experts -> combine on the GPU; returns numpy copies of every stage."""
-    L = _L()
-    T = x_np.shape[0]
-    buf = L.alloc_buffers(dl.shape, T, path)
-    x = L.to_device(x_np)
-    L.layer_step(dl, x, buf, path)
-    torch.cuda.synchronize()
-    return dict(logits=buf.logits.cpu().numpy(), ids=buf.ids.cpu().numpy(), w=L.bits_to_numpy(buf.w),
-                wsh=None if buf.wsh is None else L.bits_to_numpy(buf.wsh), y=buf.y.cpu().numpy(),
-                out=L.bits_to_numpy(buf.out))
-
-
-def out_tolerance_check(gpu_bits, ref_bits, rows=None):
-    g = O.bf16_to_f64(gpu_bits)
-    r = O.bf16_to_f64(ref_bits)
-    if rows is not None:
-        g, r = g[rows], r[rows]
-    err = np.abs(g - r)
-    ulp = O.bf16_ulp(r)
-    rms = np.sqrt(np.mean(r * r, axis=1, keepdims=True))
-    tol = np.maximum(np.maximum(2 * ulp, 1e-2 * np.abs(r)), 1e-2 * rms)
-    bad = err > tol
-    stats = dict(max_ulp=float((err / ulp).max()), frac_gt_2ulp=float((err > 2 * ulp).mean()),
-                 frac_exact=float((err == 0).mean()), n_bad=int(bad.sum()))
-    assert stats["n_bad"] == 0, stats
-    return stats
-
-
-def check_logits(gpu_logits, ref_logits, fp64_path=True):
-    """fp64-accumulated logits (T <= 16): within 1 fp32 ulp of the oracle's.
-    Matrix-core logits (T > 16, fp32 accumulation): within 2e-6 absolute."""
-    g = gpu_logits.astype(np.float32)
-    r = ref_logits.astype(np.float32)
-    if not fp64_path:
-        d = np.abs(g.astype(np.float64) - r.astype(np.float64))
-        assert d.max() <= 2e-6, d.max()
-        return float((d == 0).mean())
-    gi = g.view(np.int32).astype(np.int64)
-    ri = r.view(np.int32).astype(np.int64)
-    diff = np.abs(gi - ri)
-    assert diff.max() <= 1, diff.max()
-    return float((diff == 0).mean())
-
-
-def check_picks(gpu_ids, ref_logits, k, E):
-    ref_ids = O.topk(ref_logits[:, :E], k)
-    tie = O.near_tie_tokens(ref_logits[:, :E], k)
-    mism = (gpu_ids != ref_ids).any(axis=1)
-    assert not (mism & ~tie).any(), np.nonzero(mism & ~tie)
-    return int(tie.sum()), int((mism & tie).sum())
-
-
-def staged_route_check(gpu, res, E, k, has_shared=True):
-    """Selection step from the GPU's own logits: ids, weights and shared weight bit-exact."""
-    lg = res["logits"]
-    ids = O.topk(lg[:, :E], k)
-    assert np.array_equal(res["ids"], ids)
-    assert np.array_equal(res["w"], O.pick_weights(lg[:, :E], ids))
-    if has_shared:
-        assert np.array_equal(res["wsh"], O.shared_weight(lg[:, E]))
-
-
-def staged_layer_check(res, x_np, host_layer, E, has_shared=True):
-    """Oracle experts and combine fed the GPU's picks and weights."""
-    y, _ = O.expert_outputs(x_np, res["ids"], host_layer, E, has_shared)
-    out = O.combine(y, res["w"], res["wsh"] if has_shared else None)
-    return out_tolerance_check(res["out"], out), y
 
 
 # ------------------------------------------------------------------ packing
@@ -391,8 +294,10 @@ def test_decode_vs_prefill_same_tokens(gpu):
     # paths, a slot moves by about one bf16 step of h times the down weights
     rms = np.sqrt(np.mean(a["y"] ** 2, axis=2, keepdims=True))
     rel = (np.abs(a["y"] - b["y"]) / rms).max(axis=2)
+    record_stats(what="decode_vs_prefill_slots", n=int(rel.size), max_rel=float(rel.max()),
+                 frac_gt_1e4=float((rel > 1e-4).mean()))
     assert rel.max() < 1e-2
-    assert (rel > 1e-4).mean() < 0.25
+    assert (rel > 1e-4).mean() < 0.08  # measured 3.5 %: slots with an h rounding flip
     out_tolerance_check(b["out"], a["out"])
 
 
@@ -405,8 +310,8 @@ def test_prefill_full_size(gpu, name):
     W = O.router_matrix(c.layers[0])
     ref_logits = O.router_logits(c.x, W, c.layers[0].logit_bias, E)
     check_logits(res["logits"], ref_logits, fp64_path=False)
-    n_tie, n_flip = check_picks(res["ids"], ref_logits, k, E)
-    print(name, "near-tie tokens", n_tie, "flipped among them", n_flip)
+    n_tie, n_set, n_order = check_picks(res["ids"], ref_logits, k, E)
+    print(name, "near-tie tokens", n_tie, "set differs", n_set, "order differs", n_order)
     staged_route_check(gpu, res, E, k)
     stats, _ = staged_layer_check(res, c.x, c.layers[0], E)
     print(name, stats)
@@ -535,28 +440,3 @@ def test_rmsnorm(gpu):
     assert (o[0] == 0x3F80).all()
     d = np.abs(o.astype(np.int32) - ref.astype(np.int32))
     assert d.max() <= 1 and (d > 0).mean() < 1e-3
-
-
-@pytest.mark.parametrize("T", [1, 16])
-def test_stack_layers_staged(gpu, T):
-    """Three stacked layers: each layer's GPU output against the oracle layer fed the
-    GPU's own input to that layer (exact staged layer references)."""
-    L = _L()
-    c = synth.make_case("stack", T=T, n_layers=3)
-    sh = L.make_shape(c.shape)
-    layers = [L.DeviceLayer(sh, hl) for hl in c.layers]
-    x = L.to_device(c.x)
-    xn = torch.empty_like(x)
-    buf = L.alloc_buffers(sh, T, "decode")
-    keep = []
-    L.stack_step(layers, x, xn, buf, keep=keep)
-    torch.cuda.synchronize()
-    xs = [c.x] + [L.bits_to_numpy(k) for k in keep]
-    for l in range(3):
-        xin = xs[l]
-        xnorm = O.rmsnorm_bf16(xin)
-        st = O.layer_forward(xnorm, c.layers[l], 8)
-        ref = O.residual_bf16(xin, st["out"])
-        tie = O.near_tie_tokens(st["logits"][:, :256], 8)
-        rows = ~tie
-        out_tolerance_check(xs[l + 1], ref, rows=rows)

@@ -112,6 +112,25 @@ def test_generator_weights_are_exact_in_fp32():
     assert np.array_equal(w.astype(np.float32).astype(np.float64), w)
     w = O.dequant_int4(L.q_down, L.s_down, L.b_down)
     assert np.array_equal(w.astype(np.float32).astype(np.float64), w)
+    # 8-bit experts: scale*q + bias has at most 16 significant bits
+    sh = synth.Shape(hidden=256, inter=64, n_experts=4, top_k=2, bits=8)
+    L8 = synth.make_layer(sh, 3, 0)
+    for q, sc, b in ((L8.q_gate, L8.s_gate, L8.b_gate), (L8.q_down, L8.s_down, L8.b_down)):
+        w = O.dequant_expert(q, sc, b, 8)
+        assert np.array_equal(w.astype(np.float32).astype(np.float64), w)
+        assert np.array_equal(w, O.dequant_int8(q, sc, b))
+
+
+def test_dequant_expert_by_bit_width():
+    """4-bit codes come two per byte (low nibble first), 8-bit codes one per byte."""
+    s = np.array([[0x3F80]], dtype=np.uint16)  # scale 1
+    b = np.array([[0xC100]], dtype=np.uint16)  # bias -8
+    q4 = np.full((1, 32), 0x5A, dtype=np.uint8)  # codes 10, 5, 10, 5, ...
+    assert O.dequant_expert(q4, s, b, 4)[0, :4].tolist() == [2.0, -3.0, 2.0, -3.0]
+    q8 = np.arange(64, dtype=np.uint8).reshape(1, 64) + 100
+    assert O.dequant_expert(q8, s, b, 8)[0, :3].tolist() == [92.0, 93.0, 94.0]
+    with pytest.raises(ValueError):
+        O.dequant_expert(q8, s, b, 3)
 
 
 # ------------------------------------------------------------------ a1 router logits
@@ -293,22 +312,23 @@ def test_worked_layer_golden():
     assert (O.bf16_to_f64(st["out"]) == ex["out_value"]).all()
 
 
-def _random_layer(rng, H, I, E, router_fp32=True):
+def _random_layer(rng, H, I, E, router_fp32=True, bits=4):
     from quantized_moe_expert_fp32_amd import synth
 
     shape = synth.Shape(hidden=H, inter=I, n_experts=E, top_k=2, has_shared=1,
-                        router_fmt=synth.ROUTER_F32 if router_fp32 else synth.ROUTER_AFFINE8)
+                        router_fmt=synth.ROUTER_F32 if router_fp32 else synth.ROUTER_AFFINE8, bits=bits)
     return synth.make_layer(shape, int(rng.integers(0, 2 ** 31)), 0)
 
 
-def _bruteforce_layer(x_bits, L, E, k):
+def _bruteforce_layer(x_bits, L, E, k, bits=4):
     """The contract evaluated with exact rationals (dot products) and 60-digit
-    decimals (exp, sigmoid), reading the canonical bytes directly."""
+    decimals (exp, sigmoid), reading the canonical bytes directly (two codes per
+    byte at 4 bits, one at 8)."""
     T, H = x_bits.shape
     I = L.q_gate.shape[1]
 
     def wmat(q, s, b, e, r):
-        qs = X.unpack_int4_row(q[e, r])
+        qs = X.unpack_int4_row(q[e, r]) if bits == 4 else [int(v) for v in q[e, r]]
         return [X.frac_of_bf16(int(s[e, r, c // 64])) * qs[c] + X.frac_of_bf16(int(b[e, r, c // 64]))
                 for c in range(len(qs))]
 
@@ -361,6 +381,26 @@ def test_bruteforce_exact_tiny_layer():
         assert st["ids"][t].tolist() == bf[t]["ids"]
         assert st["w"][t].tolist() == bf[t]["w"]
         assert int(st["wsh"][t]) == bf[t]["wsh"]
+        for s in range(k + 1):
+            assert st["h"][t, s].tolist() == bf[t]["h"][s]
+        assert st["out"][t].tolist() == bf[t]["out"]
+
+
+def test_bruteforce_exact_tiny_layer_8bit_experts():
+    """The same exact evaluation with 8-bit affine experts (one code per byte, groups of 64)."""
+    rng = np.random.default_rng(2025)
+    H, I, E, k = 64, 64, 4, 2
+    L = _random_layer(rng, H, I, E, bits=8)
+    assert L.q_gate.shape == (E + 1, I, H) and O.expert_bits(L) == 8
+    L.router_f32 = (L.router_f32 * 10).astype(np.float32)
+    from quantized_moe_expert_fp32_amd import synth
+
+    x = synth.random_x(78, 2, H)
+    st = O.layer_forward(x, L, top_k=k, has_shared=True)
+    bf = _bruteforce_layer(x, L, E, k, bits=8)
+    for t in range(2):
+        assert st["ids"][t].tolist() == bf[t]["ids"]
+        assert st["w"][t].tolist() == bf[t]["w"]
         for s in range(k + 1):
             assert st["h"][t, s].tolist() == bf[t]["h"][s]
         assert st["out"][t].tolist() == bf[t]["out"]
@@ -446,3 +486,73 @@ def test_dispatch_matches_bruteforce():
         want = [t * S + s for t in range(T) for s in range(S)
                 if (ids[t, s] == e if s < k else e == E)]
         assert order[offsets[e]:offsets[e + 1]].tolist() == want
+
+
+# ------------------------------------------------------------------ comparison helpers (the test bars)
+
+def test_bf16_ulp_closed_forms():
+    """Spacing of bf16 values: 8 significant bits, subnormal step 2^-133."""
+    v = np.array([1.0, 1.99, 2.0, 0.75, -3.0, 2.0 ** -126, 2.0 ** -130, 0.0, -0.0, 3e38, 2.0 ** -133])
+    want = [2.0 ** -7, 2.0 ** -7, 2.0 ** -6, 2.0 ** -8, 2.0 ** -6, 2.0 ** -133, 2.0 ** -133, 2.0 ** -133,
+            2.0 ** -133, 2.0 ** 120, 2.0 ** -133]
+    assert O.bf16_ulp(v).tolist() == want
+
+
+def test_bf16_ulp_equals_next_bf16_step_exhaustive():
+    """For every finite positive bf16 value but the largest, the next bf16 value
+    (bit pattern + 1) lies bf16_ulp above it; zero's next value is 2^-133."""
+    p = np.arange(0, 0x7F7F, dtype=np.uint32)
+    here = (p << 16).view(np.float32).astype(np.float64)
+    nxt = ((p + 1) << 16).view(np.float32).astype(np.float64)
+    assert np.array_equal(nxt - here, O.bf16_ulp(here))
+    assert np.array_equal(O.bf16_ulp(-here), O.bf16_ulp(here))
+
+
+def _tie_logits(rank, gap, E=12):
+    """fp32 logits 0.5 - 0.01 j for rank j (expert id = rank), except that rank
+    rank+1 sits `gap` below rank `rank` (and the later ranks keep their spacing)."""
+    v = 0.5 - 0.01 * np.arange(E, dtype=np.float64)
+    v[rank + 1:] += (v[rank] - gap) - v[rank + 1]
+    return v.astype(np.float32)[None, :]
+
+
+@pytest.mark.parametrize("rank,tie_set", [(2, False), (3, True), (4, False)])
+def test_near_tie_tokens_only_at_the_k_boundary(rank, tie_set):
+    """k = 4: a gap below 1e-5 exempts the set of picks only between ranks k and k+1
+    (0-based 3 and 4); between k-1 and k or k+1 and k+2 it does not; above 1e-5 never."""
+    k = 4
+    lo = _tie_logits(rank, 0.9e-5)
+    hi = _tie_logits(rank, 1.1e-5)
+    g_lo = float(lo[0, rank]) - float(lo[0, rank + 1])
+    g_hi = float(hi[0, rank]) - float(hi[0, rank + 1])
+    assert g_lo < 1e-5 < g_hi  # the fp32 values keep the gaps on their sides of 1e-5
+    assert O.near_tie_tokens(lo, k).tolist() == [tie_set]
+    assert O.near_tie_tokens(hi, k).tolist() == [False]
+
+
+def test_picks_within_ties_accepts_only_near_tie_swaps():
+    k = 4
+    ref = np.array([[0, 1, 2, 3]])
+    # exact picks pass and are not exemptions
+    ok, se, oe = O.picks_within_ties(ref, _tie_logits(1, 0.5e-2), k)
+    assert ok.tolist() == [True] and not se.any() and not oe.any()
+    # order swap inside the top k across a near tie (ranks 2, 3): passes, same set
+    swapped = np.array([[0, 1, 3, 2]])
+    ok, se, oe = O.picks_within_ties(swapped, _tie_logits(2, 0.9e-5), k)
+    assert ok.tolist() == [True] and oe.tolist() == [True] and not se.any()
+    ok, _, _ = O.picks_within_ties(swapped, _tie_logits(2, 1.1e-5), k)
+    assert ok.tolist() == [False]
+    # set change across the k / k+1 near tie (rank 4 instead of rank 3): passes, other set
+    other = np.array([[0, 1, 2, 4]])
+    ok, se, oe = O.picks_within_ties(other, _tie_logits(3, 0.9e-5), k)
+    assert ok.tolist() == [True] and se.tolist() == [True] and not oe.any()
+    ok, _, _ = O.picks_within_ties(other, _tie_logits(3, 1.1e-5), k)
+    assert ok.tolist() == [False]
+    # a near tie between ranks k+1 and k+2 exempts nothing: rank 5 in place of rank 3 fails
+    ok, _, _ = O.picks_within_ties(np.array([[0, 1, 2, 5]]), _tie_logits(4, 0.9e-5), k)
+    assert ok.tolist() == [False]
+    # planted mistakes: a far pick, a repeated id, an id out of range
+    tie = _tie_logits(3, 0.9e-5)
+    for bad in ([0, 1, 2, 9], [0, 1, 2, 2], [0, 1, 2, 12], [0, 1, 2, -1]):
+        ok, _, _ = O.picks_within_ties(np.array([bad]), tie, k)
+        assert ok.tolist() == [False], bad
