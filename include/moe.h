@@ -175,6 +175,19 @@ moe_status moe_experts_decode(const moe_shape* shape, const void* experts_packed
                               const uint16_t* x, int32_t T, const int32_t* ids, void* ws,
                               size_t ws_bytes, float* y, void* stream);
 
+/* moe_experts_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. The h rows go to a device array inside the
+ * library (1,114,112 bytes: 16 tokens x 17 slots x 2048 intermediate values;
+ * larger T * S * inter is refused with MOE_ERR_UNSUPPORTED), one per GPU, held
+ * until the process ends. The call allocates nothing and gives the same y as
+ * moe_experts_decode bit for bit. Every call on a GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (other streams, other host threads)
+ * race and must be ordered by the caller. Errors as moe_experts_decode. */
+moe_status moe_experts_decode_noalloc(const moe_shape* shape, const void* experts_packed,
+                                      const uint16_t* x, int32_t T, const int32_t* ids, float* y,
+                                      void* stream);
+
 /* The whole decode layer (1 <= T <= 16) in one launch: router logits, selection,
  * the gate/up GEMV with SwiGLU, and the down GEMV with the combine (same
  * arithmetic as moe_route, moe_experts_decode and moe_combine, so the outputs are

@@ -1086,6 +1086,20 @@ static moe_status check_decode_args(const moe_shape* shape, const void* experts_
     return MOE_OK;
 }
 
+// The two launches of the staged expert stage (gate/up with SwiGLU into hbuf,
+// then down into y); hbuf holds T * S * I bf16 values.
+static moe_status launch_decode_experts(const moe_shape& sh, const uint8_t* p, const uint16_t* x, int T,
+                                        const int32_t* ids, uint16_t* hbuf, float* y, hipStream_t hs) {
+    const ExpertLayout L = expert_layout(sh);
+    launch_gateup(sh, L, p, x, T, ids, hbuf, hs);
+    moe_status st = check_launch("decode_gateup_kernel");
+    if (st != MOE_OK) return st;
+    hipLaunchKernelGGL(decode_down_kernel, dim3(sh.hidden / DN_ROWS, T), dim3(256), hsh_bytes(sh), hs, p, L, sh.hidden,
+                       sh.inter, sh.n_experts, sh.top_k, sh.has_shared, hbuf, ids, y, (const uint16_t*)nullptr,
+                       (const uint16_t*)nullptr, (const uint16_t*)nullptr, (uint16_t*)nullptr);
+    return check_launch("decode_down_kernel");
+}
+
 extern "C" moe_status moe_experts_decode(const moe_shape* shape, const void* experts_packed, const uint16_t* x,
                                          int32_t T, const int32_t* ids, void* ws, size_t ws_bytes, float* y,
                                          void* stream) {
@@ -1093,18 +1107,55 @@ extern "C" moe_status moe_experts_decode(const moe_shape* shape, const void* exp
     moe_status st = check_decode_args(shape, experts_packed, x, T, ws, ws_bytes);
     if (st != MOE_OK) return st;
     if (!ids || !y || !aligned16(y)) return fail(MOE_ERR_INVALID_ARG, "ids or y NULL / unaligned");
-    const moe_shape& sh = *shape;
-    const ExpertLayout L = expert_layout(sh);
-    hipStream_t hs = (hipStream_t)stream;
-    const uint8_t* p = (const uint8_t*)experts_packed;
-    uint16_t* hbuf = (uint16_t*)ws;
-    launch_gateup(sh, L, p, x, T, ids, hbuf, hs);
-    if ((st = check_launch("decode_gateup_kernel")) != MOE_OK) return st;
-    hipLaunchKernelGGL(decode_down_kernel, dim3(sh.hidden / DN_ROWS, T), dim3(256), hsh_bytes(sh), hs, p, L, sh.hidden,
-                       sh.inter,
-                       sh.n_experts, sh.top_k, sh.has_shared, hbuf, ids, y, (const uint16_t*)nullptr,
-                       (const uint16_t*)nullptr, (const uint16_t*)nullptr, (uint16_t*)nullptr);
-    return check_launch("decode_down_kernel");
+    return launch_decode_experts(*shape, (const uint8_t*)experts_packed, x, T, ids, (uint16_t*)ws, y,
+                                 (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------- allocation-free staged decode
+// moe_experts_decode_noalloc keeps the bf16 h rows in this file-scope array instead
+// of a caller workspace: at most 16 tokens x 17 slots x 2048 intermediate values.
+// Each GPU holds its own copy until the process ends. In host code `scratch` names
+// a host-side stand-in, never the device memory: kernels and copies get the
+// address from scratch_device_ptr().
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)16 * 17 * 2048 * 2;
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device: looked up with
+// hipGetSymbolAddress on the first call on each device (with that device current)
+// and kept per device. NULL if the lookup fails.
+static void* scratch_device_ptr() {
+    static std::mutex mu;
+    static void* ptr[64] = {nullptr};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        ptr[dev] = p;
+    }
+    return ptr[dev];
+}
+
+extern "C" moe_status moe_experts_decode_noalloc(const moe_shape* shape, const void* experts_packed,
+                                                 const uint16_t* x, int32_t T, const int32_t* ids, float* y,
+                                                 void* stream) {
+    clear_error();
+    moe_status st = validate_shape(shape);
+    if (st != MOE_OK) return st;
+    if (T < 1 || T > 16) return fail(MOE_ERR_INVALID_ARG, "decode path takes 1..16 rows, got T = %d", T);
+    if (!experts_packed || !x || !ids || !y || !aligned16(experts_packed) || !aligned16(x) || !aligned16(y))
+        return fail(MOE_ERR_INVALID_ARG, "NULL or unaligned pointer");
+    if (hsh_bytes(*shape) > 65536)
+        return fail(MOE_ERR_UNSUPPORTED, "decode path: (top_k + shared) * inter * 2 bytes must fit 64 KiB of LDS");
+    const size_t need = (size_t)T * n_slots(*shape) * shape->inter * 2;
+    if (need > NOALLOC_SCRATCH_BYTES)
+        return fail(MOE_ERR_UNSUPPORTED, "h rows of %zu bytes exceed the %zu-byte device scratch", need,
+                    NOALLOC_SCRATCH_BYTES);
+    void* hbuf = scratch_device_ptr();
+    if (!hbuf) return fail(MOE_ERR_HIP, "could not look up the device address of the decode scratch");
+    return launch_decode_experts(*shape, (const uint8_t*)experts_packed, x, T, ids, (uint16_t*)hbuf, y,
+                                 (hipStream_t)stream);
 }
 
 extern "C" moe_status moe_decode_layer(const moe_shape* shape, const void* router_packed, const float* logit_bias,

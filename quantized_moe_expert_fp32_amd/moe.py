@@ -87,6 +87,8 @@ _lib.moe_decode_workspace_bytes.restype = _SZ
 _lib.moe_decode_workspace_bytes.argtypes = [_S, _I32]
 _lib.moe_experts_decode.restype = _I32
 _lib.moe_experts_decode.argtypes = [_S, _P, _P, _I32, _P, _P, _SZ, _P, _P]
+_lib.moe_experts_decode_noalloc.restype = _I32
+_lib.moe_experts_decode_noalloc.argtypes = [_S, _P, _P, _I32, _P, _P, _P]
 _lib.moe_decode_layer.restype = _I32
 _lib.moe_decode_layer.argtypes = [_S, _P, _P, _P, _P, _I32, _P, _SZ, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.moe_decode_layer_check.restype = _I32
@@ -106,7 +108,8 @@ _lib.moe_rmsnorm.argtypes = [_I32, _P, _I32, ctypes.c_float, _P, _P]
 
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_last_error", "moe_shape_check",
            "moe_experts_packed_bytes", "moe_pack_experts", "moe_router_packed_bytes", "moe_pack_router",
-           "moe_route", "moe_route_from_logits", "moe_decode_workspace_bytes", "moe_experts_decode", "moe_decode_layer",
+           "moe_route", "moe_route_from_logits", "moe_decode_workspace_bytes", "moe_experts_decode",
+           "moe_experts_decode_noalloc", "moe_decode_layer",
            "moe_decode_layer_check", "moe_dispatch", "moe_prefill_workspace_bytes", "moe_prefill_dispatch_layout",
            "moe_experts_prefill", "moe_combine", "moe_rmsnorm")
 
@@ -190,6 +193,11 @@ def moe_route_from_logits(shape, logits, T, ids, w, w_shared, stream=None):
 def moe_experts_decode(shape, experts_packed, x, T, ids, ws, y, stream=None):
     _check(_lib.moe_experts_decode(ctypes.byref(shape), _ptr(experts_packed), _ptr(x), T, _ptr(ids), _ptr(ws),
                                    _nbytes(ws), _ptr(y), _stream(stream)), "moe_experts_decode")
+
+
+def moe_experts_decode_noalloc(shape, experts_packed, x, T, ids, y, stream=None):
+    _check(_lib.moe_experts_decode_noalloc(ctypes.byref(shape), _ptr(experts_packed), _ptr(x), T, _ptr(ids),
+                                           _ptr(y), _stream(stream)), "moe_experts_decode_noalloc")
 
 
 def moe_decode_layer(shape, router_packed, logit_bias, experts_packed, x, T, ws, logits, ids, w, w_shared, y,
