@@ -36,6 +36,9 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 
 EXPERT_BYTES = 1_769_472  # gate+up+down q and scale/bias for H=2048, I=512
+# 8-bit experts: one code per byte and one (scale, bias) pair per 64 codes (the
+# packed form carries one more word per group: 3,538,944 B)
+EXPERT_BYTES_8BIT = 3 * 2048 * 512 + 3 * 2048 * 512 // 64 * 4
 ROUTER_BYTES = 559_232
 
 
@@ -45,7 +48,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill512", "prefill4096", "stack1", "stack16"])
+                    choices=["decode", "prefill512", "prefill4096", "stack1", "stack16", "decode_8bit",
+                             "prefill512_8bit"])
     ap.add_argument("--copies", type=int, default=8, help="independent weight sets for the decode workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", action="store_true", help="measure the chosen workload alone (no sub-records)")
@@ -171,7 +175,7 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-WORKLOADS = ("decode", "prefill512", "prefill4096", "stack1", "stack16")
+WORKLOADS = ("decode", "prefill512", "prefill4096", "stack1", "stack16", "decode_8bit", "prefill512_8bit")
 METRIC = "MoE-layer tokens/s (decode bs1, prefill 512/4096) + % HBM/MFMA roofline"
 
 
@@ -184,13 +188,15 @@ class Inputs:
         from quantized_moe_expert_fp32_amd import synth
 
         t0 = time.time()
+        self.bits = 8 if wl.endswith("_8bit") else 4
+        wl = wl.replace("_8bit", "")
         if wl == "decode":
-            base = synth.make_case("decode")
+            base = synth.make_case("decode", bits=self.bits)
             self.hosts = [base.layers[0]] + [synth.make_layer(base.shape, base.seed, c) for c in range(1, copies)]
             self.x_host = np.concatenate([base.x, synth.random_x(base.seed, 63, 2048)], axis=0)
             self.T = 1
         elif wl in ("prefill512", "prefill4096"):
-            base = synth.make_case(wl)
+            base = synth.make_case(wl, bits=self.bits)
             self.hosts = [base.layers[0]]
             self.x_host = base.x
             self.T = base.T
@@ -203,7 +209,7 @@ class Inputs:
             self.hosts = cache["stack_hosts"]
             self.x_host = base.x
         self.shape = L.make_shape(base.shape)
-        key = "stack_layers" if wl.startswith("stack") else wl + "_layers"
+        key = "stack_layers" if wl.startswith("stack") else "%s_%d_layers" % (wl, self.bits)
         if key not in cache:
             cache[key] = [L.DeviceLayer(self.shape, h) for h in self.hosts]
         self.layers = cache[key]
@@ -226,19 +232,20 @@ def run_workload(wl, K, W, inp, no_cpu, cpu_seconds):
 
     T, shape, layers, xs = inp.T, inp.shape, inp.layers, inp.x
     path = L.pick_path(T)
+    kind = wl.replace("_8bit", "")
     buf = L.alloc_buffers(shape, T, path)
     S = shape.slots
     log("%s: %d weight sets, set-up %.1f s" % (wl, len(layers), inp.setup_s))
 
     # ---------------------------------------------------------------- the step sequence
-    if wl.startswith("stack"):
+    if kind.startswith("stack"):
         x_state = xs.clone()
         xn = torch.empty_like(x_state)
         period = 1
 
         def step(j):
             L.stack_step(layers, x_state, xn, buf, path=path)
-    elif wl == "decode":
+    elif kind == "decode":
         period = xs.shape[0]  # 64 consecutive steps cover every token and every weight copy
 
         def step(j):
@@ -306,14 +313,14 @@ def run_workload(wl, K, W, inp, no_cpu, cpu_seconds):
     log("%s: timed region %d steps in %.4f s (%.2f us per step on the stream)" % (wl, K, elapsed, region_us / K))
 
     # ---------------------------------------------------------------- dominant stage (HIP events on its stream)
-    n_ev = min(max(K, 8), 512 if not wl.startswith("stack") else 200)
+    n_ev = min(max(K, 8), 512 if not kind.startswith("stack") else 200)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     with torch.cuda.stream(stream):
         torch.cuda._sleep(200_000_000)  # keep the GPU busy while the host queues the measured launches
         for j in range(n_ev):
             dl = layers[j % len(layers)]
-            xin = xs[(j % xs.shape[0]):(j % xs.shape[0]) + 1] if wl == "decode" else xs
+            xin = xs[(j % xs.shape[0]):(j % xs.shape[0]) + 1] if kind == "decode" else xs
             if path == "fused":
                 starts[j].record(stream)
                 moe.moe_decode_layer(shape, dl.router, dl.logit_bias, dl.experts, xin, T, buf.ws, buf.logits,
@@ -328,7 +335,7 @@ def run_workload(wl, K, W, inp, no_cpu, cpu_seconds):
     durs_ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
     stage_us = float(np.mean(durs_ms) * 1e3)
     log("%s: dominant stage %.2f us average over %d event-timed launches" % (wl, stage_us, n_ev))
-    if wl == "decode":
+    if kind == "decode":
         # every step of the timed region is one decode_layer_kernel launch: the
         # events around the region give its average per-launch duration without
         # the per-launch event overhead
@@ -340,7 +347,7 @@ def run_workload(wl, K, W, inp, no_cpu, cpu_seconds):
     # buffer and the bf16 intermediate are not counted
     ids_np = buf.ids.cpu().numpy()
     distinct = len(set(ids_np.reshape(-1).tolist())) + shape.has_shared
-    alg_bytes = distinct * EXPERT_BYTES + T * 2048 * 2
+    alg_bytes = distinct * (EXPERT_BYTES_8BIT if inp.bits == 8 else EXPERT_BYTES) + T * 2048 * 2
     flops = T * S * 3 * 2 * 2048 * 512
     if path == "fused":
         alg_bytes += ROUTER_BYTES  # the launch also streams the router
@@ -358,15 +365,15 @@ def run_workload(wl, K, W, inp, no_cpu, cpu_seconds):
 
     cpu = None
     if not no_cpu:
-        cpu = cpu_baseline(wl, inp.hosts, inp.x_host, T, shape, cpu_seconds)
-    unit = "layer-tokens/s" if not wl.startswith("stack") else "tokens/s"
+        cpu = cpu_baseline(kind, inp.hosts, inp.x_host, T, shape, cpu_seconds)
+    unit = "layer-tokens/s" if not kind.startswith("stack") else "tokens/s"
     return {
         "value": value, "unit": unit, "steps": K, "warmup": W, "ms_per_step": elapsed * 1e3 / K,
         "us_per_step_stream": region_us / K,
         "config": {"workload": wl, "T": T, "hidden": 2048, "n_experts": 256, "top_k": 8, "shared": 1,
-                   "inter": 512, "weights": "int4 affine g64", "router": "8-bit affine g64",
-                   "layers": len(layers) if wl.startswith("stack") else 1,
-                   "weight_copies": len(layers) if wl == "decode" else 1, "path": path,
+                   "inter": 512, "weights": "int%d affine g64" % inp.bits, "router": "8-bit affine g64",
+                   "layers": len(layers) if kind.startswith("stack") else 1,
+                   "weight_copies": len(layers) if kind == "decode" else 1, "path": path,
                    "graph_steps": n_cap},
         "roofline": roof, "cpu_baseline": cpu, "inputs_sha256": inp.sha256, "setup_s": inp.setup_s,
     }
@@ -393,7 +400,7 @@ def main():
     torch.cuda.set_device(torch.device("cuda:0"))
     head = args.workload
     defaults = {"decode": (2048, 256), "prefill512": (200, 20), "prefill4096": (50, 5),
-                "stack1": (50, 5), "stack16": (50, 5)}
+                "stack1": (50, 5), "stack16": (50, 5), "decode_8bit": (1024, 128), "prefill512_8bit": (100, 10)}
     K = args.steps if args.steps is not None else defaults[head][0]
     W = args.warmup if args.warmup is not None else defaults[head][1]
     cache = {}
@@ -412,8 +419,8 @@ def main():
             for drop in ("setup_s",):
                 r.pop(drop, None)
             others[wl] = r
-            if wl == "prefill4096":
-                cache.pop("prefill4096_layers", None)
+            for key in [k2_ for k2_ in cache if k2_.startswith(wl.replace("_8bit", "")) and k2_.endswith("_layers")]:
+                cache.pop(key, None)  # free what no later workload reads
     line = {
         "metric": METRIC, "value": rec["value"], "unit": rec["unit"], "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": rec["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,

@@ -60,10 +60,13 @@ typedef enum moe_status {
 
 enum { MOE_ROUTER_F32 = 0, MOE_ROUTER_AFFINE8 = 1 };
 
-/* Layer shape and formats. Served: bits == 4, group == 64 ([P3-build]; any other
- * bit width or group is refused with MOE_ERR_UNSUPPORTED); hidden is a power of
- * two in [64, 8192], inter a power of two in [64, 2048]; 1 <= top_k <= min(n_experts, 16);
- * 1 <= n_experts <= 1024; has_shared in {0, 1}; router_fmt one of MOE_ROUTER_*. */
+/* Layer shape and formats. Served: bits == 4 (affine 4-bit experts) or 8 (affine
+ * 8-bit experts, the second checkpoint format of [P3-build]), group == 64 (any
+ * other bit width or group is refused with MOE_ERR_UNSUPPORTED, as [P3-build]
+ * refuses the widths a backend does not serve); hidden is a power of two in
+ * [64, 8192] (8-bit: [64, 4096]), inter a power of two in [64, 2048] (8-bit:
+ * [64, 1024]); 1 <= top_k <= min(n_experts, 16); 1 <= n_experts <= 1024;
+ * has_shared in {0, 1}; router_fmt one of MOE_ROUTER_*. */
 typedef struct moe_shape {
     int32_t hidden;     /* H: model width                          */
     int32_t inter;      /* I: expert intermediate width            */
@@ -80,6 +83,8 @@ typedef struct moe_shape {
  *   q_gate, q_up [M][I][H/2] uint8, q_down [M][H][I/2] uint8: row-major matrices
  *     [out, in] with input element 2j in the low nibble of byte j and 2j+1 in the
  *     high nibble; q in 0..15.
+ *   bits == 8: q_gate, q_up [M][I][H] uint8, q_down [M][H][I] uint8, one code q in
+ *     0..255 per byte.
  *   s_*, b_* [M][rows][in/64] bf16: scale and bias of each group of 64 consecutive
  *     input elements; the weight is scale * q + bias. */
 typedef struct moe_expert_canon {
@@ -111,6 +116,11 @@ moe_status moe_shape_check(const moe_shape* shape);
  * moe_experts_packed_bytes / M), in this order:
  *   gate/up q [I/2][H/64][4][32 B] | down q [H/4][I/64][4][32 B] |
  *   gate/up sb [I/2][H/64][4] | down sb [H/4][I/64][4]
+ * (4-bit rows; 8-bit rows are packed as 4-bit rows of twice the length: codes
+ * 0 .. K-1 of an 8-bit row of K codes become the high nibbles of its codes, with
+ * the group words (16 scale, bias), and codes K .. 2K-1 the low nibbles, with
+ * (scale, 0): 16 s hi + b + s lo = s q + b exactly. An 8-bit expert takes twice the
+ * 4-bit expert's bytes, 6 % more than its canonical 8-bit form.)
  * Rows come in blocks of four: gate/up block b holds gate rows 2b, 2b+1 and up
  * rows 2b, 2b+1 (in that slot order), down block b holds down rows 4b .. 4b+3.
  * For each block and 64-wide group g, the four rows' 32 bytes of that group

@@ -28,7 +28,8 @@ static bool pow2_in(int32_t v, int32_t lo, int32_t hi) { return v >= lo && v <= 
 
 moe_status validate_shape(const moe_shape* sh) {
     if (!sh) return fail(MOE_ERR_INVALID_ARG, "shape is NULL");
-    if (sh->bits != 4) return fail(MOE_ERR_UNSUPPORTED, "expert bit width %d is not served (4-bit only)", sh->bits);
+    if (sh->bits != 4 && sh->bits != 8)
+        return fail(MOE_ERR_UNSUPPORTED, "expert bit width %d is not served (4-bit or 8-bit only)", sh->bits);
     if (sh->group != 64) return fail(MOE_ERR_UNSUPPORTED, "group %d is not served (64 only)", sh->group);
     if (sh->router_fmt != MOE_ROUTER_F32 && sh->router_fmt != MOE_ROUTER_AFFINE8)
         return fail(MOE_ERR_UNSUPPORTED, "router format %d is not served", sh->router_fmt);
@@ -42,6 +43,9 @@ moe_status validate_shape(const moe_shape* sh) {
         return fail(MOE_ERR_INVALID_ARG, "has_shared must be 0 or 1");
     if (sh->top_k < 1 || sh->top_k > 16 || sh->top_k > sh->n_experts)
         return fail(MOE_ERR_INVALID_ARG, "top_k %d out of [1, min(n_experts, 16)]", sh->top_k);
+    if (sh->bits == 8 && (sh->hidden > 4096 || sh->inter > 1024))
+        return fail(MOE_ERR_UNSUPPORTED, "8-bit experts: hidden <= 4096 and inter <= 1024 (rows of at most 8192 "
+                    "and 2048 int4 codes)");
     return MOE_OK;
 }
 
@@ -96,16 +100,45 @@ __device__ __forceinline__ uint32_t pack_q_dword(uint32_t c) {
     return gather_nibbles(c) | (gather_nibbles(c >> 4) << 16);
 }
 
+// The high (hi = true) or low nibbles of the 4 bytes of two dwords as one dword of
+// canonical int4 codes: byte b of a gives codes 2b' ... (a's four nibbles in the low
+// 16 bits, b's in the high 16 bits, element order kept).
+__device__ __forceinline__ uint32_t nibbles_of_bytes(uint32_t a, uint32_t b, bool hi) {
+    if (hi) {
+        a >>= 4;
+        b >>= 4;
+    }
+    auto half = [](uint32_t d) -> uint32_t {
+        return (d & 0xFu) | ((d >> 4) & 0xF0u) | ((d >> 8) & 0xF00u) | ((d >> 12) & 0xF000u);
+    };
+    return half(a) | (half(b) << 16);
+}
+
 // One canonical int4 matrix [N][K/2] per expert into the blocked layout (see
 // ExpertLayout): row r goes to block r / spb, slot slot0 + r % spb, and its 16-byte
 // piece c (weights 32c .. 32c+31) to ((block * K/64 + c/2) * 4 + slot) * 2 + c % 2
-// in 16-byte units; nibbles reordered within each dword.
+// in 16-byte units; nibbles reordered within each dword. SPLIT8: the source is an
+// 8-bit matrix [N][K/2] (one code per byte, K/2 codes a row) read as the int4 row
+// of K codes that holds its high nibbles and then its low nibbles.
+template <bool SPLIT8>
 __global__ void pack_q_kernel(const uint4* __restrict__ src, size_t n16, int K, int spb, int slot0,
                               uint4* __restrict__ dst, size_t dst_stride16) {
     const size_t m = blockIdx.y;
     const size_t cpr = (size_t)K / 32, gpr = (size_t)K / 64;  // pieces and groups per row
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x) {
-        const uint4 v = src[m * n16 + i];
+        uint4 v;
+        if constexpr (SPLIT8) {
+            // piece c of the int4 row: codes 32c .. 32c+31 = nibbles of source bytes
+            // 32 (c mod cpr/2) .. +31 (high nibbles for c < cpr/2), two 16-byte units
+            const size_t r = i / cpr, c = i % cpr, h = cpr / 2;
+            const bool hi = c < h;
+            const uint4* s = src + m * n16 + r * cpr + 2 * (hi ? c : c - h);
+            const uint4 a = s[0], b = s[1];
+            v = make_uint4(nibbles_of_bytes(a.x, a.y, hi), nibbles_of_bytes(a.z, a.w, hi),
+                           nibbles_of_bytes(b.x, b.y, hi), nibbles_of_bytes(b.z, b.w, hi));
+        } else {
+            v = src[m * n16 + i];
+        }
         const size_t r = i / cpr, c = i % cpr;
         const size_t blk = r / spb, slot = slot0 + r % spb;
         const size_t o = ((blk * gpr + c / 2) * 4 + slot) * 2 + c % 2;
@@ -125,6 +158,10 @@ __global__ void pack_copy_kernel(const uint4* __restrict__ src, size_t src_strid
 // sb = scale | bias << 16 for n entries per expert. gpr > 0: the entries are
 // [N][gpr] (row, group) of an expert matrix, placed like the q rows of
 // pack_q_kernel at (block * gpr + g) * 4 + slot; gpr == 0: copied in order.
+// SPLIT8: the source holds [N][gpr / 2] groups of an 8-bit matrix; int4 group g
+// of a row is (16 scale, bias) of source group g for g < gpr / 2 (high nibbles)
+// and (scale, 0) of source group g - gpr / 2 (low nibbles).
+template <bool SPLIT8>
 __global__ void pack_sb_kernel(const uint16_t* __restrict__ s, const uint16_t* __restrict__ b, size_t n, int gpr,
                                int spb, int slot0, uint32_t* __restrict__ dst, size_t dst_stride4) {
     const size_t m = blockIdx.y;
@@ -134,7 +171,18 @@ __global__ void pack_sb_kernel(const uint16_t* __restrict__ s, const uint16_t* _
             const size_t r = i / gpr, g = i % gpr;
             o = ((r / spb) * gpr + g) * 4 + slot0 + r % spb;
         }
-        dst[m * dst_stride4 + o] = (uint32_t)s[m * n + i] | ((uint32_t)b[m * n + i] << 16);
+        uint32_t w;
+        if constexpr (SPLIT8) {
+            const size_t h = (size_t)gpr / 2, r = i / gpr, g = i % gpr;
+            const size_t si = m * (n / 2) + r * h + (g < h ? g : g - h);
+            if (g < h)  // 16 scale is exact in bf16: the exponent moves by 4
+                w = f32_to_bf16(16.f * bf16_to_f32(s[si])) | ((uint32_t)b[si] << 16);
+            else
+                w = (uint32_t)s[si];
+        } else {
+            w = (uint32_t)s[m * n + i] | ((uint32_t)b[m * n + i] << 16);
+        }
+        dst[m * dst_stride4 + o] = w;
     }
 }
 
@@ -142,14 +190,20 @@ static dim3 pack_grid(size_t n, int M) {
     return dim3((unsigned)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024), (unsigned)M);
 }
 
-// int4 expert matrix [N][K/2] per expert (canonical), into the blocked layout with
-// spb rows per block from slot slot0 (gate 2, 0; up 2, 2; down 4, 0).
+// Expert matrix [N][K/2] per expert (canonical int4), or [N][K/2] bytes of 8-bit
+// codes when split8 (K is then the int4 row length, twice the codes), into the
+// blocked layout with spb rows per block from slot slot0 (gate 2, 0; up 2, 2;
+// down 4, 0).
 static moe_status copy_q(const void* src, size_t N, int K, int spb, int slot0, char* dst, size_t stride, int M,
-                         hipStream_t st) {
+                         bool split8, hipStream_t st) {
     if (!src || !aligned16(src)) return fail(MOE_ERR_INVALID_ARG, "q source NULL or not 16-byte aligned");
     const size_t n16 = N * (size_t)K / 32;
-    hipLaunchKernelGGL(pack_q_kernel, pack_grid(n16, M), dim3(256), 0, st, (const uint4*)src, n16, K, spb, slot0,
-                       (uint4*)dst, stride / 16);
+    if (split8)
+        hipLaunchKernelGGL(pack_q_kernel<true>, pack_grid(n16, M), dim3(256), 0, st, (const uint4*)src, n16, K, spb,
+                           slot0, (uint4*)dst, stride / 16);
+    else
+        hipLaunchKernelGGL(pack_q_kernel<false>, pack_grid(n16, M), dim3(256), 0, st, (const uint4*)src, n16, K, spb,
+                           slot0, (uint4*)dst, stride / 16);
     return check_launch("pack_q_kernel");
 }
 
@@ -162,12 +216,17 @@ static moe_status copy_raw(const void* src, size_t bytes, char* dst, hipStream_t
     return check_launch("pack_copy_kernel");
 }
 
-// (scale, bias) words: n entries per expert, blocked like copy_q when gpr > 0.
+// (scale, bias) words: n entries per expert, blocked like copy_q when gpr > 0
+// (split8: n and gpr count the int4 groups, twice the source's).
 static moe_status copy_sb(const uint16_t* s, const uint16_t* b, size_t n, int gpr, int spb, int slot0, char* dst,
-                          size_t stride, int M, hipStream_t st) {
+                          size_t stride, int M, bool split8, hipStream_t st) {
     if (!s || !b) return fail(MOE_ERR_INVALID_ARG, "scale/bias source NULL");
-    hipLaunchKernelGGL(pack_sb_kernel, pack_grid(n, M), dim3(256), 0, st, s, b, n, gpr, spb, slot0, (uint32_t*)dst,
-                       stride / 4);
+    if (split8)
+        hipLaunchKernelGGL(pack_sb_kernel<true>, pack_grid(n, M), dim3(256), 0, st, s, b, n, gpr, spb, slot0,
+                           (uint32_t*)dst, stride / 4);
+    else
+        hipLaunchKernelGGL(pack_sb_kernel<false>, pack_grid(n, M), dim3(256), 0, st, s, b, n, gpr, spb, slot0,
+                           (uint32_t*)dst, stride / 4);
     return check_launch("pack_sb_kernel");
 }
 
@@ -180,18 +239,22 @@ extern "C" moe_status moe_pack_experts(const moe_shape* sh, const moe_expert_can
     const ExpertLayout L = expert_layout(*sh);
     const int M = n_mats(*sh);
     if (packed_bytes < L.stride * (size_t)M) return fail(MOE_ERR_WORKSPACE, "packed buffer too small");
-    const size_t H = sh->hidden, I = sh->inter;
+    // H, I: row lengths in int4 codes (8-bit rows are packed as int4 rows twice as long)
+    const size_t H = (size_t)sh->hidden * kmul(*sh), I = (size_t)sh->inter * kmul(*sh);
+    const size_t Ho = sh->hidden, Io = sh->inter;  // rows of the down and gate/up matrices
+    const bool sp = sh->bits == 8;
     hipStream_t s = (hipStream_t)stream;
     char* d = (char*)packed;
     const int Hi = (int)H, Ii = (int)I;
-    if ((st = copy_q(src->q_gate, I, Hi, 2, 0, d + L.gu_q, L.stride, M, s)) != MOE_OK) return st;
-    if ((st = copy_q(src->q_up, I, Hi, 2, 2, d + L.gu_q, L.stride, M, s)) != MOE_OK) return st;
-    if ((st = copy_q(src->q_down, H, Ii, 4, 0, d + L.down_q, L.stride, M, s)) != MOE_OK) return st;
-    if ((st = copy_sb(src->s_gate, src->b_gate, I * (H / 64), Hi / 64, 2, 0, d + L.gu_sb, L.stride, M, s)) != MOE_OK)
+    if ((st = copy_q(src->q_gate, Io, Hi, 2, 0, d + L.gu_q, L.stride, M, sp, s)) != MOE_OK) return st;
+    if ((st = copy_q(src->q_up, Io, Hi, 2, 2, d + L.gu_q, L.stride, M, sp, s)) != MOE_OK) return st;
+    if ((st = copy_q(src->q_down, Ho, Ii, 4, 0, d + L.down_q, L.stride, M, sp, s)) != MOE_OK) return st;
+    if ((st = copy_sb(src->s_gate, src->b_gate, Io * (H / 64), Hi / 64, 2, 0, d + L.gu_sb, L.stride, M, sp, s)) !=
+        MOE_OK)
         return st;
-    if ((st = copy_sb(src->s_up, src->b_up, I * (H / 64), Hi / 64, 2, 2, d + L.gu_sb, L.stride, M, s)) != MOE_OK)
+    if ((st = copy_sb(src->s_up, src->b_up, Io * (H / 64), Hi / 64, 2, 2, d + L.gu_sb, L.stride, M, sp, s)) != MOE_OK)
         return st;
-    if ((st = copy_sb(src->s_down, src->b_down, H * (I / 64), Ii / 64, 4, 0, d + L.down_sb, L.stride, M, s)) !=
+    if ((st = copy_sb(src->s_down, src->b_down, Ho * (I / 64), Ii / 64, 4, 0, d + L.down_sb, L.stride, M, sp, s)) !=
         MOE_OK)
         return st;
     return MOE_OK;
@@ -213,5 +276,5 @@ extern "C" moe_status moe_pack_router(const moe_shape* sh, const void* w, const 
         return copy_raw(w, R * H * 4, (char*)packed, hs);
     }
     if ((st = copy_raw(w, R * H, (char*)packed, hs)) != MOE_OK) return st;
-    return copy_sb(s, b, R * (H / 64), 0, 1, 0, (char*)packed + R * H, 0, 1, hs);
+    return copy_sb(s, b, R * (H / 64), 0, 1, 0, (char*)packed + R * H, 0, 1, false, hs);
 }

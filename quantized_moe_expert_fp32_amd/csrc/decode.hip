@@ -30,13 +30,19 @@ struct XSlice {
     float s[CPL];         // plain sum of the chunk's 32 values, in element order
 };
 
-// Chunk c of this lane covers elements [32 * (lr + lpr * c), +32) of the row. The
-// chunk sum is a chain of bf16 dot2 against (1, 1), in element order.
+// Chunk c of this lane covers weights [32 * (lr + lpr * c), +32) of a weight row,
+// whose activations are elements [32 * ch, +32) of the activation row, ch = (lr +
+// lpr * c) mod xc (xc: chunks of the activation row; a weight row of 8-bit codes
+// is twice as long as its activations). The chunk sum is a chain of bf16 dot2
+// against (1, 1), in element order.
 template <int CPL>
-__device__ __forceinline__ void load_xslice(const uint16_t* __restrict__ row, int lr, int lpr, XSlice<CPL>& xs) {
+__device__ __forceinline__ void load_xslice(const uint16_t* __restrict__ row, int lr, int lpr, int xc,
+                                            XSlice<CPL>& xs) {
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-        const uint4* src = reinterpret_cast<const uint4*>(row + 32 * (lr + lpr * c));
+        int ch = lr + lpr * c;
+        if (ch >= xc) ch -= xc;
+        const uint4* src = reinterpret_cast<const uint4*>(row + 32 * ch);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
             const uint4 v = src[q4];
@@ -130,7 +136,7 @@ __device__ __forceinline__ void gu_load(const uint8_t* __restrict__ packed, cons
 // or, with htag (the tagged copy of the same h row, one 64-bit word per bf16
 // pair), published there with tag `tag`.
 template <int CPL>
-__device__ __forceinline__ void gu_finish(const GuLoads<CPL>& ld, int H, bool valid,
+__device__ __forceinline__ void gu_finish(const GuLoads<CPL>& ld, int H, int xc, bool valid,
                                           const uint16_t* __restrict__ xrow, uint16_t* __restrict__ hrow,
                                           uint64_t* htag, uint32_t tag, int rb, int wave, int lane) {
     const int C = H / 32, lpr = C < 64 ? C : 64, rpw = 64 / lpr;
@@ -148,7 +154,7 @@ __device__ __forceinline__ void gu_finish(const GuLoads<CPL>& ld, int H, bool va
         return;
     }
     XSlice<CPL> xs;
-    load_xslice(xrow, lr, lpr, xs);
+    load_xslice(xrow, lr, lpr, xc, xs);
     uint32_t hb[GU_IT] = {0u, 0u, 0u, 0u};  // bf16 of row it*rpw + rsub, in lanes with lr == 0
 #pragma unroll
     for (int it = 0; it < GU_IT; ++it) {
@@ -185,15 +191,16 @@ __device__ __forceinline__ void gu_finish(const GuLoads<CPL>& ld, int H, bool va
     }
 }
 
-// 16 intermediate rows of expert e for one token (gate and up rows each).
+// 16 intermediate rows of expert e for one token (gate and up rows each); H is the
+// weight row length, xc the activation row's chunks of 32.
 template <int CPL>
-__device__ __forceinline__ void gateup_item(const uint8_t* __restrict__ packed, const ExpertLayout& L, int H, int e,
-                                            bool valid, const uint16_t* __restrict__ xrow,
+__device__ __forceinline__ void gateup_item(const uint8_t* __restrict__ packed, const ExpertLayout& L, int H, int xc,
+                                            int e, bool valid, const uint16_t* __restrict__ xrow,
                                             uint16_t* __restrict__ hrow, uint64_t* htag, uint32_t tag, int rb,
                                             int wave, int lane) {
     GuLoads<CPL> ld;
     gu_load<CPL>(packed, L, H, e, valid, rb, wave, lane, ld);
-    gu_finish<CPL>(ld, H, valid, xrow, hrow, htag, tag, rb, wave, lane);
+    gu_finish<CPL>(ld, H, xc, valid, xrow, hrow, htag, tag, rb, wave, lane);
 }
 
 // ---------------------------------------------------------------- down (+ combine) work item
@@ -252,19 +259,19 @@ __device__ __forceinline__ void dn_load(const uint8_t* __restrict__ packed, cons
 // `tag`. d holds the first batch's weight loads (dn_load with j0 = 0).
 template <bool TAGGED>
 __device__ __forceinline__ void dn_finish(DnLoads& d, const uint8_t* __restrict__ packed, const ExpertLayout& L,
-                                          int H, int I, int E, int k, int has_shared, int t, int n0,
+                                          int H, int I, int Iw, int E, int k, int has_shared, int t, int n0,
                                           const uint16_t* __restrict__ hbuf, const int32_t* ids_t,
                                           const uint16_t* w_t, const uint16_t* wsh_t, float* __restrict__ y,
                                           const uint16_t* residual, uint16_t* out, float (*ysh)[DN_ROWS],
                                           uint32_t* hsh, const uint64_t* htag_t, uint32_t tag, unsigned* err) {
     const int S = k + has_shared;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int lpr = I / 32, rpw = 64 / lpr;
+    const int lpr = Iw / 32, rpw = 64 / lpr;
     const int lr = lane % lpr, rsub = lane / lpr;
     const int n_dots = S * DN_ROWS;
     const int n_it = (n_dots + rpw - 1) / rpw;
     for (int j0 = 0; 4 * j0 < n_it; j0 += DN_BATCH) {
-        if (j0 > 0) dn_load(packed, L, I, E, k, has_shared, n0, ids_t, j0, d);
+        if (j0 > 0) dn_load(packed, L, Iw, E, k, has_shared, n0, ids_t, j0, d);
         if (j0 == 0) {
             const int nw = S * I / 2;
             if (TAGGED) {
@@ -290,7 +297,7 @@ __device__ __forceinline__ void dn_finish(DnLoads& d, const uint8_t* __restrict_
             float v = 0.f;
             if (d.ok[j]) {
                 XSlice<1> hs;
-                load_xslice(reinterpret_cast<const uint16_t*>(hsh) + (size_t)d.slot[j] * I, lr, lpr, hs);
+                load_xslice(reinterpret_cast<const uint16_t*>(hsh) + (size_t)d.slot[j] * I, lr, lpr, I / 32, hs);
                 v = chunk_dot(d.ld[j], hs.p[0], hs.s[0]);
             }
             v = group_sum(v, lpr);
@@ -317,22 +324,23 @@ __device__ __forceinline__ void dn_finish(DnLoads& d, const uint8_t* __restrict_
 
 // ---------------------------------------------------------------- two-launch expert stage
 // Grid (I / 16, S, T): one gate/up item per workgroup.
+// km: weight row length / activation length (1 for 4-bit experts, 2 for 8-bit).
 template <int CPL>
 __global__ __launch_bounds__(256) void decode_gateup_kernel(const uint8_t* __restrict__ packed, ExpertLayout L, int H,
-                                                            int I, int E, int k, int has_shared,
+                                                            int I, int km, int E, int k, int has_shared,
                                                             const uint16_t* __restrict__ x,
                                                             const int32_t* __restrict__ ids,
                                                             uint16_t* __restrict__ hbuf) {
     const int t = blockIdx.z, s = blockIdx.y, S = k + has_shared;
     const int e = s < k ? ids[(size_t)t * k + s] : E;
     const bool valid = s < k ? (e >= 0 && e < E) : true;
-    gateup_item<CPL>(packed, L, H, e, valid, x + (size_t)t * H, hbuf + ((size_t)t * S + s) * I, nullptr, 0u,
-                     blockIdx.x, threadIdx.x >> 6, threadIdx.x & 63);
+    gateup_item<CPL>(packed, L, H * km, H / 32, e, valid, x + (size_t)t * H, hbuf + ((size_t)t * S + s) * I, nullptr,
+                     0u, blockIdx.x, threadIdx.x >> 6, threadIdx.x & 63);
 }
 
 // Grid (H / 8, T): one down item per workgroup; combine when out is given.
 __global__ __launch_bounds__(256) void decode_down_kernel(const uint8_t* __restrict__ packed, ExpertLayout L, int H,
-                                                          int I, int E, int k, int has_shared,
+                                                          int I, int km, int E, int k, int has_shared,
                                                           const uint16_t* __restrict__ hbuf,
                                                           const int32_t* __restrict__ ids, float* __restrict__ y,
                                                           const uint16_t* __restrict__ w,
@@ -342,8 +350,8 @@ __global__ __launch_bounds__(256) void decode_down_kernel(const uint8_t* __restr
     extern __shared__ __attribute__((aligned(16))) uint32_t hsh_dyn[];
     const int t = blockIdx.y;
     DnLoads d;
-    dn_load(packed, L, I, E, k, has_shared, blockIdx.x * DN_ROWS, ids + (size_t)t * k, 0, d);
-    dn_finish<false>(d, packed, L, H, I, E, k, has_shared, t, blockIdx.x * DN_ROWS, hbuf, ids + (size_t)t * k,
+    dn_load(packed, L, I * km, E, k, has_shared, blockIdx.x * DN_ROWS, ids + (size_t)t * k, 0, d);
+    dn_finish<false>(d, packed, L, H, I, I * km, E, k, has_shared, t, blockIdx.x * DN_ROWS, hbuf, ids + (size_t)t * k,
                      w ? w + (size_t)t * k : nullptr, wsh ? wsh + t : nullptr, y, residual, out, ysh, hsh_dyn,
                      nullptr, 0u, nullptr);
 }
@@ -383,6 +391,7 @@ struct LayerArgs {
     uint64_t* th;       // tagged h [T][S][I/2] (bf16 pairs); one token: two copies, th_word
     ExpertLayout L;
     int T, H, I, E, k, has_shared, R;
+    int kmul;     // weight row length / activation length: 1 (4-bit experts) or 2 (8-bit)
     int stage_x;  // x and its chunk sums are staged in LDS (else read from global memory)
 };
 
@@ -455,22 +464,23 @@ __device__ __forceinline__ uint32_t pair_finish(const PairLoads<CPL>& ld, int H,
     return h0 | (h1 << 16);
 }
 
-// This lane's slice of token t's activations: from the workgroup's LDS copy
-// (values and chunk sums, staged by stage_x) or from global memory; both give the
-// values and sums of load_xslice.
+// This lane's slice of token t's activations for a weight row of Hw codes (H or
+// 2H): from the workgroup's LDS copy (values and chunk sums, staged by stage_x) or
+// from global memory; both give the values and sums of load_xslice.
 template <int CPL>
 __device__ __forceinline__ void token_xslice(bool lds, const uint16_t* s_x, const float* s_xs,
-                                             const uint16_t* __restrict__ gx, int t, int H, int lane,
+                                             const uint16_t* __restrict__ gx, int t, int H, int Hw, int lane,
                                              XSlice<CPL>& xs) {
-    const int C = H / 32, lpr = C < 64 ? C : 64;
+    const int C = H / 32, Cw = Hw / 32, lpr = Cw < 64 ? Cw : 64;
     const int lr = lane % lpr;
     if (!lds) {
-        load_xslice(gx + (size_t)t * H, lr, lpr, xs);
+        load_xslice(gx + (size_t)t * H, lr, lpr, C, xs);
         return;
     }
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-        const int ch = lr + lpr * c;
+        int ch = lr + lpr * c;
+        if (ch >= C) ch -= C;
         const uint4* src = reinterpret_cast<const uint4*>(s_x + (size_t)t * H + 32 * ch);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
@@ -590,6 +600,8 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
     const int G = gridDim.x, wg = blockIdx.x;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int T = TT == 1 ? 1 : a.T, H = HC ? HC : a.H, I = IC ? IC : a.I, k = KC ? KC : a.k;
+    const int KM = HC ? 1 : a.kmul;  // the served shape's instance is 4-bit
+    const int Hw = H * KM, Iw = I * KM, IXC = I / 32;  // weight row lengths; h chunks of 32
     const int E = a.E, R = a.R, hs_ = a.has_shared;
     const int S = k + hs_;
     const int npair = I / 2;
@@ -657,7 +669,7 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
     bool have = false;
     const int j0 = wg + G * wtop;
     if (hs_ && j0 < npair && wave >= npoll) {
-        pair_load<CPL>(a.experts, a.L, H, E, j0, lane, cur);
+        pair_load<CPL>(a.experts, a.L, Hw, E, j0, lane, cur);
         have = true;
     }
     // Every wavefront of this workgroup has read the epoch (the barrier above waited
@@ -772,7 +784,7 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
     // before phase C in place it still saves 0.25 us. With more tokens every
     // wavefront has a task and the barrier measured slower.
     if (!have && j0 < nB) {
-        pair_load<CPL>(a.experts, a.L, H, s_dexp[j0 / npair], j0 % npair, lane, cur);
+        pair_load<CPL>(a.experts, a.L, Hw, s_dexp[j0 / npair], j0 % npair, lane, cur);
         have = true;
     }
     if constexpr (TT == 1) __builtin_amdgcn_s_barrier();
@@ -793,14 +805,14 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
     }
     for (int j = j0; j < nB; j += G * LW) {
         const int dd = j / npair, ip = j % npair;
-        if (!have) pair_load<CPL>(a.experts, a.L, H, s_dexp[dd], ip, lane, cur);
+        if (!have) pair_load<CPL>(a.experts, a.L, Hw, s_dexp[dd], ip, lane, cur);
         have = false;
         const int cnt = s_dcnt[dd];
         for (int u = 0; u < cnt; ++u) {
             const int ent = s_dtok[dd][u], t = ent & 31, sl = ent >> 5;
             XSlice<CPL> xs;
-            token_xslice<CPL>(a.stage_x, s_x, s_xs, a.x, t, H, lane, xs);
-            uint32_t hp = pair_finish<CPL>(cur, H, xs, lane);
+            token_xslice<CPL>(a.stage_x, s_x, s_xs, a.x, t, H, Hw, lane, xs);
+            uint32_t hp = pair_finish<CPL>(cur, Hw, xs, lane);
             // after a timed-out wait in this workgroup its h pairs are NaN, so the
             // outputs of every token they reach are NaN rather than silently stale
             if (s_bad) hp = 0x7FC07FC0u;
@@ -830,18 +842,19 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
     }
 
     // ---- C: down items with the combine
-    const int lpr = I / 32, rpw = 64 / lpr;
+    const int lpr = Iw / 32, rpw = 64 / lpr;
     const int lr = lane % lpr, rsub = lane / lpr;
+    const int lrx = lr < IXC ? lr : lr - IXC;  // this lane's chunk of h
     const int n_dots = S * DR, n_it = (n_dots + rpw - 1) / rpw;
     int staged = -1;
     for (int c = c0; c < c1; ++c) {
         const int t = c / NBLK, n0 = (c % NBLK) * DR;
         float(*ysh)[DR] = ysh2[TT == 1 ? 0 : (c - c0) & 1];
-        if (!dhave) dnl_load<DR>(a.experts, a.L, I, E, k, hs_, n0, s_ids[t], 0, wave, lane, dcur);
+        if (!dhave) dnl_load<DR>(a.experts, a.L, Iw, E, k, hs_, n0, s_ids[t], 0, wave, lane, dcur);
         DnLoadsL dnxt;
         const bool nhave = c + 1 < c1;
         if (nhave)
-            dnl_load<DR>(a.experts, a.L, I, E, k, hs_, ((c + 1) % NBLK) * DR, s_ids[(c + 1) / NBLK], 0, wave, lane,
+            dnl_load<DR>(a.experts, a.L, Iw, E, k, hs_, ((c + 1) % NBLK) * DR, s_ids[(c + 1) / NBLK], 0, wave, lane,
                          dnxt);
         if (t != staged) {
             const int nw = S * npair;
@@ -867,9 +880,10 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
             if constexpr (TT != 1) {
                 // the chunk sums of h, once per token (load_xslice's arithmetic, so
                 // bit-identical to computing them per row)
-                if (tid < S * lpr) {
+                if (tid < S * IXC) {
                     XSlice<1> hx;
-                    load_xslice(reinterpret_cast<const uint16_t*>(hsh) + (size_t)(tid / lpr) * I, tid % lpr, lpr, hx);
+                    load_xslice(reinterpret_cast<const uint16_t*>(hsh) + (size_t)(tid / IXC) * I, tid % IXC, IXC, IXC,
+                                hx);
                     s_hs[tid] = hx.s[0];
                 }
                 __syncthreads();
@@ -877,7 +891,7 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
             staged = t;
         }
         for (int b0 = 0; LW * b0 < n_it; b0 += DNB) {
-            if (b0 > 0) dnl_load<DR>(a.experts, a.L, I, E, k, hs_, n0, s_ids[t], b0, wave, lane, dcur);
+            if (b0 > 0) dnl_load<DR>(a.experts, a.L, Iw, E, k, hs_, n0, s_ids[t], b0, wave, lane, dcur);
 #pragma unroll
             for (int j = 0; j < DNB; ++j) {
                 const int it = wave + LW * (b0 + j);
@@ -888,7 +902,7 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
                     XSlice<1> hx;
                     if constexpr (TT != 1) {
                         const uint4* src = reinterpret_cast<const uint4*>(
-                            reinterpret_cast<const uint16_t*>(hsh) + (size_t)dcur.slot[j] * I + 32 * lr);
+                            reinterpret_cast<const uint16_t*>(hsh) + (size_t)dcur.slot[j] * I + 32 * lrx);
 #pragma unroll
                         for (int q4 = 0; q4 < 4; ++q4) {
                             const uint4 hv = src[q4];
@@ -897,9 +911,10 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
                             hx.p[0][4 * q4 + 2] = hv.z;
                             hx.p[0][4 * q4 + 3] = hv.w;
                         }
-                        hx.s[0] = s_hs[dcur.slot[j] * lpr + lr];
+                        hx.s[0] = s_hs[dcur.slot[j] * IXC + lrx];
                     } else {
-                        load_xslice(reinterpret_cast<const uint16_t*>(hsh) + (size_t)dcur.slot[j] * I, lr, lpr, hx);
+                        load_xslice(reinterpret_cast<const uint16_t*>(hsh) + (size_t)dcur.slot[j] * I, lr, lpr, IXC,
+                                    hx);
                     }
                     v = chunk_dot(dcur.ld[j], hx.p[0], hx.s[0]);
                 }
@@ -950,15 +965,15 @@ static int cpl_for(int K) { return K / 32 <= 64 ? 1 : (K / 32) / 64; }
 
 static void launch_gateup(const moe_shape& sh, const ExpertLayout& L, const uint8_t* p, const uint16_t* x, int T,
                           const int32_t* ids, uint16_t* hbuf, hipStream_t hs) {
-    const int S = n_slots(sh), H = sh.hidden, I = sh.inter;
+    const int S = n_slots(sh), H = sh.hidden, I = sh.inter, km = kmul(sh);
     dim3 g1(I / GU_ROWS, S, T);
-    switch (cpl_for(H)) {
-        case 1: hipLaunchKernelGGL(decode_gateup_kernel<1>, g1, dim3(256), 0, hs, p, L, H, I, sh.n_experts, sh.top_k,
-                                   sh.has_shared, x, ids, hbuf); break;
-        case 2: hipLaunchKernelGGL(decode_gateup_kernel<2>, g1, dim3(256), 0, hs, p, L, H, I, sh.n_experts, sh.top_k,
-                                   sh.has_shared, x, ids, hbuf); break;
-        default: hipLaunchKernelGGL(decode_gateup_kernel<4>, g1, dim3(256), 0, hs, p, L, H, I, sh.n_experts, sh.top_k,
-                                    sh.has_shared, x, ids, hbuf); break;
+    switch (cpl_for(H * km)) {
+        case 1: hipLaunchKernelGGL(decode_gateup_kernel<1>, g1, dim3(256), 0, hs, p, L, H, I, km, sh.n_experts,
+                                   sh.top_k, sh.has_shared, x, ids, hbuf); break;
+        case 2: hipLaunchKernelGGL(decode_gateup_kernel<2>, g1, dim3(256), 0, hs, p, L, H, I, km, sh.n_experts,
+                                   sh.top_k, sh.has_shared, x, ids, hbuf); break;
+        default: hipLaunchKernelGGL(decode_gateup_kernel<4>, g1, dim3(256), 0, hs, p, L, H, I, km, sh.n_experts,
+                                    sh.top_k, sh.has_shared, x, ids, hbuf); break;
     }
 }
 
@@ -985,7 +1000,7 @@ typedef void (*LayerKernel)(LayerArgs);
 template <int CPL, int TT, int VPL>
 static LayerKernel pick_layer_v(const LayerArgs& a, bool aff8) {
     if constexpr (CPL == 1 && VPL == 4) {
-        if (aff8 && a.H == 2048 && a.I == 512 && a.k == 8)  // the served model's shape
+        if (aff8 && a.H == 2048 && a.I == 512 && a.k == 8 && a.kmul == 1)  // the served model's shape
             return decode_layer_kernel<CPL, TT, true, VPL, 2048, 512, 8>;
     }
     return aff8 ? decode_layer_kernel<CPL, TT, true, VPL, 0, 0, 0> : decode_layer_kernel<CPL, TT, false, VPL, 0, 0, 0>;
@@ -1002,7 +1017,7 @@ static LayerKernel pick_layer_tt(const LayerArgs& a, bool aff8) {
 // The kernel instance for a launch: hidden (chunks per lane), one token or more,
 // keys per lane of the selection, router format, and the served shape.
 static LayerKernel pick_layer(const LayerArgs& a, bool aff8) {
-    if (cpl_for(a.H) == 1) return a.T <= 1 ? pick_layer_tt<1, 1>(a, aff8) : pick_layer_tt<1, 16>(a, aff8);
+    if (cpl_for(a.H * a.kmul) == 1) return a.T <= 1 ? pick_layer_tt<1, 1>(a, aff8) : pick_layer_tt<1, 16>(a, aff8);
     return a.T <= 1 ? pick_layer_tt<2, 1>(a, aff8) : pick_layer_tt<2, 16>(a, aff8);
 }
 
@@ -1095,7 +1110,7 @@ static moe_status launch_decode_experts(const moe_shape& sh, const uint8_t* p, c
     moe_status st = check_launch("decode_gateup_kernel");
     if (st != MOE_OK) return st;
     hipLaunchKernelGGL(decode_down_kernel, dim3(sh.hidden / DN_ROWS, T), dim3(256), hsh_bytes(sh), hs, p, L, sh.hidden,
-                       sh.inter, sh.n_experts, sh.top_k, sh.has_shared, hbuf, ids, y, (const uint16_t*)nullptr,
+                       sh.inter, kmul(sh), sh.n_experts, sh.top_k, sh.has_shared, hbuf, ids, y, (const uint16_t*)nullptr,
                        (const uint16_t*)nullptr, (const uint16_t*)nullptr, (uint16_t*)nullptr);
     return check_launch("decode_down_kernel");
 }
@@ -1170,7 +1185,9 @@ extern "C" moe_status moe_decode_layer(const moe_shape* shape, const void* route
     if (!router_packed || !logits || !out || !aligned16(router_packed))
         return fail(MOE_ERR_INVALID_ARG, "router, logits or out NULL / unaligned");
     if (y && !aligned16(y)) return fail(MOE_ERR_INVALID_ARG, "y unaligned");
-    if (cpl_for(sh.hidden) > 2) return fail(MOE_ERR_UNSUPPORTED, "single-launch decode layer serves hidden <= 4096");
+    if (cpl_for(sh.hidden * kmul(sh)) > 2)
+        return fail(MOE_ERR_UNSUPPORTED, "single-launch decode layer serves rows of at most 4096 int4 codes (hidden "
+                    "<= 4096 with 4-bit experts, <= 2048 with 8-bit)");
     const int cus = device_cus();
     if (cus <= 0) return fail(MOE_ERR_HIP, "could not query the compute-unit count");
     hipStream_t hs = (hipStream_t)stream;
@@ -1200,6 +1217,7 @@ extern "C" moe_status moe_decode_layer(const moe_shape* shape, const void* route
     a.k = sh.top_k;
     a.has_shared = sh.has_shared;
     a.R = router_rows(sh);
+    a.kmul = kmul(sh);
     // 16 KiB covers the kernel's static LDS (selection results, distinct-expert lists)
     // h rows and their chunk sums, then (when staged) x and its chunk sums
     const size_t lds_h = hsh_bytes(sh) + (size_t)n_slots(sh) * (sh.inter / 32) * 4, lds_x = xsh_bytes(sh, T);

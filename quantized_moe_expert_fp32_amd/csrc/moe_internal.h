@@ -18,6 +18,14 @@ void clear_error();
 // Validates the shape for every entry point (formats served, size limits).
 moe_status validate_shape(const moe_shape* sh);
 
+// Expert weight rows as the kernels read them. A 4-bit row of K weights is a row of
+// K int4 codes. An 8-bit row is packed as an int4 row of 2K codes: the high nibbles
+// of its K codes (groups 0 .. K/64-1, with scale 16 * scale and the bias) and then
+// the low nibbles (groups K/64 .. 2K/64-1, with scale and bias 0), so that
+//   sum_k x_k (s q_k + b) = sum_k x_k (16 s hi_k + b) + sum_k x_k (s lo_k + 0)
+// exactly; the activation of code j is x[j mod K]. kmul = row length / K.
+inline int32_t kmul(const moe_shape& s) { return s.bits / 4; }
+
 inline int32_t n_mats(const moe_shape& s) { return s.n_experts + (s.has_shared ? 1 : 0); }
 inline int32_t n_slots(const moe_shape& s) { return s.top_k + (s.has_shared ? 1 : 0); }
 inline int32_t router_rows(const moe_shape& s) { return s.n_experts + (s.has_shared ? 1 : 0); }
@@ -36,19 +44,23 @@ struct ExpertLayout {
 };
 
 inline ExpertLayout expert_layout(const moe_shape& s) {
+    // 2 I gate/up rows of Hw int4 codes and H down rows of Iw codes (Hw = H kmul,
+    // Iw = I kmul); half a byte per code, one (scale, bias) word per 64 codes
     const size_t H = (size_t)s.hidden, I = (size_t)s.inter, G = 64;
+    const size_t Hw = H * kmul(s), Iw = I * kmul(s);
     ExpertLayout L;
     L.gu_q = 0;
-    L.down_q = L.gu_q + I * H;
-    L.gu_sb = L.down_q + H * I / 2;
-    L.down_sb = L.gu_sb + 2 * I * (H / G) * 4;
-    L.stride = L.down_sb + H * (I / G) * 4;
+    L.down_q = L.gu_q + 2 * I * Hw / 2;
+    L.gu_sb = L.down_q + H * Iw / 2;
+    L.down_sb = L.gu_sb + 2 * I * (Hw / G) * 4;
+    L.stride = L.down_sb + H * (Iw / G) * 4;
     return L;
 }
 
-// Row bases inside one expert (byte offsets). The 16-byte piece ch (weights
-// 32 ch .. 32 ch + 31) of a row is at base + (ch / 2) * 128 + (ch % 2) * 16; the
-// word of group g of a row's sb is at sb base + 16 g.
+// Row bases inside one expert (byte offsets); H and I are the weight row lengths
+// (hidden and inter times kmul). The 16-byte piece ch (weights 32 ch .. 32 ch + 31)
+// of a row is at base + (ch / 2) * 128 + (ch % 2) * 16; the word of group g of a
+// row's sb is at sb base + 16 g.
 __host__ __device__ inline size_t gu_row_q(const ExpertLayout& L, int H, int up, int i) {
     return L.gu_q + (size_t)(i >> 1) * (size_t)(H / 64) * 128 + (size_t)((up ? 2 : 0) + (i & 1)) * 32;
 }

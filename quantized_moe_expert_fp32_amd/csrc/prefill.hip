@@ -399,6 +399,7 @@ struct GemmArgs {
     uint16_t* hbuf;             // h [T*S][I] bf16, expert-sorted rows (written by gate/up, read by down)
     float* y;                   // down: [T][S][H]
     int T;
+    int km;                     // weight row length / activation length: 1 (4-bit experts) or 2 (8-bit)
 };
 
 
@@ -460,7 +461,9 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
     __shared__ uint32_t arow_lds[BM];  // byte offset of each tile row in its source, ~0 beyond the tile
     __shared__ int32_t pick_lds[BM];   // down: pick p = order[row] of each tile row (its y row)
     const int H = a.H, I = a.I, S = a.S;
-    const int K = GATEUP ? H : I;
+    // K: activations per row; the weight rows hold K * km int4 codes (8-bit rows as
+    // two planes), whose chunk c meets activation chunk c mod K/64
+    const int K = GATEUP ? H : I, Kw = K * a.km, GX = K / 64;
     const int nblk = GATEUP ? (I + HALF - 1) / HALF : (H + NBR - 1) / NBR;
     int ti, cb;
     if (!xcd_item(*a.ntiles, nblk, ti, cb)) return;
@@ -505,7 +508,7 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
     const int blk0 = GATEUP ? col0 / 2 : col0 / 4;
     auto gblock = [&](int jb) -> int { return blk0 + jb < nblk_mat ? blk0 + jb : blk0; };
     const size_t q_region = GATEUP ? a.L.gu_q : a.L.down_q, sb_region = GATEUP ? a.L.gu_sb : a.L.down_sb;
-    const int G = K / 64;
+    const int G = Kw / 64;
 
     // ---- ring layout within a stage:
     //   A: the loaded rows x 128 B, the 16-byte piece p of row r at position p ^ (r & 7);
@@ -555,7 +558,7 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
         }
         auto issue = [&](int c) __attribute__((always_inline)) {
             const uint32_t st = ring_lds + (uint32_t)((c % NS) * STAGE);
-            const uint8_t* ab = asrc + (size_t)c * (KC * 2);
+            const uint8_t* ab = asrc + (size_t)(c < GX ? c : c - GX) * (KC * 2);
 #pragma unroll
             for (int i = 0; i < NA; ++i) lds_dma16(ab, a_off[i], st + (NA * wave + i) * 1024);
             const uint8_t* bb = ebase + (size_t)c * 128;
@@ -597,7 +600,7 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
                 }
             }
         };
-        const int NC = K / KC;
+        const int NC = Kw / KC;
         for (int c = 0; c < NS - 1 && c < NC; ++c) issue(c);
         for (int c = 0; c < NC; ++c) {
             // this wavefront's loads of chunk c are done once only the later chunks'
@@ -773,6 +776,7 @@ extern "C" moe_status moe_experts_prefill(const moe_shape* shape, const void* ex
     ga.hbuf = hbuf;
     ga.y = y;
     ga.T = T;
+    ga.km = kmul(sh);
     hipLaunchKernelGGL((expert_gemm_kernel<true>), dim3(xcd_grid(W.max_tiles, (I + NBR / 2 - 1) / (NBR / 2))), dim3(256),
                        RING, hs, ga);
     if ((st = check_launch("expert_gemm_kernel<gate/up>")) != MOE_OK) return st;

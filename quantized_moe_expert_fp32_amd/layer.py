@@ -33,8 +33,10 @@ def bits_to_numpy(t: torch.Tensor) -> np.ndarray:
 
 
 def make_shape(s) -> moe.Shape:
-    """moe.Shape from any object with hidden/inter/n_experts/top_k/has_shared/router_fmt."""
-    return moe.Shape.make(s.hidden, s.inter, s.n_experts, s.top_k, s.has_shared, s.router_fmt)
+    """moe.Shape from any object with hidden/inter/n_experts/top_k/has_shared/router_fmt
+    (and optionally bits: 4 or 8)."""
+    return moe.Shape.make(s.hidden, s.inter, s.n_experts, s.top_k, s.has_shared, s.router_fmt,
+                          bits=getattr(s, "bits", 4))
 
 
 class DeviceLayer:

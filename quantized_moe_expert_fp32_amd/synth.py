@@ -211,19 +211,20 @@ def make_x(seed: int, T: int, H: int) -> np.ndarray:
     return _to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
 
 
-def workload_shape(name: str) -> Shape:
+def workload_shape(name: str, bits: int = 4) -> Shape:
     T, H, I, E, k, rf, zipf, seed, nl = WORKLOADS[name]
-    return Shape(hidden=H, inter=I, n_experts=E, top_k=k, has_shared=1, router_fmt=rf)
+    return Shape(hidden=H, inter=I, n_experts=E, top_k=k, has_shared=1, router_fmt=rf, bits=bits)
 
 
 def make_case(name: str, T: Optional[int] = None, n_layers: Optional[int] = None,
-              seed: Optional[int] = None) -> Case:
-    """Build one named workload. T, n_layers and seed override the defaults."""
+              seed: Optional[int] = None, bits: int = 4) -> Case:
+    """Build one named workload. T, n_layers and seed override the defaults; bits = 8
+    gives the same workload with 8-bit experts."""
     T0, H, I, E, k, rf, zipf, seed0, nl0 = WORKLOADS[name]
     T = T0 if T is None else T
     seed = seed0 if seed is None else seed
     n_layers = nl0 if n_layers is None else n_layers
-    shape = workload_shape(name)
+    shape = workload_shape(name, bits)
     layers = [make_layer(shape, seed, l, zipf) for l in range(n_layers)]
     return Case(name=name, seed=seed, T=T, shape=shape, x=make_x(seed, T, H), layers=layers)
 

@@ -51,7 +51,9 @@ def _big(moe, **kw):
 
 def test_shape_check_refuses_other_formats(moe):
     assert moe.moe_shape_check(_big(moe)) == moe.OK
-    assert moe.moe_shape_check(_big(moe, bits=8)) == moe.ERR_UNSUPPORTED
+    assert moe.moe_shape_check(_big(moe, bits=8)) == moe.OK
+    assert moe.moe_shape_check(_big(moe, bits=8, hidden=8192)) == moe.ERR_UNSUPPORTED
+    assert moe.moe_shape_check(_big(moe, bits=8, inter=2048)) == moe.ERR_UNSUPPORTED
     assert moe.moe_shape_check(_big(moe, bits=3)) == moe.ERR_UNSUPPORTED
     assert moe.moe_shape_check(_big(moe, group=128)) == moe.ERR_UNSUPPORTED
     assert moe.moe_shape_check(_big(moe, router_fmt=7)) == moe.ERR_UNSUPPORTED
@@ -73,7 +75,11 @@ def test_sizes(moe):
     assert moe.moe_decode_workspace_bytes(sh, 1) == 9216 + 1280 + 16384 + 2 * 8192 + 16384 + 3 * 16384
     assert moe.moe_decode_workspace_bytes(sh, 16) == 16 * 9216 + 1280 + 16384 + 16 * 2 * 8192 + 16 * 18432
     assert moe.moe_prefill_workspace_bytes(sh, 4096) > 4096 * 9 * 512 * 2
-    assert moe.moe_experts_packed_bytes(_big(moe, bits=8)) == 0
+    # 8-bit experts are packed as int4 rows twice as long (two planes), with one
+    # (scale, bias) word per 64 codes of each plane
+    per8 = 2 * 512 * 4096 // 2 + 2048 * 1024 // 2 + 2 * 512 * 64 * 4 + 2048 * 16 * 4
+    assert moe.moe_experts_packed_bytes(_big(moe, bits=8)) == 257 * per8
+    assert moe.moe_experts_packed_bytes(_big(moe, bits=5)) == 0
 
 
 def test_host_argument_checks_launch_nothing(moe):
@@ -107,7 +113,7 @@ def test_host_argument_checks_launch_nothing(moe):
     st = moe.raw_call("moe_combine", byref(sh), v(P), v(P), v(P), 1, v(P + 2), v(P), None)
     assert st == moe.ERR_INVALID_ARG
     # refused formats never reach a kernel
-    st = moe.raw_call("moe_route", byref(_big(moe, bits=8)), v(P), None, v(P), 1, v(P), v(P), v(P), v(P), None)
+    st = moe.raw_call("moe_route", byref(_big(moe, bits=2)), v(P), None, v(P), 1, v(P), v(P), v(P), v(P), None)
     assert st == moe.ERR_UNSUPPORTED
     # rmsnorm aliasing is refused
     st = moe.raw_call("moe_rmsnorm", 2048, v(P), 1, ctypes.c_float(1e-6), v(P), None)
@@ -122,9 +128,9 @@ def test_host_argument_checks_launch_nothing(moe):
 
 
 def test_last_error_message(moe):
-    sh = _big(moe, bits=8)
+    sh = _big(moe, bits=6)
     st = moe.raw_call("moe_route", ctypes.byref(sh), None, None, None, 1, None, None, None, None, None)
     assert st == moe.ERR_UNSUPPORTED
     from quantized_moe_expert_fp32_amd.moe import _lib
 
-    assert b"4-bit" in _lib.moe_last_error()
+    assert b"4-bit or 8-bit" in _lib.moe_last_error()
