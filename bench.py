@@ -10,7 +10,8 @@ batch of synthetic input already resident in HBM:
                default) and 64 tokens so weights come from HBM, not cache;
   prefill512   T=512 tokens through one layer;
   prefill4096  T=4096 tokens, Zipf(1.1) logit bias (skewed expert loads);
-  stack1/16    one decode step of T=1 / T=16 tokens through 40 stacked layers.
+  stack1/16    one decode step of T=1 / T=16 tokens through 40 stacked layers
+               (one moe_decode_block launch per layer: RMSNorm, layer, residual).
 The timed region replays HIP graphs of the step sequence (captured once): one
 graph of min(K, 64) steps replayed K // that times, and one of the remaining steps.
 The process prints one JSON line. Its headline is the chosen workload (decode by
@@ -239,12 +240,14 @@ def run_workload(wl, K, W, inp, no_cpu, cpu_seconds):
 
     # ---------------------------------------------------------------- the step sequence
     if kind.startswith("stack"):
+        # one moe_decode_block (RMSNorm, layer, residual) per layer between two state
+        # buffers; after the 40 layers the state is back in x_state
         x_state = xs.clone()
-        xn = torch.empty_like(x_state)
+        x_other = torch.empty_like(x_state)
         period = 1
 
         def step(j):
-            L.stack_step(layers, x_state, xn, buf, path=path)
+            L.stack_step_fused(layers, x_state, x_other, buf)
     elif kind == "decode":
         period = xs.shape[0]  # 64 consecutive steps cover every token and every weight copy
 
@@ -321,7 +324,12 @@ def run_workload(wl, K, W, inp, no_cpu, cpu_seconds):
         for j in range(n_ev):
             dl = layers[j % len(layers)]
             xin = xs[(j % xs.shape[0]):(j % xs.shape[0]) + 1] if kind == "decode" else xs
-            if path == "fused":
+            if kind.startswith("stack"):
+                starts[j].record(stream)
+                moe.moe_decode_block(shape, dl.router, dl.logit_bias, dl.experts, xin, T, 1e-6, buf.ws, buf.logits,
+                                     buf.ids, buf.w, buf.wsh, buf.y, buf.out)
+                ends[j].record(stream)
+            elif path == "fused":
                 starts[j].record(stream)
                 moe.moe_decode_layer(shape, dl.router, dl.logit_bias, dl.experts, xin, T, buf.ws, buf.logits,
                                      buf.ids, buf.w, buf.wsh, buf.y, None, buf.out)
@@ -357,7 +365,9 @@ def run_workload(wl, K, W, inp, no_cpu, cpu_seconds):
         roof = dict(bound="hbm", achieved=alg_bytes / (stage_us * 1e-6) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = stored_traffic(wl)
-    roof["kernel"] = ("decode_layer_kernel (router, selection, experts, combine in one launch)" if path == "fused"
+    roof["kernel"] = ("decode_layer_kernel (RMSNorm, router, selection, experts, combine and residual in one launch)"
+                      if kind.startswith("stack") else
+                      "decode_layer_kernel (router, selection, experts, combine in one launch)" if path == "fused"
                       else "experts stage (moe_experts_prefill): " + " + ".join(PREFILL_KERNELS))
     roof["avg_us"] = stage_us
     roof["alg_bytes_per_launch"] = int(alg_bytes)

@@ -218,6 +218,18 @@ moe_status moe_decode_layer(const moe_shape* shape, const void* router_packed,
                             float* logits, int32_t* ids, uint16_t* w, uint16_t* w_shared,
                             float* y, const uint16_t* residual, uint16_t* out, void* stream);
 
+/* One block of a layer stack in one launch: x_out = bf16(x + MoE(bf16(RMSNorm(x)))),
+ * RMSNorm with unit weight and epsilon eps (>= 0): the layer runs on the
+ * normalised tokens, and the residual add uses x as given (reading of the stack:
+ * a pre-norm residual block, as moe_rmsnorm followed by moe_decode_layer with
+ * residual = x; the outputs are bit-identical to those two calls). Arguments,
+ * workspace, waits and errors as moe_decode_layer; logits, ids, w, w_shared and y
+ * are the layer's; x_out [T][H] bf16 must not overlap x. [P3-build], [P1-phase]. */
+moe_status moe_decode_block(const moe_shape* shape, const void* router_packed, const float* logit_bias,
+                            const void* experts_packed, const uint16_t* x, int32_t T, float eps, void* ws,
+                            size_t ws_bytes, float* logits, int32_t* ids, uint16_t* w, uint16_t* w_shared,
+                            float* y, uint16_t* x_out, void* stream);
+
 /* Waits for `stream`, then reads and clears the error word that moe_decode_layer
  * sets in ws (same shape and T) when one of its bounded waits times out. Returns
  * MOE_OK if no call since the last check timed out, MOE_ERR_TIMEOUT if one did
@@ -275,7 +287,8 @@ moe_status moe_combine(const moe_shape* shape, const float* y, const uint16_t* w
                        uint16_t* out, void* stream);
 
 /* ---------------------------------------------------------------- a7: stack glue
- * Unit-weight RMSNorm per row: out = bf16(x / sqrt(mean(x^2) + eps)), fp32 math.
+ * Unit-weight RMSNorm per row: out = bf16(x * r), r = 1 / sqrt(mean(x^2) + eps) in
+ * fp32; the sum of squares runs in one fixed order (the one moe_decode_block uses).
  * (Reading: the pages give no norm for an MoE-only stack; a pre-norm residual block
  * x <- x + MoE(RMSNorm(x)) keeps stacked activations in range.) out may not alias x. */
 moe_status moe_rmsnorm(int32_t hidden, const uint16_t* x, int32_t T, float eps, uint16_t* out,

@@ -48,26 +48,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     *reinterpret_cast<uint2*>(out + t * H + c) = o;
 }
 
-// One block per row: sum of squares in a fixed order (per-thread strided partial
-// sums, then a tree over the block), r = 1 / sqrt(mean + eps), out = bf16(x * r).
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict__ x, int H, float eps,
+// One wavefront per row (four rows per workgroup): the sum of squares in the
+// order of row_sumsq, r = 1 / sqrt(mean + eps), out = bf16(x * r).
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict__ x, int T, int H, float eps,
                                                       uint16_t* __restrict__ out) {
-    __shared__ float red[256];
-    const uint16_t* row = x + (size_t)blockIdx.x * H;
-    float ss = 0.f;
-    for (int i = threadIdx.x; i < H; i += 256) {
-        const float v = bf16_to_f32(row[i]);
-        ss = fmaf(v, v, ss);
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const uint16_t* row = x + (size_t)t * H;
+    const float r = rms_scale(row_sumsq(row, H, lane), H, eps);
+    for (int i = 8 * lane; i < H; i += 512) {
+        const uint4 v = *reinterpret_cast<const uint4*>(row + i);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = norm_bf16(w[j] & 0xFFFFu, r) | (norm_bf16(w[j] >> 16, r) << 16);
+        *reinterpret_cast<uint4*>(out + (size_t)t * H + i) = make_uint4(o[0], o[1], o[2], o[3]);
     }
-    red[threadIdx.x] = ss;
-    __syncthreads();
-    for (int w = 128; w >= 1; w >>= 1) {
-        if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-        __syncthreads();
-    }
-    const float r = 1.f / sqrtf(red[0] / (float)H + eps);
-    for (int i = threadIdx.x; i < H; i += 256)
-        out[(size_t)blockIdx.x * H + i] = (uint16_t)f32_to_bf16(bf16_to_f32(row[i]) * r);
 }
 
 }  // namespace moe
@@ -95,7 +92,9 @@ extern "C" moe_status moe_rmsnorm(int32_t hidden, const uint16_t* x, int32_t T, 
                                   void* stream) {
     clear_error();
     if (hidden < 64 || hidden % 64 != 0) return fail(MOE_ERR_INVALID_ARG, "hidden %d must be a multiple of 64", hidden);
-    if (T < 1 || !x || !out || x == out) return fail(MOE_ERR_INVALID_ARG, "bad T or pointers");
-    hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)T), dim3(256), 0, (hipStream_t)stream, x, hidden, eps, out);
+    if (T < 1 || !x || !out || x == out || !aligned16(x) || !aligned16(out))
+        return fail(MOE_ERR_INVALID_ARG, "bad T or pointers (NULL, unaligned or aliased)");
+    hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, (hipStream_t)stream, x, T, hidden,
+                       eps, out);
     return check_launch("rmsnorm_kernel");
 }

@@ -393,6 +393,7 @@ struct LayerArgs {
     int T, H, I, E, k, has_shared, R;
     int kmul;     // weight row length / activation length: 1 (4-bit experts) or 2 (8-bit)
     int stage_x;  // x and its chunk sums are staged in LDS (else read from global memory)
+    float norm_eps;  // >= 0: the layer's input is bf16(RMSNorm(x)) (needs stage_x); < 0: x as given
 };
 
 // Tagged h of one token: word w in copy c (0, 1) sits at th_word(w, c). Blocks of
@@ -495,16 +496,24 @@ __device__ __forceinline__ void token_xslice(bool lds, const uint16_t* s_x, cons
 }
 
 // Copies x [T][H] into LDS with the chunk sums of load_xslice (one chunk of 32 per
-// thread and step).
-__device__ __forceinline__ void stage_x(const uint16_t* __restrict__ gx, int T, int H, uint16_t* s_x, float* s_xs) {
+// thread and step); with xr (per-token RMSNorm scales) it stores bf16(x * r_t).
+__device__ __forceinline__ void stage_x(const uint16_t* __restrict__ gx, int T, int H, uint16_t* s_x, float* s_xs,
+                                        const float* xr) {
     const int C = H / 32;
     for (int i = threadIdx.x; i < T * C; i += blockDim.x) {
         const uint4* src = reinterpret_cast<const uint4*>(gx + (size_t)i * 32);
         uint4* dst = reinterpret_cast<uint4*>(s_x + (size_t)i * 32);
         uint32_t w[16];
+        const float r = xr ? xr[i / C] : 1.f;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-            const uint4 v = src[q4];
+            uint4 v = src[q4];
+            if (xr) {
+                v.x = norm_bf16(v.x & 0xFFFFu, r) | (norm_bf16(v.x >> 16, r) << 16);
+                v.y = norm_bf16(v.y & 0xFFFFu, r) | (norm_bf16(v.y >> 16, r) << 16);
+                v.z = norm_bf16(v.z & 0xFFFFu, r) | (norm_bf16(v.z >> 16, r) << 16);
+                v.w = norm_bf16(v.w & 0xFFFFu, r) | (norm_bf16(v.w >> 16, r) << 16);
+            }
             dst[q4] = v;
             w[4 * q4 + 0] = v.x;
             w[4 * q4 + 1] = v.y;
@@ -590,6 +599,7 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
     __shared__ uint16_t s_dtok[MAXD][16];
     __shared__ int32_t s_nd;
     __shared__ int s_bad;  // a bounded wait of this workgroup timed out: its h and outputs become NaN
+    __shared__ float s_xr[16];  // per-token RMSNorm scales (norm_eps >= 0)
     // rows per down item: one token has one item per workgroup; more tokens run
     // items one after another, and items of 16 rows keep more loads in flight per
     // wavefront (T=16 69.4 -> 60.3 us, T=8 39.8 -> 35.6; 32 rows measured no better
@@ -648,21 +658,31 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
             const int r = (wg >> 3) * 4 + (wg & 7) + GE * wtop;
             if (r < R)
                 router_row<1, AFF8>(a.router, a.logit_bias, a.x, 0, 1, H, R, E, r, lane, a.logits, false, a.tlogits,
-                                    tag, a.tl_stride, a.tl_copy);
+                                    tag, a.tl_stride, a.tl_copy, a.norm_eps);
         }
     } else if (nrw * T + npoll <= LW) {
         if (wtop < nrw * T) {
             const int r = wg + G * (wtop / T);
             if (r < R)
                 router_row<1, AFF8>(a.router, a.logit_bias, a.x, wtop % T, 1, H, R, E, r, lane, a.logits, false,
-                                    a.tlogits, tag, a.tl_stride, a.tl_copy);
+                                    a.tlogits, tag, a.tl_stride, a.tl_copy, a.norm_eps);
         }
     } else if (wtop < T) {
         for (int r = wg; r < R; r += G)
             router_row<1, AFF8>(a.router, a.logit_bias, a.x, wtop, 1, H, R, E, r, lane, a.logits, false, a.tlogits,
-                                tag, a.tl_stride, a.tl_copy);
+                                tag, a.tl_stride, a.tl_copy, a.norm_eps);
     }
-    if (a.stage_x) stage_x(a.x, T, H, s_x, s_xs);
+    // with the norm, the layer's input is bf16(x r_t): waves t < T compute the scales
+    // (in row_sumsq's order, as the router rows do) before the staging
+    const bool norm = a.norm_eps >= 0.f;
+    if (norm) {
+        if (wave < T) {
+            const float xr = rms_scale(row_sumsq(a.x + (size_t)wave * H, H, lane), H, a.norm_eps);
+            if (lane == 0) s_xr[wave] = xr;
+        }
+        __syncthreads();
+    }
+    if (a.stage_x) stage_x(a.x, T, H, s_x, s_xs, norm ? s_xr : nullptr);
     __syncthreads();
     // the shared expert's row pairs are tasks 0 .. npair-1 of phase B
     PairLoads<CPL> cur;
@@ -1173,18 +1193,20 @@ extern "C" moe_status moe_experts_decode_noalloc(const moe_shape* shape, const v
                                  (hipStream_t)stream);
 }
 
-extern "C" moe_status moe_decode_layer(const moe_shape* shape, const void* router_packed, const float* logit_bias,
-                                       const void* experts_packed, const uint16_t* x, int32_t T, void* ws,
-                                       size_t ws_bytes, float* logits, int32_t* ids, uint16_t* w, uint16_t* w_shared,
-                                       float* y, const uint16_t* residual, uint16_t* out, void* stream) {
-    clear_error();
+// One launch of decode_layer_kernel (moe_decode_layer, moe_decode_block).
+static moe_status decode_layer_launch(const moe_shape* shape, const void* router_packed, const float* logit_bias,
+                                      const void* experts_packed, const uint16_t* x, int32_t T, void* ws,
+                                      size_t ws_bytes, float* logits, int32_t* ids, uint16_t* w, uint16_t* w_shared,
+                                      float* y, const uint16_t* residual, uint16_t* out, float norm_eps,
+                                      void* stream) {
     moe_status st = check_decode_args(shape, experts_packed, x, T, ws, ws_bytes);
     if (st != MOE_OK) return st;
     const moe_shape& sh = *shape;
     if ((st = check_route_outputs(sh, T, ids, w, w_shared)) != MOE_OK) return st;
-    if (!router_packed || !logits || !out || !aligned16(router_packed))
+    if (!router_packed || !logits || !out || !aligned16(router_packed) || !aligned16(out))
         return fail(MOE_ERR_INVALID_ARG, "router, logits or out NULL / unaligned");
-    if (y && !aligned16(y)) return fail(MOE_ERR_INVALID_ARG, "y unaligned");
+    if ((y && !aligned16(y)) || (residual && !aligned16(residual)))
+        return fail(MOE_ERR_INVALID_ARG, "y or residual unaligned");
     if (cpl_for(sh.hidden * kmul(sh)) > 2)
         return fail(MOE_ERR_UNSUPPORTED, "single-launch decode layer serves rows of at most 4096 int4 codes (hidden "
                     "<= 4096 with 4-bit experts, <= 2048 with 8-bit)");
@@ -1218,12 +1240,15 @@ extern "C" moe_status moe_decode_layer(const moe_shape* shape, const void* route
     a.has_shared = sh.has_shared;
     a.R = router_rows(sh);
     a.kmul = kmul(sh);
+    a.norm_eps = norm_eps;
     // 16 KiB covers the kernel's static LDS (selection results, distinct-expert lists)
     // h rows and their chunk sums, then (when staged) x and its chunk sums
     const size_t lds_h = hsh_bytes(sh) + (size_t)n_slots(sh) * (sh.inter / 32) * 4, lds_x = xsh_bytes(sh, T);
     const int max_lds = device_max_lds();
     if (max_lds <= 0) return fail(MOE_ERR_HIP, "could not query the LDS size");
     a.stage_x = lds_h + lds_x + 16384 <= (size_t)max_lds ? 1 : 0;
+    if (norm_eps >= 0.f && !a.stage_x)
+        return fail(MOE_ERR_UNSUPPORTED, "decode block: the normalised activations of %d tokens do not fit in LDS", T);
     const size_t lds = lds_h + (a.stage_x ? lds_x : 0);
     const int G = std::min(cus, std::max(a.R, T * (a.H / DN_ROWS)));
     const LayerKernel f = pick_layer(a, sh.router_fmt == MOE_ROUTER_AFFINE8);
@@ -1236,6 +1261,27 @@ extern "C" moe_status moe_decode_layer(const moe_shape* shape, const void* route
     const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(f), dim3(G), dim3(LTH), args, lds, hs);
     if (e != hipSuccess) return fail(MOE_ERR_HIP, "decode_layer_kernel: %s", hipGetErrorString(e));
     return check_launch("decode_layer_kernel");
+}
+
+extern "C" moe_status moe_decode_layer(const moe_shape* shape, const void* router_packed, const float* logit_bias,
+                                       const void* experts_packed, const uint16_t* x, int32_t T, void* ws,
+                                       size_t ws_bytes, float* logits, int32_t* ids, uint16_t* w, uint16_t* w_shared,
+                                       float* y, const uint16_t* residual, uint16_t* out, void* stream) {
+    clear_error();
+    return decode_layer_launch(shape, router_packed, logit_bias, experts_packed, x, T, ws, ws_bytes, logits, ids, w,
+                               w_shared, y, residual, out, -1.f, stream);
+}
+
+extern "C" moe_status moe_decode_block(const moe_shape* shape, const void* router_packed, const float* logit_bias,
+                                       const void* experts_packed, const uint16_t* x, int32_t T, float eps, void* ws,
+                                       size_t ws_bytes, float* logits, int32_t* ids, uint16_t* w,
+                                       uint16_t* w_shared, float* y, uint16_t* x_out, void* stream) {
+    clear_error();
+    if (!(eps >= 0.f)) return fail(MOE_ERR_INVALID_ARG, "eps must be >= 0");
+    if (x && x_out && (const void*)x == (const void*)x_out)
+        return fail(MOE_ERR_INVALID_ARG, "x_out may not alias x (other workgroups still read x)");
+    return decode_layer_launch(shape, router_packed, logit_bias, experts_packed, x, T, ws, ws_bytes, logits, ids, w,
+                               w_shared, y, x, x_out, eps, stream);
 }
 
 extern "C" moe_status moe_decode_layer_check(const moe_shape* shape, int32_t T, void* ws, size_t ws_bytes,

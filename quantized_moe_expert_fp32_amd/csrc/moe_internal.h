@@ -312,6 +312,42 @@ __device__ __forceinline__ float group_sum(float v, int lpr) {
     return v;
 }
 
+// ---- unit-weight RMSNorm (the stack's pre-norm reading): every kernel that
+// normalises a row computes the sum of squares in this one order, so the staged
+// norm and the norm inside the decode layer give the same bf16 values.
+// Lane l adds the squares of the 16-element pieces starting at 16 (l + 64 c),
+// c = 0, 1, ... (in element order, fp32 fused multiply-adds); group_sum's tree
+// adds the 64 lane sums. row_sumsq returns the total in every lane.
+__device__ __forceinline__ float sumsq_piece16(uint4 a, uint4 b, float ss) {
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xFFFF0000u);
+        ss = fmaf(lo, lo, ss);
+        ss = fmaf(hi, hi, ss);
+    }
+    return ss;
+}
+__device__ __forceinline__ float sumsq_total(float lane_sum) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(group_sum(lane_sum, 64)), 63));
+}
+__device__ __forceinline__ float row_sumsq(const uint16_t* __restrict__ row, int H, int lane) {
+    float ss = 0.f;
+    for (int c = 0; 16 * (lane + 64 * c) < H; ++c) {
+        const uint4* p = reinterpret_cast<const uint4*>(row + 16 * (lane + 64 * c));
+        ss = sumsq_piece16(p[0], p[1], ss);
+    }
+    return sumsq_total(ss);
+}
+// 1 / sqrt(mean(x^2) + eps) in fp32 (correctly rounded division and square root).
+__device__ __forceinline__ float rms_scale(float sumsq, int H, float eps) {
+    return 1.f / sqrtf(sumsq / (float)H + eps);
+}
+// bf16(x * r) of one bf16 value.
+__device__ __forceinline__ uint32_t norm_bf16(uint32_t xbits, float r) {
+    return f32_to_bf16(bf16_to_f32(xbits) * r);
+}
+
 __device__ __forceinline__ double dpp_f64_step(double v, int step) {
     const uint64_t u = (uint64_t)__double_as_longlong(v);
     uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);

@@ -202,11 +202,15 @@ __device__ __forceinline__ void load_words(const uint16_t* p, uint32_t* out) {
 // The logit of token t is written to logits[t][r] (coherently when `coherent`)
 // and, when `tagged` is given, published with tag `tag` to the two copies
 // tagged[t * tstride + r] and tagged[t * tstride + tcopy + r].
+// norm_eps >= 0 (one token, TT == 1): the row's input is bf16(RMSNorm(x)) of that
+// token, with the scale of rms_scale(row_sumsq); with the 8-bit router and at
+// most 4096 activations the squares come from the activations the products load
+// (in row_sumsq's order), else from a pass of row_sumsq.
 template <int TT, bool AFF8>
 __device__ __forceinline__ void router_row(const uint8_t* __restrict__ router, const float* __restrict__ logit_bias,
                                            const uint16_t* __restrict__ x, int t0, int nt, int H, int R, int E, int r,
                                            int lane, float* logits, bool coherent, uint64_t* tagged, uint32_t tag,
-                                           size_t tstride = 0, size_t tcopy = 0) {
+                                           size_t tstride = 0, size_t tcopy = 0, float norm_eps = -1.f) {
     double acc[TT];
 #pragma unroll
     for (int t = 0; t < TT; ++t) acc[t] = 0.0;
@@ -216,6 +220,11 @@ __device__ __forceinline__ void router_row(const uint8_t* __restrict__ router, c
     constexpr int TH = TT <= 4 ? TT : 0;  // tokens whose activations are loaded with the weights
     const int C = H / EPC;
     const uint32_t* sb = reinterpret_cast<const uint32_t*>(router + (size_t)R * H);
+    const bool norm = TT == 1 && norm_eps >= 0.f;
+    const bool norm_regs = AFF8 && H <= 64 * NCH * EPC;  // one pass of the loop holds the whole row
+    float xr = 1.f;  // the token's RMSNorm scale
+    if (norm && !norm_regs) xr = rms_scale(row_sumsq(x + (size_t)t0 * H, H, lane), H, norm_eps);
+    auto xin = [&](uint32_t bits) -> uint32_t { return norm ? norm_bf16(bits, xr) : bits; };
     for (int j0 = lane; j0 < C; j0 += 64 * NCH) {
         uint4 wq[NCH];
         uint32_t wg[NCH];
@@ -238,6 +247,17 @@ __device__ __forceinline__ void router_row(const uint8_t* __restrict__ router, c
                         load_words<XW>(x + (size_t)(t0 + t) * H + c0, xh[c][t]);
                     }
                 }
+            }
+        }
+        if constexpr (AFF8 && TT == 1) {
+            if (norm && norm_regs) {  // lane l holds the 16-element pieces l + 64 c of the token
+                float ss = 0.f;
+#pragma unroll
+                for (int c = 0; c < NCH; ++c)
+                    if (j0 + 64 * c < C)
+                        ss = sumsq_piece16(make_uint4(xh[c][0][0], xh[c][0][1], xh[c][0][2], xh[c][0][3]),
+                                           make_uint4(xh[c][0][4], xh[c][0][5], xh[c][0][6], xh[c][0][7]), ss);
+                xr = rms_scale(sumsq_total(ss), H, norm_eps);
             }
         }
 #pragma unroll
@@ -266,7 +286,7 @@ __device__ __forceinline__ void router_row(const uint8_t* __restrict__ router, c
 #pragma unroll
                         for (int i = 0; i < EPC; ++i) {
                             const uint32_t w = xh[c][t < TH ? t : 0][i >> 1];
-                            const uint32_t bits = (i & 1) ? (w >> 16) : (w & 0xFFFFu);
+                            const uint32_t bits = xin((i & 1) ? (w >> 16) : (w & 0xFFFFu));
                             acc[t] = fma((double)bf16_to_f32(bits), wv[i], acc[t]);
                         }
                     }
@@ -285,10 +305,10 @@ __device__ __forceinline__ void router_row(const uint8_t* __restrict__ router, c
                     for (int t = 0; t < TT; ++t) {
                         if (t < nt) {
                             const uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)(t0 + t) * H + c0 + 4 * g);
-                            acc[t] = fma((double)bf16_to_f32(xv.x & 0xFFFFu), w4[0], acc[t]);
-                            acc[t] = fma((double)bf16_to_f32(xv.x >> 16), w4[1], acc[t]);
-                            acc[t] = fma((double)bf16_to_f32(xv.y & 0xFFFFu), w4[2], acc[t]);
-                            acc[t] = fma((double)bf16_to_f32(xv.y >> 16), w4[3], acc[t]);
+                            acc[t] = fma((double)bf16_to_f32(xin(xv.x & 0xFFFFu)), w4[0], acc[t]);
+                            acc[t] = fma((double)bf16_to_f32(xin(xv.x >> 16)), w4[1], acc[t]);
+                            acc[t] = fma((double)bf16_to_f32(xin(xv.y & 0xFFFFu)), w4[2], acc[t]);
+                            acc[t] = fma((double)bf16_to_f32(xin(xv.y >> 16)), w4[3], acc[t]);
                         }
                     }
                     __builtin_amdgcn_sched_barrier(0);  // one group's activation reads in flight at a time

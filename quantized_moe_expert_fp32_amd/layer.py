@@ -131,3 +131,21 @@ def stack_step(layers, x: torch.Tensor, xn: torch.Tensor, buf: StepBuffers, eps:
         if keep is not None:
             keep.append((x.clone(), xn.clone(), buf.ids.clone()))
     return x
+
+
+def stack_step_fused(layers, x: torch.Tensor, x_other: torch.Tensor, buf: StepBuffers, eps: float = 1e-6,
+                     stream=None, keep: Optional[list] = None) -> torch.Tensor:
+    """The same stack step as stack_step for T <= 16, one launch per layer: each layer
+    is moe_decode_block (RMSNorm, the layer and the residual add), reading one state
+    buffer and writing the other. Returns the buffer that holds the final state (x
+    after an even number of layers). With `keep`, (state, ids) copies per layer."""
+    sh = layers[0].shape
+    cur, nxt = x, x_other
+    for L in layers:
+        moe.moe_decode_block(sh, L.router, L.logit_bias, L.experts, cur, buf.T, eps, buf.ws, buf.logits, buf.ids, buf.w,
+                             buf.wsh, buf.y, nxt, stream)
+        if keep is not None:
+            keep.append((nxt.clone(), buf.ids.clone()))
+        cur, nxt = nxt, cur
+    return cur
+

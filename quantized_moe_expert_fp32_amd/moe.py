@@ -91,6 +91,8 @@ _lib.moe_experts_decode_noalloc.restype = _I32
 _lib.moe_experts_decode_noalloc.argtypes = [_S, _P, _P, _I32, _P, _P, _P]
 _lib.moe_decode_layer.restype = _I32
 _lib.moe_decode_layer.argtypes = [_S, _P, _P, _P, _P, _I32, _P, _SZ, _P, _P, _P, _P, _P, _P, _P, _P]
+_lib.moe_decode_block.restype = _I32
+_lib.moe_decode_block.argtypes = [_S, _P, _P, _P, _P, _I32, ctypes.c_float, _P, _SZ, _P, _P, _P, _P, _P, _P, _P]
 _lib.moe_decode_layer_check.restype = _I32
 _lib.moe_decode_layer_check.argtypes = [_S, _I32, _P, _SZ, _P]
 _lib.moe_dispatch.restype = _I32
@@ -109,7 +111,7 @@ _lib.moe_rmsnorm.argtypes = [_I32, _P, _I32, ctypes.c_float, _P, _P]
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_last_error", "moe_shape_check",
            "moe_experts_packed_bytes", "moe_pack_experts", "moe_router_packed_bytes", "moe_pack_router",
            "moe_route", "moe_route_from_logits", "moe_decode_workspace_bytes", "moe_experts_decode",
-           "moe_experts_decode_noalloc", "moe_decode_layer",
+           "moe_experts_decode_noalloc", "moe_decode_layer", "moe_decode_block",
            "moe_decode_layer_check", "moe_dispatch", "moe_prefill_workspace_bytes", "moe_prefill_dispatch_layout",
            "moe_experts_prefill", "moe_combine", "moe_rmsnorm")
 
@@ -206,6 +208,13 @@ def moe_decode_layer(shape, router_packed, logit_bias, experts_packed, x, T, ws,
                                  _ptr(x), T, _ptr(ws), _nbytes(ws), _ptr(logits), _ptr(ids), _ptr(w),
                                  _ptr(w_shared), _ptr(y), _ptr(residual), _ptr(out), _stream(stream)),
            "moe_decode_layer")
+
+
+def moe_decode_block(shape, router_packed, logit_bias, experts_packed, x, T, eps, ws, logits, ids, w, w_shared, y,
+                     x_out, stream=None):
+    _check(_lib.moe_decode_block(ctypes.byref(shape), _ptr(router_packed), _ptr(logit_bias), _ptr(experts_packed),
+                                 _ptr(x), T, ctypes.c_float(eps), _ptr(ws), _nbytes(ws), _ptr(logits), _ptr(ids),
+                                 _ptr(w), _ptr(w_shared), _ptr(y), _ptr(x_out), _stream(stream)), "moe_decode_block")
 
 
 def moe_decode_layer_check(shape, T, ws, stream=None):

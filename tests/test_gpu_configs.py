@@ -173,3 +173,36 @@ def test_prefill_route_chunks_of_128(gpu):
         part = run_path(gpu, dl, c.x[t0:t0 + 128], "prefill")
         for key in ("logits", "ids", "w", "wsh", "y", "out"):
             assert np.array_equal(part[key], full[key][t0:t0 + 128]), (key, t0)
+
+
+@pytest.mark.parametrize("name,T,bits", [("decode", 1, 4), ("decode", 3, 4), ("decode", 16, 4), ("tiny", 1, 4),
+                                         ("tiny", 4, 4), ("decode", 2, 8)])
+def test_decode_block_equals_norm_then_layer(gpu, name, T, bits):
+    """moe_decode_block (RMSNorm folded into the single-launch layer, residual add)
+    gives the same bits as moe_rmsnorm followed by moe_decode_layer with residual,
+    over repeated launches; x is left unchanged."""
+    L = _L()
+    c = synth.make_case(name, bits=bits, seed=40 + T)
+    dl = L.DeviceLayer(L.make_shape(c.shape), c.layers[0])
+    H = c.shape.hidden
+    x_np = synth.random_x(1300 + T, T, H)
+    x = L.to_device(x_np)
+    xn = torch.empty_like(x)
+    a = L.alloc_buffers(dl.shape, T, "fused")
+    b = L.alloc_buffers(dl.shape, T, "fused")
+    staged_out = torch.empty_like(x)
+    gpu.moe_rmsnorm(H, x, T, 1e-6, xn)
+    L.layer_step(dl, xn, a, "fused", residual=x, out=staged_out)
+    x_out = torch.empty_like(x)
+    for _ in range(2):
+        gpu.moe_decode_block(dl.shape, dl.router, dl.logit_bias, dl.experts, x, T, 1e-6, b.ws, b.logits, b.ids, b.w,
+                             b.wsh, b.y, x_out)
+    torch.cuda.synchronize()
+    assert np.array_equal(L.bits_to_numpy(x), x_np)
+    assert np.array_equal(L.bits_to_numpy(x_out), L.bits_to_numpy(staged_out))
+    for key in ("logits", "ids", "w", "wsh", "y"):
+        assert np.array_equal(getattr(a, key).cpu().numpy(), getattr(b, key).cpu().numpy()), key
+    assert gpu.moe_decode_layer_check(dl.shape, T, b.ws)
+    with pytest.raises(Exception):
+        gpu.moe_decode_block(dl.shape, dl.router, dl.logit_bias, dl.experts, x, T, 1e-6, b.ws, b.logits, b.ids, b.w,
+                             b.wsh, b.y, x)  # x_out aliasing x is refused

@@ -1,13 +1,15 @@
 """The 40-layer decode stack (MoE blocks with RMSNorm and the residual add, 40
-independent layers of the 35B shape, about 18 GB of weights) at 1 and 16 tokens:
-the sequence of library calls that bench.py times is captured in a HIP graph and
-replayed three times; every replay gives the same states, and every layer of the
-last replay is checked against the oracle:
-  * the GPU's RMSNorm of the layer's input state within one bf16 step of the
-    oracle's (fp32 against float64 norm arithmetic);
-  * the oracle layer fed the GPU's own normalised input: picks within near ties,
-    and the new state bf16(x + out) within the output bar on the rows whose picks
-    equal the oracle's.
+independent layers of the 35B shape, about 18 GB of weights) at 1 and 16 tokens.
+Two call sequences, each captured in a HIP graph and replayed three times (every
+replay gives the same states):
+  * staged: moe_rmsnorm, then moe_decode_layer with the residual, per layer; every
+    layer is checked against the oracle: the GPU's RMSNorm within one bf16 step of
+    the oracle's (fp32 against float64 norm arithmetic), and the oracle layer fed
+    the GPU's own normalised input - picks within near ties, and the new state
+    bf16(x + out) within the output bar on the rows whose picks equal the oracle's;
+  * fused (the sequence bench.py times): one moe_decode_block per layer, between two
+    state buffers; every layer's state and picks equal the staged sequence's bit for
+    bit.
 """
 
 import concurrent.futures as cf
@@ -29,6 +31,27 @@ def _oracle_layer(args):
     xin, xn, host = args
     st = O.layer_forward(xn, host, 8)
     return st["logits"], st["ids"], O.residual_bf16(xin, st["out"])
+
+
+def _replays(g, x, x0, keep, T, what):
+    """Replays graph g three times from state x0; every replay's kept states are equal."""
+    L = _L()
+    first = None
+    for rep in range(3):
+        x.copy_(x0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        states = [tuple(L.bits_to_numpy(a) if a.dtype == torch.int16 else a.cpu().numpy() for a in kept)
+                  for kept in keep]
+        if first is None:
+            first = states
+        else:
+            for l in range(N_LAYERS):
+                for j in range(len(states[l])):
+                    assert np.array_equal(first[l][j], states[l][j]), (what, rep, l, j)
+        record_stats(what="stack_replay_" + what, T=T, rep=rep)
+    return first
 
 
 @pytest.mark.timeout(900)
@@ -53,20 +76,21 @@ def test_stack40_graph_replay(gpu, T):
     with torch.cuda.graph(g, stream=stream):
         L.stack_step(layers, x, xn, buf, keep=keep)
     torch.cuda.synchronize()
-    first = None
-    for rep in range(3):
-        x.copy_(x0)
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        states = [(L.bits_to_numpy(a), L.bits_to_numpy(b), ids.cpu().numpy()) for a, b, ids in keep]
-        if first is None:
-            first = states
-        else:
-            for l in range(N_LAYERS):
-                for j in range(3):
-                    assert np.array_equal(first[l][j], states[l][j]), (rep, l, j)
-        record_stats(what="stack_replay", T=T, rep=rep)
+    first = _replays(g, x, x0, keep, T, "staged")
+    # the fused sequence: one moe_decode_block per layer between two state buffers
+    xa, xb = x0.clone(), torch.empty_like(x0)
+    with torch.cuda.stream(stream):
+        L.stack_step_fused(layers, xa, xb, buf)  # eager warm-up
+    torch.cuda.synchronize()
+    keep_f = []
+    gf = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gf, stream=stream):
+        L.stack_step_fused(layers, xa, xb, buf, keep=keep_f)
+    torch.cuda.synchronize()
+    fused = _replays(gf, xa, x0, keep_f, T, "fused")
+    for l in range(N_LAYERS):
+        assert np.array_equal(fused[l][0], first[l][0]), ("state", l)
+        assert np.array_equal(fused[l][-1], first[l][-1]), ("ids", l)
     assert gpu.moe_decode_layer_check(sh, T, buf.ws) if L.pick_path(T) == "fused" else True
     ins = [c.x] + [first[l][0] for l in range(N_LAYERS - 1)]
     with cf.ThreadPoolExecutor(max_workers=8) as ex:
