@@ -581,10 +581,11 @@ __device__ __forceinline__ void dnl_load(const uint8_t* __restrict__ packed, con
 //      that token; an item's weight loads go out before that wait, and the next
 //      item's before the arithmetic.
 //
-// HC, IC, KC (when nonzero) fix hidden, inter and top_k at compile time; the
-// shape of the served model gets its own instance, with every lane layout and
-// reduction width folded.
-template <int CPL, int TT, bool AFF8, int VPL, int HC, int IC, int KC>
+// HC, IC, KC, KMC (when HC is nonzero) fix hidden, inter, top_k and the weight
+// row multiple at compile time; the shape of the served model gets its own
+// instances (4-bit and 8-bit experts), with every lane layout and reduction width
+// folded.
+template <int CPL, int TT, bool AFF8, int VPL, int HC, int IC, int KC, int KMC>
 __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
     __shared__ int32_t s_ids[16][16];
     __shared__ uint16_t s_w[16][16];
@@ -610,7 +611,7 @@ __global__ __launch_bounds__(LTH) void decode_layer_kernel(LayerArgs a) {
     const int G = gridDim.x, wg = blockIdx.x;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int T = TT == 1 ? 1 : a.T, H = HC ? HC : a.H, I = IC ? IC : a.I, k = KC ? KC : a.k;
-    const int KM = HC ? 1 : a.kmul;  // the served shape's instance is 4-bit
+    const int KM = HC ? KMC : a.kmul;
     const int Hw = H * KM, Iw = I * KM, IXC = I / 32;  // weight row lengths; h chunks of 32
     const int E = a.E, R = a.R, hs_ = a.has_shared;
     const int S = k + hs_;
@@ -1019,11 +1020,14 @@ typedef void (*LayerKernel)(LayerArgs);
 
 template <int CPL, int TT, int VPL>
 static LayerKernel pick_layer_v(const LayerArgs& a, bool aff8) {
-    if constexpr (CPL == 1 && VPL == 4) {
-        if (aff8 && a.H == 2048 && a.I == 512 && a.k == 8 && a.kmul == 1)  // the served model's shape
-            return decode_layer_kernel<CPL, TT, true, VPL, 2048, 512, 8>;
+    if constexpr (VPL == 4 && (CPL == 1 || CPL == 2)) {
+        // the served model's shape: 4-bit experts (rows of 2048 codes, one chunk per
+        // lane) and 8-bit experts (rows of 4096 codes, two)
+        if (aff8 && a.H == 2048 && a.I == 512 && a.k == 8 && a.kmul == CPL)
+            return decode_layer_kernel<CPL, TT, true, VPL, 2048, 512, 8, CPL>;
     }
-    return aff8 ? decode_layer_kernel<CPL, TT, true, VPL, 0, 0, 0> : decode_layer_kernel<CPL, TT, false, VPL, 0, 0, 0>;
+    return aff8 ? decode_layer_kernel<CPL, TT, true, VPL, 0, 0, 0, 1>
+                : decode_layer_kernel<CPL, TT, false, VPL, 0, 0, 0, 1>;
 }
 
 template <int CPL, int TT>
