@@ -33,7 +33,7 @@ struct PrefillWs {
     int n_slices;  // pick slices of the dispatch
 };
 
-constexpr int SLICE = 2048;  // picks per slice (one workgroup of the dispatch each)
+constexpr int SLICE = 1024;  // picks per slice (one workgroup of the dispatch each)
 
 static PrefillWs prefill_ws_layout(const moe_shape& s, int T) {
     PrefillWs w;
@@ -150,9 +150,11 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const int32_t* __restric
 //   scatter: every slice's workgroup reads the whole count matrix (n_slices x E) and
 //     derives the experts' totals, their offsets in the expert-sorted order and its
 //     own base within each expert (the sum over the earlier slices), then places its
-//     picks in ascending pick order, 256 at a time: each wavefront ranks its 64 picks
-//     among the lower lanes holding the same id (one ballot per id bit), and the
-//     counts of the lower wavefronts come through LDS. Workgroup 0 also writes the
+//     picks in ascending pick order: wavefront w takes the slice's picks SLICE/4 w ..
+//     SLICE/4 (w+1) - 1, 64 at a time, and ranks each among the lower lanes holding
+//     the same id (one ballot per id bit) plus the wavefront's earlier picks of that
+//     id (a per-wavefront count in LDS); after one barrier the counts of the lower
+//     wavefronts are added. One more workgroup, after the slices', writes the
 //     counts, the offsets, the shared expert's rows (it takes every token) and the
 //     tile list: every full tile first (expert order), then the partial tiles with
 //     the most row blocks first (expert order within a size), so the items that
@@ -207,10 +209,12 @@ __global__ __launch_bounds__(DT) void prefill_scatter_kernel(
     const int tid = threadIdx.x, b = blockIdx.x, wave = tid >> 6, lane = tid & 63;
     for (int i = tid; i < (DT / 64) * 1024; i += DT) (&wcnt[0][0])[i] = 0;
     const long long P = (long long)T * k, p0 = (long long)b * SLICE;
+    // pick j of this thread: p0 + DPT * 64 * wave + 64 j + lane (a wavefront's picks
+    // are consecutive)
     int ev[DPT];
 #pragma unroll
     for (int j = 0; j < DPT; ++j) {
-        const long long p = p0 + j * DT + tid;
+        const long long p = p0 + DPT * 64 * wave + 64 * j + lane;
         ev[j] = p < P ? ids[p] : -1;
     }
     for (int e = tid; e < E; e += DT) {
@@ -256,7 +260,7 @@ __global__ __launch_bounds__(DT) void prefill_scatter_kernel(
     }
     __syncthreads();
     for (int e = tid; e < E; e += DT) cur[e] += off[e];
-    if (b == 0) {
+    if (b == n_slices) {  // the extra workgroup: counts, offsets, shared rows, tile list
         for (int e = tid; e < M; e += DT) {
             counts[e] = cnt[e];
             offsets[e] = off[e];
@@ -314,30 +318,37 @@ __global__ __launch_bounds__(DT) void prefill_scatter_kernel(
                 }
             }
         }
+        return;
     }
     __syncthreads();
+    // pass 1, per wavefront (LDS accesses of one wavefront take effect in order): the
+    // rank of each pick among the wavefront's earlier picks of the same expert
     const uint64_t below = (1ull << lane) - 1ull;
+    int lpos[DPT];
 #pragma unroll
     for (int j = 0; j < DPT; ++j) {
-        const long long p = p0 + j * DT + tid;
+        const long long p = p0 + DPT * 64 * wave + 64 * j + lane;
         const int e = ev[j];
         const bool ok = p < P && e >= 0 && e < E;
         const uint64_t peers = equal_key_lanes(ok ? (uint32_t)e : 2047u);
         const int rank = __popcll(peers & below);
-        if (ok && rank == 0) wcnt[wave][e] = __popcll(peers);
-        __syncthreads();
-        if (ok) {
-            int pos = cur[e] + rank;
+        lpos[j] = ok ? wcnt[wave][e] + rank : 0;
+        if (ok && rank == 0) wcnt[wave][e] += __popcll(peers);
+    }
+    __syncthreads();
+    // pass 2: add the slice's base and the lower wavefronts' counts
+#pragma unroll
+    for (int j = 0; j < DPT; ++j) {
+        const long long p = p0 + DPT * 64 * wave + 64 * j + lane;
+        const int e = ev[j];
+        if (p >= P) continue;
+        if (e >= 0 && e < E) {
+            int pos = cur[e] + lpos[j];
             for (int w2 = 0; w2 < wave; ++w2) pos += wcnt[w2][e];
             order[pos] = (int)(p / k) * S + (int)(p % k);
-        } else if (p < P) {
+        } else {
             float* yr = y + ((size_t)(p / k) * S + (size_t)(p % k)) * H;
             for (int n = 0; n < H; ++n) yr[n] = 0.f;
-        }
-        __syncthreads();
-        if (ok && rank == 0) {  // every lane has read cur and the counts: advance, clear
-            atomicAdd(&cur[e], __popcll(peers));
-            wcnt[wave][e] = 0;
         }
     }
 }
@@ -760,7 +771,7 @@ extern "C" moe_status moe_experts_prefill(const moe_shape* shape, const void* ex
     const long long P = (long long)T * sh.top_k;
     hipLaunchKernelGGL(prefill_count_kernel, dim3((unsigned)W.n_slices), dim3(DT), 0, hs, ids, P, sh.n_experts, slices);
     if ((st = check_launch("prefill_count_kernel")) != MOE_OK) return st;
-    hipLaunchKernelGGL(prefill_scatter_kernel, dim3((unsigned)W.n_slices), dim3(DT), 0, hs, ids, T, sh.top_k,
+    hipLaunchKernelGGL(prefill_scatter_kernel, dim3((unsigned)W.n_slices + 1), dim3(DT), 0, hs, ids, T, sh.top_k,
                        sh.n_experts, sh.has_shared, H, W.n_slices, slices, counts, offsets, ntiles, tiles, order, y);
     if ((st = check_launch("prefill_scatter_kernel")) != MOE_OK) return st;
     GemmArgs ga;
