@@ -265,11 +265,12 @@ def expert_bits(layer) -> int:
     return 8 if layer.q_gate.shape[-1] == layer.q_down.shape[-2] else 4
 
 
-def expert_outputs(x_bits, ids, layer, n_experts: int, has_shared: bool):
+def expert_outputs(x_bits, ids, layer, n_experts: int, has_shared: bool, fp8: bool = False):
     """Per-slot expert outputs y [T, S, H] (float64) and h [T, S, I] (bf16 bits).
 
     Slot s < k holds expert ids[t, s]; slot k (when present) the shared expert,
-    stored as expert index E.
+    stored as expert index E. fp8: every expert through the FP8 route
+    (fp8_gate_up, fp8_down) instead of expert_ffn.
     """
     x = bf16_to_f64(x_bits)
     ids = np.asarray(ids)
@@ -289,9 +290,14 @@ def expert_outputs(x_bits, ids, layer, n_experts: int, has_shared: bool):
             rows_s = np.full(T, k)
         else:
             rows_t, rows_s = np.nonzero(ids == e)
-        he, ye = expert_ffn(x[rows_t], layer.q_gate[e], layer.s_gate[e], layer.b_gate[e],
-                            layer.q_up[e], layer.s_up[e], layer.b_up[e],
-                            layer.q_down[e], layer.s_down[e], layer.b_down[e], bits)
+        if fp8:
+            f8 = fp8_expert(layer, e)
+            he = fp8_gate_up(np.asarray(x_bits)[rows_t], f8["gate"], f8["up"])
+            ye = fp8_down(he, f8["down"])
+        else:
+            he, ye = expert_ffn(x[rows_t], layer.q_gate[e], layer.s_gate[e], layer.b_gate[e],
+                                layer.q_up[e], layer.s_up[e], layer.b_up[e],
+                                layer.q_down[e], layer.s_down[e], layer.b_down[e], bits)
         y[rows_t, rows_s] = ye
         h[rows_t, rows_s] = he
     return y, h
@@ -336,17 +342,143 @@ def residual_bf16(x_bits, out_bits) -> np.ndarray:
 
 # ---------------------------------------------------------------- whole layer
 
-def layer_forward(x_bits, layer, top_k: int, has_shared: bool = True):
-    """Route -> experts -> combine for one layer; returns every stage's output."""
+def layer_forward(x_bits, layer, top_k: int, has_shared: bool = True, fp8: bool = False):
+    """Route -> experts -> combine for one layer; returns every stage's output.
+    fp8: the experts take the FP8 route (routing and combine unchanged)."""
     W = router_matrix(layer)
     E = W.shape[0] - (1 if has_shared else 0)
     logits = router_logits(x_bits, W, getattr(layer, "logit_bias", None), E)
     ids = topk(logits[:, :E], top_k)
     w = pick_weights(logits[:, :E], ids)
     wsh = shared_weight(logits[:, E]) if has_shared else None
-    y, h = expert_outputs(x_bits, ids, layer, E, has_shared)
+    y, h = expert_outputs(x_bits, ids, layer, E, has_shared, fp8=fp8)
     out = combine(y, w, wsh)
     return {"logits": logits, "ids": ids, "w": w, "wsh": wsh, "h": h, "y": y, "out": out}
+
+
+# ---------------------------------------------------------------- FP8 route (prompt experts)
+# TensorFold #931, page 2 (the RDNA4 optimisation runway): upcast the experts to
+# FP8 so the prompt GEMMs run on the FP8 matrix units, a second route onto them.
+# The pages fix neither the FP8 format, the scaling nor the activation side;
+# readings:
+#   * OCP FP8 E4M3 (4 exponent bits, bias 7, 3 mantissa bits, subnormals, no
+#     infinities, largest finite 448), round to nearest even;
+#   * every weight row (gate, up, down) is formed as w = fp32(scale * q + bias)
+#     (one rounding of the exact value) and stored as E4M3 codes of w * 2^-e with
+#     one power-of-two scale 2^e per row, e = floor(log2 max|w|) - 7, so the row's
+#     largest magnitude lands in [128, 256) and no code saturates;
+#   * the activation rows entering each projection (the bf16 input x for gate/up,
+#     the bf16 SwiGLU intermediate h for down) are quantised the same way, one
+#     power-of-two scale per row;
+#   * a projection is 2^(e_row + e_col) * sum(code products), exact here, rounded
+#     nowhere but where the exact route rounds (h to bf16, the combined output).
+# The route keeps the exact path's routing, dispatch and combine.
+
+E4M3_BIAS = 7
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Values of E4M3 codes (float64): sign bit 7, exponent field E (bits 3..6),
+    mantissa m (bits 0..2); (8 + m) 2^(E - 10) for E > 0, m 2^-9 for E = 0 (2^-6 the
+    least normal value, m/8 of it below); codes 0x7F and 0xFF are NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    E = (c >> 3) & 15
+    m = c & 7
+    v = np.where(E > 0, np.ldexp((8 + m).astype(np.float64), E - 3 - E4M3_BIAS), np.ldexp(m.astype(np.float64), -9))
+    v = np.where(c & 0x80, -v, v)
+    return np.where((c & 0x7F) == 0x7F, np.nan, v)
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """E4M3 codes of finite values below 256 in magnitude, round to nearest even.
+
+    The quantum of a magnitude a in [2^p, 2^(p+1)) is 2^(p-3) (3 mantissa bits),
+    and 2^-9 below the normal range (a < 2^-6); a rounds to the nearest multiple
+    of its quantum, ties to the even multiple (numpy.rint). A result of 2^(p+1)
+    lands exactly on the next binade's first code, so the code follows from the
+    rounded value alone. The route never encodes 256 or more (its scales map every
+    row below 256), so saturation at 448 does not arise and is refused.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    if not np.isfinite(a).all() or (a >= 256).any():
+        raise ValueError("e4m3_encode takes finite magnitudes below 256")
+    _, p = np.frexp(a)  # a = f 2^p, f in [0.5, 1): floor(log2 a) = p - 1
+    q = np.maximum(p - 1 - 3, -9)
+    n = np.rint(np.ldexp(a, -q))
+    r = np.ldexp(n, q)  # the rounded magnitude, an E4M3 value
+    _, pr = np.frexp(r)
+    E = pr - 1 + E4M3_BIAS
+    normal = r >= 2.0 ** -6
+    mant = np.where(normal, np.ldexp(r, -(pr - 1 - 3)) - 8, 0).astype(np.int64)
+    code = np.where(normal, (E.astype(np.int64) << 3) | mant, np.ldexp(r, 9).astype(np.int64))
+    code = np.where(np.signbit(v), code | 0x80, code)
+    return code.astype(np.uint8)
+
+
+def fp8_row_exponent(amax) -> np.ndarray:
+    """e = floor(log2 amax) - 7 per row (reading above); 0 for an all-zero row."""
+    a = np.asarray(amax, dtype=np.float64)
+    _, p = np.frexp(a)
+    return np.where(a > 0, p - 1 - 7, 0).astype(np.int64)
+
+
+def fp8_quantise_rows(v):
+    """Rows of fp32-representable values -> (E4M3 codes [..., K], exponents [...]).
+
+    Each row's codes encode v * 2^-e (exact: a power-of-two scaling) with its own e.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    e = fp8_row_exponent(np.abs(v).max(axis=-1))
+    return e4m3_encode(np.ldexp(v, -e[..., None])), e
+
+
+def fp8_rows_value(codes, e) -> np.ndarray:
+    """The values a quantised row stands for: decode(code) * 2^e."""
+    return np.ldexp(e4m3_decode(codes), np.asarray(e)[..., None])
+
+
+def fp8_weight_rows(q, scale_bits, bias_bits, bits: int):
+    """An expert matrix [rows, in] upcast to E4M3 rows: (codes, exponents).
+
+    w = fp32(scale * q + bias): the exact value (scale * q has at most 16
+    significant bits) rounded once to fp32, as a fused multiply-add would. The sum
+    is checked to be exact in float64 (an error-free two-sum), so that the fp32
+    cast is a single rounding.
+    """
+    zeros = np.zeros_like(np.asarray(scale_bits, dtype=np.uint16))
+    sq = dequant_expert(q, scale_bits, zeros, bits)   # scale * q, exact
+    b = dequant_expert(q, zeros, bias_bits, bits)     # bias, repeated over each group
+    w = sq + b
+    bb = w - sq
+    err = (sq - (w - bb)) + (b - bb)
+    if (err != 0).any():
+        raise ValueError("scale * q + bias not exact in float64")
+    return fp8_quantise_rows(round_f32(w))
+
+
+def fp8_gate_up(x_bits, gate, up) -> np.ndarray:
+    """h = bf16(silu(g) * u) with g, u the FP8 projections of the rows x (bf16
+    bits [n, H]); gate, up: (codes [I, H], exponents [I]) from fp8_weight_rows."""
+    xc, xe = fp8_quantise_rows(bf16_to_f64(x_bits))
+    xv = e4m3_decode(xc)
+    g = np.ldexp(xv @ e4m3_decode(gate[0]).T, xe[:, None] + gate[1][None, :])
+    u = np.ldexp(xv @ e4m3_decode(up[0]).T, xe[:, None] + up[1][None, :])
+    return round_bf16(silu64(g) * u)
+
+
+def fp8_down(h_bits, down) -> np.ndarray:
+    """y = the FP8 down projection of the rows h (bf16 bits [n, I]), float64."""
+    hc, he = fp8_quantise_rows(bf16_to_f64(h_bits))
+    return np.ldexp(e4m3_decode(hc) @ e4m3_decode(down[0]).T, he[:, None] + down[1][None, :])
+
+
+def fp8_expert(layer, e: int):
+    """Expert e of a layer upcast: dict of (codes, exponents) for gate, up, down."""
+    bits = expert_bits(layer)
+    return {"gate": fp8_weight_rows(layer.q_gate[e], layer.s_gate[e], layer.b_gate[e], bits),
+            "up": fp8_weight_rows(layer.q_up[e], layer.s_up[e], layer.b_up[e], bits),
+            "down": fp8_weight_rows(layer.q_down[e], layer.s_down[e], layer.b_down[e], bits)}
 
 
 # ---------------------------------------------------------------- comparison helpers (test bars)

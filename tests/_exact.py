@@ -111,3 +111,30 @@ def unpack_int4_row(row_bytes):
         out.append(int(b) & 0xF)
         out.append(int(b) >> 4)
     return out
+
+
+def rne_e4m3(x) -> Fraction:
+    """Exact round-to-nearest-even of a rational to an OCP FP8 E4M3 value: 3 mantissa
+    bits, least normal magnitude 2^-6, subnormal step 2^-9, largest finite 448
+    (beyond it: ValueError). Zero keeps no sign here."""
+    x = Fraction(x)
+    sign = -1 if x < 0 else 1
+    a = abs(x)
+    if a < Fraction(1, 64):
+        return sign * Fraction(_round_half_even(a * 512), 512)
+    e = _binade(a)
+    v = _round_half_even(a / Fraction(2) ** (e - 3)) * Fraction(2) ** (e - 3)
+    if v > 448:
+        raise ValueError("beyond E4M3")
+    return sign * v
+
+
+def fp8_row_exact(vals):
+    """One row quantised with its power-of-two scale: e = floor(log2 max|v|) - 7
+    (0 for an all-zero row), each value replaced by rne_e4m3(v 2^-e) 2^e.
+    Returns (values, e)."""
+    vals = [Fraction(v) for v in vals]
+    amax = max(abs(v) for v in vals)
+    e = _binade(amax) - 7 if amax > 0 else 0
+    s = Fraction(2) ** e
+    return [rne_e4m3(v / s) * s for v in vals], e

@@ -320,17 +320,25 @@ def _random_layer(rng, H, I, E, router_fp32=True, bits=4):
     return synth.make_layer(shape, int(rng.integers(0, 2 ** 31)), 0)
 
 
-def _bruteforce_layer(x_bits, L, E, k, bits=4):
+def _bruteforce_layer(x_bits, L, E, k, bits=4, fp8=False):
     """The contract evaluated with exact rationals (dot products) and 60-digit
     decimals (exp, sigmoid), reading the canonical bytes directly (two codes per
-    byte at 4 bits, one at 8)."""
+    byte at 4 bits, one at 8). fp8: the experts' weight rows become fp32 values
+    (exact rounding) quantised row by row to E4M3 with a power-of-two scale, and
+    so do the rows x and h entering each projection (X.fp8_row_exact)."""
     T, H = x_bits.shape
     I = L.q_gate.shape[1]
 
     def wmat(q, s, b, e, r):
         qs = X.unpack_int4_row(q[e, r]) if bits == 4 else [int(v) for v in q[e, r]]
-        return [X.frac_of_bf16(int(s[e, r, c // 64])) * qs[c] + X.frac_of_bf16(int(b[e, r, c // 64]))
-                for c in range(len(qs))]
+        w = [X.frac_of_bf16(int(s[e, r, c // 64])) * qs[c] + X.frac_of_bf16(int(b[e, r, c // 64]))
+             for c in range(len(qs))]
+        if fp8:
+            w, _ = X.fp8_row_exact([Fraction(X.rne_f32(v)) for v in w])
+        return w
+
+    def act(vals):
+        return X.fp8_row_exact(vals)[0] if fp8 else vals
 
     res = []
     for t in range(T):
@@ -348,14 +356,15 @@ def _bruteforce_layer(x_bits, L, E, k, bits=4):
         weights = [X.frac_of_bf16(v) for v in w] + [X.frac_of_bf16(wsh)]
         total = [Fraction(0)] * H
         hs = []
+        xq = act(xs)
         for e, ws in zip(slots, weights):
             h = []
             for i in range(I):
-                g = sum((a * c for a, c in zip(xs, wmat(L.q_gate, L.s_gate, L.b_gate, e, i))), Fraction(0))
-                u = sum((a * c for a, c in zip(xs, wmat(L.q_up, L.s_up, L.b_up, e, i))), Fraction(0))
+                g = sum((a * c for a, c in zip(xq, wmat(L.q_gate, L.s_gate, L.b_gate, e, i))), Fraction(0))
+                u = sum((a * c for a, c in zip(xq, wmat(L.q_up, L.s_up, L.b_up, e, i))), Fraction(0))
                 h.append(X.rne_bf16_bits(X.silu_dec(g) * X.dec(u)))
             hs.append(h)
-            hf = [X.frac_of_bf16(v) for v in h]
+            hf = act([X.frac_of_bf16(v) for v in h])
             for n in range(H):
                 y = sum((a * c for a, c in zip(hf, wmat(L.q_down, L.s_down, L.b_down, e, n))), Fraction(0))
                 total[n] += ws * y
@@ -556,3 +565,207 @@ def test_picks_within_ties_accepts_only_near_tie_swaps():
     for bad in ([0, 1, 2, 9], [0, 1, 2, 2], [0, 1, 2, 12], [0, 1, 2, -1]):
         ok, _, _ = O.picks_within_ties(np.array([bad]), tie, k)
         assert ok.tolist() == [False], bad
+
+
+# ---------------------------------------------------------------- FP8 route
+
+def _e4m3_definition(code: int):
+    """OCP FP8 E4M3 from its definition: (-1)^s 2^(E-7) (1 + m/8) for E > 0,
+    (-1)^s 2^-6 (m/8) for E = 0; S.1111.111 is NaN (None here)."""
+    s, E, m = code >> 7, (code >> 3) & 15, code & 7
+    if E == 15 and m == 7:
+        return None
+    v = Fraction(2) ** (E - 7) * (1 + Fraction(m, 8)) if E else Fraction(2) ** -6 * Fraction(m, 8)
+    return -v if s else v
+
+
+def test_e4m3_decode_all_codes():
+    """Every code against the format definition and against torch's float8_e4m3fn."""
+    import torch
+
+    codes = np.arange(256, dtype=np.uint8)
+    d = O.e4m3_decode(codes)
+    t = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    for c in range(256):
+        ref = _e4m3_definition(c)
+        if ref is None:
+            assert np.isnan(d[c]) and np.isnan(t[c])
+        else:
+            assert Fraction(float(d[c])) == ref and d[c] == t[c], c
+    assert O.e4m3_decode(np.array([0x7E], np.uint8))[0] == 448.0
+    assert np.signbit(O.e4m3_decode(np.array([0x80], np.uint8))[0])
+
+
+def test_e4m3_encode_matches_torch_cast():
+    """Every bf16 value below 256 in magnitude, random fp32 values and every
+    midpoint between neighbouring codes (and its fp32 neighbours) encode as
+    torch's round-to-nearest-even cast does."""
+    import torch
+
+    allbf = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32)
+    rng = np.random.default_rng(8)
+    n = 1 << 16
+    rnd = ((rng.integers(0, 2, n).astype(np.uint32) << 31) | (rng.integers(100, 135, n).astype(np.uint32) << 23)
+           | rng.integers(0, 1 << 23, n).astype(np.uint32)).view(np.float32)
+    vals = np.sort(O.e4m3_decode(np.arange(0x7F, dtype=np.uint8)))
+    mid = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    near = np.concatenate([mid, np.nextafter(mid, np.float32(np.inf)), np.nextafter(mid, np.float32(0))])
+    v = np.concatenate([allbf, rnd, near, -near])
+    v = v[np.isfinite(v) & (np.abs(v) < 256)]
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_encode(v), ref)
+    with pytest.raises(ValueError):
+        O.e4m3_encode(np.array([256.0]))
+
+
+def test_e4m3_encode_bruteforce_nearest_even():
+    """Each code is the nearest finite value, ties to the even mantissa (exact search
+    over every code); the sign bit is the value's sign, zeros included."""
+    finite = [(c, _e4m3_definition(c)) for c in range(256) if _e4m3_definition(c) is not None]
+    rng = np.random.default_rng(81)
+    vals = list(rng.uniform(-255, 255, 300)) + list(np.ldexp(rng.uniform(-1, 1, 300), rng.integers(-12, 8, 300)))
+    pos = [(c, v) for c, v in finite if c < 0x78]  # 0 .. 240
+    vals += [float((a + b) / 2) for (_, a), (_, b) in zip(pos[:-1], pos[1:])]
+    vals += [0.0, -0.0, -2.0 ** -11, 2.0 ** -11]
+    codes = O.e4m3_encode(np.array(vals))
+    for v, c in zip(vals, codes):
+        fv = Fraction(v)
+        best = min(abs(fv - r) for _, r in finite)
+        cands = sorted({abs(r) for _, r in finite if abs(fv - r) == best})
+        mag = _e4m3_definition(int(c) & 0x7F)
+        if len(cands) > 1:  # a tie between two magnitudes: the even mantissa wins
+            even = [m for m in cands if any(cc & 1 == 0 and r == m for cc, r in finite)]
+            assert mag == even[0], (v, c)
+        else:
+            assert mag == abs(cands[0]) or (mag == 0 and cands[0] == 0), (v, c)
+        assert (int(c) >> 7) == int(np.signbit(v)), (v, c)
+        assert Fraction(float(O.e4m3_decode(np.array([c], np.uint8))[0])) == X.rne_e4m3(fv)
+
+
+def test_fp8_row_exponent_closed_forms():
+    """e = floor(log2 max|v|) - 7: powers of two, values just below them, zero rows."""
+    for j in range(-20, 21):
+        assert O.fp8_row_exponent(2.0 ** j) == j - 7
+        assert O.fp8_row_exponent(np.nextafter(2.0 ** j, 0)) == j - 8
+    assert O.fp8_row_exponent(0.0) == 0
+    rng = np.random.default_rng(82)
+    rows = np.ldexp(rng.standard_normal((64, 96)), rng.integers(-30, 30, (64, 1)))
+    codes, e = O.fp8_quantise_rows(rows)
+    amax = np.abs(rows).max(axis=1)
+    assert ((np.ldexp(amax, -e) >= 128) & (np.ldexp(amax, -e) < 256)).all()
+    z, ez = O.fp8_quantise_rows(np.zeros((2, 64)))
+    assert (z == 0).all() and (ez == 0).all()
+
+
+def test_fp8_quantise_rows_exact_and_bounded():
+    """Rows of E4M3 values times 2^j come back exactly; otherwise the error is at
+    most half a step: 2^-4 relative in the normal range, 2^(e-10) absolute below."""
+    rng = np.random.default_rng(83)
+    grid = O.e4m3_decode(np.arange(0x00, 0x78, dtype=np.uint8))  # values below 256
+    for j in (-9, 0, 5):
+        row = np.ldexp(rng.choice(grid, (4, 80)) * rng.choice([-1, 1], (4, 80)), j)
+        row[:, 0] = np.ldexp(240.0, j)  # max in [128, 256) 2^j
+        codes, e = O.fp8_quantise_rows(row)
+        assert (e == j).all() and np.array_equal(O.fp8_rows_value(codes, e), row)
+    row = rng.standard_normal((16, 512)) * 3
+    codes, e = O.fp8_quantise_rows(row)
+    back = O.fp8_rows_value(codes, e)
+    err = np.abs(back - row)
+    normal = np.abs(row) >= np.ldexp(1.0, e[:, None] - 6)
+    assert (err[normal] <= np.abs(row[normal]) * 2.0 ** -4).all()
+    assert (err[~normal] <= np.ldexp(1.0, e[:, None] - 10).repeat(512, 1)[~normal]).all()
+
+
+def test_fp8_weight_rows_round_once_to_fp32():
+    """w = fp32(scale q + bias) exactly rounded, then quantised per row; a sum that
+    float64 cannot hold exactly is refused."""
+    rng = np.random.default_rng(84)
+    L = _random_layer(rng, 128, 64, 2)
+    codes, e = O.fp8_weight_rows(L.q_gate[1], L.s_gate[1], L.b_gate[1], 4)
+    for r in (0, 17, 63):
+        w = [Fraction(X.rne_f32(v)) for v in
+             [X.frac_of_bf16(int(L.s_gate[1, r, c // 64])) * q + X.frac_of_bf16(int(L.b_gate[1, r, c // 64]))
+              for c, q in enumerate(X.unpack_int4_row(L.q_gate[1, r]))]]
+        ref, er = X.fp8_row_exact(w)
+        assert e[r] == er
+        assert [Fraction(float(v)) for v in O.fp8_rows_value(codes[r:r + 1], e[r:r + 1])[0]] == ref
+    q = np.full((1, 32), 0x11, np.uint8)  # all codes 1
+    s = np.array([[0x0D80]], np.uint16)   # 2^-100
+    b = np.array([[0x3F80]], np.uint16)   # 1.0
+    with pytest.raises(ValueError):
+        O.fp8_weight_rows(q, s, b, 4)
+
+
+def _integer_layer(rng, H, I):
+    """One expert whose weights are the integers q - 8 (scale 1, bias -8): every
+    integer of magnitude at most 16 is an E4M3 value, and so is every such integer
+    times the row's power-of-two scale."""
+    from types import SimpleNamespace
+
+    def mat(rows, cols):
+        q = rng.integers(0, 16, (1, rows, cols)).astype(np.uint8)
+        q[0, :, 0] = 0  # every row reaches |w| = 8
+        packed = (q[..., 0::2] | (q[..., 1::2] << 4)).astype(np.uint8)
+        return packed, np.full((1, rows, cols // 64), 0x3F80, np.uint16), np.full((1, rows, cols // 64), 0xC100, np.uint16)
+
+    qg, sg, bg = mat(I, H)
+    qu, su, bu = mat(I, H)
+    qd, sd, bd = mat(H, I)
+    return SimpleNamespace(q_gate=qg, s_gate=sg, b_gate=bg, q_up=qu, s_up=su, b_up=bu, q_down=qd, s_down=sd, b_down=bd)
+
+
+def test_fp8_route_equals_exact_route_on_representable_operands():
+    """When every quantisation is exact (integer weights of magnitude <= 8, inputs
+    small integers) the FP8 projections are the exact ones: gate/up gives the exact
+    route's h bit for bit, and down the exact product (H != I catches a transpose)."""
+    rng = np.random.default_rng(85)
+    H, I = 128, 64
+    L = _integer_layer(rng, H, I)
+    f8 = O.fp8_expert(L, 0)
+    for m in ("gate", "up", "down"):
+        assert (f8[m][1] == 3 - 7).all()  # max |w| = 8
+    x = np.array([[O.round_bf16(np.array([float(v)]))[0] for v in rng.integers(-16, 17, H)] for _ in range(3)],
+                 np.uint16)
+    h_exact, _ = O.expert_ffn(O.bf16_to_f64(x), L.q_gate[0], L.s_gate[0], L.b_gate[0], L.q_up[0], L.s_up[0],
+                              L.b_up[0], L.q_down[0], L.s_down[0], L.b_down[0])
+    h8 = O.fp8_gate_up(x, f8["gate"], f8["up"])
+    assert np.array_equal(h8, h_exact)
+    hi = O.round_bf16(rng.integers(-16, 17, (3, I)).astype(np.float64))
+    y8 = O.fp8_down(hi, f8["down"])
+    Wd = O.dequant_expert(L.q_down[0], L.s_down[0], L.b_down[0], 4)
+    assert np.array_equal(y8, O.bf16_to_f64(hi) @ Wd.T)
+
+
+def test_bruteforce_exact_tiny_layer_fp8():
+    """The FP8 route of a whole layer against its exact-arithmetic evaluation."""
+    rng = np.random.default_rng(2026)
+    H, I, E, k = 64, 64, 4, 2
+    L = _random_layer(rng, H, I, E)
+    L.router_f32 = (L.router_f32 * 10).astype(np.float32)
+    from quantized_moe_expert_fp32_amd import synth
+
+    x = synth.random_x(79, 2, H)
+    st = O.layer_forward(x, L, top_k=k, has_shared=True, fp8=True)
+    bf = _bruteforce_layer(x, L, E, k, fp8=True)
+    for t in range(2):
+        assert st["ids"][t].tolist() == bf[t]["ids"]
+        for s in range(k + 1):
+            assert st["h"][t, s].tolist() == bf[t]["h"][s]
+        assert st["out"][t].tolist() == bf[t]["out"]
+
+
+def test_fp8_route_close_to_exact_route():
+    """The FP8 route is lossy but near the exact layer: x, the weights and h each
+    carry an E4M3 rounding (about 3.6 % rms relative for 3 mantissa bits), about
+    6 % together; each token's result depends on its own row only."""
+    from quantized_moe_expert_fp32_amd import synth
+
+    c = synth.make_case("tiny", T=24)
+    sh = c.shape
+    ex = O.layer_forward(c.x, c.layers[0], sh.top_k, bool(sh.has_shared))
+    f8 = O.layer_forward(c.x, c.layers[0], sh.top_k, bool(sh.has_shared), fp8=True)
+    a, b = O.bf16_to_f64(ex["out"]), O.bf16_to_f64(f8["out"])
+    rel = np.sqrt(np.mean((a - b) ** 2) / np.mean(a * a))
+    assert 1e-2 < rel < 0.12
+    one = O.layer_forward(c.x[5:6], c.layers[0], sh.top_k, bool(sh.has_shared), fp8=True)
+    assert np.array_equal(one["out"][0], f8["out"][5])
