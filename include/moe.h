@@ -22,6 +22,9 @@
  *              "Phase 9b" (MoE GEMM with int4 dequant and lookup-table dispatch).
  *   [P4-run]   "Qwen-3.6-35B-A3B-SIQ-K6+K4K3", section "How to run": the shared
  *              expert gate is an N=1 projection.
+ *   [P2-next]  "R9700: the 35B only one runtime could load" (R9700 vLLM blog, part 13),
+ *              its closing list of kernel work: upcast the experts to FP8 to run them
+ *              on the FP8 matrix units, a second route onto them.
  *
  * Conventions for every call:
  *   - Pointers named *_host are host memory; every other pointer is device memory
@@ -276,6 +279,45 @@ moe_status moe_prefill_dispatch_layout(const moe_shape* shape, int32_t T, moe_pr
 moe_status moe_experts_prefill(const moe_shape* shape, const void* experts_packed,
                                const uint16_t* x, int32_t T, const int32_t* ids, void* ws,
                                size_t ws_bytes, float* y, void* stream);
+
+/* ---------------------------------------------------------------- FP8 route (prefill)
+ * [P2-next]: the experts upcast once to FP8 so the prompt GEMMs run on the FP8
+ * matrix cores. Not exact: every operand carries one FP8 rounding (about 6 % rms
+ * relative error on the layer output); the routing, dispatch and combine are the
+ * exact path's. Format (OCP FP8 E4M3, round to nearest even, no saturation):
+ *   - weight row (gate, up or down, of the canonical 4- or 8-bit expert): w =
+ *     fp32(scale * q + bias) (one rounding: a fused multiply-add), e = floor(log2
+ *     max|w|) - 7 (0 for an all-zero row), codes = E4M3(w * 2^-e), so the row's
+ *     largest magnitude maps into [128, 256); the row scale 2^e is kept as a float;
+ *   - activation rows entering a projection (x for gate/up, the bf16 SwiGLU
+ *     intermediate h for down) are quantised the same way, one 2^e per row;
+ *   - a projection output is the fp32 sum of code products times both rows' 2^e;
+ *     h = bf16(silu(gate) * up) as in the exact path.
+ * FP8 buffer, per expert m (stride = moe_experts_fp8_bytes / M, 256-byte aligned):
+ *   gate codes [I][Hp] | up codes [I][Hp] | down codes [H][Ip] |
+ *   row scales float [2I + H] (gate rows, up rows, down rows),
+ * Hp = H and Ip = I rounded up to multiples of 128, padding codes 0. */
+size_t moe_experts_fp8_bytes(const moe_shape* shape);
+
+/* Upcasts canonical experts (device arrays, 4- or 8-bit as shape->bits says, codes
+ * 8-byte aligned) into `fp8` (device, 256-byte aligned, fp8_bytes >=
+ * moe_experts_fp8_bytes). Async on `stream`. */
+moe_status moe_pack_experts_fp8(const moe_shape* shape, const moe_expert_canon* src_host,
+                                void* fp8, size_t fp8_bytes, void* stream);
+
+/* moe_experts_prefill's contract (y [T][S][H] fp32, per-slot expert outputs; rows
+ * of picks with an id outside [0, E) zeroed) through the FP8 route: dispatch with
+ * tiles of up to 256 rows, x quantised per row, the FP8 gate/up GEMM writing h, h
+ * quantised per row, the FP8 down GEMM. Each output depends on its own token's row
+ * only, in a fixed order (any T, any call). ws: device scratch of
+ * moe_prefill_fp8_workspace_bytes(shape, T) bytes (its layout is internal).
+ * MOE_ERR_UNSUPPORTED when
+ * T * Hp or T * S * Ip reaches 2^32 or the device has under 148 KiB of LDS per
+ * workgroup. */
+size_t moe_prefill_fp8_workspace_bytes(const moe_shape* shape, int32_t T);
+moe_status moe_experts_prefill_fp8(const moe_shape* shape, const void* experts_fp8,
+                                   const uint16_t* x, int32_t T, const int32_t* ids, void* ws,
+                                   size_t ws_bytes, float* y, void* stream);
 
 /* ---------------------------------------------------------------- a6: combine
  * out[t][n] = bf16( sum_{s<k} w[t][s] * y[t][s][n] + w_shared[t] * y[t][k][n] )

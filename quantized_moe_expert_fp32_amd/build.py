@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["abi.hip", "route.hip", "decode.hip", "prefill.hip", "combine.hip"]
+SOURCES = ["abi.hip", "route.hip", "decode.hip", "prefill.hip", "prefill_fp8.hip", "combine.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")

@@ -17,41 +17,45 @@
 // every activation fragment read from LDS feeds four products.
 #include "mfma_common.h"
 #include "moe_internal.h"
+#include "prefill_internal.h"
 
 namespace moe {
 
 constexpr int BM = 128;  // rows per tile
 
-struct Tile {
-    int32_t expert, row0, nrows, pad;
-};
-
-// Workspace layout for moe_experts_prefill.
-struct PrefillWs {
-    size_t counts, offsets, cursor, ntiles, tiles, order, h, slices, total;
-    int max_tiles;
-    int n_slices;  // pick slices of the dispatch
-};
-
 constexpr int SLICE = 1024;  // picks per slice (one workgroup of the dispatch each)
 
-static PrefillWs prefill_ws_layout(const moe_shape& s, int T) {
-    PrefillWs w;
-    const int M = n_mats(s), S = n_slots(s);
+DispatchWs dispatch_ws_layout(const moe_shape& s, int T, int bm, size_t& o) {
+    DispatchWs w;
+    const int M = n_mats(s);
     const long long picks = (long long)T * s.top_k;
-    const long long routed_tiles = picks / BM + (picks < s.n_experts ? picks : s.n_experts) + 1;
-    const long long shared_tiles = s.has_shared ? (T + BM - 1) / BM : 0;
+    const long long routed_tiles = picks / bm + (picks < s.n_experts ? picks : s.n_experts) + 1;
+    const long long shared_tiles = s.has_shared ? (T + bm - 1) / bm : 0;
+    w.bm = bm;
     w.max_tiles = (int)(routed_tiles + shared_tiles);
-    size_t o = 0;
     w.counts = o;  o = align_up(o + 4 * (size_t)M, 256);
     w.offsets = o; o = align_up(o + 4 * (size_t)(M + 1), 256);
     w.cursor = o;  o = align_up(o + 4 * (size_t)M, 256);
     w.ntiles = o;  o = align_up(o + 4, 256);
     w.tiles = o;   o = align_up(o + sizeof(Tile) * (size_t)w.max_tiles, 256);
-    w.order = o;   o = align_up(o + 4 * (size_t)T * S, 256);
-    w.h = o;       o = align_up(o + 2 * (size_t)T * S * s.inter, 256);
+    w.order = o;   o = align_up(o + 4 * (size_t)T * n_slots(s), 256);
     w.n_slices = (int)((picks + SLICE - 1) / SLICE);
     w.slices = o;  o = align_up(o + 4 * (size_t)w.n_slices * s.n_experts, 256);  // [n_slices][E] counts
+    return w;
+}
+
+// Workspace layout for moe_experts_prefill: the dispatch (tiles of BM rows), then h.
+struct PrefillWs {
+    DispatchWs D;
+    size_t h, total;
+};
+
+static PrefillWs prefill_ws_layout(const moe_shape& s, int T) {
+    PrefillWs w;
+    size_t o = 0;
+    w.D = dispatch_ws_layout(s, T, BM, o);
+    w.h = o;
+    o = align_up(o + 2 * (size_t)T * n_slots(s) * s.inter, 256);
     w.total = o;
     return w;
 }
@@ -196,6 +200,7 @@ __device__ __forceinline__ uint64_t equal_key_lanes(uint32_t key) {
     return m;
 }
 
+template <int TBM>
 __global__ __launch_bounds__(DT) void prefill_scatter_kernel(
     const int32_t* __restrict__ ids, int T, int k, int E, int has_shared, int H, int n_slices,
     const int32_t* __restrict__ slices, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
@@ -236,7 +241,7 @@ __global__ __launch_bounds__(DT) void prefill_scatter_kernel(
         int lc = 0, lt = 0;
         for (int i2 = beg; i2 < end; ++i2) {
             lc += cnt[i2];
-            lt += cnt[i2] / BM;
+            lt += cnt[i2] / TBM;
         }
         int ic = lc, it = lt;
         for (int d = 1; d < 64; d <<= 1) {
@@ -251,7 +256,7 @@ __global__ __launch_bounds__(DT) void prefill_scatter_kernel(
             off[i2] = rc;
             foff[i2] = rt;
             rc += cnt[i2];
-            rt += cnt[i2] / BM;
+            rt += cnt[i2] / TBM;
         }
         if (tid == 63) {
             off[M] = ic;
@@ -264,12 +269,12 @@ __global__ __launch_bounds__(DT) void prefill_scatter_kernel(
         for (int e = tid; e < M; e += DT) {
             counts[e] = cnt[e];
             offsets[e] = off[e];
-            const int nfull = cnt[e] / BM;
+            const int nfull = cnt[e] / TBM;
             for (int q = 0; q < nfull; ++q) {
                 Tile tl;
                 tl.expert = e;
-                tl.row0 = off[e] + q * BM;
-                tl.nrows = BM;
+                tl.row0 = off[e] + q * TBM;
+                tl.nrows = TBM;
                 tl.pad = 0;
                 tiles[foff[e] + q] = tl;
             }
@@ -277,21 +282,22 @@ __global__ __launch_bounds__(DT) void prefill_scatter_kernel(
         if (has_shared)
             for (int t = tid; t < T; t += DT) order[off[E] + t] = t * S + k;
         if (tid < 64) {
-            // partial tiles by size class q = 8 - (row blocks), in expert order within a
+            // partial tiles by size class q = TBM/16 - (row blocks), in expert order within a
             // class: count the classes, then place each tile at its class base plus its
             // rank among the lower experts of the class
-            int tot[9], run[9];
+            constexpr int NCL = TBM / 16;
+            int tot[NCL], run[NCL];
 #pragma unroll
-            for (int q = 0; q < 9; ++q) tot[q] = 0;
+            for (int q = 0; q < NCL; ++q) tot[q] = 0;
             for (int e0 = 0; e0 < M; e0 += 64) {
-                const int e = e0 + tid, rem = e < M ? cnt[e] % BM : 0;
-                const int cls = rem ? 8 - (rem + 15) / 16 : -1;
+                const int e = e0 + tid, rem = e < M ? cnt[e] % TBM : 0;
+                const int cls = rem ? NCL - (rem + 15) / 16 : -1;
 #pragma unroll
-                for (int q = 0; q < 9; ++q) tot[q] += __popcll(__ballot(cls == q));
+                for (int q = 0; q < NCL; ++q) tot[q] += __popcll(__ballot(cls == q));
             }
             int acc = foff[M];
 #pragma unroll
-            for (int q = 0; q < 9; ++q) {
+            for (int q = 0; q < NCL; ++q) {
                 run[q] = acc;
                 acc += tot[q];
             }
@@ -301,15 +307,15 @@ __global__ __launch_bounds__(DT) void prefill_scatter_kernel(
             }
             const uint64_t below = (1ull << tid) - 1ull;
             for (int e0 = 0; e0 < M; e0 += 64) {
-                const int e = e0 + tid, rem = e < M ? cnt[e] % BM : 0;
-                const int cls = rem ? 8 - (rem + 15) / 16 : -1;
+                const int e = e0 + tid, rem = e < M ? cnt[e] % TBM : 0;
+                const int cls = rem ? NCL - (rem + 15) / 16 : -1;
 #pragma unroll
-                for (int q = 0; q < 9; ++q) {
+                for (int q = 0; q < NCL; ++q) {
                     const uint64_t m = __ballot(cls == q);
                     if (cls == q) {
                         Tile tl;
                         tl.expert = e;
-                        tl.row0 = off[e] + (cnt[e] / BM) * BM;
+                        tl.row0 = off[e] + (cnt[e] / TBM) * TBM;
                         tl.nrows = rem;
                         tl.pad = 0;
                         tiles[run[q] + __popcll(m & below)] = tl;
@@ -353,31 +359,6 @@ __global__ __launch_bounds__(DT) void prefill_scatter_kernel(
     }
 }
 
-// ---------------------------------------------------------------- XCD-aware item mapping
-// The GEMM grids are one-dimensional over (tile, column block) items. Workgroups
-// are handed to the 8 XCDs round-robin by linear id, and each XCD has its own L2.
-// Block b runs on XCD x = b % 8 as that XCD's j-th block, j = b / 8. Tiles are
-// dealt to the XCDs in runs of XCD_RUN consecutive tiles, and an XCD takes its
-// tiles in order, all column blocks of a tile in a row: the workgroups that share
-// a tile's activations share one L2, and a tile list sorted by cost stays balanced
-// across the XCDs. Runs of one tile measured best on the 512-token and skewed
-// 4096-token workloads: longer runs keep an expert's consecutive tiles in one L2
-// but put the few heavy tiles at the head of the list on one XCD. Blocks beyond
-// the live tiles return.
-constexpr int N_XCD = 8, XCD_RUN = 1;
-
-__device__ __forceinline__ bool xcd_item(int ntiles, int nb, int& tile, int& cb) {
-    const int x = (int)blockIdx.x % N_XCD, j = (int)blockIdx.x / N_XCD;
-    const int lt = j / nb;  // this XCD's lt-th tile
-    tile = (lt / XCD_RUN) * (N_XCD * XCD_RUN) + x * XCD_RUN + lt % XCD_RUN;
-    cb = j % nb;
-    return tile < ntiles;
-}
-
-static unsigned xcd_grid(int max_tiles, int nb) {
-    const int runs = (max_tiles + N_XCD * XCD_RUN - 1) / (N_XCD * XCD_RUN);
-    return (unsigned)(runs * XCD_RUN * N_XCD * nb);
-}
 
 // ---------------------------------------------------------------- grouped GEMM
 // A workgroup multiplies one tile (up to 128 expert-sorted rows) by a block of
@@ -414,52 +395,6 @@ struct GemmArgs {
 };
 
 
-// Direct global-to-LDS loads from base + off (base wavefront-uniform, off per lane):
-// lane l's 16 (or 4) bytes land at LDS byte address lds + 16 l (4 l); lds is
-// wavefront-uniform and goes in M0, written at least one wait state before the
-// load (the s_nop). Written as inline asm so the compiler does not treat them as
-// LDS stores (it would otherwise wait for every outstanding one before the first
-// LDS read); completion is awaited explicitly with wait_vmcnt, and the memory
-// clobber keeps LDS reads behind the barrier that follows that wait.
-__device__ __forceinline__ void lds_dma16(const void* base, uint32_t off, uint32_t lds) {
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
-}
-__device__ __forceinline__ void lds_dma4(const void* base, uint32_t off, uint32_t lds) {
-    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// Workgroup barrier that also keeps the compiler from moving memory accesses
-// across it. This wavefront's LDS reads are complete before it (lgkmcnt 0), so a
-// stage every wavefront has passed the barrier after reading may be refilled; the
-// waits for outstanding global loads are explicit at the call sites.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited for
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// s_waitcnt with only the vector-memory count (expcnt and lgkmcnt left at their
-// maximum, i.e. not waited for); N < 64.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// Wait until at most min(later, L) chunks of LPC loads each are outstanding.
-template <int LPC, int L>
-__device__ __forceinline__ void wait_chunks(int later) {
-    if constexpr (L == 0) {
-        wait_vmcnt<0>();
-    } else {
-        if (later >= L) wait_vmcnt<L * LPC>();
-        else wait_chunks<LPC, L - 1>(later);
-    }
-}
 
 // GATEUP: weight rows 0..127 are gate rows cb*128 .., rows 128..255 the matching up
 // rows; the epilogue writes h = bf16(silu(gate) * up). Else (down): weight rows are
@@ -697,6 +632,21 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
 
 static_assert(BM == 128, "tile rows");
 
+moe_status launch_prefill_dispatch(const moe_shape& sh, int T, const int32_t* ids, const DispatchWs& D, char* w,
+                                   float* y, hipStream_t hs) {
+    const long long P = (long long)T * sh.top_k;
+    int32_t* slices = (int32_t*)(w + D.slices);
+    hipLaunchKernelGGL(prefill_count_kernel, dim3((unsigned)D.n_slices), dim3(DT), 0, hs, ids, P, sh.n_experts, slices);
+    moe_status st = check_launch("prefill_count_kernel");
+    if (st != MOE_OK) return st;
+    auto scatter = D.bm == 256 ? prefill_scatter_kernel<256> : prefill_scatter_kernel<128>;
+    hipLaunchKernelGGL(scatter, dim3((unsigned)D.n_slices + 1), dim3(DT), 0, hs, ids, T, sh.top_k, sh.n_experts,
+                       sh.has_shared, sh.hidden, D.n_slices, slices, (int32_t*)(w + D.counts),
+                       (int32_t*)(w + D.offsets), (int32_t*)(w + D.ntiles), (Tile*)(w + D.tiles),
+                       (int32_t*)(w + D.order), y);
+    return check_launch("prefill_scatter_kernel");
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -711,13 +661,13 @@ extern "C" moe_status moe_prefill_dispatch_layout(const moe_shape* shape, int32_
     moe_status st = validate_shape(shape);
     if (st != MOE_OK) return st;
     if (T < 1 || !v) return fail(MOE_ERR_INVALID_ARG, "T = %d or NULL view", T);
-    const PrefillWs W = prefill_ws_layout(*shape, T);
-    v->counts = W.counts;
-    v->offsets = W.offsets;
-    v->ntiles = W.ntiles;
-    v->tiles = W.tiles;
-    v->order = W.order;
-    v->max_tiles = W.max_tiles;
+    const DispatchWs D = prefill_ws_layout(*shape, T).D;
+    v->counts = D.counts;
+    v->offsets = D.offsets;
+    v->ntiles = D.ntiles;
+    v->tiles = D.tiles;
+    v->order = D.order;
+    v->max_tiles = D.max_tiles;
     v->pad = 0;
     return MOE_OK;
 }
@@ -761,19 +711,11 @@ extern "C" moe_status moe_experts_prefill(const moe_shape* shape, const void* ex
                     RING + 2048, max_lds);
     hipStream_t hs = (hipStream_t)stream;
     char* w = (char*)ws;
-    int32_t* counts = (int32_t*)(w + W.counts);
-    int32_t* offsets = (int32_t*)(w + W.offsets);
-    int32_t* ntiles = (int32_t*)(w + W.ntiles);
-    Tile* tiles = (Tile*)(w + W.tiles);
-    int32_t* order = (int32_t*)(w + W.order);
+    int32_t* ntiles = (int32_t*)(w + W.D.ntiles);
+    Tile* tiles = (Tile*)(w + W.D.tiles);
+    int32_t* order = (int32_t*)(w + W.D.order);
     uint16_t* hbuf = (uint16_t*)(w + W.h);
-    int32_t* slices = (int32_t*)(w + W.slices);
-    const long long P = (long long)T * sh.top_k;
-    hipLaunchKernelGGL(prefill_count_kernel, dim3((unsigned)W.n_slices), dim3(DT), 0, hs, ids, P, sh.n_experts, slices);
-    if ((st = check_launch("prefill_count_kernel")) != MOE_OK) return st;
-    hipLaunchKernelGGL(prefill_scatter_kernel, dim3((unsigned)W.n_slices + 1), dim3(DT), 0, hs, ids, T, sh.top_k,
-                       sh.n_experts, sh.has_shared, H, W.n_slices, slices, counts, offsets, ntiles, tiles, order, y);
-    if ((st = check_launch("prefill_scatter_kernel")) != MOE_OK) return st;
+    if ((st = launch_prefill_dispatch(sh, T, ids, W.D, w, y, hs)) != MOE_OK) return st;
     GemmArgs ga;
     ga.packed = (const uint8_t*)experts_packed;
     ga.L = L;
@@ -788,10 +730,10 @@ extern "C" moe_status moe_experts_prefill(const moe_shape* shape, const void* ex
     ga.y = y;
     ga.T = T;
     ga.km = kmul(sh);
-    hipLaunchKernelGGL((expert_gemm_kernel<true>), dim3(xcd_grid(W.max_tiles, (I + NBR / 2 - 1) / (NBR / 2))), dim3(256),
+    hipLaunchKernelGGL((expert_gemm_kernel<true>), dim3(xcd_grid(W.D.max_tiles, (I + NBR / 2 - 1) / (NBR / 2))), dim3(256),
                        RING, hs, ga);
     if ((st = check_launch("expert_gemm_kernel<gate/up>")) != MOE_OK) return st;
-    hipLaunchKernelGGL((expert_gemm_kernel<false>), dim3(xcd_grid(W.max_tiles, (H + NBR - 1) / NBR)), dim3(256), RING, hs,
+    hipLaunchKernelGGL((expert_gemm_kernel<false>), dim3(xcd_grid(W.D.max_tiles, (H + NBR - 1) / NBR)), dim3(256), RING, hs,
                        ga);
     return check_launch("expert_gemm_kernel<down>");
 }

@@ -40,9 +40,10 @@ def make_shape(s) -> moe.Shape:
 
 
 class DeviceLayer:
-    """One layer's packed expert buffer, packed router and optional logit bias on the GPU."""
+    """One layer's packed expert buffer, packed router and optional logit bias on the GPU;
+    with fp8=True also the experts upcast for the FP8 prompt route (experts_fp8)."""
 
-    def __init__(self, shape: moe.Shape, host_layer, device="cuda"):
+    def __init__(self, shape: moe.Shape, host_layer, device="cuda", fp8: bool = False):
         self.shape = shape
         self.device = device
         nb = moe.moe_experts_packed_bytes(shape)
@@ -52,6 +53,10 @@ class DeviceLayer:
         src = {n: to_device(getattr(host_layer, n), device) for n in
                ("q_gate", "s_gate", "b_gate", "q_up", "s_up", "b_up", "q_down", "s_down", "b_down")}
         moe.moe_pack_experts(shape, src, self.experts)
+        self.experts_fp8 = None
+        if fp8:
+            self.experts_fp8 = torch.empty(moe.moe_experts_fp8_bytes(shape), dtype=torch.uint8, device=device)
+            moe.moe_pack_experts_fp8(shape, src, self.experts_fp8)
         self.router = torch.empty(moe.moe_router_packed_bytes(shape), dtype=torch.uint8, device=device)
         if shape.router_fmt == moe.ROUTER_F32:
             moe.moe_pack_router(shape, to_device(host_layer.router_f32, device), None, None, self.router)
@@ -80,6 +85,7 @@ def alloc_buffers(shape: moe.Shape, T: int, path: str, device="cuda") -> StepBuf
     R = shape.n_experts + shape.has_shared
     S = shape.slots
     ws_bytes = (moe.moe_decode_workspace_bytes(shape, T) if path in ("decode", "fused")
+                else moe.moe_prefill_fp8_workspace_bytes(shape, T) if path == "fp8"
                 else moe.moe_prefill_workspace_bytes(shape, T))
     return StepBuffers(
         T=T,
@@ -100,8 +106,9 @@ def pick_path(T: int) -> str:
 def layer_step(layer: DeviceLayer, x: torch.Tensor, buf: StepBuffers, path: Optional[str] = None,
                residual: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None, stream=None):
     """One layer on one stream. path "fused" (T <= 16): moe_decode_layer (one launch);
-    "decode" / "prefill": moe_route, then moe_experts_decode or moe_experts_prefill, then
-    moe_combine."""
+    "decode" / "prefill" / "fp8": moe_route, then moe_experts_decode, moe_experts_prefill
+    or moe_experts_prefill_fp8 (the FP8 route; needs a layer built with fp8=True),
+    then moe_combine."""
     sh, T = layer.shape, buf.T
     path = path or pick_path(T)
     dst = buf.out if out is None else out
@@ -112,6 +119,10 @@ def layer_step(layer: DeviceLayer, x: torch.Tensor, buf: StepBuffers, path: Opti
     moe.moe_route(sh, layer.router, layer.logit_bias, x, T, buf.logits, buf.ids, buf.w, buf.wsh, stream)
     if path == "decode":
         moe.moe_experts_decode(sh, layer.experts, x, T, buf.ids, buf.ws, buf.y, stream)
+    elif path == "fp8":
+        if layer.experts_fp8 is None:
+            raise ValueError("the FP8 route needs a DeviceLayer built with fp8=True")
+        moe.moe_experts_prefill_fp8(sh, layer.experts_fp8, x, T, buf.ids, buf.ws, buf.y, stream)
     else:
         moe.moe_experts_prefill(sh, layer.experts, x, T, buf.ids, buf.ws, buf.y, stream)
     moe.moe_combine(sh, buf.y, buf.w, buf.wsh, T, residual, dst, stream)

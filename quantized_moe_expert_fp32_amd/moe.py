@@ -103,6 +103,14 @@ _lib.moe_prefill_dispatch_layout.restype = _I32
 _lib.moe_prefill_dispatch_layout.argtypes = [_S, _I32, ctypes.POINTER(PrefillDispatchView)]
 _lib.moe_experts_prefill.restype = _I32
 _lib.moe_experts_prefill.argtypes = [_S, _P, _P, _I32, _P, _P, _SZ, _P, _P]
+_lib.moe_experts_fp8_bytes.restype = _SZ
+_lib.moe_experts_fp8_bytes.argtypes = [_S]
+_lib.moe_pack_experts_fp8.restype = _I32
+_lib.moe_pack_experts_fp8.argtypes = [_S, ctypes.POINTER(ExpertCanon), _P, _SZ, _P]
+_lib.moe_prefill_fp8_workspace_bytes.restype = _SZ
+_lib.moe_prefill_fp8_workspace_bytes.argtypes = [_S, _I32]
+_lib.moe_experts_prefill_fp8.restype = _I32
+_lib.moe_experts_prefill_fp8.argtypes = [_S, _P, _P, _I32, _P, _P, _SZ, _P, _P]
 _lib.moe_combine.restype = _I32
 _lib.moe_combine.argtypes = [_S, _P, _P, _P, _I32, _P, _P, _P]
 _lib.moe_rmsnorm.restype = _I32
@@ -113,7 +121,8 @@ EXPORTS = ("moe_abi_version", "moe_status_str", "moe_last_error", "moe_shape_che
            "moe_route", "moe_route_from_logits", "moe_decode_workspace_bytes", "moe_experts_decode",
            "moe_experts_decode_noalloc", "moe_decode_layer", "moe_decode_block",
            "moe_decode_layer_check", "moe_dispatch", "moe_prefill_workspace_bytes", "moe_prefill_dispatch_layout",
-           "moe_experts_prefill", "moe_combine", "moe_rmsnorm")
+           "moe_experts_prefill", "moe_experts_fp8_bytes", "moe_pack_experts_fp8",
+           "moe_prefill_fp8_workspace_bytes", "moe_experts_prefill_fp8", "moe_combine", "moe_rmsnorm")
 
 
 def library_path() -> str:
@@ -241,6 +250,39 @@ def moe_prefill_dispatch_layout(shape, T) -> PrefillDispatchView:
 def moe_experts_prefill(shape, experts_packed, x, T, ids, ws, y, stream=None):
     _check(_lib.moe_experts_prefill(ctypes.byref(shape), _ptr(experts_packed), _ptr(x), T, _ptr(ids), _ptr(ws),
                                     _nbytes(ws), _ptr(y), _stream(stream)), "moe_experts_prefill")
+
+
+def moe_experts_fp8_bytes(shape: Shape) -> int:
+    return _lib.moe_experts_fp8_bytes(ctypes.byref(shape))
+
+
+def moe_pack_experts_fp8(shape, src: dict, fp8, stream=None):
+    canon = ExpertCanon(*[_ptr(src[f[0]]) for f in ExpertCanon._fields_])
+    _check(_lib.moe_pack_experts_fp8(ctypes.byref(shape), ctypes.byref(canon), _ptr(fp8), _nbytes(fp8),
+                                     _stream(stream)), "moe_pack_experts_fp8")
+
+
+def moe_prefill_fp8_workspace_bytes(shape: Shape, T: int) -> int:
+    return _lib.moe_prefill_fp8_workspace_bytes(ctypes.byref(shape), T)
+
+
+def moe_experts_prefill_fp8(shape, experts_fp8, x, T, ids, ws, y, stream=None):
+    _check(_lib.moe_experts_prefill_fp8(ctypes.byref(shape), _ptr(experts_fp8), _ptr(x), T, _ptr(ids), _ptr(ws),
+                                        _nbytes(ws), _ptr(y), _stream(stream)), "moe_experts_prefill_fp8")
+
+
+def fp8_expert_regions(shape: Shape):
+    """Byte regions of one expert in the FP8 buffer (the layout moe.h documents):
+    dict of (offset, rows, row bytes) for gate, up, down codes and (offset, count)
+    for the float row scales, plus the per-expert stride."""
+    Hp = -(-shape.hidden // 128) * 128
+    Ip = -(-shape.inter // 128) * 128
+    I, H = shape.inter, shape.hidden
+    up = I * Hp
+    down = 2 * up
+    scales = down + H * Ip
+    return {"gate": (0, I, Hp), "up": (up, I, Hp), "down": (down, H, Ip), "scales": (scales, 2 * I + H),
+            "stride": -(-(scales + 4 * (2 * I + H)) // 256) * 256}
 
 
 def moe_combine(shape, y, w, w_shared, T, residual, out, stream=None):

@@ -80,6 +80,17 @@ def test_sizes(moe):
     per8 = 2 * 512 * 4096 // 2 + 2048 * 1024 // 2 + 2 * 512 * 64 * 4 + 2048 * 16 * 4
     assert moe.moe_experts_packed_bytes(_big(moe, bits=8)) == 257 * per8
     assert moe.moe_experts_packed_bytes(_big(moe, bits=5)) == 0
+    # FP8 route: gate and up codes [512][2048], down codes [2048][512], 3072 float row
+    # scales per expert, whatever the canonical width
+    per_fp8 = 3 * 512 * 2048 + 4 * 3072
+    assert moe.moe_experts_fp8_bytes(sh) == 257 * per_fp8
+    assert moe.moe_experts_fp8_bytes(_big(moe, bits=8)) == 257 * per_fp8
+    # rows padded to multiples of 128 codes: I = 64 -> 128-code down rows
+    small = _big(moe, hidden=256, inter=64, n_experts=16, top_k=2)
+    assert moe.moe_experts_fp8_bytes(small) == 17 * -(-(2 * 64 * 256 + 256 * 128 + 4 * (128 + 256)) // 256) * 256
+    assert moe.fp8_expert_regions(sh)["stride"] == per_fp8
+    # x codes, h (bf16), h codes and both scale arrays on top of the dispatch arrays
+    assert moe.moe_prefill_fp8_workspace_bytes(sh, 4096) > 4096 * 2048 + 4096 * 9 * 512 * 3
 
 
 def test_host_argument_checks_launch_nothing(moe):
@@ -99,6 +110,16 @@ def test_host_argument_checks_launch_nothing(moe):
     # unaligned pointer
     st = moe.raw_call("moe_experts_prefill", byref(sh), v(P + 4), v(P), 512, v(P), v(P), 1 << 30, v(P), None)
     assert st == moe.ERR_INVALID_ARG
+    # FP8 route: workspace, 256-byte alignment of the FP8 buffer, the canonical source
+    st = moe.raw_call("moe_experts_prefill_fp8", byref(sh), v(P), v(P), 512, v(P), v(P), 1024, v(P), None)
+    assert st == moe.ERR_WORKSPACE
+    st = moe.raw_call("moe_experts_prefill_fp8", byref(sh), v(P + 16), v(P), 512, v(P), v(P), 1 << 30, v(P), None)
+    assert st == moe.ERR_INVALID_ARG
+    st = moe.raw_call("moe_pack_experts_fp8", byref(sh), None, v(P), 1 << 30, None)
+    assert st == moe.ERR_INVALID_ARG
+    canon = moe.ExpertCanon(*([P] * 9))
+    st = moe.raw_call("moe_pack_experts_fp8", byref(sh), byref(canon), v(P), 1024, None)
+    assert st == moe.ERR_WORKSPACE
     # T = 0
     st = moe.raw_call("moe_route", byref(sh), v(P), None, v(P), 0, v(P), v(P), v(P), v(P), None)
     assert st == moe.ERR_INVALID_ARG
