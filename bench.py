@@ -40,6 +40,8 @@ EXPERT_BYTES = 1_769_472  # gate+up+down q and scale/bias for H=2048, I=512
 # 8-bit experts: one code per byte and one (scale, bias) pair per 64 codes (the
 # packed form carries one more word per group: 3,538,944 B)
 EXPERT_BYTES_8BIT = 3 * 2048 * 512 + 3 * 2048 * 512 // 64 * 4
+FP8_EXPERT_BYTES = 3 * 2048 * 512 + 4 * (2 * 512 + 2048)  # E4M3 codes and float row scales
+FP8_PEAK_TFLOPS = 5000.0
 ROUTER_BYTES = 559_232
 
 
@@ -50,7 +52,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill512", "prefill4096", "stack1", "stack16", "decode_8bit",
-                             "prefill512_8bit"])
+                             "prefill512_8bit", "prefill512_fp8", "prefill4096_fp8"])
     ap.add_argument("--copies", type=int, default=8, help="independent weight sets for the decode workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", action="store_true", help="measure the chosen workload alone (no sub-records)")
@@ -72,15 +74,20 @@ def parse():
 # kernels of the measured stage (per-launch traffic is the sum of their per-dispatch medians)
 PREFILL_KERNELS = ["prefill_count_kernel", "prefill_scatter_kernel", "expert_gemm_kernel<true>",
                    "expert_gemm_kernel<false>"]
+FP8_KERNELS = ["prefill_count_kernel", "prefill_scatter_kernel", "quant_rows_fp8_kernel", "fp8_gemm_kernel<true>",
+               "fp8_gemm_kernel<false>"]
 TRAFFIC_KERNELS = {"decode": ["decode_layer_kernel"], "stack16": ["decode_layer_kernel"],
                    "stack1": ["decode_layer_kernel"],
-                   "prefill512": PREFILL_KERNELS, "prefill4096": PREFILL_KERNELS}
+                   "prefill512": PREFILL_KERNELS, "prefill4096": PREFILL_KERNELS,
+                   "prefill512_fp8": FP8_KERNELS, "prefill4096_fp8": FP8_KERNELS}
 # sources the measured kernels are built from: a stored traffic record holds for
 # the sources it was taken on
 DECODE_SOURCES = ["decode.hip", "route_device.h", "moe_internal.h", "abi.hip"]
-PREFILL_SOURCES = ["prefill.hip", "mfma_common.h", "moe_internal.h", "abi.hip"]
+PREFILL_SOURCES = ["prefill.hip", "prefill_internal.h", "mfma_common.h", "moe_internal.h", "abi.hip"]
+FP8_SOURCES = ["prefill_fp8.hip", "prefill.hip", "prefill_internal.h", "mfma_common.h", "moe_internal.h"]
 TRAFFIC_SOURCES = {"decode": DECODE_SOURCES, "stack16": DECODE_SOURCES, "stack1": DECODE_SOURCES,
-                   "prefill512": PREFILL_SOURCES, "prefill4096": PREFILL_SOURCES}
+                   "prefill512": PREFILL_SOURCES, "prefill4096": PREFILL_SOURCES,
+                   "prefill512_fp8": FP8_SOURCES, "prefill4096_fp8": FP8_SOURCES}
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
@@ -176,7 +183,8 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-WORKLOADS = ("decode", "prefill512", "prefill4096", "stack1", "stack16", "decode_8bit", "prefill512_8bit")
+WORKLOADS = ("decode", "prefill512", "prefill4096", "stack1", "stack16", "decode_8bit", "prefill512_8bit",
+             "prefill512_fp8", "prefill4096_fp8")
 METRIC = "MoE-layer tokens/s (decode bs1, prefill 512/4096) + % HBM/MFMA roofline"
 
 
@@ -190,7 +198,8 @@ class Inputs:
 
         t0 = time.time()
         self.bits = 8 if wl.endswith("_8bit") else 4
-        wl = wl.replace("_8bit", "")
+        self.fp8 = wl.endswith("_fp8")
+        wl = wl.replace("_8bit", "").replace("_fp8", "")
         if wl == "decode":
             base = synth.make_case("decode", bits=self.bits)
             self.hosts = [base.layers[0]] + [synth.make_layer(base.shape, base.seed, c) for c in range(1, copies)]
@@ -210,9 +219,9 @@ class Inputs:
             self.hosts = cache["stack_hosts"]
             self.x_host = base.x
         self.shape = L.make_shape(base.shape)
-        key = "stack_layers" if wl.startswith("stack") else "%s_%d_layers" % (wl, self.bits)
+        key = "stack_layers" if wl.startswith("stack") else "%s_%d%s_layers" % (wl, self.bits, "_fp8" * self.fp8)
         if key not in cache:
-            cache[key] = [L.DeviceLayer(self.shape, h) for h in self.hosts]
+            cache[key] = [L.DeviceLayer(self.shape, h, fp8=self.fp8) for h in self.hosts]
         self.layers = cache[key]
         self.x = L.to_device(self.x_host)
         # SHA-256 (first 16 hex digits) of the first layer's arrays and the activations
@@ -232,8 +241,8 @@ def run_workload(wl, K, W, inp, no_cpu, cpu_seconds):
     from quantized_moe_expert_fp32_amd import moe
 
     T, shape, layers, xs = inp.T, inp.shape, inp.layers, inp.x
-    path = L.pick_path(T)
-    kind = wl.replace("_8bit", "")
+    path = "fp8" if inp.fp8 else L.pick_path(T)
+    kind = wl.replace("_8bit", "").replace("_fp8", "")
     buf = L.alloc_buffers(shape, T, path)
     S = shape.slots
     log("%s: %d weight sets, set-up %.1f s" % (wl, len(layers), inp.setup_s))
@@ -337,7 +346,10 @@ def run_workload(wl, K, W, inp, no_cpu, cpu_seconds):
             else:
                 moe.moe_route(shape, dl.router, dl.logit_bias, xin, T, buf.logits, buf.ids, buf.w, buf.wsh)
                 starts[j].record(stream)
-                moe.moe_experts_prefill(shape, dl.experts, xin, T, buf.ids, buf.ws, buf.y)
+                if inp.fp8:
+                    moe.moe_experts_prefill_fp8(shape, dl.experts_fp8, xin, T, buf.ids, buf.ws, buf.y)
+                else:
+                    moe.moe_experts_prefill(shape, dl.experts, xin, T, buf.ids, buf.ws, buf.y)
                 ends[j].record(stream)
     torch.cuda.synchronize()
     durs_ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
@@ -355,11 +367,17 @@ def run_workload(wl, K, W, inp, no_cpu, cpu_seconds):
     # buffer and the bf16 intermediate are not counted
     ids_np = buf.ids.cpu().numpy()
     distinct = len(set(ids_np.reshape(-1).tolist())) + shape.has_shared
-    alg_bytes = distinct * (EXPERT_BYTES_8BIT if inp.bits == 8 else EXPERT_BYTES) + T * 2048 * 2
+    per_expert = FP8_EXPERT_BYTES if inp.fp8 else EXPERT_BYTES_8BIT if inp.bits == 8 else EXPERT_BYTES
+    alg_bytes = distinct * per_expert + T * 2048 * 2
     flops = T * S * 3 * 2 * 2048 * 512
     if path == "fused":
         alg_bytes += ROUTER_BYTES  # the launch also streams the router
-    if wl == "prefill4096":
+    if inp.fp8:
+        # the FP8 weights (1 byte per weight) take longer to stream at 8 TB/s than the
+        # FP8 products take at 5 PFLOP/s, at 512 and at 4096 tokens alike
+        roof = dict(bound="hbm", achieved=alg_bytes / (stage_us * 1e-6) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
+        roof["mfma_fp8_frac"] = flops / (stage_us * 1e-6) / 1e12 / FP8_PEAK_TFLOPS
+    elif wl == "prefill4096":
         roof = dict(bound="mfma", achieved=flops / (stage_us * 1e-6) / 1e12, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s")
     else:
         roof = dict(bound="hbm", achieved=alg_bytes / (stage_us * 1e-6) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
@@ -368,6 +386,7 @@ def run_workload(wl, K, W, inp, no_cpu, cpu_seconds):
     roof["kernel"] = ("decode_layer_kernel (RMSNorm, router, selection, experts, combine and residual in one launch)"
                       if kind.startswith("stack") else
                       "decode_layer_kernel (router, selection, experts, combine in one launch)" if path == "fused"
+                      else "experts stage (moe_experts_prefill_fp8): " + " + ".join(FP8_KERNELS) if inp.fp8
                       else "experts stage (moe_experts_prefill): " + " + ".join(PREFILL_KERNELS))
     roof["avg_us"] = stage_us
     roof["alg_bytes_per_launch"] = int(alg_bytes)
@@ -375,13 +394,14 @@ def run_workload(wl, K, W, inp, no_cpu, cpu_seconds):
 
     cpu = None
     if not no_cpu:
-        cpu = cpu_baseline(kind, inp.hosts, inp.x_host, T, shape, cpu_seconds)
+        cpu = cpu_baseline(kind, inp.hosts, inp.x_host, T, shape, cpu_seconds, fp8=inp.fp8)
     unit = "layer-tokens/s" if not kind.startswith("stack") else "tokens/s"
     return {
         "value": value, "unit": unit, "steps": K, "warmup": W, "ms_per_step": elapsed * 1e3 / K,
         "us_per_step_stream": region_us / K,
         "config": {"workload": wl, "T": T, "hidden": 2048, "n_experts": 256, "top_k": 8, "shared": 1,
-                   "inter": 512, "weights": "int%d affine g64" % inp.bits, "router": "8-bit affine g64",
+                   "inter": 512, "weights": ("E4M3 rows upcast from int%d affine g64" if inp.fp8 else
+                                             "int%d affine g64") % inp.bits, "router": "8-bit affine g64",
                    "layers": len(layers) if kind.startswith("stack") else 1,
                    "weight_copies": len(layers) if kind == "decode" else 1, "path": path,
                    "graph_steps": n_cap},
@@ -410,7 +430,8 @@ def main():
     torch.cuda.set_device(torch.device("cuda:0"))
     head = args.workload
     defaults = {"decode": (2048, 256), "prefill512": (200, 20), "prefill4096": (50, 5),
-                "stack1": (50, 5), "stack16": (50, 5), "decode_8bit": (1024, 128), "prefill512_8bit": (100, 10)}
+                "stack1": (50, 5), "stack16": (50, 5), "decode_8bit": (1024, 128), "prefill512_8bit": (100, 10),
+                "prefill512_fp8": (200, 20), "prefill4096_fp8": (50, 5)}
     K = args.steps if args.steps is not None else defaults[head][0]
     W = args.warmup if args.warmup is not None else defaults[head][1]
     cache = {}
@@ -429,7 +450,8 @@ def main():
             for drop in ("setup_s",):
                 r.pop(drop, None)
             others[wl] = r
-            for key in [k2_ for k2_ in cache if k2_.startswith(wl.replace("_8bit", "")) and k2_.endswith("_layers")]:
+            for key in [k2_ for k2_ in cache if k2_.startswith(wl.replace("_8bit", "").replace("_fp8", ""))
+                        and k2_.endswith("_layers")]:
                 cache.pop(key, None)  # free what no later workload reads
     line = {
         "metric": METRIC, "value": rec["value"], "unit": rec["unit"], "n_gpus": 1, "steps": K, "warmup": W,
@@ -442,8 +464,9 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(wl, hosts, xs_host, T, shape, budget_s):
-    """The FP64 oracle as it stands, on a bounded sample of the same workload."""
+def cpu_baseline(wl, hosts, xs_host, T, shape, budget_s, fp8=False):
+    """The FP64 oracle as it stands, on a bounded sample of the same workload (fp8:
+    the oracle's FP8 route)."""
     from oracle import moe_oracle as O
 
     try:
@@ -466,10 +489,11 @@ def cpu_baseline(wl, hosts, xs_host, T, shape, budget_s):
     elif wl.startswith("prefill"):
         n = min(T, 64)
         while time.perf_counter() - t0 < budget_s and layer_passes < 4:
-            O.layer_forward(xs_host[:n], hosts[0], k)
+            O.layer_forward(xs_host[:n], hosts[0], k, fp8=fp8)
             done_tokens += n
             layer_passes += 1
-        sample = "%d passes of the first %d tokens through the layer" % (layer_passes, n)
+        sample = "%d passes of the first %d tokens through the layer%s" % (layer_passes, n,
+                                                                          " (FP8 route)" if fp8 else "")
     else:
         n = xs_host.shape[0]
         x = xs_host

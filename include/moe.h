@@ -24,7 +24,7 @@
  *              expert gate is an N=1 projection.
  *   [P2-next]  "R9700: the 35B only one runtime could load" (R9700 vLLM blog, part 13),
  *              its closing list of kernel work: upcast the experts to FP8 to run them
- *              on the FP8 matrix units, a second route onto them.
+ *              on the FP8 matrix units as well.
  *
  * Conventions for every call:
  *   - Pointers named *_host are host memory; every other pointer is device memory

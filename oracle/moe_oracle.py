@@ -357,8 +357,9 @@ def layer_forward(x_bits, layer, top_k: int, has_shared: bool = True, fp8: bool 
 
 
 # ---------------------------------------------------------------- FP8 route (prompt experts)
-# TensorFold #931, page 2 (the RDNA4 optimisation runway): upcast the experts to
-# FP8 so the prompt GEMMs run on the FP8 matrix units, a second route onto them.
+# "R9700: the 35B only one runtime could load" (R9700 vLLM blog, part 13), its
+# closing list of kernel work: upcast the experts to FP8 so that the prompt GEMMs
+# can run on the FP8 matrix units as well.
 # The pages fix neither the FP8 format, the scaling nor the activation side;
 # readings:
 #   * OCP FP8 E4M3 (4 exponent bits, bias 7, 3 mantissa bits, subnormals, no

@@ -1,7 +1,7 @@
 // FP8 route of the prompt experts: the experts upcast once to FP8 so the prompt's
-// grouped GEMMs run on the FP8 matrix cores (TensorFold #931, page 2, the RDNA4
-// optimisation runway: "a second route onto the tensor units", re-designed for
-// CDNA4's v_mfma_scale_f32_16x16x128_f8f6f4).
+// grouped GEMMs run on the FP8 matrix cores ("R9700: the 35B only one runtime could
+// load", R9700 vLLM blog part 13, its closing list of kernel work; there aimed at
+// RDNA4's FP8 WMMA, here at CDNA4's v_mfma_scale_f32_16x16x128_f8f6f4).
 //
 // Numbers (OCP FP8 E4M3, round to nearest even, by v_cvt_pk_fp8_f32):
 //   * each weight row is formed as w = fma(scale, q, bias) in fp32 and stored as
@@ -13,15 +13,15 @@
 //   * a projection is acc * 2^e_row * 2^e_col with acc the fp32 MFMA sum of code
 //     products (each exact in fp32). Every output's arithmetic depends on its own
 //     activation row and weight row only, as in the exact path.
-// The route reuses the exact path's routing, dispatch (with tiles of 256 rows) and
+// The route reuses the exact path's routing, dispatch (tiles of 128 rows) and
 // combine; h stays bf16 between the two GEMMs, as there.
 //
-// Tiles: up to 256 expert-sorted rows x 128 weight rows per workgroup of four
-// wavefronts (gate/up: 64 gate rows and the matching 64 up rows; down: 128 output
-// columns). Wavefront w owns weight rows cs*64 + 16w .. +16 (cs < 2) over every
-// tile row, so each B fragment read from LDS feeds up to 16 products and a
-// wavefront holds a gate row and its up row side by side. An expert with at most
-// 256 rows is one tile, so its weights stream from HBM once per column block.
+// Tiles: up to 128 expert-sorted rows x 256 weight rows per workgroup of four
+// wavefronts (gate/up: 128 gate rows and the matching 128 up rows; down: 256
+// output columns), on v_mfma_scale_f32_32x32x64_f8f6f4. Wavefront w owns two
+// 32-row blocks of the weight rows over every tile row, so each fragment read from
+// LDS feeds two (B) or up to four (A) products, and a wavefront holds a gate row
+// block and its up row block side by side.
 #include "mfma_common.h"
 #include "moe_internal.h"
 #include "prefill_internal.h"
@@ -174,17 +174,18 @@ __global__ __launch_bounds__(256) void quant_rows_fp8_kernel(const uint16_t* __r
 }
 
 // ---------------------------------------------------------------- grouped FP8 GEMM
-// A workgroup multiplies one tile (up to 256 expert-sorted rows) by NB8 = 128
-// weight rows of the tile's expert over the whole K, in chunks of KC8 = 128 codes
-// (one MFMA depth). Per chunk, direct global-to-LDS loads stage the tile's rows x
-// 128 B and the 128 weight rows x 128 B into a ring of LDS stages that runs one
-// chunk fewer than it has stages ahead of the one being multiplied. A stage holds
-// only the A rows the tile loads, so smaller tiles get more stages.
-constexpr int BM8 = 256;
-constexpr int NB8 = 128;
-constexpr int KC8 = 128;
+// A workgroup multiplies one tile (up to 128 expert-sorted rows) by NB8 = 256
+// weight rows of the tile's expert over the whole K, in chunks of KC8 = 64 codes
+// (one depth of v_mfma_scale_f32_32x32x64_f8f6f4). Per chunk, direct
+// global-to-LDS loads stage the tile's rows x 64 B and the 256 weight rows x 64 B
+// into a ring of three LDS stages that runs two chunks ahead of the one being
+// multiplied. The ring (72 KiB) lets two workgroups share a CU, so one's prologue
+// and epilogue overlap the other's main loop.
+constexpr int BM8 = 128;
+constexpr int NB8 = 256;
+constexpr int KC8 = 64;
 constexpr int B8_BYTES = NB8 * KC8;                 // 16 KiB
-constexpr int RING8 = 3 * (BM8 * KC8 + B8_BYTES);  // 144 KiB: three stages of a full tile
+constexpr int RING8 = 3 * (BM8 * KC8 + B8_BYTES);  // 72 KiB: three stages of a full tile
 
 struct Fp8GemmArgs {
     const uint8_t* w8;  // FP8 expert buffer
@@ -200,21 +201,30 @@ struct Fp8GemmArgs {
 };
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-// D += A B over one 16 x 16 x 128 block: lane l holds row (A) / column (B) l % 16,
-// 32 codes of its k block l / 16 (16 from each uint4). Both operand scales are 2^0.
-__device__ __forceinline__ f32x4_t mfma_fp8(const uint4& a0, const uint4& a1, const uint4& b0, const uint4& b1,
-                                            const f32x4_t& c) {
+// D += A B over one 32 x 32 x 64 block: lane l holds row (A) / column (B) l % 32,
+// the 32 codes of k half l / 32 (16 from each uint4), and receives D[8 (r / 4) +
+// 4 (l / 32) + r % 4][l % 32] in register r. Both operand scales are 2^0.
+__device__ __forceinline__ f32x16_t mfma_fp8(const uint4& a0, const uint4& a1, const uint4& b0, const uint4& b1,
+                                             const f32x16_t& c) {
     const i32x8_t a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
     const i32x8_t b = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-// GATEUP: weight rows 0..63 are gate rows cb*64 .., rows 64..127 the matching up
+// 16-byte piece p of staged row r sits at position p ^ ((r >> 2) & 3) of the row's
+// 64 bytes: the rows sharing a bank window read different pieces.
+__device__ __forceinline__ int piece_pos(int r, int p) { return p ^ ((r >> 2) & 3); }
+
+// GATEUP: weight rows 0..127 are gate rows cb*128 .., rows 128..255 the matching up
 // rows; the epilogue writes h = bf16(silu(gate) * up). Else (down): weight rows are
-// down rows cb*128 ..; the epilogue writes y[t][s][n] for the row's pick p = order[row].
+// down rows cb*256 ..; the epilogue writes y[t][s][n] for the row's pick p = order[row].
+// Wavefront w owns the weight rows n0(cs) .. +32, cs < 2 (gate/up: gate rows 32w ..
+// and up rows 128 + 32w .., the same intermediate columns; down: rows 64w + 32cs ..)
+// over all tile rows.
 template <bool GATEUP>
-__global__ __launch_bounds__(256, 1) void fp8_gemm_kernel(Fp8GemmArgs a) {
+__global__ __launch_bounds__(256, 2) void fp8_gemm_kernel(Fp8GemmArgs a) {
     constexpr int NCS = 2;
     extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
     __shared__ uint32_t arow_lds[BM8];  // byte offset of each tile row in its source, ~0 beyond the tile
@@ -223,28 +233,30 @@ __global__ __launch_bounds__(256, 1) void fp8_gemm_kernel(Fp8GemmArgs a) {
     __shared__ float ws_lds[NB8];       // the weight rows' scales
     const int H = a.H, I = a.I, S = a.S;
     const int Kp = GATEUP ? a.L.Hp : a.L.Ip;  // codes per row of both operands
-    const int nblk = GATEUP ? I / 64 : (H + NB8 - 1) / NB8;
+    const int nblk = GATEUP ? (I + 127) / 128 : (H + NB8 - 1) / NB8;
     int ti, cb;
     if (!xcd_item(*a.ntiles, nblk, ti, cb)) return;
     const Tile tl = a.tiles[ti];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lg = lane >> 4, lc = lane & 15;
-    const int n_ms = (tl.nrows + 15) >> 4;
+    const int l32 = lane & 31, kh = lane >> 5;
+    const int n_ms = (tl.nrows + 31) >> 5;
     const uint8_t* ebase = a.w8 + (size_t)tl.expert * a.L.stride;
-    // weight row r of the workgroup: its byte offset in the expert and its scale's index
+    // weight row r of the workgroup: its byte offset in the expert and its scale's
+    // index; rows beyond the matrix read row 0 and are never stored
     auto wrow = [&](int r, int& sidx) -> uint32_t {
         if constexpr (GATEUP) {
-            const int i = cb * 64 + (r & 63);
-            sidx = (r < 64 ? 0 : I) + i;
-            return (uint32_t)((r < 64 ? 0 : a.L.up) + (size_t)i * Kp);
+            const int i0 = cb * 128 + (r & 127), i = i0 < I ? i0 : 0;
+            sidx = (r < 128 ? 0 : I) + i;
+            return (uint32_t)((r < 128 ? 0 : a.L.up) + (size_t)i * Kp);
         } else {
-            const int n0 = cb * NB8 + r, n = n0 < H ? n0 : 0;  // rows beyond H read row 0, never stored
+            const int n0 = cb * NB8 + r, n = n0 < H ? n0 : 0;
             sidx = 2 * I + n;
             return (uint32_t)(a.L.down + (size_t)n * Kp);
         }
     };
-    {
+    auto n0 = [&](int cs) -> int { return GATEUP ? cs * 128 + 32 * wave : 64 * wave + 32 * cs; };
+    if (tid < BM8) {
         uint32_t off = 0xFFFFFFFFu;
         float sc = 0.f;
         int pick = 0;
@@ -258,50 +270,52 @@ __global__ __launch_bounds__(256, 1) void fp8_gemm_kernel(Fp8GemmArgs a) {
         arow_lds[tid] = off;
         as_lds[tid] = sc;
         pick_lds[tid] = pick;
-        if (tid < NB8) {
-            int sidx;
-            wrow(tid, sidx);
-            ws_lds[tid] = reinterpret_cast<const float*>(ebase + a.L.scales)[sidx];
-        }
+    }
+    {
+        int sidx;
+        wrow(tid, sidx);
+        ws_lds[tid] = reinterpret_cast<const float*>(ebase + a.L.scales)[sidx];
     }
     __syncthreads();
 
-    // ---- stage layout: A: the loaded rows x 128 B, then B: 128 rows x 128 B; the
-    // 16-byte piece p of row r sits at position p ^ (r & 7) of its row, which spreads
-    // the fragment reads of neighbouring lanes over the banks. Rows beyond the tile
-    // load row 0 of the tile instead, so every lane issues every load and the wait
-    // for a chunk is an exact vector-memory count.
+    // ---- stage layout: A: the loaded rows x 64 B, then B: 256 rows x 64 B. One
+    // load instruction covers 16 rows; lane l loads piece piece_pos(r, l & 3) of row
+    // r = 16 i + (l >> 2) into position l & 3. Rows beyond the tile load row 0 of the
+    // tile instead, so every lane issues every load and the wait for a chunk is an
+    // exact vector-memory count.
     const uint32_t ring_lds = lds_addr(ring);
-    uint32_t b_off[4];  // B: instruction 4 wave + i covers rows 8 (4 wave + i) .. +8
+    uint32_t b_off[4];  // B: instruction 4 wave + i covers rows 16 (4 wave + i) .. +16
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int r = 8 * (4 * wave + i) + (lane >> 3);
+        const int r = 16 * (4 * wave + i) + (lane >> 2);
         int sidx;
-        b_off[i] = wrow(r, sidx) + 16 * ((lane & 7) ^ (r & 7));
+        b_off[i] = wrow(r, sidx) + 16 * piece_pos(r, lane & 3);
     }
 
-    f32x4_t acc[16][NCS];
+    f32x16_t acc[4][NCS];
 #pragma unroll
-    for (int m = 0; m < 16; ++m)
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int cs = 0; cs < NCS; ++cs) acc[m][cs] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // The K loop is instantiated for 1, 2, 4, 8, 12 and 16 row blocks of 16 (the
-    // tile's count rounded up), so its body is straight-line code.
+        for (int cs = 0; cs < NCS; ++cs)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[m][cs][r] = 0.f;
+    // The K loop is instantiated for 1, 2 and 4 row blocks of 32 (the tile's count
+    // rounded up), so its body is straight-line code.
     auto kloop = [&](auto nm_tag) __attribute__((always_inline)) {
         constexpr int NM = decltype(nm_tag)::value;
-        constexpr int NA = NM >= 2 ? NM / 2 : 1;  // A instructions (8 rows each) per wavefront
+        constexpr int NA = NM >= 2 ? NM / 2 : 1;  // A instructions (16 rows each) per wavefront
         constexpr int LPC = NA + 4;               // loads per wavefront and chunk
-        constexpr int SA = 4 * NA * 1024;         // A bytes per stage (32 NA rows)
+        constexpr int SA = 4 * NA * 1024;         // A bytes per stage (64 NA rows)
         constexpr int STAGE = SA + B8_BYTES;
-        constexpr int NS = RING8 / STAGE;         // stages: 3 .. 7
+        constexpr int NS = RING8 / STAGE;         // stages
         static_assert(NS >= 3 && NS * STAGE <= RING8 && LPC * (NS - 2) < 64, "ring");
         const uint32_t arow0 = arow_lds[0];
         uint32_t a_off[NA];
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
-            const int row = 8 * (NA * wave + i) + (lane >> 3);
-            const uint32_t off = arow_lds[row];
-            a_off[i] = (off == 0xFFFFFFFFu ? arow0 : off) + 16 * ((lane & 7) ^ (row & 7));
+            const int row = 16 * (NA * wave + i) + (lane >> 2);
+            const uint32_t off = row < BM8 ? arow_lds[row] : 0xFFFFFFFFu;
+            a_off[i] = (off == 0xFFFFFFFFu ? arow0 : off) + 16 * piece_pos(row, lane & 3);
         }
         auto issue = [&](int c) __attribute__((always_inline)) {
             const uint32_t st = ring_lds + (uint32_t)((c % NS) * STAGE);
@@ -317,17 +331,17 @@ __global__ __launch_bounds__(256, 1) void fp8_gemm_kernel(Fp8GemmArgs a) {
             uint4 b0[NCS], b1[NCS];
 #pragma unroll
             for (int cs = 0; cs < NCS; ++cs) {
-                const int n = cs * 64 + 16 * wave + lc;
-                const uint8_t* bp = st + SA + n * 128;
-                b0[cs] = *reinterpret_cast<const uint4*>(bp + 16 * ((2 * lg) ^ (n & 7)));
-                b1[cs] = *reinterpret_cast<const uint4*>(bp + 16 * ((2 * lg + 1) ^ (n & 7)));
+                const int n = n0(cs) + l32;
+                const uint8_t* bp = st + SA + n * 64;
+                b0[cs] = *reinterpret_cast<const uint4*>(bp + 16 * piece_pos(n, 2 * kh));
+                b1[cs] = *reinterpret_cast<const uint4*>(bp + 16 * piece_pos(n, 2 * kh + 1));
             }
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
-                const int row = 16 * m + lc;
-                const uint8_t* ar = st + row * 128;
-                const uint4 a0 = *reinterpret_cast<const uint4*>(ar + 16 * ((2 * lg) ^ (row & 7)));
-                const uint4 a1 = *reinterpret_cast<const uint4*>(ar + 16 * ((2 * lg + 1) ^ (row & 7)));
+                const int row = 32 * m + l32;
+                const uint8_t* ar = st + row * 64;
+                const uint4 a0 = *reinterpret_cast<const uint4*>(ar + 16 * piece_pos(row, 2 * kh));
+                const uint4 a1 = *reinterpret_cast<const uint4*>(ar + 16 * piece_pos(row, 2 * kh + 1));
 #pragma unroll
                 for (int cs = 0; cs < NCS; ++cs) acc[m][cs] = mfma_fp8(a0, a1, b0[cs], b1[cs], acc[m][cs]);
             }
@@ -347,26 +361,23 @@ __global__ __launch_bounds__(256, 1) void fp8_gemm_kernel(Fp8GemmArgs a) {
     };
     if (n_ms <= 1) kloop(std::integral_constant<int, 1>{});
     else if (n_ms <= 2) kloop(std::integral_constant<int, 2>{});
-    else if (n_ms <= 4) kloop(std::integral_constant<int, 4>{});
-    else if (n_ms <= 8) kloop(std::integral_constant<int, 8>{});
-    else if (n_ms <= 12) kloop(std::integral_constant<int, 12>{});
-    else kloop(std::integral_constant<int, 16>{});
+    else kloop(std::integral_constant<int, 4>{});
 
     // ---- epilogue: the ring's memory is free once every wavefront is past its last chunk
     __syncthreads();
     if constexpr (GATEUP) {
-        // h = bf16(silu(g) * u) for intermediate columns i = cb*64 + c, c = 16 wave + lc,
-        // staged as a bf16 tile in LDS, then stored with 16-byte row pieces.
-        constexpr int HS = 64 + 8;  // tile row stride (bf16)
+        // h = bf16(silu(g) * u) for intermediate columns i = cb*128 + c, c = 32 wave +
+        // l32, staged as a bf16 tile in LDS, then stored with 16-byte row pieces.
+        constexpr int HS = 128 + 8;  // tile row stride (bf16)
         uint16_t* hl = reinterpret_cast<uint16_t*>(ring);
-        const int c = 16 * wave + lc;
-        const float sg = ws_lds[c], su = ws_lds[64 + c];
+        const int c = 32 * wave + l32;
+        const float sg = ws_lds[c], su = ws_lds[128 + c];
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
+        for (int m = 0; m < 4; ++m) {
             if (m < n_ms) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * m + 4 * lg + r;
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 32 * m + 8 * (r >> 2) + 4 * kh + (r & 3);
                     const float gv = acc[m][0][r] * as_lds[row] * sg, uv = acc[m][1][r] * as_lds[row] * su;
                     // silu(g) = g / (1 + e^-g), e^-g = 2^(-g log2 e)
                     const float sl = gv * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-gv * 1.44269504088896341f));
@@ -376,39 +387,45 @@ __global__ __launch_bounds__(256, 1) void fp8_gemm_kernel(Fp8GemmArgs a) {
         }
         __syncthreads();
         for (int it = 0; it < 8; ++it) {
-            const int row = 32 * it + (tid >> 3), pc = tid & 7;
-            if (row < tl.nrows)
-                *reinterpret_cast<uint4*>(a.hbuf + (size_t)(tl.row0 + row) * I + cb * 64 + 8 * pc) =
+            const int row = 16 * it + (tid >> 4), pc = tid & 15;
+            if (row < tl.nrows && cb * 128 + 8 * pc < I)
+                *reinterpret_cast<uint4*>(a.hbuf + (size_t)(tl.row0 + row) * I + cb * 128 + 8 * pc) =
                     *reinterpret_cast<const uint4*>(hl + row * HS + 8 * pc);
         }
     } else {
-        // y[order[row]][cb*128 + n] staged as an fp32 tile in LDS, then stored with
-        // 16-byte row pieces, non-temporal (y is read once, by the combine).
+        // y[order[row]][cb*256 + n], staged 64 rows at a time as an fp32 tile in LDS
+        // and stored with 16-byte row pieces, non-temporal (y is read once, by the
+        // combine).
         constexpr int YS = NB8 + 4;  // tile row stride (floats)
-        static_assert(BM8 * YS * 4 <= RING8, "y tile");
+        static_assert(64 * YS * 4 <= RING8, "y tile");
         float* yl = reinterpret_cast<float*>(ring);
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            if (m < n_ms) {
+        for (int half = 0; half < 2; ++half) {
+            if (64 * half < tl.nrows) {
+                if (half) __syncthreads();
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * m + 4 * lg + r;
-                    const float sa = as_lds[row];
+                for (int mm = 0; mm < 2; ++mm) {
+                    const int m = 2 * half + mm;
 #pragma unroll
-                    for (int cs = 0; cs < NCS; ++cs) {
-                        const int n = cs * 64 + 16 * wave + lc;
-                        yl[row * YS + n] = acc[m][cs][r] * sa * ws_lds[n];
+                    for (int r = 0; r < 16; ++r) {
+                        const int rl = 32 * mm + 8 * (r >> 2) + 4 * kh + (r & 3);
+                        const float sa = as_lds[64 * half + rl];
+#pragma unroll
+                        for (int cs = 0; cs < NCS; ++cs) {
+                            const int n = n0(cs) + l32;
+                            yl[rl * YS + n] = acc[m][cs][r] * sa * ws_lds[n];
+                        }
                     }
                 }
+                __syncthreads();
+                for (int it = 0; it < 16; ++it) {
+                    const int rl = 4 * it + (tid >> 6), row = 64 * half + rl, pc = tid & 63;
+                    if (row < tl.nrows && cb * NB8 + 4 * pc < H)
+                        __builtin_nontemporal_store(*reinterpret_cast<const f32x4_t*>(yl + rl * YS + 4 * pc),
+                                                    reinterpret_cast<f32x4_t*>(a.y + (size_t)pick_lds[row] * H +
+                                                                               cb * NB8 + 4 * pc));
+                }
             }
-        }
-        __syncthreads();
-        for (int it = 0; it < BM8 / 8; ++it) {
-            const int row = 8 * it + (tid >> 5), pc = tid & 31;
-            if (row >= tl.nrows) break;
-            if (cb * NB8 + 4 * pc < H)
-                __builtin_nontemporal_store(*reinterpret_cast<const f32x4_t*>(yl + row * YS + 4 * pc),
-                                            reinterpret_cast<f32x4_t*>(a.y + (size_t)pick_lds[row] * H + cb * NB8 + 4 * pc));
         }
     }
 }
@@ -527,7 +544,8 @@ extern "C" moe_status moe_experts_prefill_fp8(const moe_shape* shape, const void
     ga.order = (const int32_t*)(w + W.D.order);
     ga.hbuf = hbuf;
     ga.y = y;
-    hipLaunchKernelGGL(fp8_gemm_kernel<true>, dim3(xcd_grid(W.D.max_tiles, I / 64)), dim3(256), RING8, hs, ga);
+    hipLaunchKernelGGL(fp8_gemm_kernel<true>, dim3(xcd_grid(W.D.max_tiles, (I + 127) / 128)), dim3(256), RING8, hs,
+                       ga);
     if ((st = check_launch("fp8_gemm_kernel<gate/up>")) != MOE_OK) return st;
     hipLaunchKernelGGL(quant_rows_fp8_kernel, dim3((unsigned)((P + 3) / 4)), dim3(256), 0, hs, hbuf, (long long)P,
                        (const int32_t*)(w + W.D.offsets) + M, I, L.Ip, h8, hsc);
