@@ -141,8 +141,13 @@ def write_traffic(wl, spec):
         raise SystemExit("missing counter values for %s" % kerns)
     k_fetch = known_kib / float(np.median(cf))
     k_write = known_kib / float(np.median(cw))
-    fk = sum(float(np.median(v)) for v in f)
-    wk = sum(float(np.median(v)) for v in w)
+    # per launch: each kernel's dispatches summed over the run, divided by the number
+    # of launches (the dispatch count of a kernel that runs once per launch; a kernel
+    # such as the FP8 row quantiser runs twice)
+    n_f = min(len(v) for v in f)
+    n_w = min(len(v) for v in w)
+    fk = sum(float(np.sum(v)) for v in f) / n_f
+    wk = sum(float(np.sum(v)) for v in w) / n_w
     rec = {"workload": wl, "kernels": kerns, "dispatches": [[len(v) for v in f], [len(v) for v in w]],
            "fetch_kib_per_launch": fk, "write_kib_per_launch": wk,
            "calibration_bytes": cal["bytes"], "fetch_scale": k_fetch, "write_scale": k_write,
@@ -328,6 +333,9 @@ def run_workload(wl, K, W, inp, no_cpu, cpu_seconds):
     n_ev = min(max(K, 8), 512 if not kind.startswith("stack") else 200)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    if kind.startswith("stack"):
+        # the stack's own launches: layer j % 40 on the state the previous layer left
+        st_cur, st_nxt = xs.clone(), torch.empty_like(xs)
     with torch.cuda.stream(stream):
         torch.cuda._sleep(200_000_000)  # keep the GPU busy while the host queues the measured launches
         for j in range(n_ev):
@@ -335,9 +343,10 @@ def run_workload(wl, K, W, inp, no_cpu, cpu_seconds):
             xin = xs[(j % xs.shape[0]):(j % xs.shape[0]) + 1] if kind == "decode" else xs
             if kind.startswith("stack"):
                 starts[j].record(stream)
-                moe.moe_decode_block(shape, dl.router, dl.logit_bias, dl.experts, xin, T, 1e-6, buf.ws, buf.logits,
-                                     buf.ids, buf.w, buf.wsh, buf.y, buf.out)
+                moe.moe_decode_block(shape, dl.router, dl.logit_bias, dl.experts, st_cur, T, 1e-6, buf.ws,
+                                     buf.logits, buf.ids, buf.w, buf.wsh, buf.y, st_nxt)
                 ends[j].record(stream)
+                st_cur, st_nxt = st_nxt, st_cur
             elif path == "fused":
                 starts[j].record(stream)
                 moe.moe_decode_layer(shape, dl.router, dl.logit_bias, dl.experts, xin, T, buf.ws, buf.logits,
@@ -367,8 +376,17 @@ def run_workload(wl, K, W, inp, no_cpu, cpu_seconds):
     # buffer and the bf16 intermediate are not counted
     ids_np = buf.ids.cpu().numpy()
     distinct = len(set(ids_np.reshape(-1).tolist())) + shape.has_shared
+    if kind.startswith("stack"):
+        # the stack's tokens drift together layer by layer and share more experts
+        # than the first layer's: the mean over one pass of the 40 layers
+        keep = []
+        with torch.cuda.stream(stream):
+            L.stack_step_fused(layers, xs.clone(), torch.empty_like(xs), buf, keep=keep)
+        torch.cuda.synchronize()
+        distinct = float(np.mean([len(set(ids.cpu().numpy().reshape(-1).tolist())) for _, ids in keep]))
+        distinct += shape.has_shared
     per_expert = FP8_EXPERT_BYTES if inp.fp8 else EXPERT_BYTES_8BIT if inp.bits == 8 else EXPERT_BYTES
-    alg_bytes = distinct * per_expert + T * 2048 * 2
+    alg_bytes = int(distinct * per_expert) + T * 2048 * 2
     flops = T * S * 3 * 2 * 2048 * 512
     if path == "fused":
         alg_bytes += ROUTER_BYTES  # the launch also streams the router
