@@ -71,15 +71,17 @@ __global__ __launch_bounds__(256) void router_kernel(const uint8_t* __restrict__
 // wavefront: no LDS and no barrier in the loop.
 constexpr int RG_TOK = 32;
 
+// One workgroup's tile: tokens t0 .. t0 + 31 x router rows rb0 .. rb0 + 16 NB - 1.
+// part is the workgroup's LDS for the wavefronts' partial sums.
 template <int NB>
-__global__ __launch_bounds__(256) void router_gemm_kernel(const uint8_t* __restrict__ router,
-                                                          const float* __restrict__ logit_bias,
-                                                          const uint16_t* __restrict__ x, int T, int H, int R, int E,
-                                                          float* __restrict__ logits) {
-    __shared__ float part[4][2][NB][4][64];
+__device__ __forceinline__ void router_gemm_tile(const uint8_t* __restrict__ router,
+                                                 const float* __restrict__ logit_bias,
+                                                 const uint16_t* __restrict__ x, int T, int H, int R, int E,
+                                                 float* __restrict__ logits, int t0, int rb0,
+                                                 float (*part)[2][NB][4][64]) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lg = lane >> 4, lc = lane & 15;
-    const int t0 = blockIdx.x * RG_TOK, rb = blockIdx.y * 16 * NB + lc;
+    const int rb = rb0 + lc;
     const int G = H / 64, ga = wave * G / 4, gb = (wave + 1) * G / 4;
     const uint8_t* qrow[NB];
     const uint32_t* sbrow[NB];
@@ -182,6 +184,33 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint8_t* __restr
     }
 }
 
+template <int NB>
+__global__ __launch_bounds__(256) void router_gemm_kernel(const uint8_t* __restrict__ router,
+                                                          const float* __restrict__ logit_bias,
+                                                          const uint16_t* __restrict__ x, int T, int H, int R, int E,
+                                                          float* __restrict__ logits) {
+    __shared__ float part[4][2][NB][4][64];
+    router_gemm_tile<NB>(router, logit_bias, x, T, H, R, E, logits, blockIdx.x * RG_TOK, blockIdx.y * 16 * NB, part);
+}
+
+// Thousands of tokens: row blocks of 64 (NB = 4, the activations read a quarter as
+// often) up to the last whole one, then blocks of 16 for the rows left over (the
+// shared gate's at 256 experts), so that a block of 64 mostly empty rows does not
+// take a round of workgroups of its own. A row's arithmetic is the same in both.
+__global__ __launch_bounds__(256) void router_gemm_wide_kernel(const uint8_t* __restrict__ router,
+                                                              const float* __restrict__ logit_bias,
+                                                              const uint16_t* __restrict__ x, int T, int H, int R,
+                                                              int E, float* __restrict__ logits) {
+    __shared__ float part[4][2][4][4][64];
+    const int n64 = R / 64;
+    if ((int)blockIdx.y < n64)
+        router_gemm_tile<4>(router, logit_bias, x, T, H, R, E, logits, blockIdx.x * RG_TOK, blockIdx.y * 64, part);
+    else
+        router_gemm_tile<1>(router, logit_bias, x, T, H, R, E, logits, blockIdx.x * RG_TOK,
+                            64 * n64 + 16 * ((int)blockIdx.y - n64),
+                            reinterpret_cast<float (*)[2][1][4][64]>(&part[0][0][0][0][0]));
+}
+
 static moe_status launch_topk(const moe_shape& sh, const float* logits, int T, int32_t* ids, uint16_t* w,
                               uint16_t* wsh, hipStream_t st) {
     const int R = router_rows(sh), E = sh.n_experts;
@@ -260,9 +289,9 @@ extern "C" moe_status moe_route(const moe_shape* shape, const void* router_packe
                                (const uint8_t*)router_packed, logit_bias, x, T, shape->hidden, R, shape->n_experts,
                                logits);
         else
-            hipLaunchKernelGGL(router_gemm_kernel<4>, dim3((T + RG_TOK - 1) / RG_TOK, (R + 63) / 64), dim3(256), 0, hs,
-                               (const uint8_t*)router_packed, logit_bias, x, T, shape->hidden, R, shape->n_experts,
-                               logits);
+            hipLaunchKernelGGL(router_gemm_wide_kernel, dim3((T + RG_TOK - 1) / RG_TOK, R / 64 + (R % 64 + 15) / 16),
+                               dim3(256), 0, hs, (const uint8_t*)router_packed, logit_bias, x, T, shape->hidden, R,
+                               shape->n_experts, logits);
         if ((st = check_launch("router_gemm_kernel")) != MOE_OK) return st;
     } else {
         launch_router<false>(*shape, (const uint8_t*)router_packed, logit_bias, x, T, logits, nullptr, ids, w,
