@@ -205,12 +205,14 @@ __device__ __forceinline__ void load_words(const uint16_t* p, uint32_t* out) {
 // norm_eps >= 0 (one token, TT == 1): the row's input is bf16(RMSNorm(x)) of that
 // token, with the scale of rms_scale(row_sumsq); with the 8-bit router and at
 // most 4096 activations the squares come from the activations the products load
-// (in row_sumsq's order), else from a pass of row_sumsq.
+// (in row_sumsq's order), else from a pass of row_sumsq; xr_out (optional)
+// receives that scale.
 template <int TT, bool AFF8>
 __device__ __forceinline__ void router_row(const uint8_t* __restrict__ router, const float* __restrict__ logit_bias,
                                            const uint16_t* __restrict__ x, int t0, int nt, int H, int R, int E, int r,
                                            int lane, float* logits, bool coherent, uint64_t* tagged, uint32_t tag,
-                                           size_t tstride = 0, size_t tcopy = 0, float norm_eps = -1.f) {
+                                           size_t tstride = 0, size_t tcopy = 0, float norm_eps = -1.f,
+                                           float* xr_out = nullptr) {
     double acc[TT];
 #pragma unroll
     for (int t = 0; t < TT; ++t) acc[t] = 0.0;
@@ -318,6 +320,7 @@ __device__ __forceinline__ void router_row(const uint8_t* __restrict__ router, c
     }
 #pragma unroll
     for (int t = 0; t < TT; ++t) acc[t] = wave_sum_f64(acc[t]);
+    if (norm && xr_out && lane == 0) *xr_out = xr;
     if (lane == 63) {
         const double bias = (r < E && logit_bias) ? (double)logit_bias[r] : 0.0;
 #pragma unroll
