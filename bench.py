@@ -72,8 +72,9 @@ def parse():
 # counter reads for a plain copy of known size. The record is stored with a hash
 # of the library sources; a bench run reports it only while the hash matches.
 # kernels of the measured stage (per-launch traffic is the sum of their per-dispatch medians)
-PREFILL_KERNELS = ["prefill_count_kernel", "prefill_scatter_kernel", "expert_gemm_kernel<true>",
-                   "expert_gemm_kernel<false>"]
+# (a name matches every kernel whose name holds it: both instances of the grouped GEMM)
+PREFILL_KERNELS = ["prefill_count_kernel", "prefill_scatter_kernel", "expert_gemm_kernel<true,",
+                   "expert_gemm_kernel<false,"]
 FP8_KERNELS = ["prefill_count_kernel", "prefill_scatter_kernel", "quant_rows_fp8_kernel", "fp8_gemm_kernel<true>",
                "fp8_gemm_kernel<false>"]
 TRAFFIC_KERNELS = {"decode": ["decode_layer_kernel"], "stack16": ["decode_layer_kernel"],
@@ -405,7 +406,8 @@ def run_workload(wl, K, W, inp, no_cpu, cpu_seconds):
                       if kind.startswith("stack") else
                       "decode_layer_kernel (router, selection, experts, combine in one launch)" if path == "fused"
                       else "experts stage (moe_experts_prefill_fp8): " + " + ".join(FP8_KERNELS) if inp.fp8
-                      else "experts stage (moe_experts_prefill): " + " + ".join(PREFILL_KERNELS))
+                      else "experts stage (moe_experts_prefill): " + " + ".join(k.rstrip(",") + ", …>" if k.endswith(",") else k
+                                                                     for k in PREFILL_KERNELS))
     roof["avg_us"] = stage_us
     roof["alg_bytes_per_launch"] = int(alg_bytes)
     roof["alg_flops_per_launch"] = int(flops)

@@ -379,6 +379,13 @@ constexpr int KC = 64;
 constexpr int NBR = 256;
 constexpr int B_BYTES = NBR * KC / 2, SB_BYTES = NBR * 4;
 constexpr int RING = 3 * (BM * KC * 2 + B_BYTES + SB_BYTES);  // 75 KiB: three stages of a full tile
+// Up to 1024 tokens most tiles hold a few row blocks and a workgroup's time goes to
+// streaming its weight rows, bound by the loads in flight: the kernel's second
+// instance takes at most 64 rows per pass (a tile of more rows is done in two
+// passes over the weights), with at most 168 VGPRs and a 51 KiB ring, so three
+// workgroups share a CU (at 512 tokens 141.6 -> 132.4 us for both GEMMs). A row's
+// arithmetic is the same in both instances, and so are its results, bit for bit.
+constexpr int RING3 = 3 * (64 * KC * 2 + B_BYTES + SB_BYTES);  // 51 KiB
 
 struct GemmArgs {
     const uint8_t* packed;
@@ -399,10 +406,15 @@ struct GemmArgs {
 // GATEUP: weight rows 0..127 are gate rows cb*128 .., rows 128..255 the matching up
 // rows; the epilogue writes h = bf16(silu(gate) * up). Else (down): weight rows are
 // down rows cb*256 ..; the epilogue writes y[t][s][n] for the row's pick p = order[row].
-template <bool GATEUP>
-__global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
+// WPC: workgroups per CU (2: one pass of up to 128 rows; 3: passes of 64 rows).
+template <bool GATEUP, int WPC>
+__global__ __launch_bounds__(256, WPC) void expert_gemm_kernel(GemmArgs a) {
     constexpr int NCS = NBR / 64;  // 16-column sets per wavefront
     constexpr int HALF = NBR / 2;  // gate/up: gate rows 0 .. HALF-1, up rows HALF .. NBR-1
+    static_assert(WPC == 2 || WPC == 3, "instances");
+    constexpr int MAXNM = WPC == 3 ? 4 : 8;          // row blocks of 16 per pass
+    constexpr int PR = 16 * MAXNM;                   // rows per pass
+    constexpr int RINGW = WPC == 3 ? RING3 : RING;   // the launch's dynamic LDS
     extern __shared__ __attribute__((aligned(16))) uint8_t ring[];  // ring of stages, each (A | B | sb)
     __shared__ uint32_t arow_lds[BM];  // byte offset of each tile row in its source, ~0 beyond the tile
     __shared__ int32_t pick_lds[BM];   // down: pick p = order[row] of each tile row (its y row)
@@ -417,7 +429,6 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lg = lane >> 4, lc = lane & 15;
-    const int n_ms = (tl.nrows + 15) >> 4;
     const int col0 = GATEUP ? cb * HALF : cb * NBR;
 
     if (tid < BM) {
@@ -479,9 +490,14 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
     // sb: one instruction per wavefront, blocks 16 wave .. +16, four words each
     const uint32_t sb_off = (uint32_t)(sb_region + (size_t)gblock(16 * wave + (lane >> 2)) * G * 16 + 4 * (lane & 3));
 
-    f32x4_t acc[8][NCS];
+    f32x4_t acc[MAXNM][NCS];
+    // passes over the tile's rows; a tile fits one pass of the two-per-CU instance
+    const int pass_end = WPC == 2 ? 1 : tl.nrows;
+    for (int r0 = 0; r0 < pass_end; r0 += PR) {
+    const int n_ms = min(MAXNM, (tl.nrows - r0 + 15) >> 4);
+    if (r0 > 0) __syncthreads();  // the previous pass's epilogue has read the ring
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+    for (int m = 0; m < MAXNM; ++m)
 #pragma unroll
         for (int cs = 0; cs < NCS; ++cs) acc[m][cs] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // The K loop is instantiated for 1, 2, 4 and 8 row blocks of 16 (the tile's count
@@ -492,14 +508,14 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
         constexpr int LPC = NA + 3;               // loads per wavefront and chunk
         constexpr int SA = 4 * NA * 1024;         // A bytes per stage (32 NA rows)
         constexpr int STAGE = SA + B_BYTES + SB_BYTES;
-        constexpr int NS = RING / STAGE;          // stages: 5, 4 or 3
-        static_assert(NS >= 3 && NS * STAGE <= RING && LPC * (NS - 2) < 64, "ring");
+        constexpr int NS = RINGW / STAGE;         // stages: 5, 4 or 3 (three-per-CU instance: 4, 4, 3)
+        static_assert(NS >= 3 && NS * STAGE <= RINGW && LPC * (NS - 2) < 64, "ring");
         const uint32_t arow0 = arow_lds[0];       // row 0 is always inside the tile
         uint32_t a_off[NA];
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
             const int row = 8 * (NA * wave + i) + (lane >> 3);
-            const uint32_t off = arow_lds[row];
+            const uint32_t off = arow_lds[r0 + row];
             a_off[i] = (off == 0xFFFFFFFFu ? arow0 : off) + 16 * ((lane & 7) ^ (row & 7));
         }
         auto issue = [&](int c) __attribute__((always_inline)) {
@@ -561,8 +577,8 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
     };
     if (n_ms <= 1) kloop(std::integral_constant<int, 1>{});
     else if (n_ms <= 2) kloop(std::integral_constant<int, 2>{});
-    else if (n_ms <= 4) kloop(std::integral_constant<int, 4>{});
-    else kloop(std::integral_constant<int, 8>{});
+    else if (MAXNM == 4 || n_ms <= 4) kloop(std::integral_constant<int, 4>{});
+    else kloop(std::integral_constant<int, MAXNM>{});
 
     // ---- epilogue: the ring's memory is free once every wavefront is past its last chunk
     __syncthreads();
@@ -577,50 +593,53 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
         for (int hs = 0; hs < 2; ++hs) {
             const int c = 64 * hs + 16 * wave + lc;
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
+            for (int m = 0; m < MAXNM; ++m) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * m + 4 * lg + r;
+                    const int row = 16 * m + 4 * lg + r;  // within the pass
                     const float gv = acc[m][hs][r], uv = acc[m][2 + hs][r];
                     // silu(g) = g / (1 + e^-g), e^-g = 2^(-g log2 e)
                     const float sg = gv * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-gv * 1.44269504088896341f));
                     const __bf16 hb = (__bf16)(sg * uv);
-                    hl[row * HS + c] = row < tl.nrows ? __builtin_bit_cast(uint16_t, hb) : (uint16_t)0;
+                    hl[row * HS + c] = r0 + row < tl.nrows ? __builtin_bit_cast(uint16_t, hb) : (uint16_t)0;
                 }
             }
         }
         __syncthreads();
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
+        for (int it = 0; it < MAXNM; ++it) {
             const int row = 16 * it + (tid >> 4), pc = tid & 15;
-            if (row < tl.nrows && col0 + 8 * pc < I)
-                *reinterpret_cast<uint4*>(a.hbuf + (size_t)(tl.row0 + row) * I + col0 + 8 * pc) =
+            if (r0 + row < tl.nrows && col0 + 8 * pc < I)
+                *reinterpret_cast<uint4*>(a.hbuf + (size_t)(tl.row0 + r0 + row) * I + col0 + 8 * pc) =
                     *reinterpret_cast<const uint4*>(hl + row * HS + 8 * pc);
         }
     } else {
-        // y[order[row]][col0 + n], n < 256, staged 64 rows at a time as an fp32 tile in
+        // y[order[row]][col0 + n], n < 256, staged SR rows at a time as an fp32 tile in
         // LDS and stored with 16-byte row pieces. The stores are non-temporal: y is read
         // once, by the combine, and would otherwise evict weight lines and activation
         // tiles that later workgroups read again.
         constexpr int YS = NBR + 4;  // tile row stride (floats)
+        constexpr int SR = WPC == 3 ? 32 : 64;  // rows per staging step (the ring holds SR * YS floats)
+        static_assert(SR * YS * 4 <= RINGW && PR * (128 + 8) * 2 <= RINGW, "epilogue staging fits the ring");
         float* yl = reinterpret_cast<float*>(ring);
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            if (64 * half < tl.nrows) {
-                if (half) __syncthreads();
+        for (int q = 0; q < PR / SR; ++q) {
+            if (r0 + SR * q < tl.nrows) {
+                if (q) __syncthreads();
 #pragma unroll
-                for (int mm = 0; mm < 4; ++mm) {
+                for (int mm = 0; mm < SR / 16; ++mm) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int rl = 16 * mm + 4 * lg + r;
 #pragma unroll
-                        for (int cs = 0; cs < NCS; ++cs) yl[rl * YS + cs * 64 + 16 * wave + lc] = acc[4 * half + mm][cs][r];
+                        for (int cs = 0; cs < NCS; ++cs)
+                            yl[rl * YS + cs * 64 + 16 * wave + lc] = acc[(SR / 16) * q + mm][cs][r];
                     }
                 }
                 __syncthreads();
 #pragma unroll 4
-                for (int it = 0; it < 16; ++it) {
-                    const int rl = 4 * it + (tid >> 6), row = 64 * half + rl, pc = tid & 63;
+                for (int it = 0; it < SR / 4; ++it) {
+                    const int rl = 4 * it + (tid >> 6), row = r0 + SR * q + rl, pc = tid & 63;
                     if (row < tl.nrows && col0 + 4 * pc < H)
                         __builtin_nontemporal_store(*reinterpret_cast<const f32x4_t*>(yl + rl * YS + 4 * pc),
                                                     reinterpret_cast<f32x4_t*>(a.y + (size_t)pick_lds[row] * H + col0 + 4 * pc));
@@ -628,6 +647,7 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GemmArgs a) {
             }
         }
     }
+    }  // passes
 }
 
 static_assert(BM == 128, "tile rows");
@@ -706,9 +726,12 @@ extern "C" moe_status moe_experts_prefill(const moe_shape* shape, const void* ex
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
         return fail(MOE_ERR_HIP, "cannot query the device's LDS size");
-    if (max_lds < RING + 2048)
+    // up to 1024 tokens: the three-workgroups-per-CU instance (passes of 64 rows)
+    const bool three = T <= 1024;
+    const int ring = three ? RING3 : RING;
+    if (max_lds < ring + 2048)
         return fail(MOE_ERR_UNSUPPORTED, "the grouped GEMM needs %d bytes of LDS per workgroup, the device has %d",
-                    RING + 2048, max_lds);
+                    ring + 2048, max_lds);
     hipStream_t hs = (hipStream_t)stream;
     char* w = (char*)ws;
     int32_t* ntiles = (int32_t*)(w + W.D.ntiles);
@@ -730,10 +753,11 @@ extern "C" moe_status moe_experts_prefill(const moe_shape* shape, const void* ex
     ga.y = y;
     ga.T = T;
     ga.km = kmul(sh);
-    hipLaunchKernelGGL((expert_gemm_kernel<true>), dim3(xcd_grid(W.D.max_tiles, (I + NBR / 2 - 1) / (NBR / 2))), dim3(256),
-                       RING, hs, ga);
+    const dim3 gu_grid(xcd_grid(W.D.max_tiles, (I + NBR / 2 - 1) / (NBR / 2))), dn_grid(xcd_grid(W.D.max_tiles, (H + NBR - 1) / NBR));
+    if (three) hipLaunchKernelGGL((expert_gemm_kernel<true, 3>), gu_grid, dim3(256), ring, hs, ga);
+    else hipLaunchKernelGGL((expert_gemm_kernel<true, 2>), gu_grid, dim3(256), ring, hs, ga);
     if ((st = check_launch("expert_gemm_kernel<gate/up>")) != MOE_OK) return st;
-    hipLaunchKernelGGL((expert_gemm_kernel<false>), dim3(xcd_grid(W.D.max_tiles, (H + NBR - 1) / NBR)), dim3(256), RING, hs,
-                       ga);
+    if (three) hipLaunchKernelGGL((expert_gemm_kernel<false, 3>), dn_grid, dim3(256), ring, hs, ga);
+    else hipLaunchKernelGGL((expert_gemm_kernel<false, 2>), dn_grid, dim3(256), ring, hs, ga);
     return check_launch("expert_gemm_kernel<down>");
 }
