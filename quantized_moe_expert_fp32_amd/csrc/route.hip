@@ -53,12 +53,12 @@ __global__ __launch_bounds__(256) void router_kernel(const uint8_t* __restrict__
 }
 
 // ---------------------------------------------------------------- logits, GEMM form (8-bit router, T > 16)
+constexpr int RG_TOK = 32;  // tokens per workgroup above 1024 tokens
 // logits[t][r] = sum_g ( s[r][g] * sum_{k in g} x[t][k] q[r][k] + b[r][g] * sum_{k in g} x[t][k] ) (+ bias[r])
-// on the matrix cores. A workgroup takes 32 tokens x 16 NB router rows; wavefront w
-// takes the groups [w G/4, (w+1) G/4) of K and its partial sums are added in
-// wavefront order at the end, so the result does not depend on timing. NB = 1
-// gives enough workgroups for a few hundred tokens; NB = 4 reads the activations
-// a quarter as often for thousands. Per group, 16-token block and 16 rows:
+// on the matrix cores. A workgroup takes 16 MB tokens x 16 NB router rows; wavefront
+// w takes the groups [w G/4, (w+1) G/4) of K and its partial sums are added in
+// wavefront order at the end, so the result does not depend on timing. Per group,
+// 16-token block and 16 rows:
 //   * the int8 codes are exact bf16 B operands; lane (row lc, quarter lg) holds
 //     codes 16 lg .. 16 lg + 15 of its row, the first 8 for one
 //     v_mfma_f32_16x16x32_bf16 and the last 8 for the next, and the A operand
@@ -67,18 +67,28 @@ __global__ __launch_bounds__(256) void router_kernel(const uint8_t* __restrict__
 //   * the scale multiplies the group's partial in fp32 (one FMA per output);
 //   * the bias term b * sum x comes from two more MFMAs whose B operand is b in
 //     every slot (exact products, fp32 sums), accumulated in place.
+// Every (16-token block, 16-row block) pair goes through the same operations
+// whatever MB and NB are, so a logit does not depend on the tile shape.
 // Operands come straight from global memory into a ring of PD groups per
 // wavefront: no LDS and no barrier in the loop.
-constexpr int RG_TOK = 32;
-
-// One workgroup's tile: tokens t0 .. t0 + 31 x router rows rb0 .. rb0 + 16 NB - 1.
-// part is the workgroup's LDS for the wavefronts' partial sums.
-template <int NB>
+//
+// Tile shapes. A workgroup's first loads wait on address translation: each 4 KiB
+// page it touches for the first time (an activation row is one page, two router
+// rows share one) costs it about 0.1 us, and that, not bytes or instructions,
+// sets most of its time (a timing-only build whose loads hit three pages per
+// workgroup ran 3.9 instead of 7.8 us per workgroup at 512 tokens; one page per
+// load instruction but the same pages was as slow as the real one). Up to 1024
+// tokens a workgroup takes 16 tokens x 32 rows (about 36 pages with its logit
+// stores, against 48 for 32 x 16), and the rows past the last whole 32, the
+// shared gate's, join the last row block's workgroup, so 512 tokens take exactly
+// 256 workgroups. Thousands of tokens: 32 tokens x 64 rows, which reads the
+// activations a quarter as often.
+template <int MB, int NB>
 __device__ __forceinline__ void router_gemm_tile(const uint8_t* __restrict__ router,
                                                  const float* __restrict__ logit_bias,
                                                  const uint16_t* __restrict__ x, int T, int H, int R, int E,
                                                  float* __restrict__ logits, int t0, int rb0,
-                                                 float (*part)[2][NB][4][64]) {
+                                                 float (*part)[MB][NB][4][64]) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lg = lane >> 4, lc = lane & 15;
     const int rb = rb0 + lc;
@@ -91,19 +101,19 @@ __device__ __forceinline__ void router_gemm_tile(const uint8_t* __restrict__ rou
         qrow[n] = router + (size_t)rr * H + 16 * lg;
         sbrow[n] = reinterpret_cast<const uint32_t*>(router + (size_t)R * H) + (size_t)rr * G;
     }
-    const uint16_t* xrow[2];
+    const uint16_t* xrow[MB];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
+    for (int m = 0; m < MB; ++m) {
         const int t = t0 + 16 * m + lc;
         xrow[m] = x + (size_t)(t < T ? t : 0) * H + 16 * lg;
     }
-    f32x4_t acc[2][NB];
+    f32x4_t acc[MB][NB];
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < MB; ++m)
 #pragma unroll
         for (int n = 0; n < NB; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    constexpr int PD = NB == 1 ? 4 : 3;  // groups in flight per wavefront
-    uint4 wq[PD][NB], xa[PD][2][2];
+    constexpr int PD = MB * NB <= 2 ? 4 : 3;  // groups in flight per wavefront
+    uint4 wq[PD][NB], xa[PD][MB][2];
     uint32_t ws[PD][NB];
     auto load = [&](int u, int g) {
 #pragma unroll
@@ -112,7 +122,7 @@ __device__ __forceinline__ void router_gemm_tile(const uint8_t* __restrict__ rou
             ws[u][n] = sbrow[n][g];
         }
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
+        for (int m = 0; m < MB; ++m) {
             xa[u][m][0] = *reinterpret_cast<const uint4*>(xrow[m] + 64 * g);
             xa[u][m][1] = *reinterpret_cast<const uint4*>(xrow[m] + 64 * g + 8);
         }
@@ -135,15 +145,15 @@ __device__ __forceinline__ void router_gemm_tile(const uint8_t* __restrict__ rou
                 const uint32_t bp = (ws[u][n] >> 16) | (ws[u][n] & 0xFFFF0000u);
                 bb[n] = make_uint4(bp, bp, bp, bp);
             }
-            uint4 a[2][2];
+            uint4 a[MB][2];
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
+            for (int m = 0; m < MB; ++m) {
                 a[m][0] = xa[u][m][0];
                 a[m][1] = xa[u][m][1];
             }
             if (gg + PD < gb) load(u, gg + PD);
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
+            for (int m = 0; m < MB; ++m) {
 #pragma unroll
                 for (int n = 0; n < NB; ++n) {
                     f32x4_t p = mfma16x16x32(a[m][0], b0[n], f32x4_t{0.f, 0.f, 0.f, 0.f});
@@ -157,22 +167,22 @@ __device__ __forceinline__ void router_gemm_tile(const uint8_t* __restrict__ rou
         }
     }
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < MB; ++m)
 #pragma unroll
         for (int n = 0; n < NB; ++n)
 #pragma unroll
             for (int i = 0; i < 4; ++i) part[wave][m][n][i][lane] = acc[m][n][i];
     __syncthreads();
-    // the reduction and stores are spread over the four wavefronts (one n-block
-    // each for NB = 4, wavefront 0 for NB = 1)
+    // the reduction and stores are spread over the four wavefronts: row block n goes
+    // to wavefront n % 4
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
-        if (NB == 1 ? wave != 0 : wave != n) continue;
+        if (wave != (n & 3)) continue;
         const int r = rb + 16 * n;
         if (r >= R) continue;
         const float bias = (r < E && logit_bias) ? logit_bias[r] : 0.f;
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
+        for (int m = 0; m < MB; ++m) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = t0 + 16 * m + 4 * lg + i;
@@ -184,19 +194,31 @@ __device__ __forceinline__ void router_gemm_tile(const uint8_t* __restrict__ rou
     }
 }
 
-template <int NB>
-__global__ __launch_bounds__(256) void router_gemm_kernel(const uint8_t* __restrict__ router,
-                                                          const float* __restrict__ logit_bias,
-                                                          const uint16_t* __restrict__ x, int T, int H, int R, int E,
-                                                          float* __restrict__ logits) {
-    __shared__ float part[4][2][NB][4][64];
-    router_gemm_tile<NB>(router, logit_bias, x, T, H, R, E, logits, blockIdx.x * RG_TOK, blockIdx.y * 16 * NB, part);
+// Up to 1024 tokens: 16 tokens x 32 rows per workgroup; blockIdx.y = n32 - 1 also
+// takes the rows past the last whole 32 (one or two more blocks of 16), and with
+// fewer than 32 rows one workgroup per token block takes them all.
+__global__ __launch_bounds__(256) void router_gemm_narrow_kernel(const uint8_t* __restrict__ router,
+                                                                const float* __restrict__ logit_bias,
+                                                                const uint16_t* __restrict__ x, int T, int H, int R,
+                                                                int E, float* __restrict__ logits) {
+    __shared__ float part[4][1][4][4][64];
+    const int n32 = R / 32, extra = (R % 32 + 15) / 16;  // extra: blocks of 16 past the last whole 32
+    const int t0 = blockIdx.x * 16, y = blockIdx.y, rb0 = 32 * y;
+    auto run = [&](auto nb_tag) __attribute__((always_inline)) {
+        constexpr int NB = decltype(nb_tag)::value;
+        router_gemm_tile<1, NB>(router, logit_bias, x, T, H, R, E, logits, t0, rb0,
+                                reinterpret_cast<float (*)[1][NB][4][64]>(&part[0][0][0][0][0]));
+    };
+    const int nb = y + 1 < n32 ? 2 : (n32 > 0 ? 2 : 0) + extra;  // 1 .. 4
+    if (nb == 1) run(std::integral_constant<int, 1>{});
+    else if (nb == 2) run(std::integral_constant<int, 2>{});
+    else if (nb == 3) run(std::integral_constant<int, 3>{});
+    else run(std::integral_constant<int, 4>{});
 }
 
-// Thousands of tokens: row blocks of 64 (NB = 4, the activations read a quarter as
-// often) up to the last whole one, then blocks of 16 for the rows left over (the
-// shared gate's at 256 experts), so that a block of 64 mostly empty rows does not
-// take a round of workgroups of its own. A row's arithmetic is the same in both.
+// Thousands of tokens: row blocks of 64 (NB = 4) up to the last whole one, then
+// blocks of 16 for the rows left over (the shared gate's at 256 experts), so that a
+// block of 64 mostly empty rows does not take a round of workgroups of its own.
 __global__ __launch_bounds__(256) void router_gemm_wide_kernel(const uint8_t* __restrict__ router,
                                                               const float* __restrict__ logit_bias,
                                                               const uint16_t* __restrict__ x, int T, int H, int R,
@@ -204,11 +226,11 @@ __global__ __launch_bounds__(256) void router_gemm_wide_kernel(const uint8_t* __
     __shared__ float part[4][2][4][4][64];
     const int n64 = R / 64;
     if ((int)blockIdx.y < n64)
-        router_gemm_tile<4>(router, logit_bias, x, T, H, R, E, logits, blockIdx.x * RG_TOK, blockIdx.y * 64, part);
+        router_gemm_tile<2, 4>(router, logit_bias, x, T, H, R, E, logits, blockIdx.x * RG_TOK, blockIdx.y * 64, part);
     else
-        router_gemm_tile<1>(router, logit_bias, x, T, H, R, E, logits, blockIdx.x * RG_TOK,
-                            64 * n64 + 16 * ((int)blockIdx.y - n64),
-                            reinterpret_cast<float (*)[2][1][4][64]>(&part[0][0][0][0][0]));
+        router_gemm_tile<2, 1>(router, logit_bias, x, T, H, R, E, logits, blockIdx.x * RG_TOK,
+                               64 * n64 + 16 * ((int)blockIdx.y - n64),
+                               reinterpret_cast<float (*)[2][1][4][64]>(&part[0][0][0][0][0]));
 }
 
 static moe_status launch_topk(const moe_shape& sh, const float* logits, int T, int32_t* ids, uint16_t* w,
@@ -285,7 +307,7 @@ extern "C" moe_status moe_route(const moe_shape* shape, const void* router_packe
     if (T > 16 && shape->router_fmt == MOE_ROUTER_AFFINE8) {
         const int R = router_rows(*shape);
         if (T <= 1024)
-            hipLaunchKernelGGL(router_gemm_kernel<1>, dim3((T + RG_TOK - 1) / RG_TOK, (R + 15) / 16), dim3(256), 0, hs,
+            hipLaunchKernelGGL(router_gemm_narrow_kernel, dim3((T + 15) / 16, R >= 32 ? R / 32 : 1), dim3(256), 0, hs,
                                (const uint8_t*)router_packed, logit_bias, x, T, shape->hidden, R, shape->n_experts,
                                logits);
         else

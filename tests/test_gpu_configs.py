@@ -4,7 +4,8 @@ shape, through the C ABI:
     fp32 router, one and sixteen keys per lane, no shared expert, a logit bias,
     and more h words than one staging pass of a one-token launch holds - each
     bit-identical to the staged calls and within the oracle bar;
-  * the fp32 router above 16 tokens;
+  * the fp32 router above 16 tokens, and 8-bit routers of other sizes on the
+    matrix cores (both tile shapes byte-equal);
   * the prefill path's dispatch, read back from its workspace, against the
     oracle's histogram and stable expert-sorted order;
   * the prefill path's determinism and chunk invariance: the same tokens in one
@@ -173,6 +174,40 @@ def test_prefill_route_chunks_of_128(gpu):
         part = run_path(gpu, dl, c.x[t0:t0 + 128], "prefill")
         for key in ("logits", "ids", "w", "wsh", "y", "out"):
             assert np.array_equal(part[key], full[key][t0:t0 + 128]), (key, t0)
+
+
+# 8-bit routers of other sizes on the matrix cores (T > 16); R = experts + shared gate.
+# name: (hidden, n_experts, has_shared)
+MC_ROUTER_CASES = {
+    "rows17": (256, 16, 1),   # fewer rows than one 32-row block
+    "rows49": (512, 48, 1),   # two 16-row blocks past the last whole 32
+    "rows64": (512, 64, 0),   # whole 32-row blocks only
+    "rows65": (512, 64, 1),   # one 16-row block past the last whole 32, as at 257
+}
+
+
+@pytest.mark.parametrize("name", list(MC_ROUTER_CASES))
+def test_matrix_core_router_shapes(gpu, name):
+    """The router GEMM's tile shapes (16 tokens x 32 rows up to 1024 tokens, with
+    the rows past the last whole 32 in the last row block's workgroup; 32 x 64 and
+    32 x 16 above) on routers of other sizes: a token's logits are byte-equal
+    between the two, within the matrix-core bar of the oracle's, and the picks and
+    weights follow from them."""
+    H, E, hs = MC_ROUTER_CASES[name]
+    shape = synth.Shape(hidden=H, inter=64, n_experts=E, top_k=2, has_shared=hs, router_fmt=A8)
+    host = synth.make_layer(shape, seed=40 + list(MC_ROUTER_CASES).index(name), layer=0)
+    L = _L()
+    dl = L.DeviceLayer(L.make_shape(shape), host)
+    x = synth.random_x(900, 1100, H)
+    big = run_path(gpu, dl, x, "prefill")         # above 1024 tokens
+    small = run_path(gpu, dl, x[:300], "prefill")  # up to 1024 tokens
+    for key in ("logits", "ids", "w", "wsh"):
+        if small[key] is not None:
+            assert np.array_equal(small[key], big[key][:300]), key
+    ref = O.router_logits(x[:300], O.router_matrix(host), host.logit_bias, E)
+    check_logits(small["logits"], ref, fp64_path=False)
+    check_picks(small["ids"], ref, 2, E)
+    staged_route_check(gpu, small, E, 2, has_shared=bool(hs))
 
 
 @pytest.mark.parametrize("name,T,bits", [("decode", 1, 4), ("decode", 3, 4), ("decode", 16, 4), ("tiny", 1, 4),
