@@ -438,6 +438,7 @@ def main():
         rec = copy_calibration(args.copy_calibration)
         out = os.environ.get("CALIBRATION_OUT")
         if out:
+            os.makedirs(os.path.dirname(os.path.abspath(out)), exist_ok=True)
             json.dump(rec, open(out, "w"))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
