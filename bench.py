@@ -365,12 +365,14 @@ def run_workload(wl, K, W, inp, no_cpu, cpu_seconds):
     durs_ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
     stage_us = float(np.mean(durs_ms) * 1e3)
     log("%s: dominant stage %.2f us average over %d event-timed launches" % (wl, stage_us, n_ev))
-    if kind == "decode":
-        # every step of the timed region is one decode_layer_kernel launch: the
-        # events around the region give its average per-launch duration without
-        # the per-launch event overhead
-        stage_us = region_us / K
-        log("decode: decode_layer_kernel %.2f us per launch over the timed region" % stage_us)
+    if kind == "decode" or kind.startswith("stack"):
+        # every step of the timed region is one decode_layer_kernel launch (the
+        # stack: one per layer): the events around the graph-replayed region give
+        # its average per-launch duration without the per-launch event overhead
+        # of the eager launches above (2-3 us per launch)
+        n_launch = K * (len(layers) if kind.startswith("stack") else 1)
+        stage_us = region_us / n_launch
+        log("%s: decode_layer_kernel %.2f us per launch over the timed region" % (wl, stage_us))
 
     # algorithmic work of one launch of the dominant stage: the weights of every
     # distinct expert it touches (read once) plus the activations; the fp32 slot
