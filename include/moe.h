@@ -263,8 +263,8 @@ size_t moe_prefill_workspace_bytes(const moe_shape* shape, int32_t T);
  *   counts [M] int32 (counts[E] = T for the shared expert), offsets [M+1] int32
  *   (exclusive prefix sums), ntiles one int32, tiles [max_tiles] of four int32
  *   {expert, row0, nrows, 0} (the first ntiles are the work list: a tile covers
- *   rows row0 .. row0+nrows-1 of the expert-sorted order, at most 128, all of one
- *   expert), order [T*S] int32 (pick indices t*S + s grouped by ascending expert,
+ *   rows row0 .. row0+nrows-1 of the expert-sorted order, at most tile_rows, all of
+ *   one expert), order [T*S] int32 (pick indices t*S + s grouped by ascending expert,
  *   and within an expert by ascending pick index).
  * For checks of the dispatch and for callers that reuse the expert-sorted order
  * ([P1-phase] Phase 9b: lookup-table dispatch). MOE_ERR_INVALID_ARG for a bad
@@ -272,7 +272,7 @@ size_t moe_prefill_workspace_bytes(const moe_shape* shape, int32_t T);
 typedef struct moe_prefill_dispatch_view {
     size_t counts, offsets, ntiles, tiles, order;
     int32_t max_tiles;
-    int32_t pad;
+    int32_t tile_rows;  /* the tiles' height: 64 for T <= 1024, else 128 */
 } moe_prefill_dispatch_view;
 moe_status moe_prefill_dispatch_layout(const moe_shape* shape, int32_t T, moe_prefill_dispatch_view* view_host);
 

@@ -22,6 +22,12 @@
 namespace moe {
 
 constexpr int BM = 128;  // rows per tile
+// Up to 1024 tokens the tiles are 64 rows (the three-workgroups-per-CU GEMM takes 64
+// rows per pass): a 128-row tile there ran as one item of two passes, and the shared
+// expert's 128-row items, started first, ran 85 us of the 87 us gate/up launch at
+// 512 tokens while the rest of the chip was done at about 60 us.
+constexpr int BM3 = 64;
+static int prefill_tile_rows(int T) { return T <= 1024 ? BM3 : BM; }
 
 constexpr int SLICE = 1024;  // picks per slice (one workgroup of the dispatch each)
 
@@ -53,7 +59,7 @@ struct PrefillWs {
 static PrefillWs prefill_ws_layout(const moe_shape& s, int T) {
     PrefillWs w;
     size_t o = 0;
-    w.D = dispatch_ws_layout(s, T, BM, o);
+    w.D = dispatch_ws_layout(s, T, prefill_tile_rows(T), o);
     w.h = o;
     o = align_up(o + 2 * (size_t)T * n_slots(s) * s.inter, 256);
     w.total = o;
@@ -381,10 +387,12 @@ constexpr int B_BYTES = NBR * KC / 2, SB_BYTES = NBR * 4;
 constexpr int RING = 3 * (BM * KC * 2 + B_BYTES + SB_BYTES);  // 75 KiB: three stages of a full tile
 // Up to 1024 tokens most tiles hold a few row blocks and a workgroup's time goes to
 // streaming its weight rows, bound by the loads in flight: the kernel's second
-// instance takes at most 64 rows per pass (a tile of more rows is done in two
-// passes over the weights), with at most 168 VGPRs and a 51 KiB ring, so three
-// workgroups share a CU (at 512 tokens 141.6 -> 132.4 us for both GEMMs). A row's
-// arithmetic is the same in both instances, and so are its results, bit for bit.
+// instance takes at most 64 rows per pass (the dispatch cuts tiles of 64 rows there,
+// so it makes one pass; a tile of more rows would take two passes over the
+// weights), with at most 168 VGPRs and a 51 KiB ring, so three workgroups share a
+// CU (at 512 tokens 141.6 -> 132.4 us for both GEMMs on 128-row tiles). A row's
+// arithmetic is the same in both instances and in every tile, and so are its
+// results, bit for bit.
 constexpr int RING3 = 3 * (64 * KC * 2 + B_BYTES + SB_BYTES);  // 51 KiB
 
 struct GemmArgs {
@@ -508,7 +516,7 @@ __global__ __launch_bounds__(256, WPC) void expert_gemm_kernel(GemmArgs a) {
         constexpr int LPC = NA + 3;               // loads per wavefront and chunk
         constexpr int SA = 4 * NA * 1024;         // A bytes per stage (32 NA rows)
         constexpr int STAGE = SA + B_BYTES + SB_BYTES;
-        constexpr int NS = RINGW / STAGE;         // stages: 5, 4 or 3 (three-per-CU instance: 4, 4, 3)
+        constexpr int NS = RINGW / STAGE;         // stages: 5, 4 or 3 (three-per-CU instance: 3)
         static_assert(NS >= 3 && NS * STAGE <= RINGW && LPC * (NS - 2) < 64, "ring");
         const uint32_t arow0 = arow_lds[0];       // row 0 is always inside the tile
         uint32_t a_off[NA];
@@ -659,7 +667,8 @@ moe_status launch_prefill_dispatch(const moe_shape& sh, int T, const int32_t* id
     hipLaunchKernelGGL(prefill_count_kernel, dim3((unsigned)D.n_slices), dim3(DT), 0, hs, ids, P, sh.n_experts, slices);
     moe_status st = check_launch("prefill_count_kernel");
     if (st != MOE_OK) return st;
-    auto scatter = D.bm == 256 ? prefill_scatter_kernel<256> : prefill_scatter_kernel<128>;
+    auto scatter = D.bm == 256 ? prefill_scatter_kernel<256>
+                   : D.bm == 64 ? prefill_scatter_kernel<64> : prefill_scatter_kernel<128>;
     hipLaunchKernelGGL(scatter, dim3((unsigned)D.n_slices + 1), dim3(DT), 0, hs, ids, T, sh.top_k, sh.n_experts,
                        sh.has_shared, sh.hidden, D.n_slices, slices, (int32_t*)(w + D.counts),
                        (int32_t*)(w + D.offsets), (int32_t*)(w + D.ntiles), (Tile*)(w + D.tiles),
@@ -688,7 +697,7 @@ extern "C" moe_status moe_prefill_dispatch_layout(const moe_shape* shape, int32_
     v->tiles = D.tiles;
     v->order = D.order;
     v->max_tiles = D.max_tiles;
-    v->pad = 0;
+    v->tile_rows = D.bm;
     return MOE_OK;
 }
 
@@ -726,8 +735,8 @@ extern "C" moe_status moe_experts_prefill(const moe_shape* shape, const void* ex
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
         return fail(MOE_ERR_HIP, "cannot query the device's LDS size");
-    // up to 1024 tokens: the three-workgroups-per-CU instance (passes of 64 rows)
-    const bool three = T <= 1024;
+    // up to 1024 tokens: the three-workgroups-per-CU instance on 64-row tiles
+    const bool three = W.D.bm == BM3;
     const int ring = three ? RING3 : RING;
     if (max_lds < ring + 2048)
         return fail(MOE_ERR_UNSUPPORTED, "the grouped GEMM needs %d bytes of LDS per workgroup, the device has %d",

@@ -52,7 +52,7 @@ class Shape(ctypes.Structure):
 class PrefillDispatchView(ctypes.Structure):
     _fields_ = [("counts", ctypes.c_size_t), ("offsets", ctypes.c_size_t), ("ntiles", ctypes.c_size_t),
                 ("tiles", ctypes.c_size_t), ("order", ctypes.c_size_t), ("max_tiles", ctypes.c_int32),
-                ("pad", ctypes.c_int32)]
+                ("tile_rows", ctypes.c_int32)]
 
 
 class ExpertCanon(ctypes.Structure):

@@ -93,7 +93,7 @@ def _dispatch_from_ws(gpu, shape, T, ws):
     ntiles = int(i32(v.ntiles, 1)[0])
     assert 0 < ntiles <= v.max_tiles
     return (i32(v.counts, M), i32(v.offsets, M + 1), i32(v.tiles, 4 * v.max_tiles).reshape(-1, 4)[:ntiles],
-            i32(v.order, T * S))
+            i32(v.order, T * S), v.tile_rows)
 
 
 def _expected_tiles(counts, offsets, BM=128):
@@ -112,19 +112,21 @@ def _expected_tiles(counts, offsets, BM=128):
 def test_prefill_dispatch_readback(gpu, name):
     """Counts, offsets and the expert-sorted order that moe_experts_prefill leaves in
     its workspace equal the oracle's bit for bit (ascending pick order within an
-    expert); the tile list covers every row once, in the documented order."""
+    expert); the tile list covers every row once, in the documented order, with
+    tiles of 64 rows up to 1024 tokens and 128 above."""
     c = case(name)
     dl = dev_layer(gpu, c)
     L = _L()
     buf = L.alloc_buffers(dl.shape, c.T, "prefill")
     L.layer_step(dl, L.to_device(c.x), buf, "prefill")
     torch.cuda.synchronize()
-    counts, offsets, tiles, order = _dispatch_from_ws(gpu, dl.shape, c.T, buf.ws)
+    counts, offsets, tiles, order, tile_rows = _dispatch_from_ws(gpu, dl.shape, c.T, buf.ws)
+    assert tile_rows == (64 if c.T <= 1024 else 128)
     rc, ro, rord = O.dispatch(buf.ids.cpu().numpy(), 256, True)
     assert np.array_equal(counts, rc)
     assert np.array_equal(offsets, ro)
     assert np.array_equal(order, rord)
-    assert np.array_equal(tiles, _expected_tiles(rc, ro))
+    assert np.array_equal(tiles, _expected_tiles(rc, ro, tile_rows))
 
 
 def _prefill_chunks(gpu, dl, x, ids, w, wsh, C):
