@@ -227,7 +227,9 @@ class Inputs:
         self.shape = L.make_shape(base.shape)
         key = "stack_layers" if wl.startswith("stack") else "%s_%d%s_layers" % (wl, self.bits, "_fp8" * self.fp8)
         if key not in cache:
-            cache[key] = [L.DeviceLayer(self.shape, h, fp8=self.fp8) for h in self.hosts]
+            # the prefill layout of the experts only where moe_experts_prefill reads it
+            pf = not (wl.startswith("stack") or wl.startswith("decode") or self.fp8)
+            cache[key] = [L.DeviceLayer(self.shape, h, fp8=self.fp8, prefill=pf) for h in self.hosts]
         self.layers = cache[key]
         self.x = L.to_device(self.x_host)
         # SHA-256 (first 16 hex digits) of the first layer's arrays and the activations
@@ -359,7 +361,7 @@ def run_workload(wl, K, W, inp, no_cpu, cpu_seconds):
                 if inp.fp8:
                     moe.moe_experts_prefill_fp8(shape, dl.experts_fp8, xin, T, buf.ids, buf.ws, buf.y)
                 else:
-                    moe.moe_experts_prefill(shape, dl.experts, xin, T, buf.ids, buf.ws, buf.y)
+                    moe.moe_experts_prefill(shape, dl.experts_prefill, xin, T, buf.ids, buf.ws, buf.y)
                 ends[j].record(stream)
     torch.cuda.synchronize()
     durs_ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])

@@ -255,8 +255,23 @@ moe_status moe_dispatch(const moe_shape* shape, const int32_t* ids, int32_t T, i
  * dequant and dispatch table). Same y as moe_experts_decode up to fp32
  * summation order. Runs moe_dispatch internally into `ws`, then the gate/up GEMM
  * with the SwiGLU epilogue, then the down GEMM scattering rows back to y[t][s].
- * ws: device scratch of moe_prefill_workspace_bytes(shape, T) bytes. */
+ * experts_prefill: the prefill layout that moe_pack_experts_prefill wrote (not the
+ * packed buffer itself). ws: device scratch of moe_prefill_workspace_bytes(shape, T)
+ * bytes. */
 size_t moe_prefill_workspace_bytes(const moe_shape* shape, int32_t T);
+
+/* The prefill layout of packed experts: the same bytes as moe_pack_experts' buffer
+ * (moe_experts_packed_bytes), permuted within each set of 64 consecutive four-row
+ * blocks of a matrix (the last set of a matrix may hold fewer, n): the 128-byte
+ * line of block j and group g of a set moves from set + 128 (j G + g) to
+ * set + 128 (g n + j), G groups per row, and its 16-byte (scale, bias) unit from
+ * sb set + 16 (j G + g) to sb set + 16 (g n + j). One grouped-GEMM workgroup reads
+ * one set, one group at a time, so each chunk is one contiguous run of memory.
+ * Reads experts_packed (device, moe_pack_experts' layout) and writes
+ * experts_prefill (device, bytes >= moe_experts_packed_bytes; the two must not
+ * overlap). Async on `stream`. MOE_ERR_WORKSPACE if bytes is too small. */
+moe_status moe_pack_experts_prefill(const moe_shape* shape, const void* experts_packed, void* experts_prefill,
+                                    size_t bytes, void* stream);
 
 /* Where moe_experts_prefill leaves its dispatch inside ws for a call with this
  * shape and T (byte offsets from ws; written to *view_host, host memory):
@@ -276,7 +291,7 @@ typedef struct moe_prefill_dispatch_view {
 } moe_prefill_dispatch_view;
 moe_status moe_prefill_dispatch_layout(const moe_shape* shape, int32_t T, moe_prefill_dispatch_view* view_host);
 
-moe_status moe_experts_prefill(const moe_shape* shape, const void* experts_packed,
+moe_status moe_experts_prefill(const moe_shape* shape, const void* experts_prefill,
                                const uint16_t* x, int32_t T, const int32_t* ids, void* ws,
                                size_t ws_bytes, float* y, void* stream);
 

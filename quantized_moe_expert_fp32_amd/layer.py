@@ -41,9 +41,11 @@ def make_shape(s) -> moe.Shape:
 
 class DeviceLayer:
     """One layer's packed expert buffer, packed router and optional logit bias on the GPU;
-    with fp8=True also the experts upcast for the FP8 prompt route (experts_fp8)."""
+    with prefill=True (the default) also the prefill layout of the experts that
+    moe_experts_prefill reads (experts_prefill, as many bytes again), with fp8=True
+    the experts upcast for the FP8 prompt route (experts_fp8)."""
 
-    def __init__(self, shape: moe.Shape, host_layer, device="cuda", fp8: bool = False):
+    def __init__(self, shape: moe.Shape, host_layer, device="cuda", fp8: bool = False, prefill: bool = True):
         self.shape = shape
         self.device = device
         nb = moe.moe_experts_packed_bytes(shape)
@@ -53,6 +55,10 @@ class DeviceLayer:
         src = {n: to_device(getattr(host_layer, n), device) for n in
                ("q_gate", "s_gate", "b_gate", "q_up", "s_up", "b_up", "q_down", "s_down", "b_down")}
         moe.moe_pack_experts(shape, src, self.experts)
+        self.experts_prefill = None
+        if prefill:
+            self.experts_prefill = torch.empty(nb, dtype=torch.uint8, device=device)
+            moe.moe_pack_experts_prefill(shape, self.experts, self.experts_prefill)
         self.experts_fp8 = None
         if fp8:
             self.experts_fp8 = torch.empty(moe.moe_experts_fp8_bytes(shape), dtype=torch.uint8, device=device)
@@ -124,7 +130,9 @@ def layer_step(layer: DeviceLayer, x: torch.Tensor, buf: StepBuffers, path: Opti
             raise ValueError("the FP8 route needs a DeviceLayer built with fp8=True")
         moe.moe_experts_prefill_fp8(sh, layer.experts_fp8, x, T, buf.ids, buf.ws, buf.y, stream)
     else:
-        moe.moe_experts_prefill(sh, layer.experts, x, T, buf.ids, buf.ws, buf.y, stream)
+        if layer.experts_prefill is None:
+            raise ValueError("the prefill path needs a DeviceLayer built with prefill=True")
+        moe.moe_experts_prefill(sh, layer.experts_prefill, x, T, buf.ids, buf.ws, buf.y, stream)
     moe.moe_combine(sh, buf.y, buf.w, buf.wsh, T, residual, dst, stream)
     return dst
 

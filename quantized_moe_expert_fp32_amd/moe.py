@@ -101,6 +101,8 @@ _lib.moe_prefill_workspace_bytes.restype = _SZ
 _lib.moe_prefill_workspace_bytes.argtypes = [_S, _I32]
 _lib.moe_prefill_dispatch_layout.restype = _I32
 _lib.moe_prefill_dispatch_layout.argtypes = [_S, _I32, ctypes.POINTER(PrefillDispatchView)]
+_lib.moe_pack_experts_prefill.restype = _I32
+_lib.moe_pack_experts_prefill.argtypes = [_S, _P, _P, _SZ, _P]
 _lib.moe_experts_prefill.restype = _I32
 _lib.moe_experts_prefill.argtypes = [_S, _P, _P, _I32, _P, _P, _SZ, _P, _P]
 _lib.moe_experts_fp8_bytes.restype = _SZ
@@ -121,7 +123,7 @@ EXPORTS = ("moe_abi_version", "moe_status_str", "moe_last_error", "moe_shape_che
            "moe_route", "moe_route_from_logits", "moe_decode_workspace_bytes", "moe_experts_decode",
            "moe_experts_decode_noalloc", "moe_decode_layer", "moe_decode_block",
            "moe_decode_layer_check", "moe_dispatch", "moe_prefill_workspace_bytes", "moe_prefill_dispatch_layout",
-           "moe_experts_prefill", "moe_experts_fp8_bytes", "moe_pack_experts_fp8",
+           "moe_pack_experts_prefill", "moe_experts_prefill", "moe_experts_fp8_bytes", "moe_pack_experts_fp8",
            "moe_prefill_fp8_workspace_bytes", "moe_experts_prefill_fp8", "moe_combine", "moe_rmsnorm")
 
 
@@ -247,8 +249,13 @@ def moe_prefill_dispatch_layout(shape, T) -> PrefillDispatchView:
     return v
 
 
-def moe_experts_prefill(shape, experts_packed, x, T, ids, ws, y, stream=None):
-    _check(_lib.moe_experts_prefill(ctypes.byref(shape), _ptr(experts_packed), _ptr(x), T, _ptr(ids), _ptr(ws),
+def moe_pack_experts_prefill(shape, experts_packed, experts_prefill, stream=None):
+    _check(_lib.moe_pack_experts_prefill(ctypes.byref(shape), _ptr(experts_packed), _ptr(experts_prefill),
+                                         _nbytes(experts_prefill), _stream(stream)), "moe_pack_experts_prefill")
+
+
+def moe_experts_prefill(shape, experts_prefill, x, T, ids, ws, y, stream=None):
+    _check(_lib.moe_experts_prefill(ctypes.byref(shape), _ptr(experts_prefill), _ptr(x), T, _ptr(ids), _ptr(ws),
                                     _nbytes(ws), _ptr(y), _stream(stream)), "moe_experts_prefill")
 
 

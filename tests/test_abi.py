@@ -120,6 +120,14 @@ def test_host_argument_checks_launch_nothing(moe):
     canon = moe.ExpertCanon(*([P] * 9))
     st = moe.raw_call("moe_pack_experts_fp8", byref(sh), byref(canon), v(P), 1024, None)
     assert st == moe.ERR_WORKSPACE
+    # prefill layout of the experts: buffer size, overlap, NULL source
+    nb = moe.moe_experts_packed_bytes(sh)
+    st = moe.raw_call("moe_pack_experts_prefill", byref(sh), v(P), v(P + nb + (1 << 20)), nb - 16, None)
+    assert st == moe.ERR_WORKSPACE
+    st = moe.raw_call("moe_pack_experts_prefill", byref(sh), v(P), v(P + nb - 256), nb, None)
+    assert st == moe.ERR_INVALID_ARG
+    st = moe.raw_call("moe_pack_experts_prefill", byref(sh), None, v(P), nb, None)
+    assert st == moe.ERR_INVALID_ARG
     # T = 0
     st = moe.raw_call("moe_route", byref(sh), v(P), None, v(P), 0, v(P), v(P), v(P), v(P), None)
     assert st == moe.ERR_INVALID_ARG

@@ -139,7 +139,7 @@ def _prefill_chunks(gpu, dl, x, ids, w, wsh, C):
     ws = torch.zeros(gpu.moe_prefill_workspace_bytes(dl.shape, C), dtype=torch.uint8, device="cuda")
     for t0 in range(0, T, C):
         n = min(C, T - t0)
-        gpu.moe_experts_prefill(dl.shape, dl.experts, x[t0:t0 + n], n, ids[t0:t0 + n], ws, y[t0:t0 + n])
+        gpu.moe_experts_prefill(dl.shape, dl.experts_prefill, x[t0:t0 + n], n, ids[t0:t0 + n], ws, y[t0:t0 + n])
         gpu.moe_combine(dl.shape, y[t0:t0 + n], w[t0:t0 + n], wsh[t0:t0 + n], n, None, out[t0:t0 + n])
     torch.cuda.synchronize()
     return y.cpu().numpy(), L.bits_to_numpy(out)
@@ -176,6 +176,43 @@ def test_prefill_route_chunks_of_128(gpu):
         part = run_path(gpu, dl, c.x[t0:t0 + 128], "prefill")
         for key in ("logits", "ids", "w", "wsh", "y", "out"):
             assert np.array_equal(part[key], full[key][t0:t0 + 128]), (key, t0)
+
+
+def _prefill_layout_expected(packed, shape):
+    """The prefill layout from the packed buffer, by its documented permutation: in
+    every set of 64 consecutive four-row blocks (n blocks in a shorter last set), the
+    128-byte line (block j, group g) moves from set + 128 (j G + g) to
+    set + 128 (g n + j), and the 16-byte (scale, bias) unit likewise."""
+    km = shape.bits // 4
+    H, I, M = shape.hidden, shape.inter, shape.n_experts + shape.has_shared
+    Hw, Iw = H * km, I * km
+    regions = [(0, I // 2, Hw // 64, 128), (I * Hw, H // 4, Iw // 64, 128)]
+    sb0 = I * Hw + H * Iw // 2
+    regions += [(sb0, I // 2, Hw // 64, 16), (sb0 + (I // 2) * (Hw // 64) * 16, H // 4, Iw // 64, 16)]
+    stride = len(packed) // M
+    out = packed.copy()
+    for m in range(M):
+        for base, nblk, G, ub in regions:
+            for s0 in range(0, nblk, 64):
+                n = min(64, nblk - s0)
+                a = m * stride + base + s0 * G * ub
+                src = packed[a:a + n * G * ub].reshape(n, G, ub)
+                out[a:a + n * G * ub] = src.transpose(1, 0, 2).reshape(-1)
+    return out
+
+
+@pytest.mark.parametrize("name,bits", [("tiny", 4), ("decode", 4), ("tiny", 8)])
+def test_prefill_layout_permutation(gpu, name, bits):
+    """moe_pack_experts_prefill writes the documented permutation of the packed
+    buffer, byte for byte (sets shorter than 64 blocks at 64 intermediate rows,
+    several sets at 2048 hidden, 8-bit rows twice as long)."""
+    c = synth.make_case(name, bits=bits)
+    L = _L()
+    dl = L.DeviceLayer(L.make_shape(c.shape), c.layers[0])
+    torch.cuda.synchronize()
+    packed = dl.experts.cpu().numpy()
+    got = dl.experts_prefill.cpu().numpy()
+    assert np.array_equal(got, _prefill_layout_expected(packed, c.shape))
 
 
 # 8-bit routers of other sizes on the matrix cores (T > 16); R = experts + shared gate.

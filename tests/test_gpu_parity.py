@@ -364,7 +364,7 @@ def test_invalid_ids_give_zero_rows(gpu):
             dl_mod = _moe()
             dl_mod.moe_experts_decode(dl.shape, dl.experts, x, T, ids, buf.ws, buf.y)
         else:
-            _moe().moe_experts_prefill(dl.shape, dl.experts, x, T, ids, buf.ws, buf.y)
+            _moe().moe_experts_prefill(dl.shape, dl.experts_prefill, x, T, ids, buf.ws, buf.y)
         torch.cuda.synchronize()
         y = buf.y.cpu().numpy()
         assert (y[0, 1] == 0).all() and (y[1, 1] == 0).all()

@@ -61,7 +61,7 @@ def test_stack40_graph_replay(gpu, T):
     c = synth.make_case("stack", T=T, n_layers=N_LAYERS)
     record_stats(what="stack_setup", T=T, layers=len(c.layers))
     sh = L.make_shape(c.shape)
-    layers = [L.DeviceLayer(sh, hl) for hl in c.layers]
+    layers = [L.DeviceLayer(sh, hl, prefill=False) for hl in c.layers]
     x0 = L.to_device(c.x)
     x = x0.clone()
     xn = torch.empty_like(x)
