@@ -204,12 +204,14 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const int32_t* __restric
 }
 
 // ---------------------------------------------------------------- set-up: dispatch
-// Two launches before the GEMMs. The picks p = t*k + s are cut into slices of SLICE
-// consecutive picks, one workgroup each.
-//   count: each slice's per-expert counts (an LDS histogram) go to slices[b][e].
-//   scatter: every slice's workgroup reads the whole count matrix (n_slices x E) and
-//     derives the experts' totals, their offsets in the expert-sorted order and its
-//     own base within each expert (the sum over the earlier slices), then places its
+// One or two launches before the GEMMs. The picks p = t*k + s are cut into slices of
+// SLICE consecutive picks, one workgroup each.
+//   count (more than SELF_COUNT picks): each slice's per-expert counts (an LDS
+//     histogram) go to slices[b][e].
+//   scatter: every slice's workgroup reads the whole count matrix (n_slices x E), or
+//     with at most SELF_COUNT picks counts them all itself, and derives the experts'
+//     totals, their offsets in the expert-sorted order and its own base within each
+//     expert (the picks of the earlier slices), then places its
 //     picks in ascending pick order: wavefront w takes the slice's picks SLICE/4 w ..
 //     SLICE/4 (w+1) - 1, 64 at a time, and ranks each among the lower lanes holding
 //     the same id (one ballot per id bit) plus the wavefront's earlier picks of that
@@ -219,10 +221,13 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const int32_t* __restric
 //     tile list: every full tile first (expert order), then the partial tiles with
 //     the most row blocks first (expert order within a size), so the items that
 //     start last are the cheapest.
-// Everything the two launches write is a function of the ids alone. Picks with an
+// Everything the dispatch writes is a function of the ids alone. Picks with an
 // id outside [0, E) are skipped and their y rows zeroed. A slice's picks are loaded
 // before any is counted or placed.
 constexpr int DT = 256, DPT = SLICE / DT;  // threads per workgroup, picks per thread
+// Up to this many picks (1024 tokens at top-8) the scatter workgroups count the picks
+// themselves and the count launch is skipped (one launch and its gap fewer).
+constexpr int SELF_COUNT = 8192;
 
 __global__ __launch_bounds__(DT) void prefill_count_kernel(const int32_t* __restrict__ ids, long long P, int E,
                                                            int32_t* __restrict__ slices) {
@@ -278,17 +283,42 @@ __global__ __launch_bounds__(DT) void prefill_scatter_kernel(
         const long long p = p0 + DPT * 64 * wave + 64 * j + lane;
         ev[j] = p < P ? ids[p] : -1;
     }
-    for (int e = tid; e < E; e += DT) {
-        int tot = 0, base = 0;
+    if (slices) {
+        for (int e = tid; e < E; e += DT) {
+            int tot = 0, base = 0;
 #pragma unroll 8
-        for (int s2 = 0; s2 < n_slices; ++s2) {
-            const int c = slices[(size_t)s2 * E + e];
-            base += s2 < b ? c : 0;
-            tot += c;
+            for (int s2 = 0; s2 < n_slices; ++s2) {
+                const int c = slices[(size_t)s2 * E + e];
+                base += s2 < b ? c : 0;
+                tot += c;
+            }
+            cnt[e] = tot;
+            cur[e] = base;
         }
-        cnt[e] = tot;
-        cur[e] = base;
+    } else {
+        // at most SELF_COUNT picks: the workgroup counts them all itself (the totals,
+        // and the picks before its slice for its base), all loads issued first
+        for (int e = tid; e < E; e += DT) {
+            cnt[e] = 0;
+            cur[e] = 0;
+        }
+        int ea[SELF_COUNT / DT];
+#pragma unroll
+        for (int j = 0; j < SELF_COUNT / DT; ++j) {
+            const long long p = (long long)j * DT + tid;
+            ea[j] = p < P ? ids[p] : -1;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < SELF_COUNT / DT; ++j) {
+            const long long p = (long long)j * DT + tid;
+            if (ea[j] >= 0 && ea[j] < E) {
+                atomicAdd(&cnt[ea[j]], 1);
+                if (p < p0) atomicAdd(&cur[ea[j]], 1);
+            }
+        }
     }
+    __syncthreads();
     if (has_shared && tid == 0) cnt[E] = T;
     __syncthreads();
     if (tid < 64) {  // exclusive scans of the rows and the full tiles over the experts
@@ -489,6 +519,10 @@ __global__ __launch_bounds__(256, WPC) void expert_gemm_kernel(GemmArgs a) {
     const int lg = lane >> 4, lc = lane & 15;
     const int col0 = GATEUP ? cb * HALF : cb * NBR;
 
+    // down: the tile row's pick is needed only by the epilogue, so its load stays in
+    // flight through the K loop and the value reaches pick_lds after it (the set-up
+    // barrier then waits for no global load: 1 us less per down item)
+    int pick_v = 0;
     if (tid < BM) {
         uint32_t off = 0xFFFFFFFFu;
         int src = 0;
@@ -498,7 +532,7 @@ __global__ __launch_bounds__(256, WPC) void expert_gemm_kernel(GemmArgs a) {
             off = (uint32_t)src * (uint32_t)(2 * K);
         }
         arow_lds[tid] = off;
-        if constexpr (!GATEUP) pick_lds[tid] = tid < tl.nrows ? a.order[tl.row0 + tid] : 0;
+        if constexpr (!GATEUP) pick_v = tid < tl.nrows ? a.order[tl.row0 + tid] : 0;
     }
     __syncthreads();
     const uint8_t* asrc = reinterpret_cast<const uint8_t*>(GATEUP ? a.x : a.hbuf);
@@ -644,6 +678,9 @@ __global__ __launch_bounds__(256, WPC) void expert_gemm_kernel(GemmArgs a) {
     else kloop(std::integral_constant<int, MAXNM>{});
 
     // ---- epilogue: the ring's memory is free once every wavefront is past its last chunk
+    if constexpr (!GATEUP) {
+        if (tid < BM) pick_lds[tid] = pick_v;
+    }
     __syncthreads();
     if constexpr (GATEUP) {
         // h = bf16(silu(gate) * up) for this block's 128 intermediate columns i =
@@ -718,10 +755,14 @@ static_assert(BM == 128, "tile rows");
 moe_status launch_prefill_dispatch(const moe_shape& sh, int T, const int32_t* ids, const DispatchWs& D, char* w,
                                    float* y, hipStream_t hs) {
     const long long P = (long long)T * sh.top_k;
-    int32_t* slices = (int32_t*)(w + D.slices);
-    hipLaunchKernelGGL(prefill_count_kernel, dim3((unsigned)D.n_slices), dim3(DT), 0, hs, ids, P, sh.n_experts, slices);
-    moe_status st = check_launch("prefill_count_kernel");
-    if (st != MOE_OK) return st;
+    int32_t* slices = nullptr;
+    if (P > SELF_COUNT) {
+        slices = (int32_t*)(w + D.slices);
+        hipLaunchKernelGGL(prefill_count_kernel, dim3((unsigned)D.n_slices), dim3(DT), 0, hs, ids, P, sh.n_experts,
+                           slices);
+        moe_status st = check_launch("prefill_count_kernel");
+        if (st != MOE_OK) return st;
+    }
     auto scatter = D.bm == 256 ? prefill_scatter_kernel<256>
                    : D.bm == 64 ? prefill_scatter_kernel<64> : prefill_scatter_kernel<128>;
     hipLaunchKernelGGL(scatter, dim3((unsigned)D.n_slices + 1), dim3(DT), 0, hs, ids, T, sh.top_k, sh.n_experts,
