@@ -9,6 +9,10 @@ typedef float f4_t __attribute__((ext_vector_type(4)));
 // One thread per four consecutive outputs of a token; slots are summed in slot
 // order (0..k-1, then the shared slot) with fp32 fused multiply-adds. y is read
 // once, with non-temporal loads, so it does not displace other data in the caches.
+// Every load of a thread (its k + 1 weights and slot values) is issued before the
+// first sum: a loop that loaded and summed one slot at a time waited for nine round
+// trips in turn (512 tokens: 9 us). KM >= k bounds the unrolled slots.
+template <int KM>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const uint16_t* __restrict__ w,
                                                       const uint16_t* __restrict__ wsh, int T, int H, int k, int S,
                                                       const uint16_t* residual, uint16_t* out) {
@@ -17,26 +21,41 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     if (idx >= (size_t)T * n4) return;
     const size_t t = idx / n4, c = (idx % n4) * 4;
     const float* yt = y + t * S * H + c;
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    for (int s = 0; s < k; ++s) {
-        const float ws = bf16_to_f32(w[t * k + s]);
-        const f4_t v = __builtin_nontemporal_load(reinterpret_cast<const f4_t*>(yt + (size_t)s * H));
-        a0 = fmaf(ws, v.x, a0);
-        a1 = fmaf(ws, v.y, a1);
-        a2 = fmaf(ws, v.z, a2);
-        a3 = fmaf(ws, v.w, a3);
+    uint32_t wr[KM + 1];  // raw bf16 weights, one per register: converted only when summed, so no load waits for another
+    f4_t v[KM + 1];
+#pragma unroll
+    for (int s = 0; s < KM; ++s) {
+        if (s < k) {
+            wr[s] = w[t * k + s];
+            v[s] = __builtin_nontemporal_load(reinterpret_cast<const f4_t*>(yt + (size_t)s * H));
+        }
     }
     if (wsh) {
-        const float ws = bf16_to_f32(wsh[t]);
-        const f4_t v = __builtin_nontemporal_load(reinterpret_cast<const f4_t*>(yt + (size_t)k * H));
-        a0 = fmaf(ws, v.x, a0);
-        a1 = fmaf(ws, v.y, a1);
-        a2 = fmaf(ws, v.z, a2);
-        a3 = fmaf(ws, v.w, a3);
+        wr[KM] = wsh[t];
+        v[KM] = __builtin_nontemporal_load(reinterpret_cast<const f4_t*>(yt + (size_t)k * H));
+    }
+    uint2 r = make_uint2(0u, 0u);
+    if (residual) r = *reinterpret_cast<const uint2*>(residual + t * H + c);
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+    for (int s = 0; s < KM; ++s) {
+        if (s < k) {
+            const float ws = bf16_to_f32(wr[s]);
+            a0 = fmaf(ws, v[s].x, a0);
+            a1 = fmaf(ws, v[s].y, a1);
+            a2 = fmaf(ws, v[s].z, a2);
+            a3 = fmaf(ws, v[s].w, a3);
+        }
+    }
+    if (wsh) {
+        const float ws = bf16_to_f32(wr[KM]);
+        a0 = fmaf(ws, v[KM].x, a0);
+        a1 = fmaf(ws, v[KM].y, a1);
+        a2 = fmaf(ws, v[KM].z, a2);
+        a3 = fmaf(ws, v[KM].w, a3);
     }
     uint32_t b0 = f32_to_bf16(a0), b1 = f32_to_bf16(a1), b2 = f32_to_bf16(a2), b3 = f32_to_bf16(a3);
     if (residual) {
-        const uint2 r = *reinterpret_cast<const uint2*>(residual + t * H + c);
         b0 = f32_to_bf16(bf16_to_f32(r.x & 0xFFFFu) + bf16_to_f32(b0));
         b1 = f32_to_bf16(bf16_to_f32(r.x >> 16) + bf16_to_f32(b1));
         b2 = f32_to_bf16(bf16_to_f32(r.y & 0xFFFFu) + bf16_to_f32(b2));
@@ -83,8 +102,9 @@ extern "C" moe_status moe_combine(const moe_shape* shape, const float* y, const 
         return fail(MOE_ERR_INVALID_ARG, "w_shared must be given iff the layer has a shared expert");
     const int H = shape->hidden;
     const size_t n = (size_t)T * (H / 4);
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream, y, w,
-                       w_shared, T, H, shape->top_k, n_slots(*shape), residual, out);
+    auto kern = shape->top_k <= 8 ? combine_kernel<8> : combine_kernel<16>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream, y, w, w_shared, T,
+                       H, shape->top_k, n_slots(*shape), residual, out);
     return check_launch("combine_kernel");
 }
 
