@@ -77,10 +77,12 @@ PREFILL_KERNELS = ["prefill_count_kernel", "prefill_scatter_kernel", "expert_gem
                    "expert_gemm_kernel<false,"]
 FP8_KERNELS = ["prefill_count_kernel", "prefill_scatter_kernel", "quant_rows_fp8_kernel", "fp8_gemm_kernel<true>",
                "fp8_gemm_kernel<false>"]
+# up to 8192 picks (1024 tokens at top-8) the dispatch has no count launch
 TRAFFIC_KERNELS = {"decode": ["decode_layer_kernel"], "stack16": ["decode_layer_kernel"],
                    "stack1": ["decode_layer_kernel"],
-                   "prefill512": PREFILL_KERNELS, "prefill4096": PREFILL_KERNELS,
-                   "prefill512_fp8": FP8_KERNELS, "prefill4096_fp8": FP8_KERNELS}
+                   "prefill512": PREFILL_KERNELS[1:], "prefill4096": PREFILL_KERNELS,
+                   "prefill512_fp8": FP8_KERNELS[1:], "prefill4096_fp8": FP8_KERNELS,
+                   "decode_8bit": ["decode_layer_kernel"], "prefill512_8bit": PREFILL_KERNELS[1:]}
 # sources the measured kernels are built from: a stored traffic record holds for
 # the sources it was taken on
 DECODE_SOURCES = ["decode.hip", "route_device.h", "moe_internal.h", "abi.hip"]
@@ -88,7 +90,8 @@ PREFILL_SOURCES = ["prefill.hip", "prefill_internal.h", "mfma_common.h", "moe_in
 FP8_SOURCES = ["prefill_fp8.hip", "prefill.hip", "prefill_internal.h", "mfma_common.h", "moe_internal.h"]
 TRAFFIC_SOURCES = {"decode": DECODE_SOURCES, "stack16": DECODE_SOURCES, "stack1": DECODE_SOURCES,
                    "prefill512": PREFILL_SOURCES, "prefill4096": PREFILL_SOURCES,
-                   "prefill512_fp8": FP8_SOURCES, "prefill4096_fp8": FP8_SOURCES}
+                   "prefill512_fp8": FP8_SOURCES, "prefill4096_fp8": FP8_SOURCES,
+                   "decode_8bit": DECODE_SOURCES, "prefill512_8bit": PREFILL_SOURCES}
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
@@ -409,9 +412,9 @@ def run_workload(wl, K, W, inp, no_cpu, cpu_seconds):
     roof["kernel"] = ("decode_layer_kernel (RMSNorm, router, selection, experts, combine and residual in one launch)"
                       if kind.startswith("stack") else
                       "decode_layer_kernel (router, selection, experts, combine in one launch)" if path == "fused"
-                      else "experts stage (moe_experts_prefill_fp8): " + " + ".join(FP8_KERNELS) if inp.fp8
+                      else "experts stage (moe_experts_prefill_fp8): " + " + ".join(TRAFFIC_KERNELS[wl]) if inp.fp8
                       else "experts stage (moe_experts_prefill): " + " + ".join(k.rstrip(",") + ", …>" if k.endswith(",") else k
-                                                                     for k in PREFILL_KERNELS))
+                                                                     for k in TRAFFIC_KERNELS[wl]))
     roof["avg_us"] = stage_us
     roof["alg_bytes_per_launch"] = int(alg_bytes)
     roof["alg_flops_per_launch"] = int(flops)
