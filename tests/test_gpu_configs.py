@@ -108,13 +108,16 @@ def _expected_tiles(counts, offsets, BM=128):
     return np.array(full + [t for _, _, t in sorted(part)], dtype=np.int32).reshape(-1, 4)
 
 
-@pytest.mark.parametrize("name", ["prefill512", "prefill4096"])
-def test_prefill_dispatch_readback(gpu, name):
+@pytest.mark.parametrize("name,T", [("prefill512", None), ("prefill4096", None), ("prefill512", 1024),
+                                    ("prefill512", 1025)])
+def test_prefill_dispatch_readback(gpu, name, T):
     """Counts, offsets and the expert-sorted order that moe_experts_prefill leaves in
     its workspace equal the oracle's bit for bit (ascending pick order within an
     expert); the tile list covers every row once, in the documented order, with
-    tiles of 64 rows up to 1024 tokens and 128 above."""
-    c = case(name)
+    tiles of 64 rows up to 1024 tokens and 128 above. 1024 tokens are 8192 picks,
+    the most that the scatter counts without a count launch; 1025 take the count
+    launch, 128-row tiles and the wide router GEMM."""
+    c = case(name, T)
     dl = dev_layer(gpu, c)
     L = _L()
     buf = L.alloc_buffers(dl.shape, c.T, "prefill")
