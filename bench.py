@@ -95,20 +95,46 @@ TRAFFIC_SOURCES = {"decode": DECODE_SOURCES, "stack16": DECODE_SOURCES, "stack1"
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
+def code_only(text):
+    """C/C++ source without its comments, whitespace runs collapsed: what the traffic
+    of a kernel can depend on (string and character literals are kept as written)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_hash(wl):
-    """Hash of the sources the workload's measured kernels are built from (and the headers)."""
+    """Hash of the code (comments left out) of the sources the workload's measured
+    kernels are built from, and of the headers."""
     import hashlib
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_moe_expert_fp32_amd", "csrc")
     for n in sorted(TRAFFIC_SOURCES[wl]):
         h.update(n.encode())
-        h.update(open(os.path.join(csrc, n), "rb").read())
+        h.update(code_only(open(os.path.join(csrc, n)).read()).encode())
     inc = os.path.join(ROOT, "include")
     for n in sorted(os.listdir(inc)):
         if n.endswith(".h"):
             h.update(n.encode())
-            h.update(open(os.path.join(inc, n), "rb").read())
+            h.update(code_only(open(os.path.join(inc, n)).read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -322,12 +322,12 @@ moe_status moe_pack_experts_fp8(const moe_shape* shape, const moe_expert_canon* 
 
 /* moe_experts_prefill's contract (y [T][S][H] fp32, per-slot expert outputs; rows
  * of picks with an id outside [0, E) zeroed) through the FP8 route: dispatch with
- * tiles of up to 256 rows, x quantised per row, the FP8 gate/up GEMM writing h, h
+ * tiles of up to 128 rows, x quantised per row, the FP8 gate/up GEMM writing h, h
  * quantised per row, the FP8 down GEMM. Each output depends on its own token's row
  * only, in a fixed order (any T, any call). ws: device scratch of
  * moe_prefill_fp8_workspace_bytes(shape, T) bytes (its layout is internal).
  * MOE_ERR_UNSUPPORTED when
- * T * Hp or T * S * Ip reaches 2^32 or the device has under 148 KiB of LDS per
+ * T * Hp or T * S * Ip reaches 2^32 or the device has under 76 KiB of LDS per
  * workgroup. */
 size_t moe_prefill_fp8_workspace_bytes(const moe_shape* shape, int32_t T);
 moe_status moe_experts_prefill_fp8(const moe_shape* shape, const void* experts_fp8,

@@ -31,3 +31,18 @@ def test_more_than_one_gpu_is_refused():
                        timeout=120)
     assert r.returncode != 0
     assert "--gpus 1" in r.stderr
+
+
+def test_traffic_hash_ignores_comments_only():
+    a = 'int a = 1; // note\n/* block\n note */ const char* s = "x // kept /* kept */";\nchar q = \'"\';  int b;'
+    b = 'int a = 1;\n const char* s = "x // kept /* kept */"; /* another note */\nchar q = \'"\'; // more\n int b;'
+    assert bench.code_only(a) == bench.code_only(b)
+    assert "// kept /* kept */" in bench.code_only(a)
+    assert bench.code_only(a) != bench.code_only(a.replace("int b;", "int c;"))
+    assert bench.code_only('s = "esc\\"aped // x"; t') == 's = "esc\\"aped // x"; t'
+
+
+def test_every_workload_has_a_source_hash():
+    hashes = {wl: bench.source_hash(wl) for wl in bench.WORKLOADS}
+    assert all(len(h) == 16 for h in hashes.values())
+    assert hashes["decode"] == hashes["stack1"] and hashes["decode"] != hashes["prefill512"]
